@@ -1,0 +1,345 @@
+/*
+ * spec_verify_ref.c -- plain fp64 CPU oracle of the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it. It shares no code, header or table with the HIP library.
+ *
+ * What it computes (per batch row b, positions 0-based: drafts i = 0..k-1,
+ * bonus row i = k):
+ *
+ *  Sampling mode ("Speculative Decoding: The Physics of Stolen Time", section 2,
+ *  the modified rejection sampling rule and its losslessness proof; the
+ *  speculative-decoding design note, "The acceptance math"):
+ *    p_i = softmax(target_logits[b,i,:] / T) for i <= k,
+ *    q_i = softmax(draft_logits[b,i,:]  / T) for i <  k,
+ *    for i = 0..k-1: r_i = p_i(x_i) / q_i(x_i), accept iff u[b,i,0] < r_i;
+ *    at the first rejection a: sample from norm(max(0, p_a - q_a));
+ *    if all k accepted (a = k): sample a bonus token from p_k.
+ *    Sampling from a weight vector w uses the inverse CDF in vocabulary order:
+ *    the smallest j with C_j > u*Z, C_j = sum_{x<=j} w_x, Z = C_{V-1},
+ *    with u = u[b,a,1].
+ *
+ *  Greedy mode ("The Inference Wall" part 7, "How speculative decoding works":
+ *  accept while the guess equals the target's own token, at the first mismatch
+ *  take the target's token; all matched gives k+1 tokens):
+ *    g_i = argmax target_logits[b,i,:] (lowest index on ties),
+ *    a = first i < k with x_i != g_i, else k; the emitted token is g_a.
+ *
+ *  Gap ("Speculative Pre-Positioning", Eq. 11): top-1 minus top-2 of the raw
+ *  target logits of every row i <= k (0 on ties at the top; +inf when fewer
+ *  than two finite entries exist).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - temperature divides target and draft logits alike; the gap and greedy
+ *    use raw logits; T is the float argument widened exactly to double;
+ *  - uniform channel 0 is the acceptance test, channel 1 the inverse-CDF draw;
+ *  - accept iff u < r (strict), so r >= 1 always accepts and p(x) = 0 always
+ *    rejects; q(x) = 0 gives r = +inf if p(x) > 0 and r = 0 otherwise;
+ *  - if a rejection leaves Z = 0 (only possible through rounding), the token
+ *    is drawn from p_a instead and the row is flagged;
+ *  - a row pair with NaN or +inf anywhere, a row with no finite entry, or a
+ *    draft token outside [0, V) makes batch row b invalid: accepted_len = -1
+ *    and every out_token = -1. (Greedy mode reads no draft logits.)
+ *
+ * Every sum is a Neumaier-compensated sum in vocabulary order.
+ *
+ * Margins (for the flagged near-tie policy): margin_acc[b] is the smallest
+ * |u - r_i| over the decisions actually taken, margin_cdf[b] the distance of u
+ * to the nearest edge of the chosen token's normalized CDF interval
+ * min(u - C_{j-1}/Z, C_j/Z - u). Both are +inf where no such decision exists.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { REF_F32 = 0, REF_BF16 = 1 };
+enum { REF_SAMPLE = 0, REF_GREEDY = 1 };
+
+/* Exact widening of one stored logit to double. */
+static double ref_load(const void* base, int dtype, size_t idx)
+{
+    if (dtype == REF_F32) {
+        return (double)((const float*)base)[idx];
+    }
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Neumaier compensated accumulator. */
+typedef struct { double s, c; } ref_sum_t;
+
+static void ref_sum_add(ref_sum_t* a, double x)
+{
+    double t = a->s + x;
+    if (fabs(a->s) >= fabs(x)) a->c += (a->s - t) + x;
+    else                       a->c += (x - t) + a->s;
+    a->s = t;
+}
+
+static double ref_sum_value(const ref_sum_t* a) { return a->s + a->c; }
+
+/* Row check: 1 if the row has no NaN, no +inf and at least one finite entry. */
+static int ref_row_ok(const void* base, int dtype, size_t off, int V)
+{
+    int finite = 0;
+    for (int x = 0; x < V; ++x) {
+        double v = ref_load(base, dtype, off + (size_t)x);
+        if (isnan(v) || (isinf(v) && v > 0)) return 0;
+        if (isfinite(v)) finite = 1;
+    }
+    return finite;
+}
+
+/* p[x] = exp(z_x - max z) / sum, z_x = logit_x / T. Requires ref_row_ok. */
+static void ref_softmax(const void* base, int dtype, size_t off, int V, double T, double* p)
+{
+    double m = -INFINITY;
+    for (int x = 0; x < V; ++x) {
+        double z = ref_load(base, dtype, off + (size_t)x) / T;
+        if (z > m) m = z;
+    }
+    ref_sum_t S = {0.0, 0.0};
+    for (int x = 0; x < V; ++x) {
+        double z = ref_load(base, dtype, off + (size_t)x) / T;
+        double e = isinf(z) ? 0.0 : exp(z - m);
+        p[x] = e;
+        ref_sum_add(&S, e);
+    }
+    double s = ref_sum_value(&S);
+    for (int x = 0; x < V; ++x) p[x] /= s;
+}
+
+/* Top-1 minus top-2 of the raw row (multiset, so ties give 0). */
+static double ref_gap(const void* base, int dtype, size_t off, int V)
+{
+    double t1 = -INFINITY, t2 = -INFINITY;
+    int finite = 0;
+    for (int x = 0; x < V; ++x) {
+        double v = ref_load(base, dtype, off + (size_t)x);
+        if (isnan(v)) continue;
+        if (isfinite(v)) ++finite;
+        if (v > t1) { t2 = t1; t1 = v; }
+        else if (v > t2) { t2 = v; }
+    }
+    if (finite < 2) return INFINITY;
+    return t1 - t2;
+}
+
+/* Lowest index of the maximum of the raw row (NaN entries never win). */
+static int ref_argmax(const void* base, int dtype, size_t off, int V)
+{
+    int best = 0;
+    double bv = -INFINITY;
+    int seen = 0;
+    for (int x = 0; x < V; ++x) {
+        double v = ref_load(base, dtype, off + (size_t)x);
+        if (isnan(v)) continue;
+        if (!seen || v > bv) { bv = v; best = x; seen = 1; }
+    }
+    return best;
+}
+
+/*
+ * Inverse-CDF draw from the non-negative weights w[0..V-1] with uniform u:
+ * the smallest j with C_j > u*Z. Returns -1 when Z <= 0. *margin receives the
+ * normalized distance of u to the chosen interval's nearest edge.
+ */
+static int ref_inverse_cdf(const double* w, int V, double u, double* margin)
+{
+    ref_sum_t acc = {0.0, 0.0};
+    for (int x = 0; x < V; ++x) ref_sum_add(&acc, w[x]);
+    double Z = ref_sum_value(&acc);
+    if (!(Z > 0.0)) return -1;
+    double t = u * Z;
+    ref_sum_t C = {0.0, 0.0};
+    double prev = 0.0;
+    for (int j = 0; j < V; ++j) {
+        ref_sum_add(&C, w[j]);
+        double cj = ref_sum_value(&C);
+        if (j == V - 1) cj = Z;               /* C_{V-1} is Z by definition */
+        if (cj > t) {
+            double lo = u - prev / Z, hi = cj / Z - u;
+            *margin = lo < hi ? lo : hi;
+            return j;
+        }
+        prev = cj;
+    }
+    *margin = 0.0;                           /* unreachable for u < 1 */
+    return V - 1;
+}
+
+static void ref_fill_invalid(int k, int32_t* acc_len, int32_t* out)
+{
+    *acc_len = -1;
+    for (int i = 0; i <= k; ++i) out[i] = -1;
+}
+
+/*
+ * One batch row. work must hold 3*V doubles.
+ * Returns a bit set: 1 = Z fell back to p_a (flag).
+ */
+static int ref_one_row(const void* target, const void* draft, const int32_t* tokens,
+                       const float* uniforms, double T, int mode, int k, int V, int dtype,
+                       size_t b, int32_t* acc_len, int32_t* out, double* gap,
+                       double* p_tok, double* q_tok, double* m_acc, double* m_cdf,
+                       double* work)
+{
+    const size_t rowsT = (size_t)(k + 1), rowsD = (size_t)k;
+    int flags = 0;
+    *m_acc = INFINITY;
+    *m_cdf = INFINITY;
+    for (int i = 0; i <= k; ++i) {
+        gap[i] = ref_gap(target, dtype, (b * rowsT + (size_t)i) * (size_t)V, V);
+    }
+    for (int i = 0; i < k; ++i) { p_tok[i] = NAN; q_tok[i] = NAN; }
+
+    /* validity of the whole batch row */
+    int ok = 1;
+    for (int i = 0; i < k && ok; ++i) {
+        int32_t x = tokens[b * rowsD + (size_t)i];
+        if (x < 0 || x >= V) ok = 0;
+    }
+    for (int i = 0; i <= k && ok; ++i) {
+        ok = ref_row_ok(target, dtype, (b * rowsT + (size_t)i) * (size_t)V, V);
+    }
+    if (mode == REF_SAMPLE) {
+        for (int i = 0; i < k && ok; ++i) {
+            ok = ref_row_ok(draft, dtype, (b * rowsD + (size_t)i) * (size_t)V, V);
+        }
+    }
+    if (!ok) { ref_fill_invalid(k, acc_len, out); return 0; }
+
+    if (mode == REF_GREEDY) {
+        int a = k;
+        for (int i = 0; i < k; ++i) {
+            int g = ref_argmax(target, dtype, (b * rowsT + (size_t)i) * (size_t)V, V);
+            if (tokens[b * rowsD + (size_t)i] != g) { a = i; break; }
+        }
+        *acc_len = a;
+        for (int i = 0; i < a; ++i) out[i] = tokens[b * rowsD + (size_t)i];
+        out[a] = ref_argmax(target, dtype, (b * rowsT + (size_t)a) * (size_t)V, V);
+        for (int i = a + 1; i <= k; ++i) out[i] = -1;
+        return 0;
+    }
+
+    double* p = work;
+    double* q = work + V;
+    double* w = work + 2 * (size_t)V;
+
+    /* acceptance tests, in order, up to the first rejection */
+    int a = k;
+    for (int i = 0; i < k; ++i) {
+        ref_softmax(target, dtype, (b * rowsT + (size_t)i) * (size_t)V, V, T, p);
+        ref_softmax(draft, dtype, (b * rowsD + (size_t)i) * (size_t)V, V, T, q);
+        int32_t x = tokens[b * rowsD + (size_t)i];
+        p_tok[i] = p[x];
+        q_tok[i] = q[x];
+    }
+    for (int i = 0; i < k; ++i) {
+        double P = p_tok[i], Q = q_tok[i];
+        double r = (Q > 0.0) ? P / Q : (P > 0.0 ? INFINITY : 0.0);
+        double u0 = (double)uniforms[(b * rowsT + (size_t)i) * 2 + 0];
+        double mg = fabs(u0 - r);
+        if (mg < *m_acc) *m_acc = mg;
+        if (!(u0 < r)) { a = i; break; }
+    }
+    *acc_len = a;
+    for (int i = 0; i < a; ++i) out[i] = tokens[b * rowsD + (size_t)i];
+    for (int i = a + 1; i <= k; ++i) out[i] = -1;
+
+    double u1 = (double)uniforms[(b * rowsT + (size_t)a) * 2 + 1];
+    ref_softmax(target, dtype, (b * rowsT + (size_t)a) * (size_t)V, V, T, p);
+    int tok;
+    if (a < k) {
+        ref_softmax(draft, dtype, (b * rowsD + (size_t)a) * (size_t)V, V, T, q);
+        for (int x = 0; x < V; ++x) {
+            double d = p[x] - q[x];
+            w[x] = d > 0.0 ? d : 0.0;
+        }
+        tok = ref_inverse_cdf(w, V, u1, m_cdf);
+        if (tok < 0) {                        /* Z = 0: draw from p_a, flag */
+            flags |= 1;
+            tok = ref_inverse_cdf(p, V, u1, m_cdf);
+            *m_cdf = 0.0;
+        }
+    } else {
+        tok = ref_inverse_cdf(p, V, u1, m_cdf);
+    }
+    out[a] = tok;
+    return flags;
+}
+
+/*
+ * Public entry. All buffers are host memory.
+ *  target  [B,k+1,V] (float32 or bfloat16 bits), draft [B,k,V] (may be NULL in
+ *  greedy mode), tokens [B,k] int32, uniforms [B,k+1,2] float32 (may be NULL
+ *  in greedy mode).
+ *  Outputs: acc_len [B], out_tokens [B,k+1], gap [B,k+1], p_tok/q_tok [B,k]
+ *  (NaN where not computed), margin_acc [B], margin_cdf [B], flags [B].
+ *  threads <= 0 uses the OpenMP default. Returns 0, or -1 on bad arguments.
+ */
+int spec_verify_ref(const void* target, const void* draft, const int32_t* tokens,
+                    const float* uniforms, float temperature, int mode,
+                    int B, int k, int V, int dtype,
+                    int32_t* acc_len, int32_t* out_tokens, double* gap,
+                    double* p_tok, double* q_tok, double* margin_acc,
+                    double* margin_cdf, int32_t* flags, int threads)
+{
+    if (B < 0 || k < 0 || V < 1) return -1;
+    if (dtype != REF_F32 && dtype != REF_BF16) return -1;
+    if (mode != REF_SAMPLE && mode != REF_GREEDY) return -1;
+    if (!target || (k > 0 && !tokens)) return -1;
+    if (mode == REF_SAMPLE && (!uniforms || (k > 0 && !draft))) return -1;
+    double T = (double)temperature;
+    if (mode == REF_SAMPLE && !(T > 0.0 && isfinite(T))) return -1;
+
+    int nt = threads;
+#ifdef _OPENMP
+    if (nt <= 0) nt = omp_get_max_threads();
+#else
+    nt = 1;
+#endif
+    int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+        double* work = (double*)malloc(sizeof(double) * 3 * (size_t)V);
+        if (!work) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int b = 0; b < B; ++b) {
+            if (!work) continue;
+            flags[b] = ref_one_row(target, draft, tokens, uniforms, T, mode, k, V, dtype,
+                                   (size_t)b, &acc_len[b], &out_tokens[(size_t)b * (k + 1)],
+                                   &gap[(size_t)b * (k + 1)], &p_tok[(size_t)b * k],
+                                   &q_tok[(size_t)b * k], &margin_acc[b], &margin_cdf[b], work);
+        }
+        free(work);
+    }
+    return failed ? -2 : 0;
+}
+
+/* Number of threads the OpenMP runtime would use by default. */
+int spec_verify_ref_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,361 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+Each test below ties the oracle to something other than its own code: a
+closed form worked out by hand from exact rational probabilities, the pages'
+printed number, exact enumeration, a textbook library routine, or a
+statistical law. Together they are chosen so that a plausible mistake in the
+oracle (p/q transposed, the residual sign flipped, temperature dropped on one
+side, a non-strict comparison, the wrong uniform channel, an off-by-one in the
+inverse CDF) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+from scipy.special import softmax
+
+import oracle
+from oracle import exact_enum
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+NEG = -np.inf
+
+
+def run(target, draft, tokens, uniforms, T=1.0, mode=oracle.SAMPLE):
+    t = np.asarray(target, np.float32)
+    d = None if draft is None else np.asarray(draft, np.float32)
+    k = t.shape[1] - 1
+    tok = np.asarray(tokens, np.int32).reshape(t.shape[0], k)
+    u = None if uniforms is None else np.asarray(uniforms, np.float32)
+    return oracle.spec_verify_ref(t, d, tok, u, T, mode, dtype=oracle.F32)
+
+
+def logits_of(p, T=1.0):
+    """Logits whose softmax at temperature T is p (zeros become -inf)."""
+    p = np.asarray(p, np.float64)
+    with np.errstate(divide="ignore"):
+        return (T * np.log(p)).astype(np.float32)
+
+
+# ---------------------------------------------------------------- hand-worked closed forms
+# p = (0.1, 0.2, 0.3, 0.4), q = (0.4, 0.3, 0.2, 0.1); residual max(0, p - q) =
+# (0, 0, 0.1, 0.3), Z = 0.4, normalized CDF (0, 0, 0.25, 1).
+
+P4 = [0.1, 0.2, 0.3, 0.4]
+Q4 = [0.4, 0.3, 0.2, 0.1]
+UNIF4 = [0.25, 0.25, 0.25, 0.25]          # all-zero logits: exactly uniform
+
+
+def test_hand_accept_when_ratio_above_one():
+    # x = 3: r = 0.4 / 0.1 = 4 -> accepted for any u; bonus from the uniform
+    # row with u = 0.6: CDF (0.25, 0.5, 0.75, 1) -> first C_j > 0.6 is j = 2.
+    r = run([[logits_of(P4), np.zeros(4)]], [[logits_of(Q4)]], [[3]], [[[0.99, 0.01], [0.3, 0.6]]])
+    assert r.accepted_len[0] == 1
+    assert list(r.out_tokens[0]) == [3, 2]
+    assert r.p_tok[0, 0] == pytest.approx(0.4, abs=1e-7)   # float32 logits
+    assert r.q_tok[0, 0] == pytest.approx(0.1, abs=1e-7)
+
+
+def test_hand_reject_and_residual():
+    # x = 0: r = 0.1 / 0.4 = 0.25; u0 = 0.3 >= r -> reject. Residual draw with
+    # u1 = 0.5: target 0.5 * 0.4 = 0.2 -> C = (0, 0, 0.1, 0.4) -> token 3.
+    r = run([[logits_of(P4), np.zeros(4)]], [[logits_of(Q4)]], [[0]], [[[0.3, 0.5], [0.0, 0.0]]])
+    assert r.accepted_len[0] == 0
+    assert list(r.out_tokens[0]) == [3, -1]
+    assert r.margin_acc[0] == pytest.approx(0.05, abs=1e-7)      # |0.3 - 0.25|
+    assert r.margin_cdf[0] == pytest.approx(0.25, abs=1e-7)      # u=0.5 in [0.25, 1)
+
+
+def test_hand_accept_below_ratio():
+    # Same draft token, u0 = 0.2 < 0.25 -> accepted; bonus with u = 0.1 -> token 0.
+    r = run([[logits_of(P4), np.zeros(4)]], [[logits_of(Q4)]], [[0]], [[[0.2, 0.9], [0.0, 0.1]]])
+    assert r.accepted_len[0] == 1
+    assert list(r.out_tokens[0]) == [0, 0]
+
+
+def test_hand_residual_small_uniform():
+    # x = 1: r = 0.2 / 0.3; u0 = 0.7 rejects; u1 = 0.1 -> 0.04 of Z = 0.4 -> token 2.
+    r = run([[logits_of(P4), np.zeros(4)]], [[logits_of(Q4)]], [[1]], [[[0.7, 0.1], [0.0, 0.0]]])
+    assert r.accepted_len[0] == 0
+    assert list(r.out_tokens[0]) == [2, -1]
+
+
+def test_hand_temperature_scales_both_rows():
+    # Logits are T*ln(p) with T = 0.5, so softmax(logits / T) = p exactly:
+    # p = (0.2, 0.8), q = (0.6, 0.4). x = 0: r = 1/3, u0 = 0.5 rejects; the
+    # residual is (0, 0.4) so the token is 1. Ignoring T on either row would
+    # give r = (1/3)/(0.55...) ~ 0.61 and accept instead.
+    T = 0.5
+    r = run([[logits_of([0.2, 0.8], T), np.zeros(2)]], [[logits_of([0.6, 0.4], T)]], [[0]],
+            [[[0.5, 0.3], [0.0, 0.0]]], T=T)
+    assert r.accepted_len[0] == 0
+    assert list(r.out_tokens[0]) == [1, -1]
+    assert r.p_tok[0, 0] == pytest.approx(0.2, abs=1e-7)
+    assert r.q_tok[0, 0] == pytest.approx(0.6, abs=1e-7)
+    # the gap is on raw logits: |0.5 ln 0.8 - 0.5 ln 0.2| = 0.5 ln 4
+    assert r.gap[0, 0] == pytest.approx(0.5 * math.log(4.0), abs=1e-6)
+
+
+def test_inverse_cdf_boundary_is_strict():
+    # k = 0, uniform p over 4 tokens, u = 0.5 sits exactly on C_1 = 0.5.
+    # "smallest j with C_j > u Z" gives j = 2 (a non-strict search would give 1).
+    r = run([[np.zeros(4)]], [np.zeros((0, 4))], np.zeros((1, 0)), [[[0.0, 0.5]]])
+    assert r.accepted_len[0] == 0
+    assert r.out_tokens[0, 0] == 2
+    r = run([[np.zeros(4)]], [np.zeros((0, 4))], np.zeros((1, 0)), [[[0.0, 0.0]]])
+    assert r.out_tokens[0, 0] == 0
+
+
+# ---------------------------------------------------------------- special cases of the rule
+
+
+def test_q_equals_p_accepts_all(rng=np.random.default_rng(1)):
+    # "Physics of Stolen Time", section 2: with q = p every ratio is 1 and
+    # u < 1 always accepts; all k accepted then a bonus from p_k.
+    B, k, V = 64, 5, 50
+    t = rng.normal(0, 2, (B, k + 1, V)).astype(np.float32)
+    d = t[:, :k].copy()
+    tok = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1, 2)).astype(np.float32)
+    u[:, :, 0] = np.float32(1.0) - np.float32(2.0 ** -24)   # the largest u below 1
+    r = run(t, d, tok, u)
+    assert (r.accepted_len == k).all()
+    assert (r.out_tokens[:, :k] == tok).all()
+    # bonus = textbook inverse CDF of p_k
+    for b in range(B):
+        p = softmax(t[b, k].astype(np.float64))
+        assert r.out_tokens[b, k] == np.searchsorted(np.cumsum(p), u[b, k, 1] * np.cumsum(p)[-1], "right")
+
+
+def test_disjoint_supports_reject_first_and_resample_from_p(rng=np.random.default_rng(2)):
+    # supp p and supp q disjoint: p(x) = 0 so r = 0 and even u = 0 rejects;
+    # max(0, p - q) = p, so the token is the inverse-CDF draw from p.
+    B, k, V = 40, 3, 16
+    t = rng.normal(0, 1, (B, k + 1, V)).astype(np.float32)
+    d = rng.normal(0, 1, (B, k, V)).astype(np.float32)
+    t[:, :, V // 2:] = NEG
+    d[:, :, : V // 2] = NEG
+    tok = rng.integers(V // 2, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1, 2)).astype(np.float32)
+    u[:, 0, 0] = 0.0
+    r = run(t, d, tok, u)
+    assert (r.accepted_len == 0).all()
+    for b in range(B):
+        p = softmax(t[b, 0].astype(np.float64))
+        c = np.cumsum(p)
+        assert r.out_tokens[b, 0] == np.searchsorted(c, u[b, 0, 1] * c[-1], "right")
+        assert (r.out_tokens[b, 1:] == -1).all()
+
+
+def test_k0_is_categorical_sampling(rng=np.random.default_rng(3)):
+    # With no drafts the step is one draw from p_0 = softmax(l / T).
+    B, V = 200, 37
+    for T in (0.3, 1.0, 2.5):
+        t = rng.normal(0, 2, (B, 1, V)).astype(np.float32)
+        u = rng.random((B, 1, 2)).astype(np.float32)
+        r = run(t, np.zeros((B, 0, V), np.float32), np.zeros((B, 0)), u, T=T)
+        for b in range(B):
+            p = softmax(t[b, 0].astype(np.float64) / np.float64(np.float32(T)))
+            c = np.cumsum(p)
+            assert r.out_tokens[b, 0] == np.searchsorted(c, u[b, 0, 1] * c[-1], "right")
+        assert (r.accepted_len == 0).all()
+
+
+def test_gap_and_argmax_match_numpy(rng=np.random.default_rng(4)):
+    # Gap = top-1 minus top-2 logit ("Speculative Pre-Positioning", Eq. 11);
+    # argmax = first maximum. Rows are bf16-like (coarse) so ties occur.
+    B, k, V = 100, 3, 64
+    t = np.round(rng.normal(0, 2, (B, k + 1, V)) * 4) / 4
+    t = t.astype(np.float32)
+    tok = rng.integers(0, V, (B, k)).astype(np.int32)
+    r = run(t, None, tok, None, mode=oracle.GREEDY)
+    for b in range(B):
+        for i in range(k + 1):
+            top2 = np.partition(t[b, i].astype(np.float64), -2)[-2:]
+            assert r.gap[b, i] == top2[1] - top2[0]
+    ties = sum(r.gap[b, i] == 0 for b in range(B) for i in range(k + 1))
+    assert ties > 0
+
+
+def test_greedy_rule(rng=np.random.default_rng(5)):
+    # "The Inference Wall" part 7: accept while the guess equals the target's
+    # argmax; at the first mismatch emit the target's argmax; all matched -> k+1.
+    B, k, V = 300, 4, 20
+    t = np.round(rng.normal(0, 2, (B, k + 1, V)) * 2).astype(np.float32) / 2
+    am = np.argmax(t, axis=2)
+    tok = am[:, :k].copy().astype(np.int32)
+    mism = rng.random((B, k)) < 0.3
+    tok[mism] = rng.integers(0, V, mism.sum())
+    r = run(t, None, tok, None, mode=oracle.GREEDY)
+    for b in range(B):
+        a = next((i for i in range(k) if tok[b, i] != am[b, i]), k)
+        assert r.accepted_len[b] == a
+        assert list(r.out_tokens[b, :a]) == list(tok[b, :a])
+        assert r.out_tokens[b, a] == am[b, a]
+        assert (r.out_tokens[b, a + 1:] == -1).all()
+
+
+def test_greedy_equals_sampling_on_one_hot(rng=np.random.default_rng(6)):
+    # Temperature 0 is the one-hot limit ("The Inference Wall" part 7, "Does it
+    # make the answers worse?"): with p = onehot(argmax l) and q = onehot(x),
+    # r is 1 or 0 and the residual is onehot(argmax), so the sampling rule
+    # reproduces greedy verification for every uniform.
+    B, k, V = 200, 4, 12
+    t = np.round(rng.normal(0, 2, (B, k + 1, V)) * 2).astype(np.float32) / 2
+    am = np.argmax(t, axis=2)
+    tok = am[:, :k].copy().astype(np.int32)
+    mism = rng.random((B, k)) < 0.35
+    tok[mism] = rng.integers(0, V, mism.sum())
+    g = run(t, None, tok, None, mode=oracle.GREEDY)
+    oh_t = np.full_like(t, NEG)
+    oh_d = np.full((B, k, V), NEG, np.float32)
+    for b in range(B):
+        for i in range(k + 1):
+            oh_t[b, i, am[b, i]] = 0.0
+        for i in range(k):
+            oh_d[b, i, tok[b, i]] = 0.0
+    u = rng.random((B, k + 1, 2)).astype(np.float32)
+    s = run(oh_t, oh_d, tok, u)
+    assert (s.accepted_len == g.accepted_len).all()
+    assert (s.out_tokens == g.out_tokens).all()
+
+
+def test_argmax_stable_under_small_perturbation(rng=np.random.default_rng(7)):
+    # Design note, "Axis 1 reuses the gate": if every logit moves by less than
+    # tau in sup-norm and 2 tau <= gap, the argmax cannot change.
+    B, V = 500, 40
+    t = rng.normal(0, 2, (B, 1, V)).astype(np.float32)
+    base = run(t, None, np.zeros((B, 0)), None, mode=oracle.GREEDY)
+    gap = base.gap[:, 0]
+    tau = (gap / 2) * 0.999
+    delta = (rng.random((B, 1, V)) * 2 - 1) * tau[:, None, None]
+    pert = (t.astype(np.float64) + delta).astype(np.float32)
+    # float32 rounding can move a value by half an ulp; keep |delta| < tau after it
+    ok = np.abs(pert.astype(np.float64) - t.astype(np.float64)).max(axis=(1, 2)) < gap / 2
+    moved = run(pert, None, np.zeros((B, 0)), None, mode=oracle.GREEDY)
+    assert ok.mean() > 0.95
+    assert (moved.out_tokens[ok, 0] == base.out_tokens[ok, 0]).all()
+
+
+# ---------------------------------------------------------------- distribution-level pins
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_exact_enumeration_matches_p(seed):
+    # Exact output distribution over (draft token, uniforms) for V <= 8 equals
+    # p_0 within 1e-12; given acceptance, the bonus is distributed as p_1 and
+    # acceptance has probability sum min(p, q) ("Physics of Stolen Time", section 2).
+    rng = np.random.default_rng(100 + seed)
+    V = int(rng.integers(2, 9))
+    T = float(rng.choice([0.5, 1.0, 1.7]))
+    t = rng.normal(0, 1.5, (2, V)).astype(np.float32)
+    d = (t[:1] + rng.normal(0, 1.0, (1, V))).astype(np.float32)
+    if seed % 4 == 3:
+        d[0, : V // 2] = NEG          # draft misses part of the support
+    dist0, dist1, acc = exact_enum.enumerate_k1(t, d, T)
+    out0, acc_exact, p0, p1 = exact_enum.closed_form(t, d, T)
+    assert np.abs(dist0 - p0).max() < 1e-12
+    assert np.abs(dist0 - np.array([float(x) for x in out0])).max() < 1e-12
+    assert abs(acc - float(acc_exact)) < 1e-12
+    assert np.abs(dist1 - acc * p1).max() < 1e-12
+
+
+def test_chi_square_one_million_trials():
+    # 10^6 seeded trials: x ~ q, u ~ U(0,1); the first emitted token must be
+    # indistinguishable from p_0 (losslessness, "Physics of Stolen Time", section 2).
+    rng = np.random.default_rng(2024)
+    V, n, T = 16, 1_000_000, 0.8
+    t0 = rng.normal(0, 1.5, (2, V)).astype(np.float32)
+    d0 = (t0[:1] * 0.7 + rng.normal(0, 1.0, (1, V))).astype(np.float32)
+    q = softmax(d0[0].astype(np.float64) / np.float64(np.float32(T)))
+    p = softmax(t0[0].astype(np.float64) / np.float64(np.float32(T)))
+    tok = rng.choice(V, size=(n, 1), p=q).astype(np.int32)
+    u = rng.random((n, 2, 2)).astype(np.float32)
+    r = run(np.broadcast_to(t0, (n, 2, V)), np.broadcast_to(d0, (n, 1, V)), tok, u, T=T)
+    counts = np.bincount(r.out_tokens[:, 0], minlength=V)
+    _, pval = stats.chisquare(counts, p * n)
+    assert pval > 1e-3, pval
+    # the same test must be able to see a wrong rule: accepting every draft
+    # yields q, not p
+    _, pbad = stats.chisquare(np.bincount(tok[:, 0], minlength=V), p * n)
+    assert pbad < 1e-6
+
+
+def test_accept_length_law_and_printed_expected_tokens():
+    # With the same (p, q) at every position, accept events are iid with
+    # probability alpha = sum min(p, q): P(a = j) = (1 - alpha) alpha^j (j < k),
+    # P(a = k) = alpha^k, and E[a + 1] = (1 - alpha^(k+1)) / (1 - alpha)
+    # ("Physics of Stolen Time", section 3). The page evaluates it at
+    # alpha = 0.4, k = 4 as about 1.6 (section 4).
+    g = json.load(open(os.path.join(HERE, "golden", "pages_printed.json")))["expected_tokens_per_step"]
+    alpha, k = g["alpha"], g["k"]
+    closed = (1 - alpha ** (k + 1)) / (1 - alpha)
+    assert abs(closed - g["printed"]) < g["tolerance"]
+    # p = (0.4, 0.6), q = (1, 0): sum min(p, q) = 0.4
+    rng = np.random.default_rng(9)
+    n, V = 400_000, 2
+    t = np.broadcast_to(logits_of([0.4, 0.6]), (n, k + 1, V))
+    d = np.broadcast_to(logits_of([1.0, 0.0]), (n, k, V))
+    tok = np.zeros((n, k), np.int32)
+    u = rng.random((n, k + 1, 2)).astype(np.float32)
+    r = run(t, d, tok, u)
+    law = np.array([(1 - alpha) * alpha ** j for j in range(k)] + [alpha ** k])
+    counts = np.bincount(r.accepted_len, minlength=k + 1)
+    _, pval = stats.chisquare(counts, law * n)
+    assert pval > 1e-3, (counts, law * n)
+    mean = (r.accepted_len + 1).mean()
+    sd = (r.accepted_len + 1).std() / math.sqrt(n)
+    assert abs(mean - closed) < 5 * sd
+
+
+def test_accept_length_law_random_pq():
+    # Same law with a generic (p, q) pair and x ~ q at every position.
+    rng = np.random.default_rng(10)
+    n, k, V, T = 300_000, 3, 10, 1.0
+    t1 = rng.normal(0, 1, V).astype(np.float32)
+    d1 = (t1 + rng.normal(0, 1, V)).astype(np.float32)
+    p = softmax(t1.astype(np.float64))
+    q = softmax(d1.astype(np.float64))
+    alpha = np.minimum(p, q).sum()
+    tok = rng.choice(V, size=(n, k), p=q).astype(np.int32)
+    u = rng.random((n, k + 1, 2)).astype(np.float32)
+    r = run(np.broadcast_to(t1, (n, k + 1, V)), np.broadcast_to(d1, (n, k, V)), tok, u, T=T)
+    law = np.array([(1 - alpha) * alpha ** j for j in range(k)] + [alpha ** k])
+    counts = np.bincount(r.accepted_len, minlength=k + 1)
+    _, pval = stats.chisquare(counts, law * n)
+    assert pval > 1e-3, (counts, law * n)
+
+
+# ---------------------------------------------------------------- invalid inputs
+
+
+def test_invalid_rows():
+    rng = np.random.default_rng(11)
+    B, k, V = 6, 2, 8
+    t = rng.normal(0, 1, (B, k + 1, V)).astype(np.float32)
+    d = rng.normal(0, 1, (B, k, V)).astype(np.float32)
+    tok = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1, 2)).astype(np.float32)
+    t[0, 1, 3] = np.nan              # NaN in a target row
+    d[1, 0, 5] = np.inf              # +inf in a draft row
+    t[2, 2, :] = NEG                 # bonus row with no finite entry
+    tok[3, 1] = V                    # token out of range
+    t[4, 0, :4] = NEG                # -inf masks are fine
+    r = run(t, d, tok, u)
+    assert list(r.accepted_len[:4]) == [-1, -1, -1, -1]
+    assert (r.out_tokens[:4] == -1).all()
+    assert r.accepted_len[4] >= 0 and r.accepted_len[5] >= 0
+    # greedy mode ignores draft logits but still checks the target and tokens
+    g = run(t, None, tok, None, mode=oracle.GREEDY)
+    assert list(g.accepted_len[:4]) == [-1, 0 if tok[1, 0] != np.argmax(t[1, 0]) else g.accepted_len[1], -1, -1]
+
+
+def test_argument_errors():
+    t = np.zeros((1, 2, 4), np.float32)
+    with pytest.raises(ValueError):
+        run(t, np.zeros((1, 1, 4)), [[0]], np.zeros((1, 2, 2)), T=0.0)
+    with pytest.raises(ValueError):
+        run(t, np.zeros((1, 1, 4)), [[0]], np.zeros((1, 2, 2)), T=float("nan"))

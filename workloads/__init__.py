@@ -1,0 +1,226 @@
+"""Seeded synthetic inputs for the speculative-decoding verify step.
+
+This module only draws random inputs. It holds none of the verify method's
+arithmetic (no softmax, no acceptance test, no residual sampling), and both the
+HIP path's tests and the fp64 oracle consume what it produces.
+
+Five workloads are defined, each a shape plus a recipe for the logits:
+
+* ``b1_k4_v1000_f32``    B=1,   k=4, V=1000,   fp32, T=1.0, sampling.
+  Target logits iid N(0, 2^2); draft = target + N(0, 0.5^2).
+* ``b8_k5_v32000_f32``   B=8,   k=5, V=32000,  fp32, T=0.7, sampling.
+  Target N(0, 3^2) plus +8 at one random index per row; draft = 0.8*target + N(0, 1).
+* ``b64_k5_v151936_bf16`` B=64, k=5, V=151936, bf16, T=1.0, sampling.
+  Target N(0, 2.5^2) plus +6 at 5 distinct random indices per row; draft =
+  target + N(0, 1); exactly round(0.2*B*k) draft rows (chosen without
+  replacement) are replaced by fresh N(0, 2.5^2) rows to force rejections.
+* ``b256_k3_v128256_bf16_greedy`` B=256, k=3, V=128256, bf16, greedy.
+  Target N(0, 2^2) plus a margin spike +U(0, 4) added to the row's argmax;
+  draft tokens = target argmax, with exactly round(0.3*B*k) positions (chosen
+  without replacement) replaced by a uniformly random id. No draft logits and
+  no uniforms are used in greedy mode.
+* ``b512_k8_v262144_bf16`` B=512, k=8, V=262144, bf16, T=0.8, sampling.
+  Target N(0, 2^2) plus +5 at 10 distinct random indices; draft = target + N(0, 0.7^2).
+
+Common rules: logits are drawn in float32 and, for bf16 workloads, rounded to
+bfloat16 (round to nearest even). Target rows i = 0..k (row k is the bonus
+row); draft rows i = 0..k-1. In sampling mode each draft token is drawn from
+softmax(draft_row / T) of the *stored* (rounded) draft row, by the Gumbel-max
+construction (argmax of d/T plus Gumbel noise), which is an exact sampler for
+that categorical distribution. Uniforms are float32 in [0, 1).
+
+Every batch row b is drawn from its own generator seeded from (workload, seed,
+b), so any subset of rows can be regenerated alone; the global choices (which
+draft rows are replaced, which greedy positions are replaced) come from one
+extra generator seeded from (workload, seed).
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Optional
+
+import torch
+
+SAMPLE = 0
+GREEDY = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    k: int
+    V: int
+    dtype: str          # "f32" or "bf16"
+    T: float            # temperature (ignored in greedy mode)
+    mode: int           # SAMPLE or GREEDY
+    recipe: str         # human-readable recipe
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def logit_bytes(self) -> int:
+        """Bytes of logits the verify step must read once (target + draft)."""
+        rows = self.B * (self.k + 1)
+        if self.mode == SAMPLE:
+            rows += self.B * self.k
+        return rows * self.V * self.elem_bytes
+
+    def with_batch(self, B: int) -> "Workload":
+        return dataclasses.replace(self, B=B)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("b1_k4_v1000_f32", 1, 4, 1000, "f32", 1.0, SAMPLE,
+                 "target N(0,2^2); draft = target + N(0,0.5^2)"),
+        Workload("b8_k5_v32000_f32", 8, 5, 32000, "f32", 0.7, SAMPLE,
+                 "target N(0,3^2) + 8 at one index; draft = 0.8*target + N(0,1)"),
+        Workload("b64_k5_v151936_bf16", 64, 5, 151936, "bf16", 1.0, SAMPLE,
+                 "target N(0,2.5^2) + 6 at 5 indices; draft = target + N(0,1); "
+                 "20% of draft rows replaced by N(0,2.5^2)"),
+        Workload("b256_k3_v128256_bf16_greedy", 256, 3, 128256, "bf16", 1.0, GREEDY,
+                 "target N(0,2^2) + U(0,4) on the argmax; tokens = argmax, 30% random"),
+        Workload("b512_k8_v262144_bf16", 512, 8, 262144, "bf16", 0.8, SAMPLE,
+                 "target N(0,2^2) + 5 at 10 indices; draft = target + N(0,0.7^2)"),
+    ]
+}
+
+# The workload the throughput figure is quoted on.
+HEADLINE = "b64_k5_v151936_bf16"
+
+
+def _seed(*parts) -> int:
+    h = hashlib.sha256("/".join(str(p) for p in parts).encode()).digest()
+    return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
+
+
+def _gen(device, *parts) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(*parts))
+    return g
+
+
+def _normal(shape, std, g, device):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+
+
+def _boost(rows, count, amount, g, device):
+    """Add `amount` at `count` distinct random indices of every row (in place)."""
+    n, V = rows.shape
+    for r in range(n):
+        idx = torch.randperm(V, generator=g, device=device)[:count]
+        rows[r, idx] += amount
+    return rows
+
+
+def _gumbel_tokens(draft_rows, T, g, device):
+    """One draw per row from softmax(draft_rows / T), via Gumbel-max."""
+    u = torch.rand(draft_rows.shape, generator=g, device=device, dtype=torch.float64)
+    u = u.clamp_min(1e-300)
+    gumbel = -torch.log(-torch.log(u))
+    return torch.argmax(draft_rows.double() / T + gumbel, dim=1).to(torch.int32)
+
+
+def _global_choice(w: Workload, seed: int, device):
+    """Workload-wide choices drawn before any row: replaced draft rows / positions."""
+    g = _gen(device, w.name, seed, "global")
+    n = w.B * w.k
+    if w.name.startswith("b64_k5"):
+        nrep = int(round(0.2 * n))
+        return torch.randperm(n, generator=g, device=device)[:nrep].cpu()
+    if w.mode == GREEDY:
+        nrep = int(round(0.3 * n))
+        pos = torch.randperm(n, generator=g, device=device)[:nrep].cpu()
+        ids = torch.randint(0, w.V, (nrep,), generator=g, device=device).cpu()
+        return pos, ids
+    return None
+
+
+def _rows_for_batch(w: Workload, seed: int, b: int, glob, device):
+    """Float32 target [k+1,V], float32 draft [k,V] (or None), tokens [k], uniforms [k+1,2]."""
+    g = _gen(device, w.name, seed, b)
+    k, V = w.k, w.V
+    n = k + 1
+    if w.name == "b1_k4_v1000_f32":
+        tgt = _normal((n, V), 2.0, g, device)
+        dft = tgt[:k] + _normal((k, V), 0.5, g, device)
+    elif w.name == "b8_k5_v32000_f32":
+        tgt = _boost(_normal((n, V), 3.0, g, device), 1, 8.0, g, device)
+        dft = 0.8 * tgt[:k] + _normal((k, V), 1.0, g, device)
+    elif w.name == "b64_k5_v151936_bf16":
+        tgt = _boost(_normal((n, V), 2.5, g, device), 5, 6.0, g, device)
+        dft = tgt[:k] + _normal((k, V), 1.0, g, device)
+        fresh = _normal((k, V), 2.5, g, device)
+        for i in range(k):
+            if (b * k + i) in glob:
+                dft[i] = fresh[i]
+    elif w.name == "b256_k3_v128256_bf16_greedy":
+        tgt = _normal((n, V), 2.0, g, device)
+        spike = torch.rand((n,), generator=g, device=device, dtype=torch.float32) * 4.0
+        am = torch.argmax(tgt, dim=1)
+        tgt[torch.arange(n, device=device), am] += spike
+        dft = None
+    elif w.name == "b512_k8_v262144_bf16":
+        tgt = _boost(_normal((n, V), 2.0, g, device), 10, 5.0, g, device)
+        dft = tgt[:k] + _normal((k, V), 0.7, g, device)
+    else:
+        raise KeyError(w.name)
+
+    tgt = tgt.to(w.torch_dtype)
+    if dft is not None:
+        dft = dft.to(w.torch_dtype)
+
+    if w.mode == GREEDY:
+        tok = torch.argmax(tgt[:k].float(), dim=1).to(torch.int32)  # first max on ties
+        pos, ids = glob
+        for j in range(pos.numel()):
+            p = int(pos[j])
+            if p // k == b:
+                tok[p % k] = int(ids[j])
+        uni = None
+    else:
+        tok = _gumbel_tokens(dft.float(), w.T, g, device) if k > 0 else \
+            torch.zeros((0,), dtype=torch.int32, device=device)
+        uni = torch.rand((n, 2), generator=g, device=device, dtype=torch.float32)
+    return tgt, dft, tok, uni
+
+
+def make(w: Workload | str, seed: int = 0, device="cpu", rows: Optional[range] = None):
+    """Generate the inputs of workload `w` for `seed`.
+
+    Returns a dict with ``target`` [B,k+1,V], ``draft`` [B,k,V] (None in greedy
+    mode), ``tokens`` [B,k] int32, ``uniforms`` [B,k+1,2] float32 (None in
+    greedy mode), plus ``T`` and ``mode``. With ``rows`` only those batch rows
+    are generated (identical to the same rows of the full draw).
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    device = torch.device(device)
+    glob = _global_choice(w, seed, device)
+    if isinstance(glob, torch.Tensor):
+        glob = set(int(x) for x in glob)
+    rows = range(w.B) if rows is None else rows
+    nb = len(rows)
+    target = torch.empty((nb, w.k + 1, w.V), dtype=w.torch_dtype, device=device)
+    draft = None if w.mode == GREEDY else \
+        torch.empty((nb, w.k, w.V), dtype=w.torch_dtype, device=device)
+    tokens = torch.empty((nb, w.k), dtype=torch.int32, device=device)
+    uniforms = None if w.mode == GREEDY else \
+        torch.empty((nb, w.k + 1, 2), dtype=torch.float32, device=device)
+    for j, b in enumerate(rows):
+        t, d, tok, u = _rows_for_batch(w, seed, b, glob, device)
+        target[j] = t
+        if draft is not None:
+            draft[j] = d
+            uniforms[j] = u
+        tokens[j] = tok
+    return {"target": target, "draft": draft, "tokens": tokens, "uniforms": uniforms,
+            "T": w.T, "mode": w.mode, "workload": w}
