@@ -1,0 +1,126 @@
+/*
+ * spec_verify.h -- C ABI of the batched speculative-decoding verify step on MI355X (gfx950).
+ *
+ * The operation ("Speculative Decoding: The Physics of Stolen Time", section 1
+ * stage 3 and section 2; the speculative-decoding design note, "The acceptance
+ * math"; "The Inference Wall" part 7, "How speculative decoding works";
+ * "Speculative Pre-Positioning", section 2.4, Eq. 11):
+ *
+ *   For every batch row b with draft tokens x_0..x_{k-1}:
+ *   SAMPLE mode -- p_i = softmax(target_logits[b,i,:] / T), q_i = softmax(draft_logits[b,i,:] / T);
+ *     position i is accepted iff u[b,i,0] < p_i(x_i) / q_i(x_i) (probability min(1, p/q));
+ *     at the first rejected position a the token is drawn from norm(max(0, p_a - q_a));
+ *     when all k drafts are accepted (a = k) a bonus token is drawn from p_k.
+ *     A draw from weights w uses u = u[b,a,1] and returns the smallest j with
+ *     sum_{x<=j} w_x > u * sum_x w_x (inverse CDF in vocabulary order).
+ *   GREEDY mode -- g_i = argmax target_logits[b,i,:] (lowest index on ties); a = first i
+ *     with x_i != g_i, else k; the emitted token at position a is g_a.
+ *   Both modes: gap[b,i] = top-1 minus top-2 of the raw target logits of row i (0 on a
+ *     tie at the top, +inf when the row has fewer than two finite entries).
+ *
+ * Readings of points the method leaves open: temperature divides target and draft
+ * logits alike and does not enter the gap or greedy mode; uniform channel 0 drives
+ * the acceptance test and channel 1 the inverse-CDF draw (u[b,k,0] is unused);
+ * q(x) = 0 accepts iff p(x) > 0; a rejection whose residual mass rounds to zero
+ * draws from p_a instead.
+ *
+ * Memory: every pointer argument of spec_verify is a DEVICE pointer on the current HIP
+ * device, owned by the caller. Tensors are dense, row-major, innermost index last:
+ *   target_logits [B, k+1, V]  float32 or bfloat16 (dtype)
+ *   draft_logits  [B, k,   V]  same dtype; may be NULL in GREEDY mode (never read there)
+ *   draft_tokens  [B, k]       int32
+ *   uniforms      [B, k+1, 2]  float32 in [0, 1); may be NULL in GREEDY mode
+ *   accepted_len  [B]          int32 out: number of accepted drafts 0..k, or -1 (invalid row)
+ *   out_tokens    [B, k+1]     int32 out: accepted drafts, then one sampled/argmax token,
+ *                              then -1 padding; all -1 for an invalid row
+ *   gap           [B, k+1]     float32 out
+ *   target_prob, draft_prob [B, k] float32 out, optional (NULL to skip): p_i(x_i), q_i(x_i)
+ *                              in SAMPLE mode; NaN in GREEDY mode
+ * Inputs are only read. Outputs are fully overwritten and must not alias inputs, each
+ * other or the workspace.
+ *
+ * Invalid rows (asynchronous, per batch row): a NaN or +inf logit in any row the mode
+ * reads, a row without a finite entry, or a draft token outside [0, V) gives
+ * accepted_len[b] = -1 and out_tokens[b,:] = -1. -inf logits are allowed (masked
+ * entries, probability 0).
+ *
+ * Workspace: caller-owned device memory of at least spec_verify_workspace_size() bytes
+ * (256-byte aligned). It carries the per-row and per-chunk records that one kernel of
+ * the call hands to the next; every record is written before it is read, so the
+ * workspace needs no initialisation and may be reused freely. One workspace serves one
+ * call at a time: calls that overlap in time (e.g. on two streams) need separate
+ * workspaces.
+ *
+ * Execution: spec_verify only enqueues work on `stream` (a hipStream_t; NULL = the null
+ * stream) and returns; completion is observed by synchronising that stream. It performs
+ * no allocation and no host synchronisation.
+ *
+ * Errors: 0 = enqueued. A negative return is synchronous and means nothing was enqueued;
+ * spec_verify_last_error() then describes it (thread-local string).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_DTYPE_F32 0
+#define SPEC_DTYPE_BF16 1
+
+#define SPEC_MODE_SAMPLE 0
+#define SPEC_MODE_GREEDY 1
+
+#define SPEC_MAX_K 64
+
+#define SPEC_OK 0
+#define SPEC_ERR_NULL (-1)      /* a required pointer is NULL                                   */
+#define SPEC_ERR_SHAPE (-2)     /* B < 1, k outside [0, SPEC_MAX_K], V < 1, or a size overflow  */
+#define SPEC_ERR_DTYPE (-3)     /* dtype is not SPEC_DTYPE_F32 / SPEC_DTYPE_BF16                */
+#define SPEC_ERR_MODE (-4)      /* mode is not SPEC_MODE_SAMPLE / SPEC_MODE_GREEDY              */
+#define SPEC_ERR_TEMP (-5)      /* SAMPLE mode with a temperature that is not finite and > 0    */
+#define SPEC_ERR_WORKSPACE (-6) /* workspace NULL or smaller than spec_verify_workspace_size()  */
+#define SPEC_ERR_ALIGN (-7)     /* a pointer is not aligned to its element size (4 B or 2 B),
+                                   or the workspace is not 256-B aligned                        */
+#define SPEC_ERR_HIP (-8)       /* the HIP runtime refused the launch                           */
+
+/*
+ * Enqueue the verify step. See the file comment for the meaning and layout of every
+ * argument. temperature is ignored in GREEDY mode.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V,
+                int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
+                float* draft_prob, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace spec_verify needs for these sizes (0 if the sizes are invalid).
+ * Host-only; makes no HIP call.
+ */
+size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int dtype, int mode);
+
+/*
+ * The synchronous argument checks of spec_verify, without enqueueing anything.
+ * Host-only; makes no HIP call and dereferences no pointer. Returns 0 or a
+ * SPEC_ERR_* code (and sets spec_verify_last_error()).
+ */
+int spec_verify_check_args(const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, const float* uniforms, float temperature,
+                           int mode, int32_t B, int32_t k, int32_t V, int dtype,
+                           const int32_t* accepted_len, const int32_t* out_tokens, const float* gap,
+                           const void* workspace, size_t workspace_bytes);
+
+/* Thread-local description of the last non-zero return of this library. */
+const char* spec_verify_last_error(void);
+
+/* Library version string. */
+const char* spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

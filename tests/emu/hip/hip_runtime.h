@@ -1,0 +1,189 @@
+// CPU emulation of the small HIP subset that spec_verify.hip uses.
+//
+// TEST INFRASTRUCTURE ONLY. It lets the unchanged kernel source be compiled as
+// host C++ (see ../spec_verify_emu.cpp) and run on the CPU, optionally under
+// AddressSanitizer.
+//
+// Model: a launch runs its workgroups on a pool of OS threads (emu_set_pool,
+// default 1 = workgroups strictly one after another). Inside a workgroup the
+// lanes are cooperative fibers (ucontext) on that OS thread, so __shared__
+// (mapped to static thread_local) is private to the workgroup. __syncthreads
+// and each half of a lane shuffle are fiber yields; the scheduler runs every
+// live lane up to its next yield in lane order, which is a barrier as long as
+// every lane meets the same sequence of barriers (the kernel's contract).
+// Global atomics are the GCC __atomic builtins, so workgroups on different OS
+// threads really race, spin-waits included.
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <ucontext.h>
+
+#include <atomic>
+#include <thread>
+#include <vector>
+
+#define __global__
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#define __launch_bounds__(...)
+#define __shared__ static thread_local
+
+struct dim3 {
+    unsigned x, y, z;
+    dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}
+};
+struct EmuIdx { unsigned x, y, z; };
+inline thread_local EmuIdx threadIdx{0, 0, 0};
+inline thread_local EmuIdx blockIdx{0, 0, 0};
+inline EmuIdx gridDim{1, 1, 1};
+inline EmuIdx blockDim{1, 1, 1};
+
+struct alignas(16) uint4 { unsigned x, y, z, w; };
+struct alignas(16) float4 { float x, y, z, w; };
+
+inline float __uint_as_float(unsigned u) { float f; memcpy(&f, &u, 4); return f; }
+inline int min(int a, int b) { return a < b ? a : b; }
+inline int max(int a, int b) { return a > b ? a : b; }
+
+inline float emu_fmed3f(float a, float b, float c) {
+    return fmaxf(fminf(a, b), fminf(fmaxf(a, b), c));
+}
+inline float emu_exp2f(float x) { return exp2f(x); }
+#define __builtin_amdgcn_fmed3f emu_fmed3f
+#define __builtin_amdgcn_exp2f emu_exp2f
+#define __builtin_amdgcn_s_sleep(n) std::this_thread::yield()
+
+#define __HIP_MEMORY_SCOPE_AGENT 0
+#define __hip_atomic_fetch_add(p, v, o, s) __atomic_fetch_add((p), (v), (o))
+#define __hip_atomic_store(p, v, o, s) __atomic_store_n((p), (v), (o))
+#define __hip_atomic_load(p, o, s) __atomic_load_n((p), (o))
+template <class T> inline T atomicAdd(T* p, T v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+template <class T> inline T atomicAnd(T* p, T v) { return __atomic_fetch_and(p, v, __ATOMIC_SEQ_CST); }
+template <class T> inline T atomicOr(T* p, T v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
+inline void __threadfence() { __atomic_thread_fence(__ATOMIC_SEQ_CST); }
+
+// ---------------------------------------------------------------- fibers
+struct EmuWG {
+    static constexpr size_t STACK = 512 * 1024;
+    ucontext_t sched;
+    std::vector<ucontext_t> ctx;
+    std::vector<char> stacks;
+    std::vector<char> done;
+    unsigned n = 0;
+    void (*body)(void*) = nullptr;
+    void* arg = nullptr;
+    alignas(8) unsigned char shfl[1024][8];
+};
+inline thread_local EmuWG* emu_wg = nullptr;
+
+inline void emu_yield() {
+    EmuWG* w = emu_wg;
+    const unsigned me = threadIdx.x;
+    swapcontext(&w->ctx[me], &w->sched);
+    threadIdx.x = me;
+}
+
+inline void __syncthreads() { emu_yield(); }
+
+template <class T>
+inline T __shfl_xor(T v, int mask, int width = 64) {
+    (void)width;
+    EmuWG* w = emu_wg;
+    const unsigned me = threadIdx.x;
+    const unsigned base = me & ~63u, lane = me & 63u;
+    memcpy(w->shfl[me], &v, sizeof(T));
+    emu_yield();
+    T r;
+    memcpy(&r, w->shfl[base + (lane ^ static_cast<unsigned>(mask))], sizeof(T));
+    emu_yield();
+    return r;
+}
+
+inline void emu_fiber_entry(unsigned lo, unsigned hi) {
+    (void)lo; (void)hi;
+    EmuWG* w = emu_wg;
+    const unsigned me = threadIdx.x;
+    w->body(w->arg);
+    w->done[me] = 1;
+}
+
+inline void emu_run_wg(EmuWG& w, unsigned wg, unsigned nthreads) {
+    emu_wg = &w;
+    blockIdx = EmuIdx{wg, 0, 0};
+    w.n = nthreads;
+    w.ctx.assign(nthreads, ucontext_t{});
+    w.done.assign(nthreads, 0);
+    if (w.stacks.size() < nthreads * EmuWG::STACK) w.stacks.resize(nthreads * EmuWG::STACK);
+    for (unsigned t = 0; t < nthreads; ++t) {
+        getcontext(&w.ctx[t]);
+        w.ctx[t].uc_stack.ss_sp = w.stacks.data() + t * EmuWG::STACK;
+        w.ctx[t].uc_stack.ss_size = EmuWG::STACK;
+        w.ctx[t].uc_link = &w.sched;
+        makecontext(&w.ctx[t], reinterpret_cast<void (*)()>(emu_fiber_entry), 2, 0u, 0u);
+    }
+    for (;;) {
+        bool any = false;
+        for (unsigned t = 0; t < nthreads; ++t) {
+            if (w.done[t]) continue;
+            any = true;
+            threadIdx = EmuIdx{t, 0, 0};
+            swapcontext(&w.sched, &w.ctx[t]);
+        }
+        if (!any) break;
+    }
+}
+
+inline int& emu_pool() { static int n = 1; return n; }
+
+template <class P>
+struct EmuLaunch {
+    void (*kernel)(P);
+    P params;
+    static void call(void* self) {
+        auto* s = static_cast<EmuLaunch*>(self);
+        s->kernel(s->params);
+    }
+};
+
+template <class P>
+inline void emu_launch(void (*kernel)(P), dim3 grid, dim3 block, P params) {
+    gridDim = EmuIdx{grid.x, 1, 1};
+    blockDim = EmuIdx{block.x, 1, 1};
+    EmuLaunch<P> L{kernel, params};
+    std::atomic<unsigned> next{0};
+    auto worker = [&] {
+        EmuWG w;
+        w.body = &EmuLaunch<P>::call;
+        w.arg = &L;
+        for (;;) {
+            const unsigned wg = next.fetch_add(1);
+            if (wg >= grid.x) break;
+            emu_run_wg(w, wg, block.x);
+        }
+    };
+    const int pool = emu_pool() < 1 ? 1 : emu_pool();
+    std::vector<std::thread> th;
+    for (int i = 0; i < pool; ++i) th.emplace_back(worker);
+    for (auto& t : th) t.join();
+}
+
+// ---------------------------------------------------------------- host API
+typedef int hipError_t;
+typedef void* hipStream_t;
+enum { hipSuccess = 0, hipErrorInvalidValue = 1 };
+enum hipMemcpyKind { hipMemcpyDeviceToHost = 2 };
+enum hipDeviceAttribute_t { hipDeviceAttributeMultiprocessorCount = 0 };
+
+inline int& emu_cu_count() { static int n = 1; return n; }
+inline hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+inline hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = emu_cu_count(); return hipSuccess; }
+inline hipError_t hipGetLastError() { return hipSuccess; }
+inline const char* hipGetErrorString(hipError_t) { return "emulated"; }
+inline hipError_t hipMemsetAsync(void* p, int v, size_t n, hipStream_t) { memset(p, v, n); return hipSuccess; }
+inline hipError_t hipMemcpy(void* d, const void* s, size_t n, hipMemcpyKind) { memcpy(d, s, n); return hipSuccess; }
+
+#define hipLaunchKernelGGL(kernel, grid, block, shmem, stream, ...) \
+    emu_launch(kernel, dim3(grid), dim3(block), __VA_ARGS__)

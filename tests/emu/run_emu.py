@@ -1,0 +1,174 @@
+"""Run the CPU-emulated HIP library on host inputs and compare with the oracle.
+
+TEST INFRASTRUCTURE ONLY. Invoked in a subprocess with the sanitizer runtime
+preloaded (see tests/test_emulation.py). Usage: run_emu.py <case> [<case> ...]
+"""
+import ctypes
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.dirname(HERE))
+
+import torch  # noqa: E402
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from parity import DELTA_ACC, DELTA_CDF  # noqa: E402
+
+L = ctypes.CDLL(os.path.join(HERE, "libspecverify_emu.so"))
+P, I, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+L.spec_verify.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int, P, P, P, P, P, P, S, P]
+L.spec_verify.restype = ctypes.c_int
+L.spec_verify_workspace_size.argtypes = [I, I, I, ctypes.c_int, ctypes.c_int]
+L.spec_verify_workspace_size.restype = S
+L.spec_verify_last_error.restype = ctypes.c_char_p
+L.spec_verify_emu_set_cu_count.argtypes = [ctypes.c_int]
+L.spec_verify_emu_set_pool.argtypes = [ctypes.c_int]
+
+
+
+def host(x, dtype):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        if x.dtype == torch.bfloat16:
+            return np.ascontiguousarray(x.view(torch.int16).numpy().view(np.uint16))
+        return np.ascontiguousarray(x.numpy())
+    return np.ascontiguousarray(x)
+
+
+def ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def run_case(x, cus=1, ws_reuse=None, pool=1):
+    tgt = x["target"]
+    dtype = 1 if tgt.dtype == torch.bfloat16 else 0
+    B, k1, V = tgt.shape
+    k = k1 - 1
+    mode = x["mode"]
+    t = host(tgt, dtype)
+    d = host(x["draft"], dtype)
+    tok = host(x["tokens"], None).astype(np.int32)
+    u = host(x["uniforms"], None)
+    acc = np.full(B, -7, np.int32)
+    out = np.full((B, k + 1), -7, np.int32)
+    gap = np.zeros((B, k + 1), np.float32)
+    tp = np.zeros((B, k), np.float32)
+    dp = np.zeros((B, k), np.float32)
+    n = L.spec_verify_workspace_size(B, k, V, dtype, mode)
+    # uninitialised workspace: every record must be written before it is read
+    ws = ws_reuse if ws_reuse is not None else np.frombuffer(os.urandom(n + 256), np.uint8).copy()
+    base = ws.ctypes.data
+    off = (-base) % 256
+    L.spec_verify_emu_set_cu_count(cus)
+    L.spec_verify_emu_set_pool(pool)
+    rc = L.spec_verify(ptr(t), ptr(d), ptr(tok), ptr(u), ctypes.c_float(x["T"]), mode, B, k, V, dtype,
+                       ptr(acc), ptr(out), ptr(gap), ptr(tp) if mode == 0 else None,
+                       ptr(dp) if mode == 0 else None, ctypes.c_void_p(base + off), n, None)
+    assert rc == 0, (rc, L.spec_verify_last_error())
+    # a second call on the same workspace must reproduce the first bit for bit
+    acc2, out2, gap2 = acc.copy(), out.copy(), gap.copy()
+    rc = L.spec_verify(ptr(t), ptr(d), ptr(tok), ptr(u), ctypes.c_float(x["T"]), mode, B, k, V, dtype,
+                       ptr(acc2), ptr(out2), ptr(gap2), None, None, ctypes.c_void_p(base + off), n, None)
+    assert rc == 0
+    assert (acc2 == acc).all() and (out2 == out).all() and (gap2.view(np.uint32) == gap.view(np.uint32)).all()
+    ref = oracle.spec_verify_ref(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], mode)
+    flagged = ref.flagged(DELTA_ACC, DELTA_CDF) if mode == 0 else np.zeros(B, bool)
+    same = (acc == ref.accepted_len) & (out == ref.out_tokens).all(axis=1)
+    bad = ~same & ~flagged
+    assert not bad.any(), (np.nonzero(bad)[0][:5], acc[bad][:3], ref.accepted_len[bad][:3],
+                           out[bad][:3], ref.out_tokens[bad][:3])
+    valid = ref.accepted_len >= 0
+    g = gap.astype(np.float64)[valid]
+    r = ref.gap[valid]
+    fin = np.isfinite(r)
+    assert (np.isfinite(g) == fin).all()
+    assert np.abs(g[fin] - r[fin]).max(initial=0) <= (1e-5 if dtype == 0 else 2e-3)
+    if mode == 0 and k > 0:
+        assert np.abs(tp.astype(np.float64)[valid] - ref.p_tok[valid]).max(initial=0) <= 1e-5
+        assert np.abs(dp.astype(np.float64)[valid] - ref.q_tok[valid]).max(initial=0) <= 1e-5
+    return int(flagged.sum())
+
+
+def rand_case(rng, B, k, V, dtype, T, mode=0, coarse=False):
+    t = torch.from_numpy(rng.normal(0, 2.0, (B, k + 1, V)).astype(np.float32))
+    if coarse:
+        t = torch.round(t * 2) / 2
+    d = t[:, :k] + torch.from_numpy(rng.normal(0, 1.0, (B, k, V)).astype(np.float32))
+    td = torch.float32 if dtype == 0 else torch.bfloat16
+    tok = torch.from_numpy(rng.integers(0, V, (B, k)).astype(np.int32))
+    if mode == 1:
+        am = torch.argmax(t.to(td).float(), dim=2)[:, :k].to(torch.int32)
+        keep = torch.from_numpy(rng.random((B, k)) < 0.7)
+        tok = torch.where(keep, am, tok)
+    uni = torch.from_numpy(rng.random((B, k + 1, 2)).astype(np.float32))
+    return {"target": t.to(td), "draft": None if mode == 1 else d.to(td), "tokens": tok,
+            "uniforms": None if mode == 1 else uni, "T": T, "mode": mode}
+
+
+CASES = {}
+
+
+def case(fn):
+    CASES[fn.__name__] = fn
+    return fn
+
+
+@case
+def smoke_b8():
+    w = workloads.WORKLOADS["b8_k5_v32000_f32"]
+    run_case(workloads.make(w, 0), cus=1)
+    run_case(workloads.make(w, 1), cus=3)
+
+
+@case
+def concurrent_b8():
+    # the real launch shape of this workload on 256 CUs: 680 workers, 8 at a time
+    w = workloads.WORKLOADS["b8_k5_v32000_f32"]
+    run_case(workloads.make(w, 0), cus=256, pool=8)
+
+
+@case
+def smoke_b1():
+    w = workloads.WORKLOADS["b1_k4_v1000_f32"]
+    for s in range(5):
+        run_case(workloads.make(w, s))
+
+
+@case
+def odd_shapes():
+    rng = np.random.default_rng(1)
+    for dtype in (0, 1):
+        for V in (1, 2, 3, 7, 9, 63, 65, 1001, 4097, 9001):
+            for k, T in ((0, 1.0), (1, 0.05), (3, 7.0)):
+                run_case(rand_case(rng, 3, k, V, dtype, T))
+            for k in (0, 2):
+                run_case(rand_case(rng, 3, k, V, dtype, 1.0, mode=1, coarse=True))
+
+
+@case
+def greedy_bf16():
+    rng = np.random.default_rng(2)
+    run_case(rand_case(rng, 6, 3, 20000, 1, 1.0, mode=1, coarse=True), cus=2)
+
+
+@case
+def exact_path():
+    os.environ["SPEC_VERIFY_FORCE_EXACT_PATH"] = "1"
+    rng = np.random.default_rng(3)
+    run_case(rand_case(rng, 4, 3, 9000, 0, 0.9))
+    del os.environ["SPEC_VERIFY_FORCE_EXACT_PATH"]
+
+
+if __name__ == "__main__":
+    names = sys.argv[1:] or list(CASES)
+    for nm in names:
+        print("case", nm, flush=True)
+        CASES[nm]()
+        print("ok", nm, flush=True)

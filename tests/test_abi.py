@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports exactly what the
+header declares, sizes its workspace consistently, and rejects bad arguments
+with the documented codes (spec_verify_check_args makes no HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import token_verification_amd as tv
+from token_verification_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(spec_verify\w*)\s*\(", src))
+
+
+def test_exports_match_header():
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    exported = {s for s in exported if s.startswith("spec_verify")}
+    assert declared() == exported
+    assert len(exported) == 5
+
+
+def test_version():
+    assert b"gfx950" in tv.lib().spec_verify_version()
+
+
+def test_workspace_size():
+    assert tv.workspace_size(64, 5, 151936, 1, 0) > 0
+    assert tv.workspace_size(0, 5, 100, 1, 0) == 0
+    assert tv.workspace_size(1, 65, 100, 1, 0) == 0
+    assert tv.workspace_size(1, 2, 0, 1, 0) == 0
+    assert tv.workspace_size(1, 2, 100, 7, 0) == 0
+    assert tv.workspace_size(1, 2, 100, 1, 3) == 0
+    # greedy needs no pass-2 records
+    assert tv.workspace_size(64, 5, 151936, 1, 1) < tv.workspace_size(64, 5, 151936, 1, 0)
+    for B, k, V in ((1, 0, 1), (3, 64, 7), (512, 8, 262144), (1, 4, 1 << 24)):
+        n = tv.workspace_size(B, k, V, 0, 0)
+        assert n % 256 == 0 and n >= 256
+
+
+FAKE = 0x10000          # aligned fake device address (never dereferenced)
+
+
+def args(**kw):
+    a = dict(target=FAKE, draft=FAKE, tokens=FAKE, uniforms=FAKE, T=1.0, mode=0, B=4, k=3, V=100,
+             dtype=0, acc=FAKE, out=FAKE, gap=FAKE, ws=0x100000, ws_bytes=1 << 20)
+    a.update(kw)
+    return a
+
+
+def check(**kw):
+    a = args(**kw)
+    return tv.check_args(a["target"], a["draft"], a["tokens"], a["uniforms"], a["T"], a["mode"],
+                         a["B"], a["k"], a["V"], a["dtype"], a["acc"], a["out"], a["gap"], a["ws"],
+                         a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"target": None}, -1),
+    ({"draft": None}, -1),
+    ({"draft": None, "mode": 1, "uniforms": None}, 0),
+    ({"tokens": None}, -1),
+    ({"tokens": None, "k": 0}, 0),
+    ({"uniforms": None}, -1),
+    ({"acc": None}, -1),
+    ({"gap": None}, -1),
+    ({"B": 0}, -2),
+    ({"k": -1}, -2),
+    ({"k": 65}, -2),
+    ({"V": 0}, -2),
+    ({"dtype": 2}, -3),
+    ({"mode": 2}, -4),
+    ({"T": 0.0}, -5),
+    ({"T": -1.0}, -5),
+    ({"T": float("nan")}, -5),
+    ({"T": float("inf")}, -5),
+    ({"T": 0.0, "mode": 1, "draft": None, "uniforms": None}, 0),
+    ({"ws": None}, -6),
+    ({"ws_bytes": 16}, -6),
+    ({"target": FAKE + 2}, -7),
+    ({"target": FAKE + 2, "dtype": 1}, 0),
+    ({"target": FAKE + 1, "dtype": 1}, -7),
+    ({"tokens": FAKE + 2}, -7),
+    ({"ws": 0x100000 + 64}, -7),
+])
+def test_check_args_codes(kw, code):
+    assert check(**kw) == code
+    if code != 0:
+        assert binding.last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(tv.SpecVerifyError):
+        binding.lib()
+
+
+def test_cpu_tensors_rejected():
+    import torch
+    t = torch.zeros(1, 2, 4)
+    with pytest.raises(ValueError):
+        tv.spec_verify(t, torch.zeros(1, 1, 4), torch.zeros(1, 1, dtype=torch.int32),
+                       torch.zeros(1, 2, 2), 1.0, 0)

@@ -1,0 +1,233 @@
+"""Parity of the HIP verify step (through the C ABI) with the fp64 oracle.
+
+Every test here calls token_verification_amd.spec_verify, which enqueues the
+HIP kernel through libspecverify.so, and compares against oracle.spec_verify_ref
+on the same seeded inputs (see tests/parity.py for the rules).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_verification_amd as tv
+import workloads
+from parity import DELTA_ACC, DELTA_CDF, compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_pair(x, dtype, greedy, rows=None):
+    """GPU call on device tensors x; oracle on host copies (optionally a row subset)."""
+    res = tv.spec_verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], x["mode"],
+                         return_probs=not greedy)
+    torch.cuda.synchronize()
+    sel = slice(None) if rows is None else rows
+    tgt = x["target"][sel].cpu()
+    dft = None if x["draft"] is None else x["draft"][sel].cpu()
+    tok = x["tokens"][sel].cpu()
+    uni = None if x["uniforms"] is None else x["uniforms"][sel].cpu()
+    ref = oracle.spec_verify_ref(tgt, dft, tok, uni, x["T"], x["mode"])
+    if rows is not None:
+        res = tv.binding.VerifyResult(res.accepted_len[sel], res.out_tokens[sel], res.gap[sel],
+                                      None if res.target_prob is None else res.target_prob[sel],
+                                      None if res.draft_prob is None else res.draft_prob[sel])
+    return compare(res, ref, dtype, greedy)
+
+
+def to_dev(x):
+    y = dict(x)
+    for key in ("target", "draft", "tokens", "uniforms"):
+        if y[key] is not None:
+            y[key] = y[key].to(DEV)
+    return y
+
+
+@pytest.mark.parametrize("name,seeds", [
+    ("b1_k4_v1000_f32", range(300)),
+    ("b8_k5_v32000_f32", range(40)),
+])
+def test_small_workloads(name, seeds):
+    w = workloads.WORKLOADS[name]
+    tot = {"rows": 0, "flagged": 0, "mismatch_flagged": 0}
+    for s in seeds:
+        st = run_pair(to_dev(workloads.make(w, s)), w.dtype, w.mode == workloads.GREEDY)
+        for key in tot:
+            tot[key] += st[key]
+    say(name, tot)
+    assert tot["flagged"] <= max(1, 1e-4 * tot["rows"])
+
+
+@pytest.mark.parametrize("name,seeds", [
+    ("b64_k5_v151936_bf16", range(3)),
+    ("b256_k3_v128256_bf16_greedy", range(2)),
+])
+def test_full_size_workloads(name, seeds):
+    w = workloads.WORKLOADS[name]
+    for s in seeds:
+        say(f"{name} seed {s}")
+        x = workloads.make(w, s, device=DEV)
+        st = run_pair(x, w.dtype, w.mode == workloads.GREEDY)
+        say(name, s, st)
+
+
+def test_largest_workload_sampled_rows():
+    # B=512 k=8 V=262144 bf16 at full size in the benchmarked launch shape; the
+    # oracle checks a fixed sample of 24 batch rows.
+    w = workloads.WORKLOADS["b512_k8_v262144_bf16"]
+    say("b512 generate")
+    x = workloads.make(w, 0, device=DEV)
+    rows = torch.tensor(sorted(set(list(range(0, 512, 23)) + [1, 510, 511])), device=DEV)
+    st = run_pair(x, w.dtype, False, rows=rows)
+    say("b512", st)
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+def rand_case(rng, B, k, V, dtype, T, mask_frac=0.0, spread=2.0):
+    t = torch.from_numpy(rng.normal(0, spread, (B, k + 1, V)).astype(np.float32))
+    d = t[:, :k] + torch.from_numpy(rng.normal(0, 1.0, (B, k, V)).astype(np.float32))
+    if mask_frac > 0:
+        m = torch.from_numpy(rng.random((B, k + 1, V)) < mask_frac)
+        t[m] = -float("inf")
+        md = torch.from_numpy(rng.random((B, k, V)) < mask_frac)
+        d[md] = -float("inf")
+        t[:, :, 0] = 0.0                       # keep a finite entry per row
+        d[:, :, 0] = 0.0
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    tok = torch.from_numpy(rng.integers(0, V, (B, k)).astype(np.int32))
+    uni = torch.from_numpy(rng.random((B, k + 1, 2)).astype(np.float32))
+    return {"target": t.to(td), "draft": d.to(td), "tokens": tok, "uniforms": uni, "T": T, "mode": 0}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 8, 63, 65, 1001, 4097, 40961])
+def test_odd_vocab_sampling(dtype, V):
+    rng = np.random.default_rng(V)
+    for k, T in ((0, 1.0), (1, 0.05), (3, 10.0), (5, 0.7)):
+        x = rand_case(rng, 7, k, V, dtype, T)
+        run_pair(to_dev(x), dtype, False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 5, 64, 129, 3001, 70001])
+def test_odd_vocab_greedy(dtype, V):
+    rng = np.random.default_rng(1000 + V)
+    for k in (0, 1, 4):
+        x = rand_case(rng, 9, k, V, dtype, 1.0)
+        # coarse values force exact ties at the top
+        x["target"] = (torch.round(x["target"].float() * 2) / 2).to(x["target"].dtype)
+        am = torch.argmax(x["target"].float(), dim=2)[:, :k].to(torch.int32)
+        keep = torch.from_numpy(rng.random((9, k)) < 0.7)
+        x["tokens"] = torch.where(keep, am, x["tokens"])
+        x["mode"] = 1
+        x["draft"] = None
+        x["uniforms"] = None
+        run_pair(to_dev(x), dtype, True)
+
+
+def test_masks_and_large_k():
+    rng = np.random.default_rng(5)
+    for dtype in ("f32", "bf16"):
+        x = rand_case(rng, 5, 64, 300, dtype, 0.9, mask_frac=0.5)
+        run_pair(to_dev(x), dtype, False)
+
+
+def test_q_equals_p_and_disjoint_supports():
+    rng = np.random.default_rng(6)
+    x = rand_case(rng, 16, 5, 5000, "bf16", 1.0)
+    x["draft"] = x["target"][:, :5].clone()
+    x["uniforms"][:, :, 0] = 1.0 - 2.0 ** -24
+    st = run_pair(to_dev(x), "bf16", False)
+    res = tv.spec_verify(*(to_dev(x)[key] for key in ("target", "draft", "tokens", "uniforms")), 1.0, 0)
+    assert (res.accepted_len.cpu() == 5).all()
+    y = rand_case(rng, 16, 3, 5000, "f32", 1.0)
+    y["target"][:, :, 2500:] = -float("inf")
+    y["draft"][:, :, :2500] = -float("inf")
+    y["tokens"] = torch.from_numpy(rng.integers(2500, 5000, (16, 3)).astype(np.int32))
+    y["uniforms"][:, 0, 0] = 0.0
+    run_pair(to_dev(y), "f32", False)
+    res = tv.spec_verify(*(to_dev(y)[key] for key in ("target", "draft", "tokens", "uniforms")), 1.0, 0)
+    assert (res.accepted_len.cpu() == 0).all()
+    say(st)
+
+
+def test_invalid_rows():
+    rng = np.random.default_rng(7)
+    for dtype in ("f32", "bf16"):
+        x = rand_case(rng, 8, 3, 777, dtype, 1.0)
+        t = x["target"].float()
+        d = x["draft"].float()
+        t[0, 1, 3] = float("nan")
+        d[1, 0, 5] = float("inf")
+        t[2, 3, :] = -float("inf")
+        x["tokens"][3, 2] = 777
+        x["tokens"][4, 0] = -1
+        t[5, 0, :100] = -float("inf")
+        td = x["target"].dtype
+        x["target"], x["draft"] = t.to(td), d.to(td)
+        run_pair(to_dev(x), dtype, False)
+        g = dict(x)
+        g["mode"], g["draft"], g["uniforms"] = 1, None, None
+        run_pair(to_dev(g), dtype, True)
+
+
+def test_deterministic_and_exact_path():
+    w = workloads.WORKLOADS["b8_k5_v32000_f32"]
+    x = to_dev(workloads.make(w, 3))
+    a = tv.spec_verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], 0, return_probs=True)
+    torch.cuda.synchronize()
+    a = [t.clone() for t in a]
+    b = tv.spec_verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], 0, return_probs=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    os.environ["SPEC_VERIFY_FORCE_EXACT_PATH"] = "1"
+    try:
+        c = tv.spec_verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], 0, return_probs=True)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["SPEC_VERIFY_FORCE_EXACT_PATH"]
+    assert torch.equal(a[0], c.accepted_len)
+    assert torch.equal(a[1], c.out_tokens)
+
+
+def test_chi_square_on_gpu():
+    # 10^6 trials: x ~ q, u ~ U(0,1); the first emitted token is distributed as p.
+    from scipy import stats
+    from scipy.special import softmax
+    rng = np.random.default_rng(77)
+    V, n, T = 16, 1_000_000, 0.8
+    t0 = rng.normal(0, 1.5, (2, V)).astype(np.float32)
+    d0 = (t0[:1] * 0.7 + rng.normal(0, 1.0, (1, V))).astype(np.float32)
+    q = softmax(d0[0].astype(np.float64) / np.float64(np.float32(T)))
+    p = softmax(t0[0].astype(np.float64) / np.float64(np.float32(T)))
+    tok = torch.from_numpy(rng.choice(V, size=(n, 1), p=q).astype(np.int32)).to(DEV)
+    u = torch.from_numpy(rng.random((n, 2, 2)).astype(np.float32)).to(DEV)
+    tgt = torch.from_numpy(t0).to(DEV).expand(n, 2, V).contiguous()
+    dft = torch.from_numpy(d0).to(DEV).expand(n, 1, V).contiguous()
+    res = tv.spec_verify(tgt, dft, tok, u, T, 0)
+    counts = np.bincount(res.out_tokens[:, 0].cpu().numpy(), minlength=V)
+    _, pval = stats.chisquare(counts, p * n)
+    say("chi2 p-value", pval)
+    assert pval > 1e-3
+
+
+def test_noncontiguous_rejected_and_errors():
+    x = to_dev(rand_case(np.random.default_rng(8), 2, 2, 64, "f32", 1.0))
+    with pytest.raises(tv.SpecVerifyError) as e:
+        tv.spec_verify(x["target"], x["draft"], x["tokens"], x["uniforms"], 0.0, 0)
+    assert e.value.code == -5
+    with pytest.raises(tv.SpecVerifyError) as e:
+        tv.spec_verify(x["target"], None, x["tokens"], x["uniforms"], 1.0, 0)
+    assert e.value.code == -1

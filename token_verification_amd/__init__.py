@@ -1,0 +1,17 @@
+"""MI355X-native batched speculative-decoding verify step.
+
+The computation runs in ``libspecverify.so`` (hand-written HIP for gfx950, C ABI
+in ``include/spec_verify.h``). This package only marshals torch tensors into
+that ABI: it checks dtypes, shapes and devices, allocates the outputs and a
+cached workspace, and passes the current HIP stream. There is no fallback: if
+the library is not built, importing the binding raises.
+"""
+from .binding import (  # noqa: F401
+    GREEDY,
+    SAMPLE,
+    SpecVerifyError,
+    check_args,
+    lib,
+    spec_verify,
+    workspace_size,
+)

@@ -1,0 +1,162 @@
+"""ctypes binding of libspecverify.so (argument marshalling only).
+
+Every step of the verify computation runs in the HIP library; this module
+checks tensor dtypes/shapes/devices, allocates outputs, keeps one workspace
+per (device, stream), and passes raw device pointers plus the
+current stream to the C ABI declared in ``include/spec_verify.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import NamedTuple, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SAMPLE = 0
+GREEDY = 1
+F32 = 0
+BF16 = 1
+
+_ERRORS = {
+    -1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_DTYPE", -4: "SPEC_ERR_MODE",
+    -5: "SPEC_ERR_TEMP", -6: "SPEC_ERR_WORKSPACE", -7: "SPEC_ERR_ALIGN", -8: "SPEC_ERR_HIP",
+}
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """The loaded HIP library. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise SpecVerifyError(
+                        -8, f"{LIB_PATH} is missing: build it with `python -m token_verification_amd.build`")
+                L = ctypes.CDLL(LIB_PATH)
+                P, I, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+                L.spec_verify.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
+                                          P, P, P, P, P, P, S, P]
+                L.spec_verify.restype = ctypes.c_int
+                L.spec_verify_workspace_size.argtypes = [I, I, I, ctypes.c_int, ctypes.c_int]
+                L.spec_verify_workspace_size.restype = S
+                L.spec_verify_check_args.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
+                                                     P, P, P, P, S]
+                L.spec_verify_check_args.restype = ctypes.c_int
+                L.spec_verify_last_error.restype = ctypes.c_char_p
+                L.spec_verify_version.restype = ctypes.c_char_p
+                _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().spec_verify_last_error().decode()
+
+
+def workspace_size(B: int, k: int, V: int, dtype: int, mode: int) -> int:
+    return int(lib().spec_verify_workspace_size(B, k, V, dtype, mode))
+
+
+def check_args(target_ptr, draft_ptr, tokens_ptr, uniforms_ptr, temperature, mode, B, k, V, dtype,
+               acc_ptr, out_ptr, gap_ptr, ws_ptr, ws_bytes) -> int:
+    """Host-only argument check on raw pointer values (no HIP call)."""
+    return int(lib().spec_verify_check_args(target_ptr, draft_ptr, tokens_ptr, uniforms_ptr,
+                                            ctypes.c_float(temperature), mode, B, k, V, dtype,
+                                            acc_ptr, out_ptr, gap_ptr, ws_ptr, ws_bytes))
+
+
+class VerifyResult(NamedTuple):
+    accepted_len: torch.Tensor   # [B] int32
+    out_tokens: torch.Tensor     # [B, k+1] int32
+    gap: torch.Tensor            # [B, k+1] float32
+    target_prob: Optional[torch.Tensor]   # [B, k] float32 or None
+    draft_prob: Optional[torch.Tensor]
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
+                uniforms: Optional[torch.Tensor], temperature: float = 1.0, mode: int = SAMPLE, *,
+                workspace: Optional[torch.Tensor] = None, return_probs: bool = False,
+                out: Optional[VerifyResult] = None) -> VerifyResult:
+    """Batched verify step on device tensors (see include/spec_verify.h).
+
+    target [B,k+1,V] and draft [B,k,V] are float32 or bfloat16 (draft may be
+    None in greedy mode), tokens [B,k] int32, uniforms [B,k+1,2] float32 (None
+    allowed in greedy mode). Work is enqueued on the current stream of the
+    target's device; the returned tensors are ready once that stream is.
+    """
+    if not isinstance(target, torch.Tensor) or target.dim() != 3:
+        raise ValueError("target must be a [B, k+1, V] tensor")
+    if not target.is_cuda:
+        raise ValueError("target must be a device tensor")
+    if target.dtype == torch.float32:
+        dtype = F32
+    elif target.dtype == torch.bfloat16:
+        dtype = BF16
+    else:
+        raise ValueError(f"unsupported logit dtype {target.dtype}")
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if draft is not None:
+        if draft.shape != (B, k, V) or draft.dtype != target.dtype or draft.device != dev:
+            raise ValueError("draft must match target's dtype/device with shape [B, k, V]")
+    if tokens.shape != (B, k) or tokens.dtype != torch.int32 or tokens.device != dev:
+        raise ValueError("tokens must be int32 [B, k] on the target's device")
+    if uniforms is not None:
+        if uniforms.shape != (B, k + 1, 2) or uniforms.dtype != torch.float32 or uniforms.device != dev:
+            raise ValueError("uniforms must be float32 [B, k+1, 2] on the target's device")
+    for t in (target, draft, tokens, uniforms):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        otok = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+        gap = torch.empty((B, k + 1), dtype=torch.float32, device=dev)
+        tp = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+        dp = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+        out = VerifyResult(acc, otok, gap, tp, dp)
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = workspace_size(B, k, V, dtype, mode)
+    if need == 0:
+        raise SpecVerifyError(-2, f"unsupported sizes B={B} k={k} V={V}")
+    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    rc = lib().spec_verify(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms),
+                           ctypes.c_float(temperature), int(mode), B, k, V, dtype,
+                           _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
+                           _ptr(out.target_prob), _ptr(out.draft_prob),
+                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, last_error())
+    return out
