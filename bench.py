@@ -45,6 +45,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
+    ap.add_argument("--probe", choices=["copy", "sum"], default=None,
+                    help="instead of the verify step, time a plain 1 GiB device copy (or a "
+                         "read-only sum): achievable-bandwidth context and the known-size "
+                         "kernel used to calibrate HBM traffic counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -54,6 +58,9 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.probe:
+        return probe(args, torch, np)
 
     import token_verification_amd as tv
     import workloads
@@ -149,6 +156,31 @@ def main() -> int:
                                 "sample": f"{n} full calls of {name} (B={B}) on host copies, "
                                           f"{t_cpu:.1f} s of oracle time"}
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def probe(args, torch, np) -> int:
+    n = 1 << 30
+    dev = torch.device("cuda:0")
+    src = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
+    dst = torch.empty_like(src)
+    src16 = src.view(torch.bfloat16)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        if i >= args.warmup:
+            ev[i - args.warmup][0].record()
+        if args.probe == "copy":
+            dst.copy_(src)
+        else:
+            src16.sum(dtype=torch.float32)
+        if i >= args.warmup:
+            ev[i - args.warmup][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    moved = 2 * n if args.probe == "copy" else n
+    print(json.dumps({"probe": args.probe, "bytes_read": n, "bytes_written": n if args.probe == "copy" else 0,
+                      "ms": round(ms, 4), "GBps": round(moved / ms / 1e6, 1)}), flush=True)
     return 0
 
 

@@ -41,8 +41,8 @@ inline thread_local EmuIdx blockIdx{0, 0, 0};
 inline EmuIdx gridDim{1, 1, 1};
 inline EmuIdx blockDim{1, 1, 1};
 
-struct alignas(16) uint4 { unsigned x, y, z, w; };
-struct alignas(16) float4 { float x, y, z, w; };
+
+
 
 inline float __uint_as_float(unsigned u) { float f; memcpy(&f, &u, 4); return f; }
 inline int min(int a, int b) { return a < b ? a : b; }
@@ -55,6 +55,7 @@ inline float emu_exp2f(float x) { return exp2f(x); }
 #define __builtin_amdgcn_fmed3f emu_fmed3f
 #define __builtin_amdgcn_exp2f emu_exp2f
 #define __builtin_amdgcn_s_sleep(n) std::this_thread::yield()
+#define __builtin_amdgcn_sched_barrier(n) ((void)0)
 
 #define __HIP_MEMORY_SCOPE_AGENT 0
 #define __hip_atomic_fetch_add(p, v, o, s) __atomic_fetch_add((p), (v), (o))
@@ -181,6 +182,12 @@ inline int& emu_cu_count() { static int n = 1; return n; }
 inline hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
 inline hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = emu_cu_count(); return hipSuccess; }
 inline hipError_t hipGetLastError() { return hipSuccess; }
+inline int& emu_blocks_per_cu() { static int n = 8; return n; }
+template <class K>
+inline hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* n, K, int, size_t) {
+    *n = emu_blocks_per_cu();
+    return hipSuccess;
+}
 inline const char* hipGetErrorString(hipError_t) { return "emulated"; }
 inline hipError_t hipMemsetAsync(void* p, int v, size_t n, hipStream_t) { memset(p, v, n); return hipSuccess; }
 inline hipError_t hipMemcpy(void* d, const void* s, size_t n, hipMemcpyKind) { memcpy(d, s, n); return hipSuccess; }

@@ -43,9 +43,12 @@ def test_workspace_size():
     assert tv.workspace_size(1, 2, 100, 1, 3) == 0
     # greedy needs no pass-2 records
     assert tv.workspace_size(64, 5, 151936, 1, 1) < tv.workspace_size(64, 5, 151936, 1, 0)
-    for B, k, V in ((1, 0, 1), (3, 64, 7), (512, 8, 262144), (1, 4, 1 << 24)):
+    for B, k, V in ((1, 0, 1), (3, 64, 7), (512, 8, 262144), (1, 4, 1 << 23)):
         n = tv.workspace_size(B, k, V, 0, 0)
         assert n % 256 == 0 and n >= 256
+    # the sampling draw supports V up to 2^23; greedy mode has no such cap
+    assert tv.workspace_size(1, 4, (1 << 23) + 1, 1, 0) == 0
+    assert tv.workspace_size(1, 4, 1 << 24, 1, 1) > 0
 
 
 FAKE = 0x10000          # aligned fake device address (never dereferenced)

@@ -7,20 +7,22 @@
 //
 // Pipeline (stream-ordered kernels; no workgroup ever waits on another):
 //
-//  1. row_scan_kernel -- one workgroup per split of one logit row. 16-byte vector
-//     loads; per lane the top-2 raw logits (v_max/v_med3 on element pairs) and,
+//  1. row_scan_kernel -- one resident round of workgroups, each streaming an
+//     equal slice of the flattened (row, element) space (a slice may span row
+//     boundaries and emits one record per row segment). 16-byte vector loads,
+//     ping-pong pipelined; per lane the top-2 raw logits (v_max/v_med3 on pairs) and,
 //     in sampling mode, an online sum s = sum 2^(x*c - ref) with c = log2(e)/T in
 //     fp32 and an integer reference ref = ceil(max*c), so rescaling when the
-//     running max grows is an exact power-of-two ldexp. Lanes, waves and splits
+//     running max grows is an exact power-of-two ldexp. Lanes, waves and segments
 //     merge the same way. Greedy mode also finds the first index of the max.
-//  2. decide_kernel -- one workgroup per batch row: merges the splits of its
+//  2. decide_kernel -- one workgroup per batch row: merges the segments of its
 //     rows, writes the gaps, evaluates every acceptance test
 //     r_i = p_i(x_i)/q_i(x_i) in the log2 domain in fp64 from the pass-1 sums,
 //     finds the first rejection a and writes every output except the one token
 //     the sampling draw will produce.
 //  3. residual_chunk_kernel (sampling) -- the residual max(0, p_a - q_a), or the
 //     bonus p_k, is drawn by an inverse CDF that must resolve ~1e-13 of the mass
-//     at V ~ 10^5, so this pass is fp64 with the device's double exp. One
+//     at V ~ 10^5, so this pass is fp64 (table-driven double exp). One
 //     workgroup covers CHUNK elements of the selected row pair. The residual is
 //     linearised, w_x = (e_x - lambda f_x)/S_p with lambda = S_p/S_q, so a single
 //     read gives S_p, S_q and, over the elements whose sign is certain under
@@ -49,25 +51,33 @@ constexpr int NT = 256;                 // threads per workgroup (4 wave64)
 constexpr int NWAVE = NT / 64;
 constexpr int MAX_AMB = 4;              // band elements recorded per chunk
 constexpr int MAXC = 2048;              // max pass-2 chunks per row (LDS capacity)
-constexpr int MIN_CHUNK = 4096;         // pass-2 chunk length floor (elements)
+constexpr int CHUNK = 4096;             // pass-2 chunk length (elements)
+constexpr int EPT = CHUNK / NT;         // pass-2 elements per thread (contiguous)
+constexpr int MAX_V = MAXC * CHUNK;     // largest supported vocabulary
 constexpr double ETA = 1e-5;            // relative band around pass 1's lambda estimate
-constexpr int TARGET_TILES = 2048;      // pass-1 workgroup count the split heuristic aims at
-constexpr int MIN_TILE = 4096;          // pass-1 split floor (elements)
-constexpr int MAX_SPLITS = 64;
+constexpr int G_MAX = 16384;            // most pass-1 workgroups one launch uses
+constexpr int MIN_SLICE = 8192;         // smallest pass-1 slice (elements) worth a workgroup
 
 enum : int { K_TARGET = 0, K_DRAFT = 1, K_GREEDY = 2 };
 
 // ------------------------------------------------------------------ element types
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Each element type streams 16-byte vectors. stream() is a non-temporal load
+// (the logits are read once per call): on MI355X it sustains ~7 TB/s where
+// ordinary loads level off near 6.
 struct Bf16 {
     static constexpr int VE = 8;        // elements per 16-byte vector
     static constexpr int ES = 2;
-    using vec = uint4;
+    using vec = u32x4;
+    __device__ static inline vec stream(const vec* p) { return __builtin_nontemporal_load(p); }
     __device__ static inline float load1(const void* base, size_t i) {
         const unsigned short h = reinterpret_cast<const unsigned short*>(base)[i];
         return __uint_as_float(static_cast<unsigned>(h) << 16);
     }
-    __device__ static inline void unpack(const uint4& w, float (&x)[8]) {
+    __device__ static inline void unpack(const vec& w, float (&x)[8]) {
         x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
         x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
         x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xffff0000u);
@@ -78,11 +88,12 @@ struct Bf16 {
 struct F32 {
     static constexpr int VE = 4;
     static constexpr int ES = 4;
-    using vec = float4;
+    using vec = f32x4;
+    __device__ static inline vec stream(const vec* p) { return __builtin_nontemporal_load(p); }
     __device__ static inline float load1(const void* base, size_t i) {
         return reinterpret_cast<const float*>(base)[i];
     }
-    __device__ static inline void unpack(const float4& w, float (&x)[4]) {
+    __device__ static inline void unpack(const vec& w, float (&x)[4]) {
         x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
     }
 };
@@ -122,11 +133,15 @@ struct Params {
     float* gap;
     float* tprob;
     float* dprob;
-    int B, k, V, rpb, splits, tile_len, nchunk, chunk;
+    int B, k, V, rpb, nchunk, chunk;
+    int G;                     // pass-1 workgroups: one resident round
+    long long L;               // elements per pass-1 workgroup (last one may get fewer)
+    long long N;               // B * rpb * V: the flattened (row, element) space
     int mode, force_exact;
+    int vec_ok;                // rows start 16-byte aligned: pass 2 may use vector loads
     float c;                   // log2(e)/T (fp32), pass-1 exponent scale
     double invT;               // 1/T in double, pass 2
-    TileRec* tiles;            // [B*rpb*splits]
+    TileRec* tiles;            // [B*rpb + G] segment records, slot = row + workgroup
     RowRec* rows;              // [B*rpb]
     int* desc;                 // [B] row of the sampling draw, -1 = none
     double* lam_hat;           // [B] pass-1 estimate of S_p/S_q at that row
@@ -372,22 +387,49 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, float c, Red& R) {
     st.t1 = -INFINITY; st.t2 = -INFINITY; st.mref = -INFINITY; st.ref = 0.0f;
     st.s = 0.0; st.bvec = -1; st.nan = 0;
 
+    // Ping-pong pipelined body: while one batch of U vectors is consumed the
+    // next batch is in flight. Loads are never skipped by a branch (a batch past
+    // the end re-reads a valid address and is not consumed), so the compiler's
+    // wait counts stay exact instead of draining every load each iteration.
     constexpr int U = 4;
     int v = tid;
-    for (; v + (U - 1) * NT < nvec; v += U * NT) {
-        vec w[U];
+    const int step = U * NT;
+    auto batch_ok = [&](int at) { return at + (U - 1) * NT < nvec; };
+    vec A[U], Bv[U];
+    if (batch_ok(v)) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) w[u] = vp[v + u * NT];
+        for (int u = 0; u < U; ++u) A[u] = E::stream(vp + v + u * NT);
+    }
+    while (batch_ok(v)) {
+        const int v1 = v + step;
+        const int l1 = batch_ok(v1) ? v1 : v;
+#pragma unroll
+        for (int u = 0; u < U; ++u) Bv[u] = E::stream(vp + l1 + u * NT);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float x[VE];
-            E::unpack(w[u], x);
+            E::unpack(A[u], x);
             consume_vec<KIND, VE>(st, x, v + u * NT, c);
         }
+        v = v1;
+        if (!batch_ok(v)) break;
+        const int v2 = v + step;
+        const int l2 = batch_ok(v2) ? v2 : v;
+#pragma unroll
+        for (int u = 0; u < U; ++u) A[u] = E::stream(vp + l2 + u * NT);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[VE];
+            E::unpack(Bv[u], x);
+            consume_vec<KIND, VE>(st, x, v + u * NT, c);
+        }
+        v = v2;
     }
     for (; v < nvec; v += NT) {
         float x[VE];
-        E::unpack(vp[v], x);
+        E::unpack(E::stream(vp + v), x);
         consume_vec<KIND, VE>(st, x, v, c);
     }
 
@@ -433,27 +475,35 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, float c, Red& R) {
 template <class E, int MODE>
 __global__ __launch_bounds__(NT) void row_scan_kernel(Params P) {
     __shared__ Red R;
-    const int tile = blockIdx.x;
-    const int row = tile / P.splits;          // global row: b * rpb + j
-    const int sp = tile % P.splits;
-    const int b = row / P.rpb, j = row % P.rpb;
+    // Workgroup w owns the flattened elements [w*L, (w+1)*L) of all B*rpb rows,
+    // so every workgroup streams the same number of bytes and the grid is one
+    // resident round. It emits one record per row segment, in slot row + w.
+    const long long w = blockIdx.x;
+    const long long g0 = w * P.L;
+    const long long g1 = g0 + P.L < P.N ? g0 + P.L : P.N;
     const int k = P.k, V = P.V;
-    const bool is_target = j <= k;
-    const char* rowp;
-    if (is_target)
-        rowp = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + j) * V * E::ES;
-    else
-        rowp = static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + (j - k - 1)) * V * E::ES;
-    const int e0 = sp * P.tile_len;
-    const int e1 = min(V, e0 + P.tile_len);
-    TileRec tr;
-    if constexpr (MODE == SPEC_MODE_GREEDY) {
-        tr = tile_scan<E, K_GREEDY>(rowp, e0, e1, P.c, R);
-    } else {
-        if (is_target) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, P.c, R);
-        else tr = tile_scan<E, K_DRAFT>(rowp, e0, e1, P.c, R);
+    for (long long g = g0; g < g1;) {
+        const long long row = g / V;
+        const int e0 = static_cast<int>(g - row * V);
+        const long long rend = (row + 1) * V < g1 ? (row + 1) * V : g1;
+        const int e1 = static_cast<int>(rend - row * V);
+        const int b = static_cast<int>(row / P.rpb), j = static_cast<int>(row % P.rpb);
+        const bool is_target = j <= k;
+        const char* rowp;
+        if (is_target)
+            rowp = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + j) * V * E::ES;
+        else
+            rowp = static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + (j - k - 1)) * V * E::ES;
+        TileRec tr;
+        if constexpr (MODE == SPEC_MODE_GREEDY) {
+            tr = tile_scan<E, K_GREEDY>(rowp, e0, e1, P.c, R);
+        } else {
+            if (is_target) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, P.c, R);
+            else tr = tile_scan<E, K_DRAFT>(rowp, e0, e1, P.c, R);
+        }
+        if (threadIdx.x == 0) P.tiles[row + w] = tr;
+        g = rend;
     }
-    if (threadIdx.x == 0) P.tiles[tile] = tr;
 }
 
 // ------------------------------------------------------------------ decisions
@@ -473,20 +523,48 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     const int k = P.k, V = P.V, rpb = P.rpb;
     constexpr bool sample = MODE == SPEC_MODE_SAMPLE;
 
-    // merge the splits of every row of batch row b, in split order
+    // Independent loads first: the draft token of position tid, its uniform,
+    // and (as soon as the token is known to be in range) the two logits it
+    // picks; they overlap the merge of the split records below.
+    int x = -1;
+    bool inr = false;
+    double u0 = 0.0, lt = 0.0, ld = 0.0;
+    if (tid < k) {
+        x = P.tok[static_cast<size_t>(b) * k + tid];
+        inr = x >= 0 && x < V;
+        const size_t rowT = static_cast<size_t>(b) * (k + 1) + tid;
+        if constexpr (sample) {
+            u0 = P.uni[rowT * 2 + 0];
+            if (inr) {
+                lt = E::load1(P.tgt, rowT * V + x);
+                ld = E::load1(P.dft, (static_cast<size_t>(b) * k + tid) * V + x);
+            }
+        }
+    }
+
+    // merge the segments of every row of batch row b, in element order
     if (tid < rpb) {
         const size_t row = static_cast<size_t>(b) * rpb + tid;
-        const TileRec* t = P.tiles + row * P.splits;
-        TileRec m = t[0];
-        for (int q = 1; q < P.splits; ++q) {
-            const TileRec o = t[q];
-            const float prev = m.t1;
-            top2_merge(m.t1, m.t2, o.t1, o.t2);
-            if constexpr (MODE == SPEC_MODE_GREEDY) {
-                if (o.t1 > prev) m.idx = o.idx;          // earlier split wins ties
-                m.nan |= o.nan;
-            } else {
-                sref_merge(m.ref, m.s, o.ref, o.s);
+        // segments of this row, in element order: workgroups w0..w1, slot row + w
+        const long long r0 = static_cast<long long>(row) * V;
+        const long long w0 = r0 / P.L, w1 = (r0 + V - 1) / P.L;
+        const TileRec* t = P.tiles + row;
+        TileRec m = t[w0];
+        for (long long q0 = w0 + 1; q0 <= w1; q0 += 4) {
+            TileRec o[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) if (q0 + u <= w1) o[u] = t[q0 + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (q0 + u > w1) break;
+                const float prev = m.t1;
+                top2_merge(m.t1, m.t2, o[u].t1, o[u].t2);
+                if constexpr (MODE == SPEC_MODE_GREEDY) {
+                    if (o[u].t1 > prev) m.idx = o[u].idx;    // earlier segment wins ties
+                    m.nan |= o[u].nan;
+                } else {
+                    sref_merge(m.ref, m.s, o[u].ref, o[u].s);
+                }
             }
         }
         RowRec rr;
@@ -508,8 +586,6 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     int ok = 1;
     if (tid <= k) ok = D.rec[tid].valid;                  // target rows 0..k
     if (tid < k) {
-        const int x = P.tok[static_cast<size_t>(b) * k + tid];
-        const bool inr = x >= 0 && x < V;
         if (!inr) ok = 0;
         if (sample && !D.rec[k + 1 + tid].valid) ok = 0;
         int acc = 0;
@@ -518,17 +594,12 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
             const RowRec& rt = D.rec[tid];
             if constexpr (sample) {
                 const RowRec& rd = D.rec[k + 1 + tid];
-                const size_t rowT = static_cast<size_t>(b) * (k + 1) + tid;
-                const size_t rowD = static_cast<size_t>(b) * k + tid;
-                const double lt = E::load1(P.tgt, rowT * V + x);
-                const double ld = E::load1(P.dft, rowD * V + x);
                 const double c = P.c;
                 const double lp = lt == -INFINITY ? -INFINITY : lt * c - rt.ref - log2(rt.s);
                 const double lq = ld == -INFINITY ? -INFINITY : ld * c - rd.ref - log2(rd.s);
                 double r;
                 if (lq == -INFINITY) r = (lp == -INFINITY) ? 0.0 : INFINITY;
                 else r = exp2(lp - lq);
-                const double u0 = P.uni[rowT * 2 + 0];
                 acc = u0 < r;
                 pf = static_cast<float>(exp2(lp));
                 qf = static_cast<float>(exp2(lq));
@@ -553,7 +624,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     if (tid <= k) {
         int o;
         if (!valid) o = -1;
-        else if (tid < a) o = P.tok[static_cast<size_t>(b) * k + tid];
+        else if (tid < a) o = x;
         else if (tid == a) o = sample ? -1 : D.rec[a].idx;    // sampling: the draw kernel writes it
         else o = -1;
         P.out_tok[static_cast<size_t>(b) * (k + 1) + tid] = o;
@@ -579,6 +650,68 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
 
 // ------------------------------------------------------------------ pass 2
 
+// exp(x) for x <= 0 in double precision, by the table-driven method of
+// P. T. P. Tang ("Table-driven implementation of the exponential function in
+// IEEE floating-point arithmetic", ACM TOMS 15(2), 1989): write
+// x = (64 m + j) ln2/64 + r with |r| <= ln2/128, so exp(x) = 2^m 2^(j/64) e^r;
+// ln2/64 is split into a 36-bit head (so (64 m + j) * head is exact) and a
+// tail, and e^r - 1 is its Taylor polynomial of degree 6 (truncation below
+// r^7/7! < 3e-20). T[j] = 2^(j/64) is built per workgroup with the device
+// exp2. Total error is a few ulp. Inputs below -745 give 0 (also -inf).
+constexpr double EXP_INV_L = 0x1.71547652b82fep+6;    // 64 / ln 2
+constexpr double EXP_L1 = 0x1.62e42fefa0000p-7;       // ln 2 / 64, leading 36 bits
+constexpr double EXP_L2 = 0x1.cf79abc9e3b3ap-46;      // ln 2 / 64 - EXP_L1
+constexpr double EXP_C3 = 0x1.5555555555555p-3;       // 1/3!
+constexpr double EXP_C4 = 0x1.5555555555555p-5;       // 1/4!
+constexpr double EXP_C5 = 0x1.1111111111111p-7;       // 1/5!
+constexpr double EXP_C6 = 0x1.6c16c16c16c17p-10;      // 1/6!
+
+__device__ inline double exp_tab(double x, const double* T) {
+    if (!(x > -745.0)) return 0.0;
+    const double kf = rint(x * EXP_INV_L);
+    double r = fma(-kf, EXP_L1, x);
+    r = fma(-kf, EXP_L2, r);
+    const int k = static_cast<int>(kf);
+    double p = fma(r, EXP_C6, EXP_C5);
+    p = fma(r, p, EXP_C4);
+    p = fma(r, p, EXP_C3);
+    p = fma(r, p, 0.5);
+    p = fma(r, p, 1.0);
+    p *= r;
+    const double t = T[k & 63];
+    return ldexp(fma(t, p, t), k >> 6);
+}
+
+__device__ inline void exp_table_init(double* T) {
+    if (threadIdx.x < 64) T[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / 64.0);
+}
+
+// EPT contiguous elements [j0, j0 + EPT) of a row clipped to [.., hi): 16-byte
+// vector loads when the row is aligned and the run is whole, else element loads.
+// Elements at or past hi read as -inf (weight 0).
+template <class E>
+__device__ inline void load_run(const void* row, int j0, int hi, bool vec_ok, float (&x)[EPT]) {
+    constexpr int VE = E::VE;
+    if (vec_ok && j0 + EPT <= hi) {
+        const typename E::vec* vp =
+            reinterpret_cast<const typename E::vec*>(static_cast<const char*>(row) + static_cast<size_t>(j0) * E::ES);
+        typename E::vec w[EPT / VE];
+#pragma unroll
+        for (int u = 0; u < EPT / VE; ++u) w[u] = vp[u];
+#pragma unroll
+        for (int u = 0; u < EPT / VE; ++u) {
+            float y[VE];
+            E::unpack(w[u], y);
+#pragma unroll
+            for (int q = 0; q < VE; ++q) x[u * VE + q] = y[q];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < EPT; ++q)
+            x[q] = (j0 + q < hi) ? E::load1(row, static_cast<size_t>(j0) + q) : -INFINITY;
+    }
+}
+
 struct Pass2 {
     const void* rowT;
     const void* rowD;
@@ -602,29 +735,26 @@ __device__ inline Pass2 pass2_setup(const Params& P, int b, int a) {
     return Q;
 }
 
-template <class E>
-__device__ inline double pexp(const Pass2& Q, size_t j) {
-    const double x = E::load1(Q.rowT, j);
-    return exp((x - Q.mp) * Q.invT);
-}
-
-template <class E>
-__device__ inline double qexp(const Pass2& Q, size_t j) {
-    const double x = E::load1(Q.rowD, j);
-    return exp((x - Q.mq) * Q.invT);
-}
-
-template <class E>
-__device__ inline double weight(const Pass2& Q, size_t j) {
-    const double e = pexp<E>(Q, j);
+// Residual weight e - lambda f (clamped at 0), or e for the bonus draw, of one
+// element given its target and draft logits.
+__device__ inline double weight_of(const Pass2& Q, float xt, float xd, const double* T) {
+    const double e = exp_tab((static_cast<double>(xt) - Q.mp) * Q.invT, T);
     if (!Q.resid) return e;
-    const double f = qexp<E>(Q, j);
+    const double f = exp_tab((static_cast<double>(xd) - Q.mq) * Q.invT, T);
     const double w = e - Q.lam * f;
     return w > 0.0 ? w : 0.0;
 }
 
+template <class E>
+__device__ inline double weight_at(const Pass2& Q, int j, const double* T) {
+    const float xt = E::load1(Q.rowT, j);
+    const float xd = Q.resid ? E::load1(Q.rowD, j) : 0.0f;
+    return weight_of(Q, xt, xd, T);
+}
+
 struct ChunkLds {
     Red R;
+    double T[64];
     int namb;
     int amb[MAX_AMB];
 };
@@ -636,24 +766,30 @@ __global__ __launch_bounds__(NT) void residual_chunk_kernel(Params P) {
     const int b = blockIdx.x / P.nchunk, c = blockIdx.x % P.nchunk;
     const int a = P.desc[b];
     if (a < 0) return;                                     // uniform: whole block leaves
+    exp_table_init(S.T);
     if (tid == 0) S.namb = 0;
-    __syncthreads();
     const Pass2 Q = pass2_setup<E>(P, b, a);
     const double lh = P.lam_hat[b];
     const double hi_b = lh * (1.0 + ETA), lo_b = lh * (1.0 - ETA);
+    const int lo = c * CHUNK, hi = min(P.V, lo + CHUNK);
+    const int j0 = lo + tid * EPT;
+    float xt[EPT], xd[EPT];
+    load_run<E>(Q.rowT, j0, hi, P.vec_ok, xt);
+    if (Q.resid) load_run<E>(Q.rowD, j0, hi, P.vec_ok, xd);
+    __syncthreads();                                       // table ready
     double v[4] = {0.0, 0.0, 0.0, 0.0};
-    const int lo = c * P.chunk, hi = min(P.V, lo + P.chunk);
-    for (int j = lo + tid; j < hi; j += NT) {
-        const double e = pexp<E>(Q, j);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const double e = exp_tab((static_cast<double>(xt[q]) - Q.mp) * Q.invT, S.T);
         v[0] += e;
         if (Q.resid) {
-            const double f = qexp<E>(Q, j);
+            const double f = exp_tab((static_cast<double>(xd[q]) - Q.mq) * Q.invT, S.T);
             v[1] += f;
             if (e > 0.0) {
                 if (e > hi_b * f) { v[2] += e; v[3] += f; }
                 else if (e >= lo_b * f) {
                     const int slot = atomicAdd(&S.namb, 1);
-                    if (slot < MAX_AMB) S.amb[slot] = j;
+                    if (slot < MAX_AMB) S.amb[slot] = j0 + q;
                 }
             }
         }
@@ -672,6 +808,7 @@ __global__ __launch_bounds__(NT) void residual_chunk_kernel(Params P) {
 
 struct DrawLds {
     Red R;
+    double T[64];
     double mass[MAXC];
     double scan[NT];
     double base;
@@ -679,11 +816,11 @@ struct DrawLds {
 
 // Mass of chunk c recomputed element by element (whole block, ordered).
 template <class E>
-__device__ double chunk_exact(const Params& P, const Pass2& Q, int c, Red& R) {
-    const int lo = c * P.chunk, hi = min(P.V, lo + P.chunk);
+__device__ double chunk_exact(const Params& P, const Pass2& Q, int c, DrawLds& S) {
+    const int lo = c * CHUNK, hi = min(P.V, lo + CHUNK);
     double acc[1] = {0.0};
-    for (int j = lo + static_cast<int>(threadIdx.x); j < hi; j += NT) acc[0] += weight<E>(Q, j);
-    block_sum<1>(R, acc);
+    for (int j = lo + static_cast<int>(threadIdx.x); j < hi; j += NT) acc[0] += weight_at<E>(Q, j, S.T);
+    block_sum<1>(S.R, acc);
     return acc[0];
 }
 
@@ -696,14 +833,16 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
     if (a < 0) return;                                     // uniform: whole block leaves
     const int k = P.k, V = P.V, NC = P.nchunk;
     const ChunkRec* recs = P.chunks + static_cast<size_t>(b) * NC;
+    exp_table_init(S.T);
     Pass2 Q = pass2_setup<E>(P, b, a);
+    const double u1 = P.uni[(static_cast<size_t>(b) * (k + 1) + a) * 2 + 1];
+    const double lh = P.lam_hat[b];
 
     // exact normalisers
     double sums[2] = {0.0, 0.0};
     for (int c = tid; c < NC; c += NT) { sums[0] += recs[c].sp; sums[1] += recs[c].sq; }
-    block_sum<2>(S.R, sums);
+    block_sum<2>(S.R, sums);                               // also publishes the table
     Q.lam = Q.resid ? sums[0] / sums[1] : 0.0;
-    const double lh = P.lam_hat[b];
     const bool band_ok = !Q.resid ||
         (!P.force_exact && Q.lam >= lh * (1.0 - ETA) && Q.lam <= lh * (1.0 + ETA));
 
@@ -725,7 +864,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
                 for (int q = 0; q < n; ++q) id[q] = r.amb[q];
                 for (int x = 1; x < n; ++x)                // sort: fixed summation order
                     for (int y = x; y > 0 && id[y - 1] > id[y]; --y) { const int t = id[y]; id[y] = id[y - 1]; id[y - 1] = t; }
-                for (int q = 0; q < n; ++q) m += weight<E>(Q, id[q]);
+                for (int q = 0; q < n; ++q) m += weight_at<E>(Q, id[q], S.T);
             }
             M[c] = m;
         }
@@ -733,7 +872,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
         for (int c = 0; c < NC; ++c) {                    // rare: exact recompute
             if (M[c] != M[c]) {
                 __syncthreads();
-                const double m = chunk_exact<E>(P, Q, c, S.R);
+                const double m = chunk_exact<E>(P, Q, c, S);
                 if (tid == 0) M[c] = m;
                 __syncthreads();
             }
@@ -751,7 +890,6 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
             __syncthreads();
             continue;
         }
-        const double u1 = P.uni[(static_cast<size_t>(b) * (k + 1) + a) * 2 + 1];
         const double tgt = u1 * Z;
         // chunk holding the target
         int cstar = 0x7fffffff;
@@ -775,25 +913,31 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
             for (int c = c0; c < cstar; ++c) run += M[c];
             S.base = run;                                   // mass before c*
         }
-        __syncthreads();
-        const double base = S.base;
-        __syncthreads();
-        // rescan c* in element order: contiguous elements per thread
-        const int lo = cstar * P.chunk, hi = min(V, lo + P.chunk);
-        const int ept = (P.chunk + NT - 1) / NT;
-        const int j0 = min(hi, lo + tid * ept), j1 = min(hi, j0 + ept);
+        // rescan c* in element order: EPT contiguous elements per thread, kept in registers
+        const int lo = cstar * CHUNK, hi = min(V, lo + CHUNK);
+        const int j0 = lo + tid * EPT;
+        float xt[EPT], xd[EPT];
+        load_run<E>(Q.rowT, j0, hi, P.vec_ok, xt);
+        if (Q.resid) load_run<E>(Q.rowD, j0, hi, P.vec_ok, xd);
+        double w[EPT];
         double wsum = 0.0;
-        for (int j = j0; j < j1; ++j) wsum += weight<E>(Q, j);
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            w[q] = weight_of(Q, xt[q], Q.resid ? xd[q] : 0.0f, S.T);
+            wsum += w[q];
+        }
+        __syncthreads();                                    // S.base visible
+        const double base = S.base;
         double tot;
         const double wpre = block_exscan(S.scan, wsum, tot);
         int tok = 0x7fffffff, lastpos = -1;
         {
             double run = base + wpre;
-            for (int j = j0; j < j1; ++j) {
-                const double w = weight<E>(Q, j);
-                if (w > 0.0) lastpos = j;
-                run += w;
-                if (run > tgt) { tok = j; break; }
+#pragma unroll
+            for (int q = 0; q < EPT; ++q) {
+                if (w[q] > 0.0) lastpos = j0 + q;
+                run += w[q];
+                if (run > tgt && tok == 0x7fffffff) tok = j0 + q;
             }
         }
         tok = block_min(S.R, tok);
@@ -820,7 +964,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 struct Plan {
-    int rpb, splits, tile_len, nchunk, chunk;
+    int rpb, nchunk, chunk;
     size_t rows_total;
     // workspace offsets (bytes)
     size_t o_tiles, o_rows, o_desc, o_lam, o_chunks, total;
@@ -834,29 +978,17 @@ bool make_plan(int32_t B, int32_t k, int32_t V, int mode, Plan& p) {
     p.rpb = mode == SPEC_MODE_SAMPLE ? 2 * k + 1 : k + 1;
     p.rows_total = static_cast<size_t>(B) * p.rpb;
     if (p.rows_total > (1u << 26)) return false;
-    long want = (TARGET_TILES + static_cast<long>(p.rows_total) - 1) / static_cast<long>(p.rows_total);
-    long cap = V / MIN_TILE;
-    if (cap < 1) cap = 1;
-    if (want > cap) want = cap;
-    if (want > MAX_SPLITS) want = MAX_SPLITS;
-    if (want < 1) want = 1;
-    long tl = (V + want - 1) / want;
-    tl = (tl + 63) / 64 * 64;
-    p.tile_len = static_cast<int>(tl > V ? V : tl);
-    p.splits = static_cast<int>((V + p.tile_len - 1) / p.tile_len);
     if (mode == SPEC_MODE_SAMPLE) {
-        long ch = MIN_CHUNK;
-        if ((V + ch - 1) / ch > MAXC) ch = ((V + MAXC - 1) / MAXC + NT - 1) / NT * NT;
-        p.chunk = static_cast<int>(ch);
-        p.nchunk = static_cast<int>((V + ch - 1) / ch);
+        if (V > MAX_V) return false;
+        p.chunk = CHUNK;
+        p.nchunk = (V + CHUNK - 1) / CHUNK;
     } else {
         p.chunk = 0;
         p.nchunk = 0;
     }
-    if (p.rows_total * static_cast<size_t>(p.splits) > 0x7fffffffUL) return false;
     if (static_cast<size_t>(B) * static_cast<size_t>(p.nchunk) > 0x7fffffffUL) return false;
     size_t o = 0;
-    p.o_tiles = o; o = align256(o + p.rows_total * p.splits * sizeof(TileRec));
+    p.o_tiles = o; o = align256(o + (p.rows_total + G_MAX) * sizeof(TileRec));
     p.o_rows = o; o = align256(o + p.rows_total * sizeof(RowRec));
     p.o_desc = o; o = align256(o + static_cast<size_t>(B) * sizeof(int));
     p.o_lam = o; o = align256(o + static_cast<size_t>(B) * sizeof(double));
@@ -899,10 +1031,28 @@ int check(const void* tgt, const void* dft, const int32_t* tok, const float* uni
     return SPEC_OK;
 }
 
+// Resident workgroups per CU of the pass-1 kernel, cached per device.
 template <class E, int MODE>
-hipError_t launch_all(const Params& P, const Plan& plan, hipStream_t s) {
-    const unsigned tiles = static_cast<unsigned>(plan.rows_total * plan.splits);
-    hipLaunchKernelGGL((row_scan_kernel<E, MODE>), dim3(tiles), dim3(NT), 0, s, P);
+int scan_blocks_per_cu(int dev) {
+    static int cache[64] = {0};
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_scan_kernel<E, MODE>, NT, 0) != hipSuccess || n < 1)
+        n = 1;
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    return n;
+}
+
+template <class E, int MODE>
+hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
+    long long G = static_cast<long long>(ncu) * scan_blocks_per_cu<E, MODE>(dev);
+    const long long by_size = (P.N + MIN_SLICE - 1) / MIN_SLICE;
+    if (G > by_size) G = by_size;
+    if (G > G_MAX) G = G_MAX;
+    if (G < 1) G = 1;
+    P.L = (P.N + G - 1) / G;
+    P.G = static_cast<int>((P.N + P.L - 1) / P.L);
+    hipLaunchKernelGGL((row_scan_kernel<E, MODE>), dim3(P.G), dim3(NT), 0, s, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
@@ -957,28 +1107,36 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
     P.tprob = k > 0 ? target_prob : nullptr;
     P.dprob = k > 0 ? draft_prob : nullptr;
     P.B = B; P.k = k; P.V = V;
-    P.rpb = plan.rpb; P.splits = plan.splits; P.tile_len = plan.tile_len;
+    P.rpb = plan.rpb;
     P.nchunk = plan.nchunk; P.chunk = plan.chunk;
+    P.N = static_cast<long long>(plan.rows_total) * V;
+    P.G = 0; P.L = 0;
     P.mode = mode;
     const char* fe = getenv("SPEC_VERIFY_FORCE_EXACT_PATH");
     P.force_exact = (fe && fe[0] == '1') ? 1 : 0;
     const double Td = mode == SPEC_MODE_SAMPLE ? static_cast<double>(temperature) : 1.0;
     P.c = static_cast<float>(1.4426950408889634 / Td);
     P.invT = 1.0 / Td;
+    P.vec_ok = aligned(target_logits, 16) && (draft_logits == nullptr || aligned(draft_logits, 16)) &&
+               (static_cast<size_t>(V) * (dtype == SPEC_DTYPE_F32 ? 4 : 2)) % 16 == 0;
     P.tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
     P.rows = reinterpret_cast<RowRec*>(ws + plan.o_rows);
     P.desc = reinterpret_cast<int*>(ws + plan.o_desc);
     P.lam_hat = reinterpret_cast<double*>(ws + plan.o_lam);
     P.chunks = reinterpret_cast<ChunkRec*>(ws + plan.o_chunks);
 
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+        return fail(SPEC_ERR_HIP, "cannot query the current HIP device");
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == SPEC_DTYPE_BF16)
-        e = mode == SPEC_MODE_SAMPLE ? launch_all<Bf16, SPEC_MODE_SAMPLE>(P, plan, s)
-                                     : launch_all<Bf16, SPEC_MODE_GREEDY>(P, plan, s);
+        e = mode == SPEC_MODE_SAMPLE ? launch_all<Bf16, SPEC_MODE_SAMPLE>(P, dev, ncu, s)
+                                     : launch_all<Bf16, SPEC_MODE_GREEDY>(P, dev, ncu, s);
     else
-        e = mode == SPEC_MODE_SAMPLE ? launch_all<F32, SPEC_MODE_SAMPLE>(P, plan, s)
-                                     : launch_all<F32, SPEC_MODE_GREEDY>(P, plan, s);
+        e = mode == SPEC_MODE_SAMPLE ? launch_all<F32, SPEC_MODE_SAMPLE>(P, dev, ncu, s)
+                                     : launch_all<F32, SPEC_MODE_GREEDY>(P, dev, ncu, s);
     if (e != hipSuccess) return fail(SPEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return SPEC_OK;
 }
