@@ -36,6 +36,26 @@ def algorithmic_bytes(w) -> int:
     return rows * V * s + small + outs
 
 
+def counter_traffic(name: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None
+    when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    summary = os.path.join(ROOT, "profiles", f"spec_verify_{name}.md")
+    src = os.path.join(ROOT, "token_verification_amd", "csrc", "spec_verify.hip")
+    if not os.path.exists(summary):
+        return None
+    fields = {}
+    for line in open(summary):
+        if ":" in line and line.split(":")[0] in ("source_sha256", "traffic_bytes_per_call"):
+            key, val = line.split(":", 1)
+            fields[key] = val.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "traffic_bytes_per_call" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_call"])
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,7 +154,7 @@ def main() -> int:
                       "p90": round(float(np.percentile(kms, 90)) * 1e3, 2)},
         "positions_per_s_kernel": round(positions / (k_avg * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(name),
                      "algorithmic_bytes_per_launch": alg,
                      "bytes_per_position": round(alg / positions, 1)},
     }
