@@ -45,11 +45,11 @@
  * entries, probability 0).
  *
  * Workspace: caller-owned device memory of at least spec_verify_workspace_size() bytes
- * (256-byte aligned). It carries the per-row and per-chunk records that one kernel of
- * the call hands to the next; every record is written before it is read, so the
- * workspace needs no initialisation and may be reused freely. One workspace serves one
- * call at a time: calls that overlap in time (e.g. on two streams) need separate
- * workspaces.
+ * (256-byte aligned). It carries the per-segment, per-batch-row and per-chunk records
+ * that one kernel of the call hands to the next; every record is written before it is
+ * read, so the workspace needs no initialisation and may be reused freely. One
+ * workspace serves one call at a time: calls that overlap in time (e.g. on two
+ * streams) need separate workspaces.
  *
  * Execution: spec_verify only enqueues work on `stream` (a hipStream_t; NULL = the null
  * stream) and returns; completion is observed by synchronising that stream. It performs
@@ -80,7 +80,7 @@ extern "C" {
 #define SPEC_OK 0
 #define SPEC_ERR_NULL (-1)      /* a required pointer is NULL                                   */
 #define SPEC_ERR_SHAPE (-2)     /* B < 1, k outside [0, SPEC_MAX_K], V < 1, V > SPEC_MAX_V_SAMPLE
-                                   in SAMPLE mode, or a size overflow                           */
+                                   in SAMPLE mode, V > 2^29, or a size overflow                 */
 #define SPEC_ERR_DTYPE (-3)     /* dtype is not SPEC_DTYPE_F32 / SPEC_DTYPE_BF16                */
 #define SPEC_ERR_MODE (-4)      /* mode is not SPEC_MODE_SAMPLE / SPEC_MODE_GREEDY              */
 #define SPEC_ERR_TEMP (-5)      /* SAMPLE mode with a temperature that is not finite and > 0    */

@@ -76,7 +76,9 @@ class RefResult:
     q_tok: np.ndarray          # [B,k] float64
     margin_acc: np.ndarray     # [B] float64, +inf where no test was taken
     margin_cdf: np.ndarray     # [B] float64, +inf where no draw was taken
-    flags: np.ndarray          # [B] int32, bit 0: residual mass was zero
+    flags: np.ndarray          # [B] int32, bit 0: residual mass was zero; bit 1: the
+                               # residual draw is within 1e-13 (of p's total mass) of a
+                               # CDF boundary, below what fp64 resolves
 
     def flagged(self, delta_acc: float, delta_cdf: float) -> np.ndarray:
         return (self.margin_acc < delta_acc) | (self.margin_cdf < delta_cdf) | (self.flags != 0)

@@ -152,11 +152,12 @@ static int ref_argmax(const void* base, int dtype, size_t off, int V)
  * the smallest j with C_j > u*Z. Returns -1 when Z <= 0. *margin receives the
  * normalized distance of u to the chosen interval's nearest edge.
  */
-static int ref_inverse_cdf(const double* w, int V, double u, double* margin)
+static int ref_inverse_cdf(const double* w, int V, double u, double* margin, double* Zout)
 {
     ref_sum_t acc = {0.0, 0.0};
     for (int x = 0; x < V; ++x) ref_sum_add(&acc, w[x]);
     double Z = ref_sum_value(&acc);
+    *Zout = Z;
     if (!(Z > 0.0)) return -1;
     double t = u * Z;
     ref_sum_t C = {0.0, 0.0};
@@ -183,8 +184,19 @@ static void ref_fill_invalid(int k, int32_t* acc_len, int32_t* out)
 }
 
 /*
+ * Smallest distance, in units of the target distribution's total mass, between
+ * the residual draw's point u*Z and a CDF boundary that fp64 can resolve. The
+ * residual weights max(0, p - q) are differences of two probability vectors,
+ * so any double-precision evaluation of them (this one included) carries
+ * absolute errors of order 1e-15 of the total mass; a draw closer than this to
+ * a boundary is flagged (bit 2), whatever its distance relative to Z.
+ */
+#define REF_RESID_ABS_MARGIN 1e-13
+
+/*
  * One batch row. work must hold 3*V doubles.
- * Returns a bit set: 1 = Z fell back to p_a (flag).
+ * Returns a bit set: 1 = Z fell back to p_a, 2 = the residual draw is within
+ * REF_RESID_ABS_MARGIN of a CDF boundary (both are flags).
  */
 static int ref_one_row(const void* target, const void* draft, const int32_t* tokens,
                        const float* uniforms, double T, int mode, int k, int V, int dtype,
@@ -258,20 +270,23 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
     double u1 = (double)uniforms[(b * rowsT + (size_t)a) * 2 + 1];
     ref_softmax(target, dtype, (b * rowsT + (size_t)a) * (size_t)V, V, T, p);
     int tok;
+    double Z;
     if (a < k) {
         ref_softmax(draft, dtype, (b * rowsD + (size_t)a) * (size_t)V, V, T, q);
         for (int x = 0; x < V; ++x) {
             double d = p[x] - q[x];
             w[x] = d > 0.0 ? d : 0.0;
         }
-        tok = ref_inverse_cdf(w, V, u1, m_cdf);
+        tok = ref_inverse_cdf(w, V, u1, m_cdf, &Z);
         if (tok < 0) {                        /* Z = 0: draw from p_a, flag */
             flags |= 1;
-            tok = ref_inverse_cdf(p, V, u1, m_cdf);
+            tok = ref_inverse_cdf(p, V, u1, m_cdf, &Z);
             *m_cdf = 0.0;
+        } else if (*m_cdf * Z < REF_RESID_ABS_MARGIN) {
+            flags |= 2;
         }
     } else {
-        tok = ref_inverse_cdf(p, V, u1, m_cdf);
+        tok = ref_inverse_cdf(p, V, u1, m_cdf, &Z);
     }
     out[a] = tok;
     return flags;

@@ -55,7 +55,34 @@ inline float emu_exp2f(float x) { return exp2f(x); }
 #define __builtin_amdgcn_fmed3f emu_fmed3f
 #define __builtin_amdgcn_exp2f emu_exp2f
 #define __builtin_amdgcn_s_sleep(n) std::this_thread::yield()
+
+// raw buffer loads: base + byte range; a load past the range reads zeros
+typedef unsigned emu_u32x4 __attribute__((ext_vector_type(4)));
+struct EmuRsrc { const char* base; unsigned bytes; };
+#define __amdgpu_buffer_rsrc_t EmuRsrc
+inline EmuRsrc emu_make_rsrc(void* p, int, int bytes, int) {
+    return EmuRsrc{static_cast<const char*>(p), static_cast<unsigned>(bytes)};
+}
+inline emu_u32x4 emu_raw_load_b128(EmuRsrc r, int voff, int soff, int) {
+    const unsigned off = static_cast<unsigned>(voff) + static_cast<unsigned>(soff);
+    emu_u32x4 v = {0u, 0u, 0u, 0u};
+    if (static_cast<unsigned long long>(off) + 16ull <= r.bytes) memcpy(&v, r.base + off, 16);
+    return v;
+}
+#define __builtin_amdgcn_make_buffer_rsrc emu_make_rsrc
+#define __builtin_amdgcn_raw_buffer_load_b128 emu_raw_load_b128
+
+inline int __double2loint(double d) { uint64_t u; memcpy(&u, &d, 8); return static_cast<int>(static_cast<uint32_t>(u)); }
+inline int __double2hiint(double d) { uint64_t u; memcpy(&u, &d, 8); return static_cast<int>(static_cast<uint32_t>(u >> 32)); }
+inline double __hiloint2double(int hi, int lo) {
+    const uint64_t u = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+    double d; memcpy(&d, &u, 8); return d;
+}
 #define __builtin_amdgcn_sched_barrier(n) ((void)0)
+#define __builtin_amdgcn_s_waitcnt(n) __atomic_thread_fence(__ATOMIC_SEQ_CST)
+#define __builtin_amdgcn_fence(...) __atomic_thread_fence(__ATOMIC_SEQ_CST)
+#define __builtin_amdgcn_s_barrier() __syncthreads()
+#define __builtin_amdgcn_readfirstlane(x) (x)
 
 #define __HIP_MEMORY_SCOPE_AGENT 0
 #define __hip_atomic_fetch_add(p, v, o, s) __atomic_fetch_add((p), (v), (o))
@@ -99,6 +126,20 @@ inline T __shfl_xor(T v, int mask, int width = 64) {
     emu_yield();
     T r;
     memcpy(&r, w->shfl[base + (lane ^ static_cast<unsigned>(mask))], sizeof(T));
+    emu_yield();
+    return r;
+}
+
+template <class T>
+inline T __shfl_up(T v, unsigned delta, int width = 64) {
+    (void)width;
+    EmuWG* w = emu_wg;
+    const unsigned me = threadIdx.x;
+    const unsigned base = me & ~63u, lane = me & 63u;
+    memcpy(w->shfl[me], &v, sizeof(T));
+    emu_yield();
+    T r;
+    memcpy(&r, w->shfl[lane >= delta ? base + lane - delta : me], sizeof(T));
     emu_yield();
     return r;
 }

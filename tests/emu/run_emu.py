@@ -153,6 +153,21 @@ def odd_shapes():
 
 
 @case
+def masks_large_k():
+    # -inf entries (probability 0) in half of every row, k at its maximum
+    rng = np.random.default_rng(4)
+    for dtype, T in ((0, 0.9), (1, 1.3), (1, 1.0)):
+        x = rand_case(rng, 3, 64, 300, dtype, T)
+        for key in ("target", "draft"):
+            t = x[key].float()
+            m = torch.from_numpy(rng.random(tuple(t.shape)) < 0.5)
+            t[m] = -float("inf")
+            t[:, :, 0] = 0.0
+            x[key] = t.to(x[key].dtype)
+        run_case(x, cus=2)
+
+
+@case
 def greedy_bf16():
     rng = np.random.default_rng(2)
     run_case(rand_case(rng, 6, 3, 20000, 1, 1.0, mode=1, coarse=True), cus=2)

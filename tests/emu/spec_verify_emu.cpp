@@ -6,13 +6,17 @@ extern "C" void spec_verify_emu_set_cu_count(int n) { emu_cu_count() = n; }
 extern "C" void spec_verify_emu_set_pool(int n) { emu_pool() = n; }
 
 // The table-driven double exp of pass 2, evaluated on the host with the same
-// 2^(j/64) table construction, for accuracy tests against libm.
+// 2^(j/N) table construction, for accuracy tests against libm.
 extern "C" double spec_verify_emu_exp(double x) {
-    static double T[64];
+    static double T[EXP_N];
     static bool init = false;
     if (!init) {
-        for (int j = 0; j < 64; ++j) T[j] = exp2(static_cast<double>(j) / 64.0);
+        for (int j = 0; j < EXP_N; ++j) T[j] = exp2(static_cast<double>(j) / EXP_N);
         init = true;
     }
-    return exp_tab(x, T);
+    return exp_fast(x, T);
 }
+
+// The lean double log2 / exp2 of the decisions, for accuracy tests against libm.
+extern "C" double spec_verify_emu_log2(double x) { return log2_lean(x); }
+extern "C" double spec_verify_emu_exp2(double x) { return exp2_lean(x); }

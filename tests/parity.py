@@ -10,7 +10,12 @@ except rows the oracle flags as near-ties:
     mass, so about 11% of rows would be flagged. The GPU computes this draw in
     double precision (normalized CDF error ~1e-15), so 1e-12 is used; the
     literal-threshold fraction is reported next to it.
-  * rows whose residual mass rounded to zero (oracle flag bit 0).
+  * rows whose residual mass rounded to zero (oracle flag bit 0), and rows
+    whose residual draw lies within 1e-13 of the target's total mass of a CDF
+    boundary (flag bit 1): the residual max(0, p - q) is a difference of two
+    probability vectors, so every fp64 evaluation of it carries absolute
+    errors near 1e-15, and such a draw is decided by rounding (this happens
+    when p and q nearly coincide, e.g. both one-hot at a low temperature).
 Flagged rows must stay at or below MAX_FLAG_FRACTION (0.01% of rows) in
 aggregate over the seeds of a workload.
 

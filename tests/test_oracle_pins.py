@@ -359,3 +359,26 @@ def test_argument_errors():
         run(t, np.zeros((1, 1, 4)), [[0]], np.zeros((1, 2, 2)), T=0.0)
     with pytest.raises(ValueError):
         run(t, np.zeros((1, 1, 4)), [[0]], np.zeros((1, 2, 2)), T=float("nan"))
+
+
+def test_residual_below_fp64_resolution_is_flagged():
+    # Two nearly one-hot distributions on the same token (T = 0.05): the exact
+    # residual mass max(0, p - q) is ~1e-17 of p's total mass, below what fp64
+    # can resolve in p - q, so the draw is flagged (bit 1). An ordinary pair
+    # (residual mass ~0.4) is not.
+    t = np.array([[[0.3046875, 0.36328125, -0.20019531, 0.0390625, -0.27734375, -3.140625, 2.546875],
+                   [0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0]]], np.float32)
+    d = np.array([[[1.0078125, -0.640625, -1.125, 0.6015625, -1.0859375, -2.546875, 2.953125]]], np.float32)
+    tok = np.array([[0]], np.int32)
+    u = np.array([[[0.21016294, 0.44941747], [0.5, 0.5]]], np.float32)
+    r = oracle.spec_verify_ref(t, d, tok, u, 0.05, oracle.SAMPLE)
+    assert r.accepted_len[0] == 0
+    assert r.flags[0] & 2
+    rng = np.random.default_rng(11)
+    t2 = rng.normal(0, 2, (1, 2, 50)).astype(np.float32)
+    d2 = (t2[:, :1] + rng.normal(0, 1, (1, 1, 50))).astype(np.float32)
+    u2 = np.array([[[0.999, 0.3], [0.5, 0.5]]], np.float32)   # u = 0.999 rejects
+    r2 = oracle.spec_verify_ref(t2, d2, np.array([[int(np.argmax(d2[0, 0]))]], np.int32), u2, 1.0, oracle.SAMPLE)
+    if r2.accepted_len[0] == 0:
+        assert r2.flags[0] == 0
+

@@ -91,6 +91,8 @@ _ws_cache: dict = {}
 
 
 def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    """One workspace per (device, stream); every record in it is written before
+    it is read, so it needs no initialisation."""
     key = (device.index, stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -5,32 +5,35 @@
 // greedy argmax matching of "The Inference Wall" part 7; the top-1 minus top-2
 // logit gap of "Speculative Pre-Positioning", Eq. 11).
 //
-// Pipeline (stream-ordered kernels; no workgroup ever waits on another):
+// Four stream-ordered kernels per call; no workgroup ever waits on another
+// (every hand-over between them is a kernel boundary).
 //
-//  1. row_scan_kernel -- one resident round of workgroups, each streaming an
-//     equal slice of the flattened (row, element) space (a slice may span row
-//     boundaries and emits one record per row segment). 16-byte vector loads,
-//     ping-pong pipelined; per lane the top-2 raw logits (v_max/v_med3 on pairs) and,
-//     in sampling mode, an online sum s = sum 2^(x*c - ref) with c = log2(e)/T in
-//     fp32 and an integer reference ref = ceil(max*c), so rescaling when the
-//     running max grows is an exact power-of-two ldexp. Lanes, waves and segments
-//     merge the same way. Greedy mode also finds the first index of the max.
+//  1. scan_kernel -- one resident round of workgroups, each streaming an equal
+//     slice of the flattened (row, element) space (a slice may span row
+//     boundaries and emits one record per row segment). 16-byte non-temporal
+//     buffer loads, ping-pong pipelined; per lane the top-2 raw logits
+//     (v_max/v_med3 on pairs) and, in sampling mode, an online sum
+//     s = sum 2^(x*c - ref) with c = log2(e)/T split into fp32 head and tail
+//     (so the rounding of c to fp32 cannot shift p/q) and an integer reference
+//     ref = ceil(max*c), so rescaling when the running max grows is an exact
+//     power-of-two ldexp. The lane whose vector holds the row's draft token
+//     keeps that logit. Greedy mode also finds the first index of the max.
 //  2. decide_kernel -- one workgroup per batch row: merges the segments of its
 //     rows, writes the gaps, evaluates every acceptance test
-//     r_i = p_i(x_i)/q_i(x_i) in the log2 domain in fp64 from the pass-1 sums,
-//     finds the first rejection a and writes every output except the one token
-//     the sampling draw will produce.
-//  3. residual_chunk_kernel (sampling) -- the residual max(0, p_a - q_a), or the
-//     bonus p_k, is drawn by an inverse CDF that must resolve ~1e-13 of the mass
-//     at V ~ 10^5, so this pass is fp64 (table-driven double exp). One
+//     r_i = p_i(x_i)/q_i(x_i) in the log2 domain in fp64, finds the first
+//     rejection a and writes every output except the token the sampling draw
+//     will produce.
+//  3. chunk_kernel (sampling) -- the residual max(0, p_a - q_a), or the bonus
+//     p_k, is drawn by an inverse CDF that must resolve ~1e-13 of the mass at
+//     V ~ 10^5, so this pass is fp64 (branch-free table-driven double exp). One
 //     workgroup covers CHUNK elements of the selected row pair. The residual is
 //     linearised, w_x = (e_x - lambda f_x)/S_p with lambda = S_p/S_q, so a single
 //     read gives S_p, S_q and, over the elements whose sign is certain under
 //     pass 1's estimate of lambda (relative band ETA), the sums E, F; elements
 //     inside the band are recorded by index and settled once lambda is exact.
 //  4. draw_kernel (sampling) -- one workgroup per batch row: exact lambda, chunk
-//     masses, ordered block scan to the chunk holding u*Z, fp64 rescan of that
-//     chunk in vocabulary order.
+//     masses, ordered scan to the chunk holding u*Z, fp64 rescan of that chunk
+//     in vocabulary order.
 //
 // Every reduction uses a fixed order, so results are bitwise reproducible.
 
@@ -49,14 +52,17 @@ namespace {
 
 constexpr int NT = 256;                 // threads per workgroup (4 wave64)
 constexpr int NWAVE = NT / 64;
-constexpr int MAX_AMB = 4;              // band elements recorded per chunk
-constexpr int MAXC = 2048;              // max pass-2 chunks per row (LDS capacity)
-constexpr int CHUNK = 4096;             // pass-2 chunk length (elements)
-constexpr int EPT = CHUNK / NT;         // pass-2 elements per thread (contiguous)
+constexpr int MAX_AMB = 4;              // band elements recorded per chunk (the draw sorts 4)
+constexpr int NT2 = 512;                // threads per pass-2 workgroup (8 wave64)
+constexpr int MAXC = 1024;              // max pass-2 chunks per row (LDS capacity)
+constexpr int CHUNK = 8192;             // pass-2 chunk length (elements)
 constexpr int MAX_V = MAXC * CHUNK;     // largest supported vocabulary
 constexpr double ETA = 1e-5;            // relative band around pass 1's lambda estimate
 constexpr int G_MAX = 16384;            // most pass-1 workgroups one launch uses
 constexpr int MIN_SLICE = 8192;         // smallest pass-1 slice (elements) worth a workgroup
+constexpr int EXP_N = 1024;             // entries of the 2^(j/N) table of the fp64 exp
+constexpr unsigned TAB_BASE = 103u << 7;  // bf16 magnitude bits of 2^-24 (start of the value table)
+constexpr int TAB_MAX = 8192;           // value-table entries: two signs of at most 32 binades of 128
 
 enum : int { K_TARGET = 0, K_DRAFT = 1, K_GREEDY = 2 };
 
@@ -65,14 +71,13 @@ enum : int { K_TARGET = 0, K_DRAFT = 1, K_GREEDY = 2 };
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Each element type streams 16-byte vectors. stream() is a non-temporal load
-// (the logits are read once per call): on MI355X it sustains ~7 TB/s where
-// ordinary loads level off near 6.
+// Each element type streams 16-byte vectors (pass 1 loads them non-temporal:
+// the logits are read once per call, and on MI355X non-temporal 16-byte loads
+// sustain ~7 TB/s where ordinary loads level off near 6).
 struct Bf16 {
     static constexpr int VE = 8;        // elements per 16-byte vector
     static constexpr int ES = 2;
     using vec = u32x4;
-    __device__ static inline vec stream(const vec* p) { return __builtin_nontemporal_load(p); }
     __device__ static inline float load1(const void* base, size_t i) {
         const unsigned short h = reinterpret_cast<const unsigned short*>(base)[i];
         return __uint_as_float(static_cast<unsigned>(h) << 16);
@@ -89,7 +94,6 @@ struct F32 {
     static constexpr int VE = 4;
     static constexpr int ES = 4;
     using vec = f32x4;
-    __device__ static inline vec stream(const vec* p) { return __builtin_nontemporal_load(p); }
     __device__ static inline float load1(const void* base, size_t i) {
         return reinterpret_cast<const float*>(base)[i];
     }
@@ -100,20 +104,29 @@ struct F32 {
 
 // ------------------------------------------------------------------ workspace records
 
-struct alignas(32) TileRec {   // one split of one row
+struct alignas(32) TileRec {   // one segment of one row
     float t1, t2, ref;
     int idx;                   // greedy: row index of the first maximum (INT_MAX if none)
     double s;                  // sampling: sum 2^(x*c - ref)
-    int nan;                   // greedy: a NaN was seen
-    int pad;
+    float lx;                  // sampling: the row's draft-token logit, if in this segment
+    int flags;                 // bit 0: a NaN was seen (greedy); bit 1: lx is set
 };
 
-struct alignas(32) RowRec {
-    float m, t2, ref;
+struct RowRec {
+    float m, t2;
     int idx;
-    double s;
     int valid;
+    double lg;                 // sampling: log2 of the row's normaliser sum 2^(x*c)
+    float lx;                  // sampling: the draft-token logit (draft-token rows)
+    int has_lx;
+};
+
+struct alignas(32) BatchRec {  // what pass 2 needs of one batch row
+    int a;                     // row of the draw (k = bonus), -1 = no draw (invalid row)
     int pad;
+    float mp, mq;              // max raw logit of target row a and (a < k) draft row a
+    double lam;                // pass-1 estimate of S_p/S_q at row a (a < k)
+    double pad2;
 };
 
 struct alignas(64) ChunkRec {
@@ -133,19 +146,23 @@ struct Params {
     float* gap;
     float* tprob;
     float* dprob;
-    int B, k, V, rpb, nchunk, chunk;
+    int B, k, V, rpb, nchunk;
     int G;                     // pass-1 workgroups: one resident round
     long long L;               // elements per pass-1 workgroup (last one may get fewer)
     long long N;               // B * rpb * V: the flattened (row, element) space
     int mode, force_exact;
     int vec_ok;                // rows start 16-byte aligned: pass 2 may use vector loads
-    float c;                   // log2(e)/T (fp32), pass-1 exponent scale
+    float ch, cl;              // log2(e)/T = ch + cl (fp32 head, fp32 tail), pass-1 exponent scale
+    double c;                  // ch + cl in double: the scale the decisions use
     double invT;               // 1/T in double, pass 2
     TileRec* tiles;            // [B*rpb + G] segment records, slot = row + workgroup
-    RowRec* rows;              // [B*rpb]
-    int* desc;                 // [B] row of the sampling draw, -1 = none
-    double* lam_hat;           // [B] pass-1 estimate of S_p/S_q at that row
+    BatchRec* bat;             // [B]
     ChunkRec* chunks;          // [B*nchunk]
+    double* exptab;            // [EXP_N] 2^(j/EXP_N), written by pass 1 for pass 2
+    double* tautab;            // [2*tab_range] exp(v/T - tab_c) of bf16 values v, written by pass 1
+    int tab_range;             // bf16 table entries per sign (0: no table)
+    double tab_lim;            // the table covers 2^-24 <= |v| < tab_lim
+    double tab_c;
 };
 
 // ------------------------------------------------------------------ small helpers
@@ -192,14 +209,26 @@ __device__ inline int wave_max(int v) {
 
 // ------------------------------------------------------------------ block reductions
 
-struct Red {
-    float t1[NWAVE], t2[NWAVE], ref[NWAVE];
-    double s[NWAVE];
-    int i[NWAVE];
-    int j[NWAVE];
-    double d[4][NWAVE];
+// Workgroup barrier that orders LDS accesses only (every hand-over between the
+// threads of a workgroup goes through LDS): global loads stay in flight across
+// it instead of being drained, so a prefetch survives the reductions.
+__device__ inline void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// LDS of the block reductions of a workgroup of NW waves.
+template <int NW>
+struct RedT {
+    float t1[NW], t2[NW], ref[NW];
+    double s[NW];
+    int i[NW];
+    int j[NW];
+    double d[4][NW];
     float bt1, bt2;
 };
+using Red = RedT<NWAVE>;
 
 // Block top-2 of (t1, t2): every thread returns the block's top-2.
 __device__ void block_top2(Red& R, float& t1, float& t2) {
@@ -209,15 +238,15 @@ __device__ void block_top2(Red& R, float& t1, float& t2) {
         top2_merge(t1, t2, o1, o2);
     }
     if (lane == 0) { R.t1[w] = t1; R.t2[w] = t2; }
-    __syncthreads();
+    lds_sync();
     if (threadIdx.x == 0) {
         float a1 = R.t1[0], a2 = R.t2[0];
         for (int q = 1; q < NWAVE; ++q) top2_merge(a1, a2, R.t1[q], R.t2[q]);
         R.bt1 = a1; R.bt2 = a2;
     }
-    __syncthreads();
+    lds_sync();
     t1 = R.bt1; t2 = R.bt2;
-    __syncthreads();
+    lds_sync();
 }
 
 // Block merge of (ref, s); result valid in thread 0.
@@ -229,71 +258,85 @@ __device__ void block_sref(Red& R, float& ref, double& s) {
         sref_merge(ref, s, orf, os);
     }
     if (lane == 0) { R.ref[w] = ref; R.s[w] = s; }
-    __syncthreads();
+    lds_sync();
     if (threadIdx.x == 0) {
         float r = R.ref[0];
         double a = R.s[0];
         for (int q = 1; q < NWAVE; ++q) sref_merge(r, a, R.ref[q], R.s[q]);
         ref = r; s = a;
     }
-    __syncthreads();
+    lds_sync();
 }
 
-__device__ int block_min(Red& R, int v) {
+template <int NW>
+__device__ int block_min(RedT<NW>& R, int v) {
     v = wave_min(v);
     if ((threadIdx.x & 63) == 0) R.i[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_sync();
     int r = R.i[0];
-    for (int q = 1; q < NWAVE; ++q) r = min(r, R.i[q]);
-    __syncthreads();
+    for (int q = 1; q < NW; ++q) r = min(r, R.i[q]);
+    lds_sync();
     return r;
 }
 
-__device__ int block_max(Red& R, int v) {
+template <int NW>
+__device__ int block_max(RedT<NW>& R, int v) {
     v = wave_max(v);
     if ((threadIdx.x & 63) == 0) R.j[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_sync();
     int r = R.j[0];
-    for (int q = 1; q < NWAVE; ++q) r = max(r, R.j[q]);
-    __syncthreads();
+    for (int q = 1; q < NW; ++q) r = max(r, R.j[q]);
+    lds_sync();
     return r;
 }
 
 // Ordered block sum of up to 4 doubles; every thread returns the sums.
-template <int N>
-__device__ void block_sum(Red& R, double (&v)[N]) {
+template <int N, int NW>
+__device__ void block_sum(RedT<NW>& R, double (&v)[N]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int q = 0; q < N; ++q) {
         v[q] = wave_sum(v[q]);
         if (lane == 0) R.d[q][w] = v[q];
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int q = 0; q < N; ++q) {
         double a = R.d[q][0];
-        for (int z = 1; z < NWAVE; ++z) a += R.d[q][z];
+        for (int z = 1; z < NW; ++z) a += R.d[q][z];
         v[q] = a;
     }
-    __syncthreads();
+    lds_sync();
 }
 
-// Exclusive scan of one double per thread in thread order (fixed Hillis-Steele
-// order: deterministic). `a` is NT doubles of shared memory. Returns the
-// exclusive prefix and sets `total`.
-__device__ double block_exscan(double* a, double v, double& total) {
-    a[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-        const double add = threadIdx.x >= static_cast<unsigned>(off) ? a[threadIdx.x - off] : 0.0;
-        __syncthreads();
-        a[threadIdx.x] += add;
-        __syncthreads();
+// Exclusive scan of one double per thread in thread order, in a fixed order
+// (so it is deterministic): an inclusive Hillis-Steele scan inside each
+// wave64 with lane shuffles, then the NW wave totals added in wave order
+// through `wt` (NW doubles of shared memory). Returns the exclusive prefix
+// and sets `total`.
+template <int NW>
+__device__ double block_exscan(double* wt, double v, double& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
-    const double incl = a[threadIdx.x];
-    total = a[NT - 1];
-    __syncthreads();
-    return incl - v;
+    double ex = __shfl_up(x, 1, 64);                       // exclusive within the wave
+    if (lane == 0) ex = 0.0;
+    if (lane == 63) wt[w] = x;
+    lds_sync();
+    double before = 0.0, all = 0.0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+        const double t = wt[q];
+        if (q < w) before += t;
+        all += t;
+    }
+    lds_sync();
+    total = all;
+    return before + ex;
 }
 
 // ------------------------------------------------------------------ pass 1
@@ -305,9 +348,9 @@ struct Lane {
     int nan;
 };
 
-__device__ inline void lane_rescale(Lane& st, float c) {
+__device__ inline void lane_rescale(Lane& st, float ch) {
     if (st.t1 > st.mref) {
-        const float nr = ceilf(st.t1 * c);
+        const float nr = ceilf(st.t1 * ch);
         if (!(nr <= 3.0e38f)) {           // +inf logit or overflow: poison the sum
             st.s = __builtin_nan("");
             st.ref = 0.0f;
@@ -320,8 +363,14 @@ __device__ inline void lane_rescale(Lane& st, float c) {
     }
 }
 
+// 2^(x*c - ref) with c = ch + cl: the head product is exact for bf16 inputs
+// (ch carries 16 significant bits), so only the final roundings remain.
+__device__ inline float exp_term(float x, float ch, float cl, float ref) {
+    return __builtin_amdgcn_exp2f(fmaf(x, cl, fmaf(x, ch, -ref)));
+}
+
 template <int KIND, int VE>
-__device__ inline void consume_vec(Lane& st, const float (&x)[VE], int vidx, float c) {
+__device__ inline void consume_vec(Lane& st, const float (&x)[VE], int vidx, float ch, float cl) {
     if constexpr (KIND == K_DRAFT) {
 #pragma unroll
         for (int j = 0; j < VE; j += 2) st.t1 = fmaxf(st.t1, fmaxf(x[j], x[j + 1]));
@@ -341,10 +390,10 @@ __device__ inline void consume_vec(Lane& st, const float (&x)[VE], int vidx, flo
         }
     }
     if constexpr (KIND != K_GREEDY) {
-        lane_rescale(st, c);
+        lane_rescale(st, ch);
         float e[VE];
 #pragma unroll
-        for (int j = 0; j < VE; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[j], c, -st.ref));
+        for (int j = 0; j < VE; ++j) e[j] = exp_term(x[j], ch, cl, st.ref);
 #pragma unroll
         for (int w = 1; w < VE; w <<= 1) {
 #pragma unroll
@@ -355,7 +404,7 @@ __device__ inline void consume_vec(Lane& st, const float (&x)[VE], int vidx, flo
 }
 
 template <int KIND>
-__device__ inline void consume_one(Lane& st, float x, float c) {
+__device__ inline void consume_one(Lane& st, float x, float ch, float cl) {
     if constexpr (KIND == K_DRAFT) {
         st.t1 = fmaxf(st.t1, x);
     } else {
@@ -364,14 +413,30 @@ __device__ inline void consume_one(Lane& st, float x, float c) {
         if constexpr (KIND == K_GREEDY) st.nan |= (x != x);
     }
     if constexpr (KIND != K_GREEDY) {
-        lane_rescale(st, c);
-        st.s += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, c, -st.ref)));
+        lane_rescale(st, ch);
+        st.s += static_cast<double>(exp_term(x, ch, cl, st.ref));
     }
 }
 
-// Scan split [e0, e1) of the row at rowp; the split's record is complete in thread 0.
+// 16-byte loads through a buffer resource: one VGPR holds the lane's byte
+// offset, the per-vector stride sits in an SGPR, and a load past num_records
+// returns zeros instead of faulting (such lanes are never consumed).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+template <class E>
+__device__ inline typename E::vec load_nt(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 2);
+    return __builtin_bit_cast(typename E::vec, w);
+}
+
+// Scan segment [e0, e1) of the row at `row`; the segment's record is complete
+// in thread 0. xs is the row's draft-token index (or -1): if it lies in the
+// segment, thread 0 loads that logit up front (its latency hides behind the
+// stream) and keeps it for the record.
 template <class E, int KIND>
-__device__ TileRec tile_scan(const char* row, int e0, int e1, float c, Red& R) {
+__device__ TileRec tile_scan(const char* row, int e0, int e1, int xs, float ch, float cl, Red& R) {
     using vec = typename E::vec;
     constexpr int VE = E::VE;
     const int tid = threadIdx.x;
@@ -382,55 +447,52 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, float c, Red& R) {
     const int nvec = (len - head) / VE;
     const int tail = len - head - nvec * VE;
     const vec* vp = reinterpret_cast<const vec*>(start + static_cast<size_t>(head) * E::ES);
+    float lx = 0.0f;
+    const bool got = tid == 0 && xs >= e0 && xs < e1;
+    if (got) lx = E::load1(row, static_cast<size_t>(xs));
 
     Lane st;
     st.t1 = -INFINITY; st.t2 = -INFINITY; st.mref = -INFINITY; st.ref = 0.0f;
     st.s = 0.0; st.bvec = -1; st.nan = 0;
 
-    // Ping-pong pipelined body: while one batch of U vectors is consumed the
-    // next batch is in flight. Loads are never skipped by a branch (a batch past
-    // the end re-reads a valid address and is not consumed), so the compiler's
-    // wait counts stay exact instead of draining every load each iteration.
+    // Batch i holds vectors (i*U + u)*NT + tid, u < U. Batches are ping-pong
+    // pipelined (one in flight while the other is consumed); every branch on i
+    // is uniform, and only the last batch can hold vectors past nvec, which
+    // load as zeros and are skipped.
     constexpr int U = 4;
-    int v = tid;
-    const int step = U * NT;
-    auto batch_ok = [&](int at) { return at + (U - 1) * NT < nvec; };
+    constexpr unsigned BSTRIDE = NT * 16u;                 // bytes between u and u+1
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vp, static_cast<unsigned>(nvec) * 16u);
+    const unsigned voff = static_cast<unsigned>(tid) * 16u;
+    const int nb = (nvec + U * NT - 1) / (U * NT);
+    auto consume = [&](const vec (&X)[U], int i) {
+        const bool full = (i + 1) * U * NT <= nvec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int vi = (i * U + u) * NT + tid;
+            if (full || vi < nvec) {
+                float x[VE];
+                E::unpack(X[u], x);
+                consume_vec<KIND, VE>(st, x, vi, ch, cl);
+            }
+        }
+    };
     vec A[U], Bv[U];
-    if (batch_ok(v)) {
+    if (nb > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) A[u] = E::stream(vp + v + u * NT);
+        for (int u = 0; u < U; ++u) A[u] = load_nt<E>(rs, voff, u * BSTRIDE);
     }
-    while (batch_ok(v)) {
-        const int v1 = v + step;
-        const int l1 = batch_ok(v1) ? v1 : v;
+    for (int i = 0; i < nb; i += 2) {
+        if (i + 1 < nb) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) Bv[u] = E::stream(vp + l1 + u * NT);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[VE];
-            E::unpack(A[u], x);
-            consume_vec<KIND, VE>(st, x, v + u * NT, c);
+            for (int u = 0; u < U; ++u) Bv[u] = load_nt<E>(rs, voff, ((i + 1) * U + u) * BSTRIDE);
         }
-        v = v1;
-        if (!batch_ok(v)) break;
-        const int v2 = v + step;
-        const int l2 = batch_ok(v2) ? v2 : v;
+        consume(A, i);
+        if (i + 1 >= nb) break;
+        if (i + 2 < nb) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) A[u] = E::stream(vp + l2 + u * NT);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[VE];
-            E::unpack(Bv[u], x);
-            consume_vec<KIND, VE>(st, x, v + u * NT, c);
+            for (int u = 0; u < U; ++u) A[u] = load_nt<E>(rs, voff, ((i + 2) * U + u) * BSTRIDE);
         }
-        v = v2;
-    }
-    for (; v < nvec; v += NT) {
-        float x[VE];
-        E::unpack(E::stream(vp + v), x);
-        consume_vec<KIND, VE>(st, x, v, c);
+        consume(Bv, i + 1);
     }
 
     // head / tail elements: at most 2*VE-2 of them, one per thread
@@ -442,13 +504,13 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, float c, Red& R) {
         const int rel = tid < head ? tid : head + nvec * VE + (tid - head);
         sx = E::load1(row, static_cast<size_t>(e0) + rel);
         sidx = e0 + rel;
-        consume_one<KIND>(st, sx, c);
+        consume_one<KIND>(st, sx, ch, cl);
     }
 
     float t1 = st.t1, t2 = st.t2;
     block_top2(R, t1, t2);
     TileRec out;
-    out.t1 = t1; out.t2 = t2; out.idx = 0x7fffffff; out.nan = 0; out.ref = 0.0f; out.s = 0.0; out.pad = 0;
+    out.t1 = t1; out.t2 = t2; out.idx = 0x7fffffff; out.ref = 0.0f; out.s = 0.0; out.lx = 0.0f; out.flags = 0;
 
     if constexpr (KIND == K_GREEDY) {
         int cand = 0x7fffffff;
@@ -462,26 +524,96 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, float c, Red& R) {
         }
         if (sx == t1 && sidx < cand) cand = sidx;
         out.idx = block_min(R, cand);
-        out.nan = block_max(R, st.nan);
+        out.flags = block_max(R, st.nan) ? 1 : 0;
     } else {
         float ref = st.ref;
         double s = st.s;
         block_sref(R, ref, s);
         out.ref = ref; out.s = s;
+        if (got) { out.lx = lx; out.flags = 2; }
     }
     return out;
 }
 
+// ------------------------------------------------------------------ decisions
+
+// log2(s) for finite s > 0 in double precision with few registers (the
+// library routine would raise the occupancy-limiting register count of the
+// whole scan kernel): s = m 2^e with m in [sqrt(1/2), sqrt(2)), and
+// ln m = 2 atanh(z), z = (m - 1)/(m + 1), |z| <= 0.172, by its odd series
+// (terms through z^21, truncation below 3e-17).
+__device__ inline double log2_lean(double s) {
+    int e;
+    double m = frexp(s, &e);                         // m in [0.5, 1)
+    if (m < 0.70710678118654752) { m *= 2.0; --e; }
+    const double z = (m - 1.0) / (m + 1.0);
+    const double z2 = z * z;
+    double t = 1.0 / 21.0;
+    t = fma(t, z2, 1.0 / 19.0);
+    t = fma(t, z2, 1.0 / 17.0);
+    t = fma(t, z2, 1.0 / 15.0);
+    t = fma(t, z2, 1.0 / 13.0);
+    t = fma(t, z2, 1.0 / 11.0);
+    t = fma(t, z2, 1.0 / 9.0);
+    t = fma(t, z2, 1.0 / 7.0);
+    t = fma(t, z2, 1.0 / 5.0);
+    t = fma(t, z2, 1.0 / 3.0);
+    t = fma(t, z2, 1.0);
+    return static_cast<double>(e) + (2.0 * z * t) * 1.4426950408889634;
+}
+
+// 2^d in double precision with few registers: d = n + f, |f| <= 1/2, and
+// 2^f = e^(f ln 2) by its Taylor series through degree 13 (truncation below
+// 4e-18); 2^n by ldexp. -inf gives 0, +inf gives +inf.
+__device__ inline double exp2_lean(double d) {
+    if (!(d > -1100.0)) return 0.0;
+    if (!(d < 1100.0)) return INFINITY;
+    const double n = rint(d);
+    const double g = (d - n) * 0.69314718055994531;
+    double t = 1.0 / 6227020800.0;                   // 1/13!
+    t = fma(t, g, 1.0 / 479001600.0);
+    t = fma(t, g, 1.0 / 39916800.0);
+    t = fma(t, g, 1.0 / 3628800.0);
+    t = fma(t, g, 1.0 / 362880.0);
+    t = fma(t, g, 1.0 / 40320.0);
+    t = fma(t, g, 1.0 / 5040.0);
+    t = fma(t, g, 1.0 / 720.0);
+    t = fma(t, g, 1.0 / 120.0);
+    t = fma(t, g, 1.0 / 24.0);
+    t = fma(t, g, 1.0 / 6.0);
+    t = fma(t, g, 0.5);
+    t = fma(t, g, 1.0);
+    t = fma(t, g, 1.0);
+    return ldexp(t, static_cast<int>(n));
+}
+
+
 template <class E, int MODE>
-__global__ __launch_bounds__(NT) void row_scan_kernel(Params P) {
+__global__ __launch_bounds__(NT) void scan_kernel(Params P) {
     __shared__ Red R;
+    const int tid = threadIdx.x;
+    const int k = P.k, V = P.V;
     // Workgroup w owns the flattened elements [w*L, (w+1)*L) of all B*rpb rows,
     // so every workgroup streams the same number of bytes and the grid is one
     // resident round. It emits one record per row segment, in slot row + w.
     const long long w = blockIdx.x;
+    if constexpr (MODE == SPEC_MODE_SAMPLE) {
+        // pass 2's tables, spread over the workgroups: 2^(j/N) of the fp64 exp,
+        // and (bf16) exp(v/T - C) of every bf16 value v the table covers
+        const long long gi0 = w * NT + tid, gstride = static_cast<long long>(gridDim.x) * NT;
+        for (long long j = gi0; j < EXP_N; j += gstride) P.exptab[j] = exp2(static_cast<double>(j) / EXP_N);
+        if constexpr (E::ES == 2) {
+            const int range = P.tab_range;
+            for (long long j = gi0; j < 2LL * range; j += gstride) {
+                const unsigned sgn = j >= range ? 1u : 0u;
+                const unsigned bits = (sgn << 15) | (static_cast<unsigned>(j - sgn * range) + TAB_BASE);
+                const double v = __uint_as_float(bits << 16);
+                P.tautab[j] = exp(fma(v, P.invT, -P.tab_c));
+            }
+        }
+    }
     const long long g0 = w * P.L;
     const long long g1 = g0 + P.L < P.N ? g0 + P.L : P.N;
-    const int k = P.k, V = P.V;
     for (long long g = g0; g < g1;) {
         const long long row = g / V;
         const int e0 = static_cast<int>(g - row * V);
@@ -496,12 +628,15 @@ __global__ __launch_bounds__(NT) void row_scan_kernel(Params P) {
             rowp = static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + (j - k - 1)) * V * E::ES;
         TileRec tr;
         if constexpr (MODE == SPEC_MODE_GREEDY) {
-            tr = tile_scan<E, K_GREEDY>(rowp, e0, e1, P.c, R);
+            tr = tile_scan<E, K_GREEDY>(rowp, e0, e1, -1, P.ch, P.cl, R);
         } else {
-            if (is_target) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, P.c, R);
-            else tr = tile_scan<E, K_DRAFT>(rowp, e0, e1, P.c, R);
+            // the draft token of this row's position (target rows i < k, draft rows)
+            const int pos = is_target ? j : j - k - 1;
+            const int xs = pos < k ? P.tok[static_cast<size_t>(b) * k + pos] : -1;
+            if (is_target) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, xs, P.ch, P.cl, R);
+            else tr = tile_scan<E, K_DRAFT>(rowp, e0, e1, xs, P.ch, P.cl, R);
         }
-        if (threadIdx.x == 0) P.tiles[row + w] = tr;
+        if (tid == 0) P.tiles[row + w] = tr;
         g = rend;
     }
 }
@@ -515,6 +650,40 @@ struct Dec {
     int valid;
 };
 
+// Merge the segment records t[w0..w1] of one row in element order (earlier
+// segments win ties of the greedy argmax); the first four are loaded together.
+template <int MODE>
+__device__ inline RowRec merge_row(const TileRec* t, long long w0, long long w1) {
+    TileRec m = t[w0];
+    for (long long q0 = w0 + 1; q0 <= w1; q0 += 4) {
+        TileRec o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) if (q0 + u <= w1) o[u] = t[q0 + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (q0 + u > w1) break;
+            const float prev = m.t1;
+            top2_merge(m.t1, m.t2, o[u].t1, o[u].t2);
+            if constexpr (MODE == SPEC_MODE_GREEDY) {
+                if (o[u].t1 > prev) m.idx = o[u].idx;
+                m.flags |= o[u].flags & 1;
+            } else {
+                sref_merge(m.ref, m.s, o[u].ref, o[u].s);
+                if (o[u].flags & 2) { m.lx = o[u].lx; m.flags |= 2; }
+            }
+        }
+    }
+    RowRec rr;
+    rr.m = m.t1; rr.t2 = m.t2; rr.idx = m.idx; rr.lg = 0.0; rr.lx = m.lx; rr.has_lx = (m.flags & 2) != 0;
+    if constexpr (MODE == SPEC_MODE_GREEDY) {
+        rr.valid = !(m.flags & 1) && m.t1 > -INFINITY && m.t1 < INFINITY;
+    } else {
+        rr.valid = (m.s == m.s) && m.s > 0.0 && m.s < INFINITY && m.t1 > -INFINITY && m.t1 < INFINITY;
+        if (rr.valid) rr.lg = static_cast<double>(m.ref) + log2_lean(m.s);
+    }
+    return rr;
+}
+
 template <class E, int MODE>
 __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     __shared__ Dec D;
@@ -523,86 +692,52 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     const int k = P.k, V = P.V, rpb = P.rpb;
     constexpr bool sample = MODE == SPEC_MODE_SAMPLE;
 
-    // Independent loads first: the draft token of position tid, its uniform,
-    // and (as soon as the token is known to be in range) the two logits it
-    // picks; they overlap the merge of the split records below.
+    // One round of independent loads: the draft token and uniform of position
+    // tid, and the segment records of row tid (the draft-token logits came with
+    // the records).
     int x = -1;
-    bool inr = false;
-    double u0 = 0.0, lt = 0.0, ld = 0.0;
+    double u0 = 0.0;
     if (tid < k) {
         x = P.tok[static_cast<size_t>(b) * k + tid];
-        inr = x >= 0 && x < V;
-        const size_t rowT = static_cast<size_t>(b) * (k + 1) + tid;
-        if constexpr (sample) {
-            u0 = P.uni[rowT * 2 + 0];
-            if (inr) {
-                lt = E::load1(P.tgt, rowT * V + x);
-                ld = E::load1(P.dft, (static_cast<size_t>(b) * k + tid) * V + x);
-            }
-        }
+        if constexpr (sample) u0 = P.uni[(static_cast<size_t>(b) * (k + 1) + tid) * 2];
     }
-
-    // merge the segments of every row of batch row b, in element order
     if (tid < rpb) {
         const size_t row = static_cast<size_t>(b) * rpb + tid;
-        // segments of this row, in element order: workgroups w0..w1, slot row + w
         const long long r0 = static_cast<long long>(row) * V;
-        const long long w0 = r0 / P.L, w1 = (r0 + V - 1) / P.L;
-        const TileRec* t = P.tiles + row;
-        TileRec m = t[w0];
-        for (long long q0 = w0 + 1; q0 <= w1; q0 += 4) {
-            TileRec o[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) if (q0 + u <= w1) o[u] = t[q0 + u];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (q0 + u > w1) break;
-                const float prev = m.t1;
-                top2_merge(m.t1, m.t2, o[u].t1, o[u].t2);
-                if constexpr (MODE == SPEC_MODE_GREEDY) {
-                    if (o[u].t1 > prev) m.idx = o[u].idx;    // earlier segment wins ties
-                    m.nan |= o[u].nan;
-                } else {
-                    sref_merge(m.ref, m.s, o[u].ref, o[u].s);
-                }
-            }
-        }
-        RowRec rr;
-        rr.m = m.t1; rr.t2 = m.t2; rr.ref = m.ref; rr.idx = m.idx; rr.s = m.s; rr.pad = 0;
-        if constexpr (MODE == SPEC_MODE_GREEDY)
-            rr.valid = !m.nan && m.t1 > -INFINITY && m.t1 < INFINITY;
-        else
-            rr.valid = (m.s == m.s) && m.s > 0.0 && m.s < INFINITY && m.t1 > -INFINITY && m.t1 < INFINITY;
+        const RowRec rr = merge_row<MODE>(P.tiles + row, r0 / P.L, (r0 + V - 1) / P.L);
         D.rec[tid] = rr;
-        if constexpr (sample) P.rows[row] = rr;
         if (tid <= k) {
-            const float g = (m.t2 == -INFINITY) ? INFINITY : m.t1 - m.t2;
+            const float g = (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
             P.gap[static_cast<size_t>(b) * (k + 1) + tid] = g;
         }
     }
     if (tid == 0) { D.valid = 1; D.a = k; }
-    __syncthreads();
+    lds_sync();
 
     int ok = 1;
     if (tid <= k) ok = D.rec[tid].valid;                  // target rows 0..k
     if (tid < k) {
+        const bool inr = x >= 0 && x < V;
         if (!inr) ok = 0;
         if (sample && !D.rec[k + 1 + tid].valid) ok = 0;
+        if (sample && ok && !(D.rec[tid].has_lx && D.rec[k + 1 + tid].has_lx)) ok = 0;
         int acc = 0;
         float pf = __builtin_nanf(""), qf = __builtin_nanf("");
         if (ok) {
             const RowRec& rt = D.rec[tid];
             if constexpr (sample) {
+                // log2 p(x) = x*c - lg_p and log2 q(x) = x*c - lg_q, in double
                 const RowRec& rd = D.rec[k + 1 + tid];
+                const double lt = rt.lx, ld = rd.lx;
                 const double c = P.c;
-                const double lp = lt == -INFINITY ? -INFINITY : lt * c - rt.ref - log2(rt.s);
-                const double lq = ld == -INFINITY ? -INFINITY : ld * c - rd.ref - log2(rd.s);
+                const double lp = lt == -INFINITY ? -INFINITY : lt * c - rt.lg;
+                const double lq = ld == -INFINITY ? -INFINITY : ld * c - rd.lg;
                 double r;
                 if (lq == -INFINITY) r = (lp == -INFINITY) ? 0.0 : INFINITY;
-                else r = exp2(lp - lq);
+                else r = exp2_lean(lp - lq);
                 acc = u0 < r;
-                pf = static_cast<float>(exp2(lp));
-                qf = static_cast<float>(exp2(lq));
+                pf = exp2f(static_cast<float>(lp));
+                qf = exp2f(static_cast<float>(lq));
             } else {
                 acc = (x == rt.idx);
             }
@@ -612,236 +747,444 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
         if (P.dprob) P.dprob[static_cast<size_t>(b) * k + tid] = ok ? qf : __builtin_nanf("");
     }
     if (!ok) atomicAnd(&D.valid, 0);
-    __syncthreads();
+    lds_sync();
     const int valid = D.valid;
     if (tid == 0) {
         int a = k;
         for (int i = 0; i < k; ++i) if (!D.acc[i]) { a = i; break; }
         D.a = a;
     }
-    __syncthreads();
+    lds_sync();
     const int a = D.a;
     if (tid <= k) {
         int o;
         if (!valid) o = -1;
         else if (tid < a) o = x;
-        else if (tid == a) o = sample ? -1 : D.rec[a].idx;    // sampling: the draw kernel writes it
+        else if (tid == a) o = sample ? -1 : D.rec[a].idx;    // sampling: the draw writes it
         else o = -1;
         P.out_tok[static_cast<size_t>(b) * (k + 1) + tid] = o;
     }
     if (tid == 0) {
         P.acc_len[b] = valid ? a : -1;
         if constexpr (sample) {
-            P.desc[b] = valid ? a : -1;
-            double lh = 0.0;
+            BatchRec br;
+            br.a = valid ? a : -1;
+            br.pad = 0;
+            br.mp = D.rec[a].m;
+            br.mq = a < k ? D.rec[k + 1 + a].m : 0.0f;
+            br.lam = 0.0;
+            br.pad2 = 0.0;
             if (valid && a < k) {
+                // S_p/S_q in the exp((x - m)/T) normalisation of pass 2: only
+                // used to place a relative band of ETA, so 2^d is taken as
+                // 2^round(d) * exp2f(d - round(d)) (relative error ~1e-7)
                 const RowRec& rt = D.rec[a];
                 const RowRec& rd = D.rec[k + 1 + a];
                 const double c = P.c;
-                // pass-1 sums rescaled to the exp((x - m)/T) normalisation of pass 2
-                const double lp = static_cast<double>(rt.ref) - static_cast<double>(rt.m) * c;
-                const double lq = static_cast<double>(rd.ref) - static_cast<double>(rd.m) * c;
-                lh = (rt.s / rd.s) * exp2(lp - lq);
+                const double d = (rt.lg - static_cast<double>(rt.m) * c) - (rd.lg - static_cast<double>(rd.m) * c);
+                const double n = rint(d);
+                br.lam = ldexp(static_cast<double>(exp2f(static_cast<float>(d - n))), static_cast<int>(n));
             }
-            P.lam_hat[b] = lh;
+            P.bat[b] = br;
         }
     }
 }
 
 // ------------------------------------------------------------------ pass 2
 
-// exp(x) for x <= 0 in double precision, by the table-driven method of
-// P. T. P. Tang ("Table-driven implementation of the exponential function in
-// IEEE floating-point arithmetic", ACM TOMS 15(2), 1989): write
-// x = (64 m + j) ln2/64 + r with |r| <= ln2/128, so exp(x) = 2^m 2^(j/64) e^r;
-// ln2/64 is split into a 36-bit head (so (64 m + j) * head is exact) and a
-// tail, and e^r - 1 is its Taylor polynomial of degree 6 (truncation below
-// r^7/7! < 3e-20). T[j] = 2^(j/64) is built per workgroup with the device
-// exp2. Total error is a few ulp. Inputs below -745 give 0 (also -inf).
-constexpr double EXP_INV_L = 0x1.71547652b82fep+6;    // 64 / ln 2
-constexpr double EXP_L1 = 0x1.62e42fefa0000p-7;       // ln 2 / 64, leading 36 bits
-constexpr double EXP_L2 = 0x1.cf79abc9e3b3ap-46;      // ln 2 / 64 - EXP_L1
-constexpr double EXP_C3 = 0x1.5555555555555p-3;       // 1/3!
-constexpr double EXP_C4 = 0x1.5555555555555p-5;       // 1/4!
-constexpr double EXP_C5 = 0x1.1111111111111p-7;       // 1/5!
-constexpr double EXP_C6 = 0x1.6c16c16c16c17p-10;      // 1/6!
+// exp(y) for y <= 0 in double precision, table-driven (P. T. P. Tang, "Table-
+// driven implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989) and free of branches: write
+// y = (N m + j) ln2/N + r with N = 1024 and |r| <= ln2/2048, so
+// exp(y) = 2^m 2^(j/N) e^r. The nearest integer to y N/ln2 comes from adding
+// 1.5*2^52 (its low word is the integer); ln2/N is split into a 32-bit head
+// (so its product with the integer is exact) and a tail (the fdlibm split of
+// ln 2); e^r - 1 is its Taylor polynomial of degree 3 (truncation below
+// r^4/24 < 6e-16); 2^m is added to the exponent field of T[j] = 2^(j/N).
+// Inputs at or below -708 give 0 (also -inf): those terms lie below 1e-307
+// relative to the row maximum.
+constexpr double EXP_INV_L = 0x1.71547652b82fep+10;   // N / ln 2
+constexpr double EXP_L1 = 0x1.62e42fee00000p-11;      // head of ln 2 / N (32 bits)
+constexpr double EXP_L2 = 0x1.a39ef35793c76p-43;      // ln 2 / N - EXP_L1
+constexpr double EXP_SHIFT = 0x1.8p52;
+constexpr double EXP_C3 = 1.0 / 6.0;
 
-__device__ inline double exp_tab(double x, const double* T) {
-    if (!(x > -745.0)) return 0.0;
-    const double kf = rint(x * EXP_INV_L);
-    double r = fma(-kf, EXP_L1, x);
+__device__ inline double exp_fast(double y, const double* T) {
+    const double t = fma(y, EXP_INV_L, EXP_SHIFT);
+    const double kf = t - EXP_SHIFT;
+    double r = fma(-kf, EXP_L1, y);
     r = fma(-kf, EXP_L2, r);
-    const int k = static_cast<int>(kf);
-    double p = fma(r, EXP_C6, EXP_C5);
-    p = fma(r, p, EXP_C4);
-    p = fma(r, p, EXP_C3);
-    p = fma(r, p, 0.5);
-    p = fma(r, p, 1.0);
-    p *= r;
-    const double t = T[k & 63];
-    return ldexp(fma(t, p, t), k >> 6);
+    const int k = __double2loint(t);
+    const double p = fma(r * r, fma(r, EXP_C3, 0.5), r);
+    const double tj = T[k & (EXP_N - 1)];
+    // (k >> 10) << 20, in unsigned arithmetic (two's complement wrap)
+    const unsigned hi = static_cast<unsigned>(__double2hiint(tj)) + (static_cast<unsigned>(k & ~(EXP_N - 1)) << 10);
+    const double s = __hiloint2double(static_cast<int>(hi), __double2loint(tj));
+    const double res = fma(s, p, s);
+    return y > -708.0 ? res : 0.0;
 }
 
-__device__ inline void exp_table_init(double* T) {
-    if (threadIdx.x < 64) T[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / 64.0);
-}
+// ------------------------------------------------------------------ pass-2 element values
 
-// EPT contiguous elements [j0, j0 + EPT) of a row clipped to [.., hi): 16-byte
-// vector loads when the row is aligned and the run is whole, else element loads.
-// Elements at or past hi read as -inf (weight 0).
-template <class E>
-__device__ inline void load_run(const void* row, int j0, int hi, bool vec_ok, float (&x)[EPT]) {
-    constexpr int VE = E::VE;
-    if (vec_ok && j0 + EPT <= hi) {
-        const typename E::vec* vp =
-            reinterpret_cast<const typename E::vec*>(static_cast<const char*>(row) + static_cast<size_t>(j0) * E::ES);
-        typename E::vec w[EPT / VE];
-#pragma unroll
-        for (int u = 0; u < EPT / VE; ++u) w[u] = vp[u];
-#pragma unroll
-        for (int u = 0; u < EPT / VE; ++u) {
-            float y[VE];
-            E::unpack(w[u], y);
-#pragma unroll
-            for (int q = 0; q < VE; ++q) x[u * VE + q] = y[q];
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < EPT; ++q)
-            x[q] = (j0 + q < hi) ? E::load1(row, static_cast<size_t>(j0) + q) : -INFINITY;
-    }
-}
+// A bf16 logit takes one of 2^16 values, so for bf16 inputs pass 2 reads
+// tau(v) = exp(v/T - C) from a table indexed by the value's bits for every v
+// with 2^-24 <= |v| < 2^kmax (kmax <= 8, the largest with 2^kmax/T <= 700; C
+// centres the range so that a sum of V entries cannot overflow). Other values
+// (zero, tiny, -inf, very negative) take the fp64 exp of the same argument. A
+// batch row uses the table when its rows' maxima lie inside it; otherwise
+// every element takes the fp64 exp normalised by its row maximum. Either way
+// only ratios of sums enter the draw, so the common scale does not matter.
 
 struct Pass2 {
     const void* rowT;
     const void* rowD;
-    double mp, mq, invT, lam;
+    double invT;
+    double offT, offD;         // added to x/T inside the exp: -C (table) or -m/T (row max)
+    double lam;                // S_p/S_q in this batch row's units (set by the draw)
+    double lam_hat;            // pass 1's estimate of it, same units
+    int tab;                   // values come from the bf16 table
+    int range;                 // table entries per sign
     bool resid;
 };
 
 template <class E>
-__device__ inline Pass2 pass2_setup(const Params& P, int b, int a) {
-    const int k = P.k, V = P.V;
-    const size_t rpbase = static_cast<size_t>(b) * P.rpb;
+__device__ inline Pass2 pass2_setup(const Params& P, int b, const BatchRec& br, const double* TE) {
+    const int k = P.k, V = P.V, a = br.a < 0 ? 0 : br.a;
     Pass2 Q;
     Q.resid = a < k;
     Q.rowT = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + a) * V * E::ES;
     Q.rowD = Q.resid ? static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + a) * V * E::ES
-                     : nullptr;
-    Q.mp = P.rows[rpbase + a].m;
-    Q.mq = Q.resid ? P.rows[rpbase + k + 1 + a].m : 0.0;
+                     : Q.rowT;
     Q.invT = P.invT;
+    const double mp = br.mp, mq = Q.resid ? static_cast<double>(br.mq) : mp;
+    const double dm = (mp - mq) * P.invT;
+    Q.tab = E::ES == 2 && P.tab_range > 0 && fabs(mp) < P.tab_lim && fabs(mq) < P.tab_lim && fabs(dm) < 600.0;
+    Q.range = P.tab_range;
+    Q.offT = Q.tab ? -P.tab_c : -mp * P.invT;
+    Q.offD = Q.tab ? -P.tab_c : -mq * P.invT;
     Q.lam = 0.0;
+    // pass 1 estimates S_p/S_q with both sums normalised by their row maxima;
+    // in table units each sum carries exp(m/T - C) more
+    Q.lam_hat = Q.tab ? br.lam * exp_fast(dm, TE) : br.lam;
     return Q;
 }
 
-// Residual weight e - lambda f (clamped at 0), or e for the bonus draw, of one
-// element given its target and draft logits.
-__device__ inline double weight_of(const Pass2& Q, float xt, float xd, const double* T) {
-    const double e = exp_tab((static_cast<double>(xt) - Q.mp) * Q.invT, T);
-    if (!Q.resid) return e;
-    const double f = exp_tab((static_cast<double>(xd) - Q.mq) * Q.invT, T);
-    const double w = e - Q.lam * f;
-    return w > 0.0 ? w : 0.0;
+// Value of one element: bits of a bf16 logit, or an fp32 logit.
+__device__ inline double val_bf16(unsigned bits, double off, const Pass2& Q, const double* TT, const double* TE) {
+    if (Q.tab) {
+        const unsigned key = (bits & 0x7fffu) - TAB_BASE;
+        if (key < static_cast<unsigned>(Q.range)) return TT[key + (bits >> 15) * static_cast<unsigned>(Q.range)];
+    }
+    return exp_fast(fma(static_cast<double>(__uint_as_float(bits << 16)), Q.invT, off), TE);
+}
+
+__device__ inline double val_f32(float x, double off, const Pass2& Q, const double* TE) {
+    return exp_fast(fma(static_cast<double>(x), Q.invT, off), TE);
 }
 
 template <class E>
-__device__ inline double weight_at(const Pass2& Q, int j, const double* T) {
-    const float xt = E::load1(Q.rowT, j);
-    const float xd = Q.resid ? E::load1(Q.rowD, j) : 0.0f;
-    return weight_of(Q, xt, xd, T);
+__device__ inline double val_at(const void* row, int j, double off, const Pass2& Q, const double* TT, const double* TE) {
+    if constexpr (E::ES == 2)
+        return val_bf16(reinterpret_cast<const unsigned short*>(row)[j], off, Q, TT, TE);
+    else
+        return val_f32(reinterpret_cast<const float*>(row)[j], off, Q, TE);
 }
 
+// Bits of element q of a 16-byte bf16 vector.
+__device__ inline unsigned bf16_bits(const u32x4& w, int q) {
+    const unsigned word = (q >> 1) == 0 ? w.x : (q >> 1) == 1 ? w.y : (q >> 1) == 2 ? w.z : w.w;
+    return (q & 1) ? (word >> 16) : (word & 0xffffu);
+}
+
+// Values of elements q0 .. q0+3 of a 16-byte vector. With the bf16 table,
+// every lane first reads all four table entries (out-of-range values read
+// entry 0), so the LDS reads issue back to back; the rare out-of-range values
+// then take the fp64 exp in one divergent fix-up.
+template <class E>
+__device__ inline void vals4(const typename E::vec& w, int q0, double off, const Pass2& Q, const double* TT,
+                             const double* TE, double (&out)[4]) {
+    if constexpr (E::ES == 2) {
+        if (Q.tab) {
+            const unsigned range = static_cast<unsigned>(Q.range);
+            unsigned oor = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const unsigned bits = bf16_bits(w, q0 + q);
+                const unsigned key = (bits & 0x7fffu) - TAB_BASE;
+                const bool in = key < range;
+                out[q] = TT[in ? key + (bits >> 15) * range : 0u];
+                oor |= in ? 0u : (1u << q);
+            }
+            if (oor) {                                     // rare: one value at a time
+                for (int q = 0; q < 4; ++q) {
+                    if (oor & (1u << q)) {
+                        const double y = fma(static_cast<double>(__uint_as_float(bf16_bits(w, q0 + q) << 16)), Q.invT, off);
+                        const double ev = exp_fast(y, TE);
+                        out[0] = q == 0 ? ev : out[0];
+                        out[1] = q == 1 ? ev : out[1];
+                        out[2] = q == 2 ? ev : out[2];
+                        out[3] = q == 3 ? ev : out[3];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                out[q] = exp_fast(fma(static_cast<double>(__uint_as_float(bf16_bits(w, q0 + q) << 16)), Q.invT, off), TE);
+        }
+    } else {
+        const float x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = exp_fast(fma(static_cast<double>(x[q]), Q.invT, off), TE);
+    }
+}
+
+// Residual weight e - lambda f (clamped at 0), or e for the bonus draw, of element j.
+template <class E>
+__device__ inline double weight_at(const Pass2& Q, int j, const double* TT, const double* TE) {
+    const double e = val_at<E>(Q.rowT, j, Q.offT, Q, TT, TE);
+    if (!Q.resid) return e;
+    const double w = e - Q.lam * val_at<E>(Q.rowD, j, Q.offD, Q, TT, TE);
+    return w > 0.0 ? w : 0.0;
+}
+
+// Vector u of thread t in a chunk covers elements lo + (u*NT2 + t)*VE + [0, VE):
+// every vector load instruction reads NT2*16 contiguous bytes.
+template <class E>
+struct ChunkLayout {
+    static constexpr int VE = E::VE;
+    static constexpr int NV = CHUNK / (NT2 * VE);     // vectors per thread per row
+    static_assert(NV * NT2 * VE == CHUNK, "chunk is whole vectors per thread");
+};
+
+// 16-byte buffer loads of the NV vectors of this thread in chunk `lo` of a row
+// of `bytes` bytes (bytes = 0 reads zeros without touching memory).
+template <class E>
+__device__ inline void load_chunk(const void* row, unsigned bytes, int lo, typename E::vec (&x)[ChunkLayout<E>::NV]) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, bytes);
+    const unsigned voff = (static_cast<unsigned>(lo) / E::VE + threadIdx.x) * 16u;
+#pragma unroll
+    for (int u = 0; u < ChunkLayout<E>::NV; ++u) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff), u * NT2 * 16, 0);
+        x[u] = __builtin_bit_cast(typename E::vec, w);
+    }
+}
+
+template <class E>
 struct ChunkLds {
-    Red R;
-    double T[64];
+    RedT<NT2 / 64> R;
+    alignas(16) double TT[E::ES == 2 ? TAB_MAX : 2];
+    alignas(16) double TE[EXP_N];
     int namb;
     int amb[MAX_AMB];
 };
 
-template <class E>
-__global__ __launch_bounds__(NT) void residual_chunk_kernel(Params P) {
-    __shared__ ChunkLds S;
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x / P.nchunk, c = blockIdx.x % P.nchunk;
-    const int a = P.desc[b];
-    if (a < 0) return;                                     // uniform: whole block leaves
-    exp_table_init(S.T);
-    if (tid == 0) S.namb = 0;
-    const Pass2 Q = pass2_setup<E>(P, b, a);
-    const double lh = P.lam_hat[b];
-    const double hi_b = lh * (1.0 + ETA), lo_b = lh * (1.0 - ETA);
-    const int lo = c * CHUNK, hi = min(P.V, lo + CHUNK);
-    const int j0 = lo + tid * EPT;
-    float xt[EPT], xd[EPT];
-    load_run<E>(Q.rowT, j0, hi, P.vec_ok, xt);
-    if (Q.resid) load_run<E>(Q.rowD, j0, hi, P.vec_ok, xd);
-    __syncthreads();                                       // table ready
-    double v[4] = {0.0, 0.0, 0.0, 0.0};
+// Copy n doubles (n even) from global memory to LDS with 16-byte loads, up to
+// eight in flight per thread before any is stored (a workgroup of NT2 threads).
+__device__ inline void copy_to_lds(double* dst, const double* src, int n) {
+    const u32x4* s = reinterpret_cast<const u32x4*>(src);
+    u32x4* d = reinterpret_cast<u32x4*>(dst);
+    const int n16 = n / 2;
+    for (int base = 0; base < n16; base += 8 * NT2) {
+        u32x4 v[8];
 #pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-        const double e = exp_tab((static_cast<double>(xt[q]) - Q.mp) * Q.invT, S.T);
-        v[0] += e;
-        if (Q.resid) {
-            const double f = exp_tab((static_cast<double>(xd[q]) - Q.mq) * Q.invT, S.T);
-            v[1] += f;
-            if (e > 0.0) {
-                if (e > hi_b * f) { v[2] += e; v[3] += f; }
-                else if (e >= lo_b * f) {
-                    const int slot = atomicAdd(&S.namb, 1);
-                    if (slot < MAX_AMB) S.amb[slot] = j0 + q;
-                }
-            }
+        for (int q = 0; q < 8; ++q) {
+            const int i = base + q * NT2 + static_cast<int>(threadIdx.x);
+            if (i < n16) v[q] = s[i];
         }
-    }
-    block_sum<4>(S.R, v);
-    if (tid == 0) {
-        ChunkRec r;
-        r.sp = v[0]; r.sq = v[1]; r.e = v[2]; r.f = v[3];
-        const int n = S.namb;
-        r.namb = n < MAX_AMB + 1 ? n : MAX_AMB + 1;
-        for (int q = 0; q < MAX_AMB; ++q) r.amb[q] = q < n ? S.amb[q] : 0;
-        r.pad[0] = r.pad[1] = r.pad[2] = 0;
-        P.chunks[static_cast<size_t>(b) * P.nchunk + c] = r;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int i = base + q * NT2 + static_cast<int>(threadIdx.x);
+            if (i < n16) d[i] = v[q];
+        }
     }
 }
 
-struct DrawLds {
-    Red R;
-    double T[64];
+// pass 2's tables into LDS (visible after the caller's next barrier)
+template <class E>
+__device__ inline void load_tables(const Params& P, double* TT, double* TE) {
+    copy_to_lds(TE, P.exptab, EXP_N);
+    if constexpr (E::ES == 2) copy_to_lds(TT, P.tautab, 2 * P.tab_range);
+}
+
+// Chunk records of the selected row pair (or bonus row) of every batch row.
+// Persistent workgroups walk the items (b, c) round robin; the next item's
+// vectors are loaded before the current one is reduced, and the item after
+// that has its batch record loaded, so loads overlap the fp64 arithmetic.
+// Rows that are not 16-byte aligned take element loads (VEC = false).
+template <class E, bool VEC>
+__global__ __launch_bounds__(NT2) void chunk_kernel(Params P) {
+    __shared__ ChunkLds<E> S;
+    using vec = typename E::vec;
+    constexpr int VE = E::VE;
+    constexpr int NV = ChunkLayout<E>::NV;
+    const int tid = threadIdx.x;
+    const int NC = P.nchunk;
+    const int nitems = P.B * NC;
+    const int G = gridDim.x;
+    const unsigned rowbytes = static_cast<unsigned>(P.V) * E::ES;
+    load_tables<E>(P, S.TT, S.TE);
+
+    auto row_of = [&](const BatchRec& br, int b, bool draft) -> const void* {
+        const int k = P.k, a = br.a < 0 ? 0 : br.a;
+        if (draft && a < k) return static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + a) * P.V * E::ES;
+        return static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + a) * P.V * E::ES;
+    };
+    // the item to prefetch may not exist: then it loads zeros from a zero-size range
+    auto issue = [&](int it, const BatchRec& br, vec (&xt)[NV], vec (&xd)[NV]) {
+        const bool ok = it < nitems && br.a >= 0;
+        const int b = ok ? it / NC : 0, c = ok ? it % NC : 0;
+        const bool resid = ok && br.a < P.k;
+        load_chunk<E>(row_of(br, b, false), ok ? rowbytes : 0u, c * CHUNK, xt);
+        load_chunk<E>(row_of(br, b, true), resid ? rowbytes : 0u, c * CHUNK, xd);
+    };
+    // the batch record of an item, moved to scalar registers (it is uniform)
+    auto batch_of = [&](int it) -> BatchRec {
+        const unsigned* src = reinterpret_cast<const unsigned*>(P.bat + (it < nitems ? it : nitems - 1) / NC);
+        unsigned w[sizeof(BatchRec) / 4];
+#pragma unroll
+        for (unsigned q = 0; q < sizeof(BatchRec) / 4; ++q)
+            w[q] = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(src[q])));
+        BatchRec br;
+        memcpy(&br, w, sizeof(BatchRec));
+        if (it >= nitems) br.a = -1;                       // past the last item: nothing to do
+        return br;
+    };
+
+    int it = blockIdx.x;
+    BatchRec brA = batch_of(it);
+    vec tA[NV], dA[NV];
+    if constexpr (VEC) issue(it, brA, tA, dA);
+    BatchRec brB = batch_of(it + G);
+    lds_sync();                                       // tables ready
+    for (; it < nitems; it += G) {
+        // the batch record two items ahead first: a wait for it then does not
+        // drain the vector loads issued after it
+        const BatchRec brC = batch_of(it + 2 * G);
+        vec tB[NV], dB[NV];
+        if constexpr (VEC) issue(it + G, brB, tB, dB);
+        if (tid == 0) S.namb = 0;
+        lds_sync();                                   // thread 0 read the last item's band list
+        const int b = it / NC, c = it % NC;
+        if (brA.a >= 0) {                                  // uniform: invalid rows have no draw
+            const Pass2 Q = pass2_setup<E>(P, b, brA, S.TE);
+            const double hi_b = Q.lam_hat * (1.0 + ETA), lo_b = Q.lam_hat * (1.0 - ETA);
+            const int lo = c * CHUNK, hi = min(P.V, lo + CHUNK);
+            const bool partial = hi < lo + CHUNK;
+            double v[4] = {0.0, 0.0, 0.0, 0.0};
+            unsigned amb = 0;
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+#pragma unroll
+                for (int h = 0; h < VE; h += 4) {                 // four elements at a time
+                    const int jv = lo + (u * NT2 + tid) * VE + h;
+                    double e[4], f[4];
+                    if constexpr (VEC) {
+                        vals4<E>(tA[u], h, Q.offT, Q, S.TT, S.TE, e);
+                        if (Q.resid) vals4<E>(dA[u], h, Q.offD, Q, S.TT, S.TE, f);
+                        if (partial) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) if (jv + q >= hi) { e[q] = 0.0; f[q] = 0.0; }
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const bool in = jv + q < hi;
+                            e[q] = in ? val_at<E>(Q.rowT, jv + q, Q.offT, Q, S.TT, S.TE) : 0.0;
+                            if (Q.resid) f[q] = in ? val_at<E>(Q.rowD, jv + q, Q.offD, Q, S.TT, S.TE) : 0.0;
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v[0] += e[q];
+                        if (Q.resid) {
+                            v[1] += f[q];
+                            // certain positive: e > lambda f for every lambda in
+                            // the band; band element: neither certainly positive
+                            // nor certainly non-positive
+                            const bool pos = e[q] > hi_b * f[q];
+                            v[2] += pos ? e[q] : 0.0;
+                            v[3] += pos ? f[q] : 0.0;
+                            amb |= (!pos && e[q] > lo_b * f[q]) ? (1u << (u * VE + h + q)) : 0u;
+                        }
+                    }
+                }
+            }
+            if (amb) {
+                for (int u = 0; u < NV; ++u)
+                    for (int q = 0; q < VE; ++q)
+                        if (amb & (1u << (u * VE + q))) {
+                            const int slot = atomicAdd(&S.namb, 1);
+                            if (slot < MAX_AMB) S.amb[slot] = lo + (u * NT2 + tid) * VE + q;
+                        }
+            }
+            block_sum<4>(S.R, v);
+            if (tid == 0) {
+                ChunkRec r;
+                r.sp = v[0]; r.sq = v[1]; r.e = v[2]; r.f = v[3];
+                const int n = S.namb;
+                r.namb = n < MAX_AMB + 1 ? n : MAX_AMB + 1;
+                for (int q = 0; q < MAX_AMB; ++q) r.amb[q] = q < n ? S.amb[q] : 0;
+                r.pad[0] = r.pad[1] = r.pad[2] = 0;
+                P.chunks[static_cast<size_t>(b) * NC + c] = r;
+            }
+        }
+        brA = brB;
+        brB = brC;
+        if constexpr (VEC) {
+#pragma unroll
+            for (int u = 0; u < NV; ++u) { tA[u] = tB[u]; dA[u] = dB[u]; }
+        }
+    }
+}
+
+struct DrawLdsBase {
+    RedT<NT2 / 64> R;
+    alignas(16) double TE[EXP_N];
     double mass[MAXC];
-    double scan[NT];
+    double scan[NT2 / 64];
     double base;
 };
 
+template <class E>
+struct DrawLds : DrawLdsBase {};
+
 // Mass of chunk c recomputed element by element (whole block, ordered).
 template <class E>
-__device__ double chunk_exact(const Params& P, const Pass2& Q, int c, DrawLds& S) {
+__device__ double chunk_exact(const Params& P, const Pass2& Q, int c, DrawLds<E>& S) {
     const int lo = c * CHUNK, hi = min(P.V, lo + CHUNK);
     double acc[1] = {0.0};
-    for (int j = lo + static_cast<int>(threadIdx.x); j < hi; j += NT) acc[0] += weight_at<E>(Q, j, S.T);
+    for (int j = lo + static_cast<int>(threadIdx.x); j < hi; j += NT2) acc[0] += weight_at<E>(Q, j, nullptr, S.TE);
     block_sum<1>(S.R, acc);
     return acc[0];
 }
 
+// The draw of batch row b: one workgroup per batch row.
 template <class E>
-__global__ __launch_bounds__(NT) void draw_kernel(Params P) {
-    __shared__ DrawLds S;
+__global__ __launch_bounds__(NT2) void draw_kernel(Params P) {
+    __shared__ DrawLds<E> S;
+    constexpr int VE = E::VE;
+    constexpr int NV = ChunkLayout<E>::NV;
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
-    const int a = P.desc[b];
-    if (a < 0) return;                                     // uniform: whole block leaves
+    const BatchRec br = P.bat[b];
+    if (br.a < 0) return;                                  // uniform: whole block leaves
+    copy_to_lds(S.TE, P.exptab, EXP_N);
     const int k = P.k, V = P.V, NC = P.nchunk;
+    const int a = br.a;
     const ChunkRec* recs = P.chunks + static_cast<size_t>(b) * NC;
-    exp_table_init(S.T);
-    Pass2 Q = pass2_setup<E>(P, b, a);
+    double sums[2] = {0.0, 0.0};
+    for (int c = tid; c < NC; c += NT2) { sums[0] += recs[c].sp; sums[1] += recs[c].sq; }
     const double u1 = P.uni[(static_cast<size_t>(b) * (k + 1) + a) * 2 + 1];
-    const double lh = P.lam_hat[b];
+    block_sum<2>(S.R, sums);                               // also publishes the exp table
+    Pass2 Q = pass2_setup<E>(P, b, br, S.TE);
+    const double lh = Q.lam_hat;
+    // The draw evaluates its few elements with the fp64 exp in the same units
+    // as the chunk records (for the bf16 table, exp(v/T - C) agrees with the
+    // table entry to ~1e-15 relative), so it needs no copy of the table.
+    Q.tab = 0;
 
     // exact normalisers
-    double sums[2] = {0.0, 0.0};
-    for (int c = tid; c < NC; c += NT) { sums[0] += recs[c].sp; sums[1] += recs[c].sq; }
-    block_sum<2>(S.R, sums);                               // also publishes the table
     Q.lam = Q.resid ? sums[0] / sums[1] : 0.0;
     const bool band_ok = !Q.resid ||
         (!P.force_exact && Q.lam >= lh * (1.0 - ETA) && Q.lam <= lh * (1.0 + ETA));
@@ -849,7 +1192,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
     double* M = S.mass;
     for (int attempt = 0; attempt < 2; ++attempt) {
         // chunk masses; NaN marks a chunk that must be recomputed exactly
-        for (int c = tid; c < NC; c += NT) {
+        for (int c = tid; c < NC; c += NT2) {
             const ChunkRec& r = recs[c];
             double m;
             if (!Q.resid) {
@@ -859,35 +1202,40 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
             } else {
                 m = r.e - Q.lam * r.f;
                 if (!(m > 0.0)) m = 0.0;
-                int id[MAX_AMB];
+                // band elements in index order (fixed summation order): a
+                // sorting network on four registers, unused slots last
                 const int n = r.namb;
-                for (int q = 0; q < n; ++q) id[q] = r.amb[q];
-                for (int x = 1; x < n; ++x)                // sort: fixed summation order
-                    for (int y = x; y > 0 && id[y - 1] > id[y]; --y) { const int t = id[y]; id[y] = id[y - 1]; id[y - 1] = t; }
-                for (int q = 0; q < n; ++q) m += weight_at<E>(Q, id[q], S.T);
+                int i0 = n > 0 ? r.amb[0] : 0x7fffffff, i1 = n > 1 ? r.amb[1] : 0x7fffffff;
+                int i2 = n > 2 ? r.amb[2] : 0x7fffffff, i3 = n > 3 ? r.amb[3] : 0x7fffffff;
+                auto cswap = [](int& x, int& y) { const int lo = min(x, y), hi = max(x, y); x = lo; y = hi; };
+                cswap(i0, i1); cswap(i2, i3); cswap(i0, i2); cswap(i1, i3); cswap(i1, i2);
+                if (n > 0) m += weight_at<E>(Q, i0, nullptr, S.TE);
+                if (n > 1) m += weight_at<E>(Q, i1, nullptr, S.TE);
+                if (n > 2) m += weight_at<E>(Q, i2, nullptr, S.TE);
+                if (n > 3) m += weight_at<E>(Q, i3, nullptr, S.TE);
             }
             M[c] = m;
         }
-        __syncthreads();
+        lds_sync();
         for (int c = 0; c < NC; ++c) {                    // rare: exact recompute
             if (M[c] != M[c]) {
-                __syncthreads();
+                lds_sync();
                 const double m = chunk_exact<E>(P, Q, c, S);
                 if (tid == 0) M[c] = m;
-                __syncthreads();
+                lds_sync();
             }
         }
-        __syncthreads();
+        lds_sync();
         // contiguous chunk ranges per thread -> ordered scan
-        const int cpt = (NC + NT - 1) / NT;
+        const int cpt = (NC + NT2 - 1) / NT2;
         const int c0 = min(NC, tid * cpt), c1 = min(NC, c0 + cpt);
         double mine = 0.0;
         for (int c = c0; c < c1; ++c) mine += M[c];
         double Z;
-        const double pre = block_exscan(S.scan, mine, Z);
+        const double pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
         if (Q.resid && !(Z > 0.0)) {                      // residual mass rounded to zero: use p_a
             Q.resid = false;
-            __syncthreads();
+            lds_sync();
             continue;
         }
         const double tgt = u1 * Z;
@@ -904,7 +1252,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
         cstar = block_min(S.R, cstar);
         if (cstar == 0x7fffffff) {                         // rounding: last chunk with mass
             int last = -1;
-            for (int c = tid; c < NC; c += NT) if (M[c] > 0.0) last = max(last, c);
+            for (int c = tid; c < NC; c += NT2) if (M[c] > 0.0) last = max(last, c);
             cstar = block_max(S.R, last);
             if (cstar < 0) cstar = 0;
         }
@@ -913,32 +1261,56 @@ __global__ __launch_bounds__(NT) void draw_kernel(Params P) {
             for (int c = c0; c < cstar; ++c) run += M[c];
             S.base = run;                                   // mass before c*
         }
-        // rescan c* in element order: EPT contiguous elements per thread, kept in registers
+        // rescan c* in element order: vector u of every thread in thread order
+        // covers [lo + u*NT2*VE, lo + (u+1)*NT2*VE), so the scan runs u by u
         const int lo = cstar * CHUNK, hi = min(V, lo + CHUNK);
-        const int j0 = lo + tid * EPT;
-        float xt[EPT], xd[EPT];
-        load_run<E>(Q.rowT, j0, hi, P.vec_ok, xt);
-        if (Q.resid) load_run<E>(Q.rowD, j0, hi, P.vec_ok, xd);
-        double w[EPT];
-        double wsum = 0.0;
-#pragma unroll
-        for (int q = 0; q < EPT; ++q) {
-            w[q] = weight_of(Q, xt[q], Q.resid ? xd[q] : 0.0f, S.T);
-            wsum += w[q];
-        }
-        __syncthreads();                                    // S.base visible
-        const double base = S.base;
-        double tot;
-        const double wpre = block_exscan(S.scan, wsum, tot);
+        lds_sync();                                    // S.base visible
+        double run0 = S.base;
         int tok = 0x7fffffff, lastpos = -1;
-        {
-            double run = base + wpre;
+        typename E::vec xt[NV], xd[NV];
+        if (P.vec_ok) {
+            const unsigned rowbytes = static_cast<unsigned>(V) * E::ES;
+            load_chunk<E>(Q.rowT, rowbytes, lo, xt);
+            load_chunk<E>(Q.rowD, Q.resid ? rowbytes : 0u, lo, xd);
+        }
+        for (int u = 0; u < NV; ++u) {
+            const int jv = lo + (u * NT2 + tid) * VE;
+            double w[VE];
+            double wsum = 0.0;
+            if (P.vec_ok) {
 #pragma unroll
-            for (int q = 0; q < EPT; ++q) {
-                if (w[q] > 0.0) lastpos = j0 + q;
-                run += w[q];
-                if (run > tgt && tok == 0x7fffffff) tok = j0 + q;
+                for (int h = 0; h < VE; h += 4) {
+                    double e[4], f[4] = {0.0, 0.0, 0.0, 0.0};
+                    vals4<E>(xt[u], h, Q.offT, Q, nullptr, S.TE, e);
+                    if (Q.resid) vals4<E>(xd[u], h, Q.offD, Q, nullptr, S.TE, f);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        double x = Q.resid ? e[q] - Q.lam * f[q] : e[q];
+                        if (!(x > 0.0) || jv + h + q >= hi) x = 0.0;
+                        w[h + q] = x;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < VE; ++q) w[q] = jv + q < hi ? weight_at<E>(Q, jv + q, nullptr, S.TE) : 0.0;
             }
+#pragma unroll
+            for (int q = 0; q < VE; ++q) wsum += w[q];
+            double tot;
+            const double wpre = block_exscan<NT2 / 64>(S.scan, wsum, tot);
+            if (tok == 0x7fffffff) {
+                double run = run0 + wpre;
+#pragma unroll
+                for (int q = 0; q < VE; ++q) {
+                    if (w[q] > 0.0) lastpos = jv + q;
+                    run += w[q];
+                    if (run > tgt && tok == 0x7fffffff) tok = jv + q;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < VE; ++q) if (w[q] > 0.0) lastpos = jv + q;
+            }
+            run0 += tot;
         }
         tok = block_min(S.R, tok);
         if (tok == 0x7fffffff) {
@@ -964,10 +1336,10 @@ int fail(int code, const char* fmt, ...) {
 }
 
 struct Plan {
-    int rpb, nchunk, chunk;
+    int rpb, nchunk;
     size_t rows_total;
     // workspace offsets (bytes)
-    size_t o_tiles, o_rows, o_desc, o_lam, o_chunks, total;
+    size_t o_tiles, o_bat, o_chunks, o_exp, o_tau, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -978,21 +1350,20 @@ bool make_plan(int32_t B, int32_t k, int32_t V, int mode, Plan& p) {
     p.rpb = mode == SPEC_MODE_SAMPLE ? 2 * k + 1 : k + 1;
     p.rows_total = static_cast<size_t>(B) * p.rpb;
     if (p.rows_total > (1u << 26)) return false;
+    if (V > (1 << 29)) return false;                       // a row must fit one buffer resource
     if (mode == SPEC_MODE_SAMPLE) {
         if (V > MAX_V) return false;
-        p.chunk = CHUNK;
         p.nchunk = (V + CHUNK - 1) / CHUNK;
     } else {
-        p.chunk = 0;
         p.nchunk = 0;
     }
     if (static_cast<size_t>(B) * static_cast<size_t>(p.nchunk) > 0x7fffffffUL) return false;
     size_t o = 0;
     p.o_tiles = o; o = align256(o + (p.rows_total + G_MAX) * sizeof(TileRec));
-    p.o_rows = o; o = align256(o + p.rows_total * sizeof(RowRec));
-    p.o_desc = o; o = align256(o + static_cast<size_t>(B) * sizeof(int));
-    p.o_lam = o; o = align256(o + static_cast<size_t>(B) * sizeof(double));
+    p.o_bat = o; o = align256(o + static_cast<size_t>(B) * sizeof(BatchRec));
     p.o_chunks = o; o = align256(o + static_cast<size_t>(B) * p.nchunk * sizeof(ChunkRec));
+    p.o_exp = o; o = align256(o + EXP_N * sizeof(double));
+    p.o_tau = o; o = align256(o + TAB_MAX * sizeof(double));
     p.total = o;
     return true;
 }
@@ -1037,7 +1408,18 @@ int scan_blocks_per_cu(int dev) {
     static int cache[64] = {0};
     if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_scan_kernel<E, MODE>, NT, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<E, MODE>, NT, 0) != hipSuccess || n < 1)
+        n = 1;
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    return n;
+}
+
+template <class E, bool VEC>
+int chunk_blocks_per_cu(int dev) {
+    static int cache[64] = {0};
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<E, VEC>, NT2, 0) != hipSuccess || n < 1)
         n = 1;
     if (dev >= 0 && dev < 64) cache[dev] = n;
     return n;
@@ -1052,17 +1434,22 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     if (G < 1) G = 1;
     P.L = (P.N + G - 1) / G;
     P.G = static_cast<int>((P.N + P.L - 1) / P.L);
-    hipLaunchKernelGGL((row_scan_kernel<E, MODE>), dim3(P.G), dim3(NT), 0, s, P);
+    hipLaunchKernelGGL((scan_kernel<E, MODE>), dim3(P.G), dim3(NT), 0, s, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
     e = hipGetLastError();
     if (e != hipSuccess || MODE == SPEC_MODE_GREEDY) return e;
-    const unsigned nch = static_cast<unsigned>(P.B) * static_cast<unsigned>(P.nchunk);
-    hipLaunchKernelGGL((residual_chunk_kernel<E>), dim3(nch), dim3(NT), 0, s, P);
+    // persistent chunk workgroups: one resident round
+    const long long items = static_cast<long long>(P.B) * P.nchunk;
+    long long G2 = static_cast<long long>(ncu) * (P.vec_ok ? chunk_blocks_per_cu<E, true>(dev) : chunk_blocks_per_cu<E, false>(dev));
+    if (G2 > items) G2 = items;
+    if (G2 < 1) G2 = 1;
+    if (P.vec_ok) hipLaunchKernelGGL((chunk_kernel<E, true>), dim3(static_cast<unsigned>(G2)), dim3(NT2), 0, s, P);
+    else hipLaunchKernelGGL((chunk_kernel<E, false>), dim3(static_cast<unsigned>(G2)), dim3(NT2), 0, s, P);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((draw_kernel<E>), dim3(P.B), dim3(NT), 0, s, P);
+    hipLaunchKernelGGL((draw_kernel<E>), dim3(P.B), dim3(NT2), 0, s, P);
     return hipGetLastError();
 }
 
@@ -1108,22 +1495,56 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
     P.dprob = k > 0 ? draft_prob : nullptr;
     P.B = B; P.k = k; P.V = V;
     P.rpb = plan.rpb;
-    P.nchunk = plan.nchunk; P.chunk = plan.chunk;
+    P.nchunk = plan.nchunk;
     P.N = static_cast<long long>(plan.rows_total) * V;
     P.G = 0; P.L = 0;
     P.mode = mode;
     const char* fe = getenv("SPEC_VERIFY_FORCE_EXACT_PATH");
     P.force_exact = (fe && fe[0] == '1') ? 1 : 0;
     const double Td = mode == SPEC_MODE_SAMPLE ? static_cast<double>(temperature) : 1.0;
-    P.c = static_cast<float>(1.4426950408889634 / Td);
+    const double c = 1.4426950408889634 / Td;
+    // c = ch + cl. ch: c rounded toward zero to (bf16) 16 or (fp32) 24
+    // significant bits, so x*ch is exact for bf16 x. cl: the rest, kept
+    // strictly positive so that x = -inf gives -inf (not -inf + inf) in
+    // x*ch - ref + x*cl.
+    float ch = static_cast<float>(c);
+    uint32_t u;
+    memcpy(&u, &ch, 4);
+    if (static_cast<double>(ch) > c) --u;                  // toward zero
+    const uint32_t unit = dtype == SPEC_DTYPE_BF16 ? 0x100u : 0x1u;
+    u &= ~(unit - 1u);
+    memcpy(&ch, &u, 4);
+    if (static_cast<double>(ch) == c && u >= unit) {
+        u -= unit;
+        memcpy(&ch, &u, 4);
+    }
+    float cl = static_cast<float>(c - static_cast<double>(ch));
+    if (!(cl > 0.0f)) cl = 1.17549435e-38f;                // smallest normal float
+    P.ch = ch;
+    P.cl = cl;
+    P.c = static_cast<double>(P.ch) + static_cast<double>(P.cl);
     P.invT = 1.0 / Td;
     P.vec_ok = aligned(target_logits, 16) && (draft_logits == nullptr || aligned(draft_logits, 16)) &&
                (static_cast<size_t>(V) * (dtype == SPEC_DTYPE_F32 ? 4 : 2)) % 16 == 0;
     P.tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
-    P.rows = reinterpret_cast<RowRec*>(ws + plan.o_rows);
-    P.desc = reinterpret_cast<int*>(ws + plan.o_desc);
-    P.lam_hat = reinterpret_cast<double*>(ws + plan.o_lam);
+    P.bat = reinterpret_cast<BatchRec*>(ws + plan.o_bat);
     P.chunks = reinterpret_cast<ChunkRec*>(ws + plan.o_chunks);
+    P.exptab = reinterpret_cast<double*>(ws + plan.o_exp);
+    P.tautab = reinterpret_cast<double*>(ws + plan.o_tau);
+    // bf16 value table: |v| in [2^-24, 2^kmax), kmax <= 8 the largest with
+    // 2^kmax / T <= 700, centred by C = 2^kmax/T - 600
+    P.tab_range = 0;
+    P.tab_lim = 0.0;
+    P.tab_c = 0.0;
+    if (dtype == SPEC_DTYPE_BF16 && mode == SPEC_MODE_SAMPLE) {
+        int kmax = static_cast<int>(floor(log2(700.0 * Td)));
+        if (kmax > 8) kmax = 8;
+        if (kmax > -20) {
+            P.tab_range = (kmax + 24) * 128;
+            P.tab_lim = ldexp(1.0, kmax);
+            P.tab_c = P.tab_lim / Td - 600.0;
+        }
+    }
 
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -1143,6 +1564,6 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
 
 const char* spec_verify_last_error(void) { return g_err; }
 
-const char* spec_verify_version(void) { return "specverify 0.2.0 (gfx950)"; }
+const char* spec_verify_version(void) { return "specverify 0.3.0 (gfx950)"; }
 
 }  // extern "C"
