@@ -83,6 +83,8 @@ inline double __hiloint2double(int hi, int lo) {
 #define __builtin_amdgcn_fence(...) __atomic_thread_fence(__ATOMIC_SEQ_CST)
 #define __builtin_amdgcn_s_barrier() __syncthreads()
 #define __builtin_amdgcn_readfirstlane(x) (x)
+// the occupancy hint of a kernel means nothing here
+#define amdgpu_waves_per_eu(...) unused
 
 #define __HIP_MEMORY_SCOPE_AGENT 0
 #define __hip_atomic_fetch_add(p, v, o, s) __atomic_fetch_add((p), (v), (o))
@@ -115,6 +117,9 @@ inline void emu_yield() {
 }
 
 inline void __syncthreads() { emu_yield(); }
+// a wave barrier: every lane of the workgroup reaches it (the kernels call it
+// in wave-uniform code), so a yield orders the lanes of each wave as well
+inline void __builtin_amdgcn_wave_barrier() { emu_yield(); }
 
 template <class T>
 inline T __shfl_xor(T v, int mask, int width = 64) {

@@ -168,6 +168,15 @@ def masks_large_k():
 
 
 @case
+def bf16_long_rows():
+    # bf16 rows long enough that each pass-2 wave loads several groups of
+    # vectors (one CU: one workgroup per batch row), aligned and unaligned rows
+    rng = np.random.default_rng(5)
+    for V in (60000, 60001):
+        run_case(rand_case(rng, 8, 2, V, 1, 1.0), cus=1)
+
+
+@case
 def greedy_bf16():
     rng = np.random.default_rng(2)
     run_case(rand_case(rng, 6, 3, 20000, 1, 1.0, mode=1, coarse=True), cus=2)

@@ -57,6 +57,10 @@ def test_emulated_masks_and_largest_k(emu_lib):
     run_cases("masks_large_k")
 
 
+def test_emulated_bf16_long_rows(emu_lib):
+    run_cases("bf16_long_rows")
+
+
 def test_emulated_concurrent_workgroups(emu_lib):
     run_cases("concurrent_b8")
 

@@ -5,8 +5,9 @@
 // greedy argmax matching of "The Inference Wall" part 7; the top-1 minus top-2
 // logit gap of "Speculative Pre-Positioning", Eq. 11).
 //
-// Four stream-ordered kernels per call; no workgroup ever waits on another
-// (every hand-over between them is a kernel boundary).
+// Three stream-ordered kernels per call in sampling mode (two in greedy mode);
+// no workgroup ever waits on another (every hand-over between them is a kernel
+// boundary).
 //
 //  1. scan_kernel -- one resident round of workgroups, each streaming an equal
 //     slice of the flattened (row, element) space (a slice may span row
@@ -18,22 +19,24 @@
 //     ref = ceil(max*c), so rescaling when the running max grows is an exact
 //     power-of-two ldexp. The lane whose vector holds the row's draft token
 //     keeps that logit. Greedy mode also finds the first index of the max.
-//  2. decide_kernel -- one workgroup per batch row: merges the segments of its
+//  2. The decision of a batch row (decide_batch): merges the segments of its
 //     rows, writes the gaps, evaluates every acceptance test
 //     r_i = p_i(x_i)/q_i(x_i) in the log2 domain in fp64, finds the first
 //     rejection a and writes every output except the token the sampling draw
-//     will produce.
-//  3. chunk_kernel (sampling) -- the residual max(0, p_a - q_a), or the bonus
+//     will produce. Greedy mode runs it as decide_kernel; sampling mode runs
+//     it at the start of every pass-2 workgroup.
+//  3. seg_kernel (sampling) -- the residual max(0, p_a - q_a), or the bonus
 //     p_k, is drawn by an inverse CDF that must resolve ~1e-13 of the mass at
-//     V ~ 10^5, so this pass is fp64 (branch-free table-driven double exp). One
-//     workgroup covers CHUNK elements of the selected row pair. The residual is
-//     linearised, w_x = (e_x - lambda f_x)/S_p with lambda = S_p/S_q, so a single
-//     read gives S_p, S_q and, over the elements whose sign is certain under
-//     pass 1's estimate of lambda (relative band ETA), the sums E, F; elements
-//     inside the band are recorded by index and settled once lambda is exact.
-//  4. draw_kernel (sampling) -- one workgroup per batch row: exact lambda, chunk
-//     masses, ordered scan to the chunk holding u*Z, fp64 rescan of that chunk
-//     in vocabulary order.
+//     V ~ 10^5, so this pass is fp64 (a value table for bf16 logits, else a
+//     table-driven double exp). The selected row pair is split into one
+//     segment per wave. The residual is linearised, w_x = (e_x - lambda f_x)/S_p
+//     with lambda = S_p/S_q, so a single read gives S_p, S_q and, over the
+//     elements whose sign is certain under pass 1's estimate of lambda
+//     (relative band ETA), the sums E, F; elements inside the band are
+//     recorded with their values and settled once lambda is exact.
+//  4. draw_kernel (sampling) -- one workgroup per batch row: exact lambda,
+//     segment masses, ordered scan to the segment holding u*Z, fp64 rescan of
+//     that segment in vocabulary order.
 //
 // Every reduction uses a fixed order, so results are bitwise reproducible.
 
@@ -54,15 +57,20 @@ constexpr int NT = 256;                 // threads per workgroup (4 wave64)
 constexpr int NWAVE = NT / 64;
 constexpr int MAX_AMB = 4;              // band elements recorded per chunk (the draw sorts 4)
 constexpr int NT2 = 512;                // threads per pass-2 workgroup (8 wave64)
-constexpr int MAXC = 1024;              // max pass-2 chunks per row (LDS capacity)
-constexpr int CHUNK = 8192;             // pass-2 chunk length (elements)
-constexpr int MAX_V = MAXC * CHUNK;     // largest supported vocabulary
+constexpr int W_CAP = 512;              // most pass-2 workgroups per batch row
+constexpr int MAXS = W_CAP * (NT2 / 64); // most pass-2 segments per row (one per wave)
+constexpr int SEG_U = 6;                // vectors per lane and row loaded together in pass 2
+constexpr int SLOTS_CAP = 4096;         // most resident pass-2 workgroups assumed by the workspace
+constexpr int MAX_V = SPEC_MAX_V_SAMPLE; // largest vocabulary of sampling mode
 constexpr double ETA = 1e-5;            // relative band around pass 1's lambda estimate
 constexpr int G_MAX = 16384;            // most pass-1 workgroups one launch uses
 constexpr int MIN_SLICE = 8192;         // smallest pass-1 slice (elements) worth a workgroup
 constexpr int EXP_N = 1024;             // entries of the 2^(j/N) table of the fp64 exp
-constexpr unsigned TAB_BASE = 103u << 7;  // bf16 magnitude bits of 2^-24 (start of the value table)
-constexpr int TAB_MAX = 8192;           // value-table entries: two signs of at most 32 binades of 128
+constexpr unsigned TAB_BASE = 111u << 7;  // bf16 magnitude bits of 2^-16 (start of the value table)
+constexpr unsigned TAB_RANGE = 24u << 7;  // magnitudes per sign: 24 binades, 2^-16 <= |v| < 2^8
+constexpr unsigned TAB_TOP = TAB_BASE + TAB_RANGE - 1u;
+constexpr unsigned TAB_NEG = 4096;      // entry of the first negative value
+constexpr int TAB_MAX = TAB_NEG + TAB_RANGE;  // value-table entries (entries RANGE..NEG-1 unused)
 
 enum : int { K_TARGET = 0, K_DRAFT = 1, K_GREEDY = 2 };
 
@@ -121,18 +129,19 @@ struct RowRec {
     int has_lx;
 };
 
-struct alignas(32) BatchRec {  // what pass 2 needs of one batch row
+struct alignas(32) BatchRec {  // what pass 2 and the draw need of one batch row
     int a;                     // row of the draw (k = bonus), -1 = no draw (invalid row)
-    int pad;
+    float u1;                  // uniform of the draw, u[b, a, 1]
     float mp, mq;              // max raw logit of target row a and (a < k) draft row a
-    double lam;                // pass-1 estimate of S_p/S_q at row a (a < k)
-    double pad2;
+    double lam;                // pass-1 estimate of S_p/S_q at row a (a < k), max-normalised
+    double lam_hat;            // the same in pass 2's units (written by pass 2)
 };
 
-struct alignas(64) ChunkRec {
+struct alignas(64) SegRec {    // one pass-2 segment (one wave's share of a row pair)
     double sp, sq, e, f;       // sum e, sum f, sums over the certain-positive set
+    double ae[MAX_AMB], af[MAX_AMB];  // e and f of the recorded band elements
     int namb;                  // band elements seen (> MAX_AMB: overflow)
-    int amb[MAX_AMB];
+    int amb[MAX_AMB];          // their indices
     int pad[3];
 };
 
@@ -146,7 +155,10 @@ struct Params {
     float* gap;
     float* tprob;
     float* dprob;
-    int B, k, V, rpb, nchunk;
+    int B, k, V, rpb;
+    int nvec;                  // 16-byte vectors per row: ceil(V / VE)
+    int wpb;                   // pass-2 workgroups per batch row (sampling)
+    int nseg, vps;             // pass-2 segments per row (one per wave) and vectors per segment
     int G;                     // pass-1 workgroups: one resident round
     long long L;               // elements per pass-1 workgroup (last one may get fewer)
     long long N;               // B * rpb * V: the flattened (row, element) space
@@ -157,11 +169,11 @@ struct Params {
     double invT;               // 1/T in double, pass 2
     TileRec* tiles;            // [B*rpb + G] segment records, slot = row + workgroup
     BatchRec* bat;             // [B]
-    ChunkRec* chunks;          // [B*nchunk]
+    SegRec* segs;              // [B*nseg]
     double* exptab;            // [EXP_N] 2^(j/EXP_N), written by pass 1 for pass 2
-    double* tautab;            // [2*tab_range] exp(v/T - tab_c) of bf16 values v, written by pass 1
-    int tab_range;             // bf16 table entries per sign (0: no table)
-    double tab_lim;            // the table covers 2^-24 <= |v| < tab_lim
+    double* tautab;            // [TAB_MAX] exp(v/T - tab_c) of bf16 values v, written by pass 1
+    int tab_on;                // the bf16 value table is built and usable
+    double tab_lim;            // the table covers 2^-16 <= |v| < tab_lim
     double tab_c;
 };
 
@@ -603,12 +615,12 @@ __global__ __launch_bounds__(NT) void scan_kernel(Params P) {
         const long long gi0 = w * NT + tid, gstride = static_cast<long long>(gridDim.x) * NT;
         for (long long j = gi0; j < EXP_N; j += gstride) P.exptab[j] = exp2(static_cast<double>(j) / EXP_N);
         if constexpr (E::ES == 2) {
-            const int range = P.tab_range;
-            for (long long j = gi0; j < 2LL * range; j += gstride) {
-                const unsigned sgn = j >= range ? 1u : 0u;
-                const unsigned bits = (sgn << 15) | (static_cast<unsigned>(j - sgn * range) + TAB_BASE);
+            for (long long j = gi0; j < TAB_MAX; j += gstride) {
+                const unsigned sgn = j >= TAB_NEG ? 1u : 0u;
+                const unsigned mi = static_cast<unsigned>(j) - sgn * TAB_NEG;
+                const unsigned bits = (sgn << 15) | (mi + TAB_BASE);
                 const double v = __uint_as_float(bits << 16);
-                P.tautab[j] = exp(fma(v, P.invT, -P.tab_c));
+                P.tautab[j] = mi < TAB_RANGE ? exp(fma(v, P.invT, -P.tab_c)) : 0.0;
             }
         }
     }
@@ -646,8 +658,10 @@ __global__ __launch_bounds__(NT) void scan_kernel(Params P) {
 struct Dec {
     RowRec rec[2 * SPEC_MAX_K + 1];
     int acc[SPEC_MAX_K + 1];
+    float u1[SPEC_MAX_K + 1];
     int a;
     int valid;
+    BatchRec br;
 };
 
 // Merge the segment records t[w0..w1] of one row in element order (earlier
@@ -684,11 +698,13 @@ __device__ inline RowRec merge_row(const TileRec* t, long long w0, long long w1)
     return rr;
 }
 
+// Decide batch row b in one workgroup (any size of at least k + 1 and rpb
+// threads): merge the segment records of its rows, evaluate the acceptance
+// tests, and return (in every thread) what pass 2 needs. With `write`, also
+// write the outputs and the batch record.
 template <class E, int MODE>
-__global__ __launch_bounds__(NT) void decide_kernel(Params P) {
-    __shared__ Dec D;
+__device__ BatchRec decide_batch(const Params& P, Dec& D, int b, bool write) {
     const int tid = threadIdx.x;
-    const int b = blockIdx.x;
     const int k = P.k, V = P.V, rpb = P.rpb;
     constexpr bool sample = MODE == SPEC_MODE_SAMPLE;
 
@@ -701,12 +717,13 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
         x = P.tok[static_cast<size_t>(b) * k + tid];
         if constexpr (sample) u0 = P.uni[(static_cast<size_t>(b) * (k + 1) + tid) * 2];
     }
+    if (sample && tid <= k) D.u1[tid] = P.uni[(static_cast<size_t>(b) * (k + 1) + tid) * 2 + 1];
     if (tid < rpb) {
         const size_t row = static_cast<size_t>(b) * rpb + tid;
         const long long r0 = static_cast<long long>(row) * V;
         const RowRec rr = merge_row<MODE>(P.tiles + row, r0 / P.L, (r0 + V - 1) / P.L);
         D.rec[tid] = rr;
-        if (tid <= k) {
+        if (write && tid <= k) {
             const float g = (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
             P.gap[static_cast<size_t>(b) * (k + 1) + tid] = g;
         }
@@ -743,8 +760,8 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
             }
         }
         D.acc[tid] = acc;
-        if (P.tprob) P.tprob[static_cast<size_t>(b) * k + tid] = ok ? pf : __builtin_nanf("");
-        if (P.dprob) P.dprob[static_cast<size_t>(b) * k + tid] = ok ? qf : __builtin_nanf("");
+        if (write && P.tprob) P.tprob[static_cast<size_t>(b) * k + tid] = ok ? pf : __builtin_nanf("");
+        if (write && P.dprob) P.dprob[static_cast<size_t>(b) * k + tid] = ok ? qf : __builtin_nanf("");
     }
     if (!ok) atomicAnd(&D.valid, 0);
     lds_sync();
@@ -756,7 +773,7 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     }
     lds_sync();
     const int a = D.a;
-    if (tid <= k) {
+    if (write && tid <= k) {
         int o;
         if (!valid) o = -1;
         else if (tid < a) o = x;
@@ -765,29 +782,36 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
         P.out_tok[static_cast<size_t>(b) * (k + 1) + tid] = o;
     }
     if (tid == 0) {
-        P.acc_len[b] = valid ? a : -1;
-        if constexpr (sample) {
-            BatchRec br;
-            br.a = valid ? a : -1;
-            br.pad = 0;
-            br.mp = D.rec[a].m;
-            br.mq = a < k ? D.rec[k + 1 + a].m : 0.0f;
-            br.lam = 0.0;
-            br.pad2 = 0.0;
-            if (valid && a < k) {
-                // S_p/S_q in the exp((x - m)/T) normalisation of pass 2: only
-                // used to place a relative band of ETA, so 2^d is taken as
-                // 2^round(d) * exp2f(d - round(d)) (relative error ~1e-7)
-                const RowRec& rt = D.rec[a];
-                const RowRec& rd = D.rec[k + 1 + a];
-                const double c = P.c;
-                const double d = (rt.lg - static_cast<double>(rt.m) * c) - (rd.lg - static_cast<double>(rd.m) * c);
-                const double n = rint(d);
-                br.lam = ldexp(static_cast<double>(exp2f(static_cast<float>(d - n))), static_cast<int>(n));
-            }
-            P.bat[b] = br;
+        if (write) P.acc_len[b] = valid ? a : -1;
+        BatchRec br;
+        br.a = valid ? a : -1;
+        br.u1 = sample ? D.u1[a] : 0.0f;
+        br.mp = D.rec[a].m;
+        br.mq = sample && a < k ? D.rec[k + 1 + a].m : 0.0f;
+        br.lam = 0.0;
+        br.lam_hat = 0.0;
+        if (sample && valid && a < k) {
+            // S_p/S_q in the exp((x - m)/T) normalisation of pass 2: only
+            // used to place a relative band of ETA, so 2^d is taken as
+            // 2^round(d) * exp2f(d - round(d)) (relative error ~1e-7)
+            const RowRec& rt = D.rec[a];
+            const RowRec& rd = D.rec[k + 1 + a];
+            const double c = P.c;
+            const double d = (rt.lg - static_cast<double>(rt.m) * c) - (rd.lg - static_cast<double>(rd.m) * c);
+            const double n = rint(d);
+            br.lam = ldexp(static_cast<double>(exp2f(static_cast<float>(d - n))), static_cast<int>(n));
         }
+        D.br = br;
     }
+    lds_sync();
+    return D.br;
+}
+
+// Greedy mode: the decisions are the whole result after pass 1.
+template <class E, int MODE>
+__global__ __launch_bounds__(NT) void decide_kernel(Params P) {
+    __shared__ Dec D;
+    decide_batch<E, MODE>(P, D, blockIdx.x, true);
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -828,8 +852,11 @@ __device__ inline double exp_fast(double y, const double* T) {
 
 // A bf16 logit takes one of 2^16 values, so for bf16 inputs pass 2 reads
 // tau(v) = exp(v/T - C) from a table indexed by the value's bits for every v
-// with 2^-24 <= |v| < 2^kmax (kmax <= 8, the largest with 2^kmax/T <= 700; C
-// centres the range so that a sum of V entries cannot overflow). Other values
+// with 2^-16 <= |v| < 2^8 (positive values at entry m - TAB_BASE for
+// magnitude bits m, negative ones TAB_NEG entries further). The table is used
+// for a batch row only when both rows' maxima lie below 2^kmax (kmax <= 8,
+// the largest with 2^kmax/T <= 700); C = 2^kmax/T - 600 keeps every entry
+// such a row can read finite, and a sum of V of them from overflowing. Other values
 // (zero, tiny, -inf, very negative) take the fp64 exp of the same argument. A
 // batch row uses the table when its rows' maxima lie inside it; otherwise
 // every element takes the fp64 exp normalised by its row maximum. Either way
@@ -838,34 +865,35 @@ __device__ inline double exp_fast(double y, const double* T) {
 struct Pass2 {
     const void* rowT;
     const void* rowD;
+    unsigned bytes;            // bytes of one row
     double invT;
     double offT, offD;         // added to x/T inside the exp: -C (table) or -m/T (row max)
+    double dm;                 // (m_p - m_q)/T
     double lam;                // S_p/S_q in this batch row's units (set by the draw)
     double lam_hat;            // pass 1's estimate of it, same units
     int tab;                   // values come from the bf16 table
-    int range;                 // table entries per sign
     bool resid;
 };
 
+// Rows, exponent offsets and table choice of the draw of batch row b at row
+// br.a (lam_hat is still in pass 1's units here).
 template <class E>
-__device__ inline Pass2 pass2_setup(const Params& P, int b, const BatchRec& br, const double* TE) {
+__device__ inline Pass2 pass2_rows(const Params& P, int b, const BatchRec& br) {
     const int k = P.k, V = P.V, a = br.a < 0 ? 0 : br.a;
     Pass2 Q;
     Q.resid = a < k;
     Q.rowT = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + a) * V * E::ES;
     Q.rowD = Q.resid ? static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + a) * V * E::ES
                      : Q.rowT;
+    Q.bytes = static_cast<unsigned>(V) * E::ES;
     Q.invT = P.invT;
     const double mp = br.mp, mq = Q.resid ? static_cast<double>(br.mq) : mp;
-    const double dm = (mp - mq) * P.invT;
-    Q.tab = E::ES == 2 && P.tab_range > 0 && fabs(mp) < P.tab_lim && fabs(mq) < P.tab_lim && fabs(dm) < 600.0;
-    Q.range = P.tab_range;
+    Q.dm = (mp - mq) * P.invT;
+    Q.tab = E::ES == 2 && P.tab_on && fabs(mp) < P.tab_lim && fabs(mq) < P.tab_lim && fabs(Q.dm) < 600.0;
     Q.offT = Q.tab ? -P.tab_c : -mp * P.invT;
     Q.offD = Q.tab ? -P.tab_c : -mq * P.invT;
     Q.lam = 0.0;
-    // pass 1 estimates S_p/S_q with both sums normalised by their row maxima;
-    // in table units each sum carries exp(m/T - C) more
-    Q.lam_hat = Q.tab ? br.lam * exp_fast(dm, TE) : br.lam;
+    Q.lam_hat = br.lam;
     return Q;
 }
 
@@ -873,7 +901,7 @@ __device__ inline Pass2 pass2_setup(const Params& P, int b, const BatchRec& br, 
 __device__ inline double val_bf16(unsigned bits, double off, const Pass2& Q, const double* TT, const double* TE) {
     if (Q.tab) {
         const unsigned key = (bits & 0x7fffu) - TAB_BASE;
-        if (key < static_cast<unsigned>(Q.range)) return TT[key + (bits >> 15) * static_cast<unsigned>(Q.range)];
+        if (key < TAB_RANGE) return TT[key + (bits >> 15) * TAB_NEG];
     }
     return exp_fast(fma(static_cast<double>(__uint_as_float(bits << 16)), Q.invT, off), TE);
 }
@@ -896,41 +924,54 @@ __device__ inline unsigned bf16_bits(const u32x4& w, int q) {
     return (q & 1) ? (word >> 16) : (word & 0xffffu);
 }
 
-// Values of elements q0 .. q0+3 of a 16-byte vector. With the bf16 table,
-// every lane first reads all four table entries (out-of-range values read
-// entry 0), so the LDS reads issue back to back; the rare out-of-range values
-// then take the fp64 exp in one divergent fix-up.
-template <class E>
-__device__ inline void vals4(const typename E::vec& w, int q0, double off, const Pass2& Q, const double* TT,
-                             const double* TE, double (&out)[4]) {
-    if constexpr (E::ES == 2) {
-        if (Q.tab) {
-            const unsigned range = static_cast<unsigned>(Q.range);
-            unsigned oor = 0;
+// out[q] = v where q == z, every other entry kept (z is not known at compile
+// time; the array stays in registers).
+template <int N>
+__device__ inline void put_at(double (&out)[N], int z, double v) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const unsigned bits = bf16_bits(w, q0 + q);
-                const unsigned key = (bits & 0x7fffu) - TAB_BASE;
-                const bool in = key < range;
-                out[q] = TT[in ? key + (bits >> 15) * range : 0u];
-                oor |= in ? 0u : (1u << q);
+    for (int q = 0; q < N; ++q) out[q] = q == z ? v : out[q];
+}
+
+// The fp64 exp of element q (0..7) of a bf16 vector, in pass 2's units.
+__device__ inline double val_exp_bf16(const u32x4& w, int q, double off, const Pass2& Q, const double* TE) {
+    return exp_fast(fma(static_cast<double>(__uint_as_float(bf16_bits(w, q) << 16)), Q.invT, off), TE);
+}
+
+// Values of the VE elements of one 16-byte vector. With the bf16 table every
+// lane reads all eight entries first (a magnitude outside the table is clamped
+// to its edge, so the read stays inside it), so the LDS reads issue back to
+// back; the rare out-of-range values then take the fp64 exp in a compact
+// divergent loop. TAB = false: every value by the fp64 exp, unrolled (the
+// draw's few elements).
+template <class E, bool TAB = true>
+__device__ inline void vals_vec(const typename E::vec& w, double off, const Pass2& Q, const double* TT,
+                                const double* TE, double (&out)[E::VE]) {
+    if constexpr (E::ES == 2 && !TAB) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) out[q] = val_exp_bf16(w, q, off, Q, TE);
+    } else if constexpr (E::ES == 2) {
+        if (Q.tab) {
+            bool oor = false;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const unsigned word = (q >> 1) == 0 ? w.x : (q >> 1) == 1 ? w.y : (q >> 1) == 2 ? w.z : w.w;
+                // magnitude bits, and TAB_NEG for a negative value
+                const unsigned m = (q & 1) ? (word >> 16) & 0x7fffu : word & 0x7fffu;
+                const unsigned sg = (q & 1) ? (word >> 19) & TAB_NEG : (word & 0x8000u) >> 3;
+                const unsigned mc = min(max(m, TAB_BASE), TAB_TOP);
+                oor |= mc != m;
+                out[q] = TT[mc - TAB_BASE + sg];
             }
-            if (oor) {                                     // rare: one value at a time
-                for (int q = 0; q < 4; ++q) {
-                    if (oor & (1u << q)) {
-                        const double y = fma(static_cast<double>(__uint_as_float(bf16_bits(w, q0 + q) << 16)), Q.invT, off);
-                        const double ev = exp_fast(y, TE);
-                        out[0] = q == 0 ? ev : out[0];
-                        out[1] = q == 1 ? ev : out[1];
-                        out[2] = q == 2 ? ev : out[2];
-                        out[3] = q == 3 ? ev : out[3];
-                    }
+            if (oor) {                                     // rare
+#pragma unroll 1
+                for (int q = 0; q < 8; ++q) {
+                    if ((bf16_bits(w, q) & 0x7fffu) - TAB_BASE >= TAB_RANGE)
+                        put_at(out, q, val_exp_bf16(w, q, off, Q, TE));
                 }
             }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                out[q] = exp_fast(fma(static_cast<double>(__uint_as_float(bf16_bits(w, q0 + q) << 16)), Q.invT, off), TE);
+        } else {                                           // rows outside the table's range
+#pragma unroll 1
+            for (int q = 0; q < 8; ++q) put_at(out, q, val_exp_bf16(w, q, off, Q, TE));
         }
     } else {
         const float x[4] = {w.x, w.y, w.z, w.w};
@@ -948,356 +989,423 @@ __device__ inline double weight_at(const Pass2& Q, int j, const double* TT, cons
     return w > 0.0 ? w : 0.0;
 }
 
-// Vector u of thread t in a chunk covers elements lo + (u*NT2 + t)*VE + [0, VE):
-// every vector load instruction reads NT2*16 contiguous bytes.
+// Elements q >= n of a vector set to -inf (weight 0): the row's last vector
+// when V is not a multiple of VE.
 template <class E>
-struct ChunkLayout {
-    static constexpr int VE = E::VE;
-    static constexpr int NV = CHUNK / (NT2 * VE);     // vectors per thread per row
-    static_assert(NV * NT2 * VE == CHUNK, "chunk is whole vectors per thread");
-};
-
-// 16-byte buffer loads of the NV vectors of this thread in chunk `lo` of a row
-// of `bytes` bytes (bytes = 0 reads zeros without touching memory).
-template <class E>
-__device__ inline void load_chunk(const void* row, unsigned bytes, int lo, typename E::vec (&x)[ChunkLayout<E>::NV]) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, bytes);
-    const unsigned voff = (static_cast<unsigned>(lo) / E::VE + threadIdx.x) * 16u;
+__device__ inline void mask_tail(typename E::vec& x, int n) {
+    if constexpr (E::ES == 2) {
+        unsigned wd[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int u = 0; u < ChunkLayout<E>::NV; ++u) {
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff), u * NT2 * 16, 0);
-        x[u] = __builtin_bit_cast(typename E::vec, w);
+        for (int q = 0; q < 8; ++q)
+            if (q >= n) wd[q >> 1] = (q & 1) ? ((wd[q >> 1] & 0xffffu) | 0xff800000u) : ((wd[q >> 1] & 0xffff0000u) | 0xff80u);
+        x.x = wd[0]; x.y = wd[1]; x.z = wd[2]; x.w = wd[3];
+    } else {
+        float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q >= n) v[q] = -INFINITY;
+        x.x = v[0]; x.y = v[1]; x.z = v[2]; x.w = v[3];
     }
 }
 
+// Vector vi (VE elements, 16 bytes) of a row: one buffer load when rows are
+// 16-byte aligned (VEC), else VE element loads. A lane that is not `in` reads
+// zeros without touching memory. Elements past V are not masked here.
+template <class E, bool VEC>
+__device__ inline typename E::vec load_vec(__amdgpu_buffer_rsrc_t rs, const void* row, unsigned bytes, int vi,
+                                           int V, bool in) {
+    if constexpr (VEC) {
+        const unsigned voff = in ? static_cast<unsigned>(vi) * 16u : bytes;
+        return __builtin_bit_cast(typename E::vec, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff), 0, 0));
+    } else {
+        (void)rs; (void)bytes;
+        const int j0 = vi * E::VE;
+        if constexpr (E::ES == 2) {
+            const unsigned short* r = static_cast<const unsigned short*>(row);
+            unsigned h[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) h[q] = (in && j0 + q < V) ? r[j0 + q] : 0u;
+            u32x4 w;
+            w.x = h[0] | (h[1] << 16); w.y = h[2] | (h[3] << 16);
+            w.z = h[4] | (h[5] << 16); w.w = h[6] | (h[7] << 16);
+            return w;
+        } else {
+            const float* r = static_cast<const float*>(row);
+            f32x4 w;
+            w.x = (in && j0 < V) ? r[j0] : 0.0f;
+            w.y = (in && j0 + 1 < V) ? r[j0 + 1] : 0.0f;
+            w.z = (in && j0 + 2 < V) ? r[j0 + 2] : 0.0f;
+            w.w = (in && j0 + 3 < V) ? r[j0 + 3] : 0.0f;
+            return w;
+        }
+    }
+}
+
+// Band elements seen by one wave (pass 2): index and both values.
+struct WaveAmb {
+    int n;
+    int idx[MAX_AMB];
+    double e[MAX_AMB], f[MAX_AMB];
+};
+
 template <class E>
-struct ChunkLds {
+struct SegLds {
     RedT<NT2 / 64> R;
     alignas(16) double TT[E::ES == 2 ? TAB_MAX : 2];
     alignas(16) double TE[EXP_N];
-    int namb;
-    int amb[MAX_AMB];
+    Dec D;
+    WaveAmb A[NT2 / 64];
 };
 
-// Copy n doubles (n even) from global memory to LDS with 16-byte loads, up to
-// eight in flight per thread before any is stored (a workgroup of NT2 threads).
-__device__ inline void copy_to_lds(double* dst, const double* src, int n) {
-    const u32x4* s = reinterpret_cast<const u32x4*>(src);
-    u32x4* d = reinterpret_cast<u32x4*>(dst);
-    const int n16 = n / 2;
-    for (int base = 0; base < n16; base += 8 * NT2) {
-        u32x4 v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int i = base + q * NT2 + static_cast<int>(threadIdx.x);
-            if (i < n16) v[q] = s[i];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int i = base + q * NT2 + static_cast<int>(threadIdx.x);
-            if (i < n16) d[i] = v[q];
-        }
-    }
-}
-
-// pass 2's tables into LDS (visible after the caller's next barrier)
+// pass 2's tables held in registers between their loads and the LDS stores,
+// so the loads overlap the decision (NT2 threads: one vector of the exp table
+// and up to six of the value table per thread)
 template <class E>
-__device__ inline void load_tables(const Params& P, double* TT, double* TE) {
-    copy_to_lds(TE, P.exptab, EXP_N);
-    if constexpr (E::ES == 2) copy_to_lds(TT, P.tautab, 2 * P.tab_range);
-}
+struct TableRegs {
+    static constexpr int NTT = E::ES == 2 ? (TAB_MAX / 2 + NT2 - 1) / NT2 : 0;
+    static_assert(E::ES != 2 || NTT * NT2 * 2 == TAB_MAX, "whole vectors per thread");
+    u32x4 te;
+    u32x4 tt[NTT > 0 ? NTT : 1];
+};
 
-// Chunk records of the selected row pair (or bonus row) of every batch row.
-// Persistent workgroups walk the items (b, c) round robin; the next item's
-// vectors are loaded before the current one is reduced, and the item after
-// that has its batch record loaded, so loads overlap the fp64 arithmetic.
-// Rows that are not 16-byte aligned take element loads (VEC = false).
-template <class E, bool VEC>
-__global__ __launch_bounds__(NT2) void chunk_kernel(Params P) {
-    __shared__ ChunkLds<E> S;
-    using vec = typename E::vec;
-    constexpr int VE = E::VE;
-    constexpr int NV = ChunkLayout<E>::NV;
-    const int tid = threadIdx.x;
-    const int NC = P.nchunk;
-    const int nitems = P.B * NC;
-    const int G = gridDim.x;
-    const unsigned rowbytes = static_cast<unsigned>(P.V) * E::ES;
-    load_tables<E>(P, S.TT, S.TE);
-
-    auto row_of = [&](const BatchRec& br, int b, bool draft) -> const void* {
-        const int k = P.k, a = br.a < 0 ? 0 : br.a;
-        if (draft && a < k) return static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + a) * P.V * E::ES;
-        return static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + a) * P.V * E::ES;
-    };
-    // the item to prefetch may not exist: then it loads zeros from a zero-size range
-    auto issue = [&](int it, const BatchRec& br, vec (&xt)[NV], vec (&xd)[NV]) {
-        const bool ok = it < nitems && br.a >= 0;
-        const int b = ok ? it / NC : 0, c = ok ? it % NC : 0;
-        const bool resid = ok && br.a < P.k;
-        load_chunk<E>(row_of(br, b, false), ok ? rowbytes : 0u, c * CHUNK, xt);
-        load_chunk<E>(row_of(br, b, true), resid ? rowbytes : 0u, c * CHUNK, xd);
-    };
-    // the batch record of an item, moved to scalar registers (it is uniform)
-    auto batch_of = [&](int it) -> BatchRec {
-        const unsigned* src = reinterpret_cast<const unsigned*>(P.bat + (it < nitems ? it : nitems - 1) / NC);
-        unsigned w[sizeof(BatchRec) / 4];
+template <class E>
+__device__ inline void tables_fetch(const Params& P, TableRegs<E>& R) {
+    static_assert(EXP_N / 2 == NT2, "one exp-table vector per thread");
+    R.te = reinterpret_cast<const u32x4*>(P.exptab)[threadIdx.x];
+    if constexpr (E::ES == 2) {
+        if (P.tab_on) {
 #pragma unroll
-        for (unsigned q = 0; q < sizeof(BatchRec) / 4; ++q)
-            w[q] = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(src[q])));
-        BatchRec br;
-        memcpy(&br, w, sizeof(BatchRec));
-        if (it >= nitems) br.a = -1;                       // past the last item: nothing to do
-        return br;
-    };
-
-    int it = blockIdx.x;
-    BatchRec brA = batch_of(it);
-    vec tA[NV], dA[NV];
-    if constexpr (VEC) issue(it, brA, tA, dA);
-    BatchRec brB = batch_of(it + G);
-    lds_sync();                                       // tables ready
-    for (; it < nitems; it += G) {
-        // the batch record two items ahead first: a wait for it then does not
-        // drain the vector loads issued after it
-        const BatchRec brC = batch_of(it + 2 * G);
-        vec tB[NV], dB[NV];
-        if constexpr (VEC) issue(it + G, brB, tB, dB);
-        if (tid == 0) S.namb = 0;
-        lds_sync();                                   // thread 0 read the last item's band list
-        const int b = it / NC, c = it % NC;
-        if (brA.a >= 0) {                                  // uniform: invalid rows have no draw
-            const Pass2 Q = pass2_setup<E>(P, b, brA, S.TE);
-            const double hi_b = Q.lam_hat * (1.0 + ETA), lo_b = Q.lam_hat * (1.0 - ETA);
-            const int lo = c * CHUNK, hi = min(P.V, lo + CHUNK);
-            const bool partial = hi < lo + CHUNK;
-            double v[4] = {0.0, 0.0, 0.0, 0.0};
-            unsigned amb = 0;
-#pragma unroll
-            for (int u = 0; u < NV; ++u) {
-#pragma unroll
-                for (int h = 0; h < VE; h += 4) {                 // four elements at a time
-                    const int jv = lo + (u * NT2 + tid) * VE + h;
-                    double e[4], f[4];
-                    if constexpr (VEC) {
-                        vals4<E>(tA[u], h, Q.offT, Q, S.TT, S.TE, e);
-                        if (Q.resid) vals4<E>(dA[u], h, Q.offD, Q, S.TT, S.TE, f);
-                        if (partial) {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) if (jv + q >= hi) { e[q] = 0.0; f[q] = 0.0; }
-                        }
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const bool in = jv + q < hi;
-                            e[q] = in ? val_at<E>(Q.rowT, jv + q, Q.offT, Q, S.TT, S.TE) : 0.0;
-                            if (Q.resid) f[q] = in ? val_at<E>(Q.rowD, jv + q, Q.offD, Q, S.TT, S.TE) : 0.0;
-                        }
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        v[0] += e[q];
-                        if (Q.resid) {
-                            v[1] += f[q];
-                            // certain positive: e > lambda f for every lambda in
-                            // the band; band element: neither certainly positive
-                            // nor certainly non-positive
-                            const bool pos = e[q] > hi_b * f[q];
-                            v[2] += pos ? e[q] : 0.0;
-                            v[3] += pos ? f[q] : 0.0;
-                            amb |= (!pos && e[q] > lo_b * f[q]) ? (1u << (u * VE + h + q)) : 0u;
-                        }
-                    }
-                }
-            }
-            if (amb) {
-                for (int u = 0; u < NV; ++u)
-                    for (int q = 0; q < VE; ++q)
-                        if (amb & (1u << (u * VE + q))) {
-                            const int slot = atomicAdd(&S.namb, 1);
-                            if (slot < MAX_AMB) S.amb[slot] = lo + (u * NT2 + tid) * VE + q;
-                        }
-            }
-            block_sum<4>(S.R, v);
-            if (tid == 0) {
-                ChunkRec r;
-                r.sp = v[0]; r.sq = v[1]; r.e = v[2]; r.f = v[3];
-                const int n = S.namb;
-                r.namb = n < MAX_AMB + 1 ? n : MAX_AMB + 1;
-                for (int q = 0; q < MAX_AMB; ++q) r.amb[q] = q < n ? S.amb[q] : 0;
-                r.pad[0] = r.pad[1] = r.pad[2] = 0;
-                P.chunks[static_cast<size_t>(b) * NC + c] = r;
-            }
-        }
-        brA = brB;
-        brB = brC;
-        if constexpr (VEC) {
-#pragma unroll
-            for (int u = 0; u < NV; ++u) { tA[u] = tB[u]; dA[u] = dB[u]; }
+            for (int q = 0; q < TableRegs<E>::NTT; ++q)
+                R.tt[q] = reinterpret_cast<const u32x4*>(P.tautab)[q * NT2 + static_cast<int>(threadIdx.x)];
         }
     }
 }
 
-struct DrawLdsBase {
+template <class E>
+__device__ inline void tables_store(const Params& P, const TableRegs<E>& R, double* TT, double* TE) {
+    reinterpret_cast<u32x4*>(TE)[threadIdx.x] = R.te;
+    if constexpr (E::ES == 2) {
+        if (P.tab_on) {
+#pragma unroll
+            for (int q = 0; q < TableRegs<E>::NTT; ++q)
+                reinterpret_cast<u32x4*>(TT)[q * NT2 + static_cast<int>(threadIdx.x)] = R.tt[q];
+        }
+    }
+}
+
+// Sums of one wave's segment: S_p, S_q and, over the elements that are
+// certainly positive for every lambda in the band around lam_hat, E and F;
+// band elements go to the wave's list.
+template <class E, bool RESID>
+__device__ inline void seg_vector(const typename E::vec& xt, const typename E::vec& xd, int j0, const Pass2& Q,
+                                  double hi_b, double lo_b, const double* TT, const double* TE, WaveAmb& A,
+                                  double (&acc)[4]) {
+    constexpr int VE = E::VE;
+    double e[VE], f[VE];
+    vals_vec<E>(xt, Q.offT, Q, TT, TE, e);
+    if constexpr (RESID) vals_vec<E>(xd, Q.offD, Q, TT, TE, f);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) {
+        acc[0] += e[q];
+        if constexpr (RESID) {
+            acc[1] += f[q];
+            const bool pos = e[q] > hi_b * f[q];
+            const double pd = pos ? 1.0 : 0.0;
+            acc[2] = fma(e[q], pd, acc[2]);
+            acc[3] = fma(f[q], pd, acc[3]);
+            if (!pos && e[q] > lo_b * f[q]) {              // rare: inside the band
+                const int slot = atomicAdd(&A.n, 1);
+                if (slot < MAX_AMB) { A.idx[slot] = j0 + q; A.e[slot] = e[q]; A.f[slot] = f[q]; }
+            }
+        }
+    }
+}
+
+// Vectors per lane and row loaded together (element loads take more registers).
+template <bool VEC>
+struct SegU {
+    static constexpr int U = VEC ? SEG_U : 2;
+};
+
+template <class E, bool VEC, bool RESID>
+__device__ inline void seg_group(const Params& P, const Pass2& Q, __amdgpu_buffer_rsrc_t rsT,
+                                 __amdgpu_buffer_rsrc_t rsD, int v0, int v1, int t0, int T, double hi_b,
+                                 double lo_b, const double* TT, const double* TE, WaveAmb& A, double (&acc)[4],
+                                 const typename E::vec (&xt)[SegU<VEC>::U], const typename E::vec (&xd)[SegU<VEC>::U]) {
+    const int lane = threadIdx.x & 63;
+    const int tailn = P.V - (P.nvec - 1) * E::VE;          // elements of the row's last vector
+#pragma unroll
+    for (int u = 0; u < SegU<VEC>::U; ++u) {
+        const int vi = v0 + ((t0 + u) << 6) + lane;
+        if (t0 + u < T && vi < v1) {
+            typename E::vec a = xt[u], d = xd[u];
+            if (vi == P.nvec - 1 && tailn < E::VE) {       // rare: the row's partial last vector
+                mask_tail<E>(a, tailn);
+                if constexpr (RESID) mask_tail<E>(d, tailn);
+            }
+            seg_vector<E, RESID>(a, d, vi * E::VE, Q, hi_b, lo_b, TT, TE, A, acc);
+        }
+    }
+}
+
+template <class E, bool VEC, bool RESID>
+__device__ inline void seg_issue(const Pass2& Q, __amdgpu_buffer_rsrc_t rsT, __amdgpu_buffer_rsrc_t rsD, int V,
+                                 int v0, int v1, int t0, int T, typename E::vec (&xt)[SegU<VEC>::U],
+                                 typename E::vec (&xd)[SegU<VEC>::U]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < SegU<VEC>::U; ++u) {
+        const int vi = v0 + ((t0 + u) << 6) + lane;
+        const bool in = t0 + u < T && vi < v1;
+        xt[u] = load_vec<E, VEC>(rsT, Q.rowT, Q.bytes, vi, V, in);
+        if constexpr (RESID) xd[u] = load_vec<E, VEC>(rsD, Q.rowD, Q.bytes, vi, V, in);
+    }
+}
+
+// One wave's segment of a batch row, then its record.
+template <class E, bool VEC, bool RESID>
+__device__ inline void seg_run(const Params& P, const Pass2& Q, int b, int s, int v0, int v1, SegLds<E>& S) {
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(Q.rowT, Q.bytes);
+    const __amdgpu_buffer_rsrc_t rsD = make_rsrc(Q.rowD, RESID ? Q.bytes : 0u);
+    const int T = (v1 - v0 + 63) >> 6;
+    const double hi_b = Q.lam_hat * (1.0 + ETA), lo_b = Q.lam_hat * (1.0 - ETA);
+    WaveAmb& A = S.A[wv];
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int t0 = 0; t0 < T; t0 += SegU<VEC>::U) {
+        typename E::vec xt[SegU<VEC>::U], xd[SegU<VEC>::U];
+        seg_issue<E, VEC, RESID>(Q, rsT, rsD, P.V, v0, v1, t0, T, xt, xd);
+        seg_group<E, VEC, RESID>(P, Q, rsT, rsD, v0, v1, t0, T, hi_b, lo_b, S.TT, S.TE, A, acc, xt, xd);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = wave_sum(acc[q]);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    if (lane == 0) {
+        SegRec r;
+        r.sp = acc[0]; r.sq = acc[1]; r.e = acc[2]; r.f = acc[3];
+        const int n = A.n;
+        r.namb = n < MAX_AMB + 1 ? n : MAX_AMB + 1;
+#pragma unroll
+        for (int q = 0; q < MAX_AMB; ++q) {
+            const bool h = q < n;
+            r.amb[q] = h ? A.idx[q] : 0;
+            r.ae[q] = h ? A.e[q] : 0.0;
+            r.af[q] = h ? A.f[q] : 0.0;
+        }
+        r.pad[0] = r.pad[1] = r.pad[2] = 0;
+        P.segs[static_cast<size_t>(b) * P.nseg + s] = r;
+    }
+}
+
+// Pass 2, sampling mode. Batch row b has W = P.wpb workgroups of NT2/64 waves
+// and its selected row pair (or bonus row) is split into 8W equal segments of
+// whole 16-byte vectors, one per wave. Each workgroup decides b itself (the W
+// copies agree; workgroup 0 writes the outputs and the batch record), issues
+// its waves' loads, and then every wave streams its segment with lane-
+// interleaved vectors and no workgroup barrier, ending with one record.
+template <class E, bool VEC>
+__global__ __launch_bounds__(NT2) __attribute__((amdgpu_waves_per_eu(4))) void seg_kernel(Params P) {
+    __shared__ SegLds<E> S;
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
+    const int W = P.wpb;
+    const int b = blockIdx.x / W, w = blockIdx.x % W;
+    const int s = w * (NT2 / 64) + wv;
+    const int v0 = min(P.nvec, s * P.vps), v1 = min(P.nvec, v0 + P.vps);
+
+    TableRegs<E> TR;
+    tables_fetch<E>(P, TR);                                // in flight during the decision
+    BatchRec br = decide_batch<E, SPEC_MODE_SAMPLE>(P, S.D, b, w == 0);
+    tables_store<E>(P, TR, S.TT, S.TE);                    // arrived before the decision's loads
+    Pass2 Q = pass2_rows<E>(P, b, br);
+    if ((tid & 63) == 0) S.A[wv].n = 0;
+    lds_sync();                                            // tables and band lists ready
+    if (Q.tab) Q.lam_hat = br.lam * exp_fast(Q.dm, S.TE);  // into table units
+    if (w == 0 && tid == 0) {
+        br.lam_hat = Q.lam_hat;
+        P.bat[b] = br;
+    }
+    if (br.a < 0) return;                                  // uniform: whole block leaves
+    if (Q.resid) seg_run<E, VEC, true>(P, Q, b, s, v0, v1, S);
+    else seg_run<E, VEC, false>(P, Q, b, s, v0, v1, S);
+}
+
+struct DrawLds {
     RedT<NT2 / 64> R;
     alignas(16) double TE[EXP_N];
-    double mass[MAXC];
+    double mass[MAXS];
     double scan[NT2 / 64];
     double base;
 };
 
-template <class E>
-struct DrawLds : DrawLdsBase {};
+// Vectors [v0, v1) of segment s.
+__device__ inline void seg_range(const Params& P, int s, int& v0, int& v1) {
+    v0 = min(P.nvec, s * P.vps);
+    v1 = min(P.nvec, v0 + P.vps);
+}
 
-// Mass of chunk c recomputed element by element (whole block, ordered).
+// Mass of segment s recomputed element by element (whole block, ordered).
 template <class E>
-__device__ double chunk_exact(const Params& P, const Pass2& Q, int c, DrawLds<E>& S) {
-    const int lo = c * CHUNK, hi = min(P.V, lo + CHUNK);
+__device__ double seg_exact(const Params& P, const Pass2& Q, int s, DrawLds& S) {
+    int v0, v1;
+    seg_range(P, s, v0, v1);
+    const int lo = v0 * E::VE, hi = min(P.V, v1 * E::VE);
     double acc[1] = {0.0};
     for (int j = lo + static_cast<int>(threadIdx.x); j < hi; j += NT2) acc[0] += weight_at<E>(Q, j, nullptr, S.TE);
     block_sum<1>(S.R, acc);
     return acc[0];
 }
 
-// The draw of batch row b: one workgroup per batch row.
+// Mass of one segment from its record (NaN: must be recomputed exactly).
+__device__ inline double seg_mass(const SegRec& r, const Pass2& Q, bool band_ok) {
+    if (!Q.resid) return r.sp;
+    if (!band_ok || r.namb > MAX_AMB) return __builtin_nan("");
+    double m = r.e - Q.lam * r.f;
+    if (!(m > 0.0)) m = 0.0;
+    // band elements in index order (fixed summation order): a sorting network
+    // on four (index, slot) keys, unused slots last
+    const int n = r.namb;
+    int k0 = n > 0 ? r.amb[0] * 4 + 0 : 0x7fffffff, k1 = n > 1 ? r.amb[1] * 4 + 1 : 0x7fffffff;
+    int k2 = n > 2 ? r.amb[2] * 4 + 2 : 0x7fffffff, k3 = n > 3 ? r.amb[3] * 4 + 3 : 0x7fffffff;
+    auto cswap = [](int& x, int& y) { const int lo = min(x, y), hi = max(x, y); x = lo; y = hi; };
+    cswap(k0, k1); cswap(k2, k3); cswap(k0, k2); cswap(k1, k3); cswap(k1, k2);
+    const int ks[4] = {k0, k1, k2, k3};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q < n) {
+            const int sl = ks[q] & 3;
+            const double ae = sl == 0 ? r.ae[0] : sl == 1 ? r.ae[1] : sl == 2 ? r.ae[2] : r.ae[3];
+            const double af = sl == 0 ? r.af[0] : sl == 1 ? r.af[1] : sl == 2 ? r.af[2] : r.af[3];
+            const double w = ae - Q.lam * af;
+            m += w > 0.0 ? w : 0.0;
+        }
+    }
+    return m;
+}
+
+// The draw of batch row b: one workgroup per batch row. Exact lambda from the
+// segment sums, segment masses, ordered scan to the segment holding u*Z, and
+// an fp64 rescan of that segment in vocabulary order.
 template <class E>
 __global__ __launch_bounds__(NT2) void draw_kernel(Params P) {
-    __shared__ DrawLds<E> S;
+    __shared__ DrawLds S;
     constexpr int VE = E::VE;
-    constexpr int NV = ChunkLayout<E>::NV;
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
+    const int k = P.k, V = P.V, NS = P.nseg;
+    const SegRec* recs = P.segs + static_cast<size_t>(b) * NS;
+    // one round of independent loads: exp table, batch record, this thread's first segment record
+    const u32x4 te = reinterpret_cast<const u32x4*>(P.exptab)[tid];
     const BatchRec br = P.bat[b];
+    SegRec r0;
+    if (tid < NS) r0 = recs[tid];
+    reinterpret_cast<u32x4*>(S.TE)[tid] = te;
     if (br.a < 0) return;                                  // uniform: whole block leaves
-    copy_to_lds(S.TE, P.exptab, EXP_N);
-    const int k = P.k, V = P.V, NC = P.nchunk;
     const int a = br.a;
-    const ChunkRec* recs = P.chunks + static_cast<size_t>(b) * NC;
-    double sums[2] = {0.0, 0.0};
-    for (int c = tid; c < NC; c += NT2) { sums[0] += recs[c].sp; sums[1] += recs[c].sq; }
-    const double u1 = P.uni[(static_cast<size_t>(b) * (k + 1) + a) * 2 + 1];
-    block_sum<2>(S.R, sums);                               // also publishes the exp table
-    Pass2 Q = pass2_setup<E>(P, b, br, S.TE);
-    const double lh = Q.lam_hat;
+    Pass2 Q = pass2_rows<E>(P, b, br);
+    Q.lam_hat = br.lam_hat;
     // The draw evaluates its few elements with the fp64 exp in the same units
-    // as the chunk records (for the bf16 table, exp(v/T - C) agrees with the
+    // as the segment records (for the bf16 table, exp(v/T - C) agrees with the
     // table entry to ~1e-15 relative), so it needs no copy of the table.
     Q.tab = 0;
-
-    // exact normalisers
+    double sums[2] = {tid < NS ? r0.sp : 0.0, tid < NS ? r0.sq : 0.0};
+    for (int s = tid + NT2; s < NS; s += NT2) { sums[0] += recs[s].sp; sums[1] += recs[s].sq; }
+    block_sum<2>(S.R, sums);                               // also publishes the exp table
+    const double lh = Q.lam_hat;
     Q.lam = Q.resid ? sums[0] / sums[1] : 0.0;
     const bool band_ok = !Q.resid ||
         (!P.force_exact && Q.lam >= lh * (1.0 - ETA) && Q.lam <= lh * (1.0 + ETA));
+    const double u1 = br.u1;
 
     double* M = S.mass;
     for (int attempt = 0; attempt < 2; ++attempt) {
-        // chunk masses; NaN marks a chunk that must be recomputed exactly
-        for (int c = tid; c < NC; c += NT2) {
-            const ChunkRec& r = recs[c];
-            double m;
-            if (!Q.resid) {
-                m = r.sp;
-            } else if (!band_ok || r.namb > MAX_AMB) {
-                m = __builtin_nan("");
-            } else {
-                m = r.e - Q.lam * r.f;
-                if (!(m > 0.0)) m = 0.0;
-                // band elements in index order (fixed summation order): a
-                // sorting network on four registers, unused slots last
-                const int n = r.namb;
-                int i0 = n > 0 ? r.amb[0] : 0x7fffffff, i1 = n > 1 ? r.amb[1] : 0x7fffffff;
-                int i2 = n > 2 ? r.amb[2] : 0x7fffffff, i3 = n > 3 ? r.amb[3] : 0x7fffffff;
-                auto cswap = [](int& x, int& y) { const int lo = min(x, y), hi = max(x, y); x = lo; y = hi; };
-                cswap(i0, i1); cswap(i2, i3); cswap(i0, i2); cswap(i1, i3); cswap(i1, i2);
-                if (n > 0) m += weight_at<E>(Q, i0, nullptr, S.TE);
-                if (n > 1) m += weight_at<E>(Q, i1, nullptr, S.TE);
-                if (n > 2) m += weight_at<E>(Q, i2, nullptr, S.TE);
-                if (n > 3) m += weight_at<E>(Q, i3, nullptr, S.TE);
-            }
-            M[c] = m;
-        }
+        if (tid < NS) M[tid] = seg_mass(r0, Q, band_ok);
+        for (int s = tid + NT2; s < NS; s += NT2) M[s] = seg_mass(recs[s], Q, band_ok);
         lds_sync();
-        for (int c = 0; c < NC; ++c) {                    // rare: exact recompute
-            if (M[c] != M[c]) {
-                lds_sync();
-                const double m = chunk_exact<E>(P, Q, c, S);
-                if (tid == 0) M[c] = m;
-                lds_sync();
-            }
-        }
-        lds_sync();
-        // contiguous chunk ranges per thread -> ordered scan
-        const int cpt = (NC + NT2 - 1) / NT2;
-        const int c0 = min(NC, tid * cpt), c1 = min(NC, c0 + cpt);
+        // contiguous segment ranges per thread -> ordered scan
+        const int cpt = (NS + NT2 - 1) / NT2;
+        const int c0 = min(NS, tid * cpt), c1 = min(NS, c0 + cpt);
         double mine = 0.0;
         for (int c = c0; c < c1; ++c) mine += M[c];
         double Z;
-        const double pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
+        double pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
+        if (Z != Z) {                                      // rare: a segment must be recomputed exactly
+            for (int s = 0; s < NS; ++s) {
+                if (M[s] != M[s]) {
+                    const double m = seg_exact<E>(P, Q, s, S);
+                    if (tid == 0) M[s] = m;
+                    lds_sync();
+                }
+            }
+            mine = 0.0;
+            for (int c = c0; c < c1; ++c) mine += M[c];
+            pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
+        }
         if (Q.resid && !(Z > 0.0)) {                      // residual mass rounded to zero: use p_a
             Q.resid = false;
             lds_sync();
             continue;
         }
         const double tgt = u1 * Z;
-        // chunk holding the target
-        int cstar = 0x7fffffff;
+        // segment holding the target
+        int sstar = 0x7fffffff;
         {
             double run = pre;
             for (int c = c0; c < c1; ++c) {
                 const double nx = run + M[c];
-                if (nx > tgt) { cstar = c; break; }
+                if (nx > tgt) { sstar = c; break; }
                 run = nx;
             }
         }
-        cstar = block_min(S.R, cstar);
-        if (cstar == 0x7fffffff) {                         // rounding: last chunk with mass
+        sstar = block_min(S.R, sstar);
+        if (sstar == 0x7fffffff) {                         // rounding: last segment with mass
             int last = -1;
-            for (int c = tid; c < NC; c += NT2) if (M[c] > 0.0) last = max(last, c);
-            cstar = block_max(S.R, last);
-            if (cstar < 0) cstar = 0;
+            for (int c = tid; c < NS; c += NT2) if (M[c] > 0.0) last = max(last, c);
+            sstar = block_max(S.R, last);
+            if (sstar < 0) sstar = 0;
         }
-        if (c0 <= cstar && cstar < c1) {
+        if (c0 <= sstar && sstar < c1) {
             double run = pre;
-            for (int c = c0; c < cstar; ++c) run += M[c];
-            S.base = run;                                   // mass before c*
+            for (int c = c0; c < sstar; ++c) run += M[c];
+            S.base = run;                                   // mass before s*
         }
-        // rescan c* in element order: vector u of every thread in thread order
-        // covers [lo + u*NT2*VE, lo + (u+1)*NT2*VE), so the scan runs u by u
-        const int lo = cstar * CHUNK, hi = min(V, lo + CHUNK);
-        lds_sync();                                    // S.base visible
+        // rescan s* in element order: round r covers vectors v0 + r*NT2 + [0, NT2)
+        int v0, v1;
+        seg_range(P, sstar, v0, v1);
+        lds_sync();                                        // S.base visible
         double run0 = S.base;
         int tok = 0x7fffffff, lastpos = -1;
-        typename E::vec xt[NV], xd[NV];
-        if (P.vec_ok) {
-            const unsigned rowbytes = static_cast<unsigned>(V) * E::ES;
-            load_chunk<E>(Q.rowT, rowbytes, lo, xt);
-            load_chunk<E>(Q.rowD, Q.resid ? rowbytes : 0u, lo, xd);
-        }
-        for (int u = 0; u < NV; ++u) {
-            const int jv = lo + (u * NT2 + tid) * VE;
+        const __amdgpu_buffer_rsrc_t rsT = make_rsrc(Q.rowT, Q.bytes);
+        const __amdgpu_buffer_rsrc_t rsD = make_rsrc(Q.rowD, Q.resid ? Q.bytes : 0u);
+        const int tailn = V - (P.nvec - 1) * VE;
+        for (int vb = v0; vb < v1; vb += NT2) {
+            const int vi = vb + tid;
+            const bool in = vi < v1;
+            typename E::vec xt, xd;
+            if (P.vec_ok) {
+                xt = load_vec<E, true>(rsT, Q.rowT, Q.bytes, vi, V, in);
+                xd = load_vec<E, true>(rsD, Q.rowD, Q.bytes, vi, V, in && Q.resid);
+            } else {
+                xt = load_vec<E, false>(rsT, Q.rowT, Q.bytes, vi, V, in);
+                xd = load_vec<E, false>(rsD, Q.rowD, Q.bytes, vi, V, in && Q.resid);
+            }
+            if (vi == P.nvec - 1 && tailn < VE) { mask_tail<E>(xt, tailn); mask_tail<E>(xd, tailn); }
             double w[VE];
             double wsum = 0.0;
-            if (P.vec_ok) {
+            double e[VE], f[VE];
+            vals_vec<E, false>(xt, Q.offT, Q, nullptr, S.TE, e);
+            if (Q.resid) vals_vec<E, false>(xd, Q.offD, Q, nullptr, S.TE, f);
 #pragma unroll
-                for (int h = 0; h < VE; h += 4) {
-                    double e[4], f[4] = {0.0, 0.0, 0.0, 0.0};
-                    vals4<E>(xt[u], h, Q.offT, Q, nullptr, S.TE, e);
-                    if (Q.resid) vals4<E>(xd[u], h, Q.offD, Q, nullptr, S.TE, f);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        double x = Q.resid ? e[q] - Q.lam * f[q] : e[q];
-                        if (!(x > 0.0) || jv + h + q >= hi) x = 0.0;
-                        w[h + q] = x;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < VE; ++q) w[q] = jv + q < hi ? weight_at<E>(Q, jv + q, nullptr, S.TE) : 0.0;
+            for (int q = 0; q < VE; ++q) {
+                double x = Q.resid ? e[q] - Q.lam * f[q] : e[q];
+                if (!(x > 0.0) || !in) x = 0.0;
+                w[q] = x;
+                wsum += x;
             }
-#pragma unroll
-            for (int q = 0; q < VE; ++q) wsum += w[q];
             double tot;
             const double wpre = block_exscan<NT2 / 64>(S.scan, wsum, tot);
+            const int jv = vi * VE;
             if (tok == 0x7fffffff) {
                 double run = run0 + wpre;
 #pragma unroll
@@ -1315,7 +1423,7 @@ __global__ __launch_bounds__(NT2) void draw_kernel(Params P) {
         tok = block_min(S.R, tok);
         if (tok == 0x7fffffff) {
             tok = block_max(S.R, lastpos);
-            if (tok < 0) tok = lo;
+            if (tok < 0) tok = v0 * VE;
         }
         if (tid == 0) P.out_tok[static_cast<size_t>(b) * (k + 1) + a] = tok;
         break;
@@ -1336,32 +1444,42 @@ int fail(int code, const char* fmt, ...) {
 }
 
 struct Plan {
-    int rpb, nchunk;
+    int rpb;
+    int nvec;                  // 16-byte vectors per row
+    int wmax;                  // most pass-2 workgroups per batch row (sampling; 0 in greedy mode)
     size_t rows_total;
     // workspace offsets (bytes)
-    size_t o_tiles, o_bat, o_chunks, o_exp, o_tau, total;
+    size_t o_tiles, o_bat, o_segs, o_exp, o_tau, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-bool make_plan(int32_t B, int32_t k, int32_t V, int mode, Plan& p) {
+bool make_plan(int32_t B, int32_t k, int32_t V, int mode, int dtype, Plan& p) {
     if (B < 1 || k < 0 || k > SPEC_MAX_K || V < 1) return false;
     if (mode != SPEC_MODE_SAMPLE && mode != SPEC_MODE_GREEDY) return false;
     p.rpb = mode == SPEC_MODE_SAMPLE ? 2 * k + 1 : k + 1;
     p.rows_total = static_cast<size_t>(B) * p.rpb;
     if (p.rows_total > (1u << 26)) return false;
+    if (B > (1 << 22)) return false;                       // grid sizes stay below 2^32 threads
     if (V > (1 << 29)) return false;                       // a row must fit one buffer resource
+    const int ve = dtype == SPEC_DTYPE_F32 ? 4 : 8;
+    p.nvec = (V + ve - 1) / ve;
+    p.wmax = 0;
     if (mode == SPEC_MODE_SAMPLE) {
         if (V > MAX_V) return false;
-        p.nchunk = (V + CHUNK - 1) / CHUNK;
-    } else {
-        p.nchunk = 0;
+        // pass 2: enough workgroups per batch row to fill SLOTS_CAP resident
+        // slots, but at least one vector per lane
+        long long w = (p.nvec + NT2 - 1) / NT2;
+        const long long by_slots = (SLOTS_CAP + B - 1) / B;
+        if (w > by_slots) w = by_slots;
+        if (w > W_CAP) w = W_CAP;
+        if (w < 1) w = 1;
+        p.wmax = static_cast<int>(w);
     }
-    if (static_cast<size_t>(B) * static_cast<size_t>(p.nchunk) > 0x7fffffffUL) return false;
     size_t o = 0;
     p.o_tiles = o; o = align256(o + (p.rows_total + G_MAX) * sizeof(TileRec));
     p.o_bat = o; o = align256(o + static_cast<size_t>(B) * sizeof(BatchRec));
-    p.o_chunks = o; o = align256(o + static_cast<size_t>(B) * p.nchunk * sizeof(ChunkRec));
+    p.o_segs = o; o = align256(o + static_cast<size_t>(B) * p.wmax * (NT2 / 64) * sizeof(SegRec));
     p.o_exp = o; o = align256(o + EXP_N * sizeof(double));
     p.o_tau = o; o = align256(o + TAB_MAX * sizeof(double));
     p.total = o;
@@ -1379,7 +1497,7 @@ int check(const void* tgt, const void* dft, const int32_t* tok, const float* uni
         return fail(SPEC_ERR_MODE, "mode %d is not SPEC_MODE_SAMPLE or SPEC_MODE_GREEDY", mode);
     if (B < 1 || k < 0 || k > SPEC_MAX_K || V < 1)
         return fail(SPEC_ERR_SHAPE, "need B >= 1, 0 <= k <= %d, V >= 1 (got B=%d k=%d V=%d)", SPEC_MAX_K, B, k, V);
-    if (!make_plan(B, k, V, mode, plan))
+    if (!make_plan(B, k, V, mode, dtype, plan))
         return fail(SPEC_ERR_SHAPE, "sizes B=%d k=%d V=%d exceed the supported range", B, k, V);
     const unsigned long long elems = static_cast<unsigned long long>(B) * (k + 1) * static_cast<unsigned long long>(V);
     if (elems > (1ull << 46)) return fail(SPEC_ERR_SHAPE, "B*(k+1)*V = %llu is too large", elems);
@@ -1415,11 +1533,11 @@ int scan_blocks_per_cu(int dev) {
 }
 
 template <class E, bool VEC>
-int chunk_blocks_per_cu(int dev) {
+int seg_blocks_per_cu(int dev) {
     static int cache[64] = {0};
     if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<E, VEC>, NT2, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, seg_kernel<E, VEC>, NT2, 0) != hipSuccess || n < 1)
         n = 1;
     if (dev >= 0 && dev < 64) cache[dev] = n;
     return n;
@@ -1437,16 +1555,23 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     hipLaunchKernelGGL((scan_kernel<E, MODE>), dim3(P.G), dim3(NT), 0, s, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
-    e = hipGetLastError();
-    if (e != hipSuccess || MODE == SPEC_MODE_GREEDY) return e;
-    // persistent chunk workgroups: one resident round
-    const long long items = static_cast<long long>(P.B) * P.nchunk;
-    long long G2 = static_cast<long long>(ncu) * (P.vec_ok ? chunk_blocks_per_cu<E, true>(dev) : chunk_blocks_per_cu<E, false>(dev));
-    if (G2 > items) G2 = items;
-    if (G2 < 1) G2 = 1;
-    if (P.vec_ok) hipLaunchKernelGGL((chunk_kernel<E, true>), dim3(static_cast<unsigned>(G2)), dim3(NT2), 0, s, P);
-    else hipLaunchKernelGGL((chunk_kernel<E, false>), dim3(static_cast<unsigned>(G2)), dim3(NT2), 0, s, P);
+    if constexpr (MODE == SPEC_MODE_GREEDY) {
+        hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
+        return hipGetLastError();
+    }
+    // pass 2: one resident round of workgroups, split evenly over the batch rows
+    long long slots = static_cast<long long>(ncu) *
+        (P.vec_ok ? seg_blocks_per_cu<E, true>(dev) : seg_blocks_per_cu<E, false>(dev));
+    if (slots > SLOTS_CAP) slots = SLOTS_CAP;
+    long long W = (slots + P.B - 1) / P.B;
+    if (W > P.wpb) W = P.wpb;                              // the plan's bound (workspace size)
+    if (W < 1) W = 1;
+    P.wpb = static_cast<int>(W);
+    P.nseg = P.wpb * (NT2 / 64);
+    P.vps = (P.nvec + P.nseg - 1) / P.nseg;
+    const unsigned G2 = static_cast<unsigned>(static_cast<long long>(P.B) * W);
+    if (P.vec_ok) hipLaunchKernelGGL((seg_kernel<E, true>), dim3(G2), dim3(NT2), 0, s, P);
+    else hipLaunchKernelGGL((seg_kernel<E, false>), dim3(G2), dim3(NT2), 0, s, P);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((draw_kernel<E>), dim3(P.B), dim3(NT2), 0, s, P);
@@ -1460,7 +1585,7 @@ extern "C" {
 size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int dtype, int mode) {
     if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return 0;
     Plan p;
-    if (!make_plan(B, k, V, mode, p)) return 0;
+    if (!make_plan(B, k, V, mode, dtype, p)) return 0;
     return p.total;
 }
 
@@ -1495,7 +1620,10 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
     P.dprob = k > 0 ? draft_prob : nullptr;
     P.B = B; P.k = k; P.V = V;
     P.rpb = plan.rpb;
-    P.nchunk = plan.nchunk;
+    P.nvec = plan.nvec;
+    P.wpb = plan.wmax;                                     // launch_all picks the count (<= this)
+    P.nseg = 0;
+    P.vps = 0;
     P.N = static_cast<long long>(plan.rows_total) * V;
     P.G = 0; P.L = 0;
     P.mode = mode;
@@ -1528,19 +1656,20 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
                (static_cast<size_t>(V) * (dtype == SPEC_DTYPE_F32 ? 4 : 2)) % 16 == 0;
     P.tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
     P.bat = reinterpret_cast<BatchRec*>(ws + plan.o_bat);
-    P.chunks = reinterpret_cast<ChunkRec*>(ws + plan.o_chunks);
+    P.segs = reinterpret_cast<SegRec*>(ws + plan.o_segs);
     P.exptab = reinterpret_cast<double*>(ws + plan.o_exp);
     P.tautab = reinterpret_cast<double*>(ws + plan.o_tau);
-    // bf16 value table: |v| in [2^-24, 2^kmax), kmax <= 8 the largest with
-    // 2^kmax / T <= 700, centred by C = 2^kmax/T - 600
-    P.tab_range = 0;
+    // bf16 value table: |v| in [2^-16, 2^8), usable for rows whose maxima lie
+    // below 2^kmax, kmax <= 8 the largest with 2^kmax / T <= 700, centred by
+    // C = 2^kmax/T - 600
+    P.tab_on = 0;
     P.tab_lim = 0.0;
     P.tab_c = 0.0;
     if (dtype == SPEC_DTYPE_BF16 && mode == SPEC_MODE_SAMPLE) {
         int kmax = static_cast<int>(floor(log2(700.0 * Td)));
         if (kmax > 8) kmax = 8;
-        if (kmax > -20) {
-            P.tab_range = (kmax + 24) * 128;
+        if (kmax > -12) {
+            P.tab_on = 1;
             P.tab_lim = ldexp(1.0, kmax);
             P.tab_c = P.tab_lim / Td - 600.0;
         }
