@@ -135,6 +135,20 @@ inline T __shfl_xor(T v, int mask, int width = 64) {
     return r;
 }
 
+// wave vote: does any lane of this thread's wave pass a nonzero predicate
+inline int __any(int pred) {
+    EmuWG* w = emu_wg;
+    const unsigned me = threadIdx.x;
+    const unsigned base = me & ~63u;
+    const int p = pred != 0;
+    memcpy(w->shfl[me], &p, sizeof(int));
+    emu_yield();
+    int r = 0;
+    for (unsigned l = base; l < base + 64 && l < w->n; ++l) { int q; memcpy(&q, w->shfl[l], sizeof(int)); r |= q; }
+    emu_yield();
+    return r;
+}
+
 template <class T>
 inline T __shfl_up(T v, unsigned delta, int width = 64) {
     (void)width;

@@ -72,7 +72,11 @@ constexpr unsigned TAB_TOP = TAB_BASE + TAB_RANGE - 1u;
 constexpr unsigned TAB_NEG = 4096;      // entry of the first negative value
 constexpr int TAB_MAX = TAB_NEG + TAB_RANGE;  // value-table entries (entries RANGE..NEG-1 unused)
 
-enum : int { K_TARGET = 0, K_DRAFT = 1, K_GREEDY = 2 };
+// Row kinds of pass 1: K_TARGET (top-2 and exp-sum: target rows with a draft
+// token), K_DRAFT (max and exp-sum), K_GREEDY (top-2, first argmax, NaN flag),
+// K_TOP2 (top-2 and NaN flag: the bonus target row of sampling mode, whose
+// normaliser only the bonus draw needs, and pass 2 computes it there).
+enum : int { K_TARGET = 0, K_DRAFT = 1, K_GREEDY = 2, K_TOP2 = 3 };
 
 // ------------------------------------------------------------------ element types
 
@@ -261,25 +265,6 @@ __device__ void block_top2(Red& R, float& t1, float& t2) {
     lds_sync();
 }
 
-// Block merge of (ref, s); result valid in thread 0.
-__device__ void block_sref(Red& R, float& ref, double& s) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int m = 32; m >= 1; m >>= 1) {
-        const float orf = __shfl_xor(ref, m, 64);
-        const double os = __shfl_xor(s, m, 64);
-        sref_merge(ref, s, orf, os);
-    }
-    if (lane == 0) { R.ref[w] = ref; R.s[w] = s; }
-    lds_sync();
-    if (threadIdx.x == 0) {
-        float r = R.ref[0];
-        double a = R.s[0];
-        for (int q = 1; q < NWAVE; ++q) sref_merge(r, a, R.ref[q], R.s[q]);
-        ref = r; s = a;
-    }
-    lds_sync();
-}
-
 template <int NW>
 __device__ int block_min(RedT<NW>& R, int v) {
     v = wave_min(v);
@@ -395,13 +380,15 @@ __device__ inline void consume_vec(Lane& st, const float (&x)[VE], int vidx, flo
         }
         if constexpr (KIND == K_GREEDY) {
             if (st.t1 > before) st.bvec = vidx;
+        }
+        if constexpr (KIND == K_GREEDY || KIND == K_TOP2) {
             int n = 0;
 #pragma unroll
             for (int j = 0; j < VE; ++j) n |= (x[j] != x[j]);
             st.nan |= n;
         }
     }
-    if constexpr (KIND != K_GREEDY) {
+    if constexpr (KIND == K_TARGET || KIND == K_DRAFT) {
         lane_rescale(st, ch);
         float e[VE];
 #pragma unroll
@@ -422,9 +409,9 @@ __device__ inline void consume_one(Lane& st, float x, float ch, float cl) {
     } else {
         st.t2 = fmaxf(st.t2, fminf(st.t1, x));
         st.t1 = fmaxf(st.t1, x);
-        if constexpr (KIND == K_GREEDY) st.nan |= (x != x);
+        if constexpr (KIND == K_GREEDY || KIND == K_TOP2) st.nan |= (x != x);
     }
-    if constexpr (KIND != K_GREEDY) {
+    if constexpr (KIND == K_TARGET || KIND == K_DRAFT) {
         lane_rescale(st, ch);
         st.s += static_cast<double>(exp_term(x, ch, cl, st.ref));
     }
@@ -443,12 +430,46 @@ __device__ inline typename E::vec load_nt(__amdgpu_buffer_rsrc_t r, unsigned vof
     return __builtin_bit_cast(typename E::vec, w);
 }
 
+// Wave-level part of a sampling segment's reduction: top-2 (or max), the
+// (ref, s) sum rescaled to the wave's largest reference, the NaN flag; lane 0
+// leaves them in R slot `w`.
+template <int KIND>
+__device__ inline void wave_rec(Red& R, const Lane& st) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    float t1 = st.t1, t2 = st.t2;
+    for (int m = 32; m >= 1; m >>= 1) {
+        const float o1 = __shfl_xor(t1, m, 64);
+        if constexpr (KIND == K_DRAFT) {
+            t1 = fmaxf(t1, o1);
+        } else {
+            const float o2 = __shfl_xor(t2, m, 64);
+            top2_merge(t1, t2, o1, o2);
+        }
+    }
+    float ref = st.ref;
+    double s = st.s;
+    int nan = st.nan;
+    if constexpr (KIND == K_TARGET || KIND == K_DRAFT) {
+        // a lane with no sum carries no reference
+        float r = s == 0.0 ? -INFINITY : ref;
+        for (int m = 32; m >= 1; m >>= 1) r = fmaxf(r, __shfl_xor(r, m, 64));
+        s = (s == 0.0 || s != s) ? s : scale2(s, ref - r);
+        s = wave_sum(s);
+        ref = r == -INFINITY ? 0.0f : r;
+    } else {
+        nan = __any(nan) ? 1 : 0;
+    }
+    if (lane == 0) { R.t1[w] = t1; R.t2[w] = t2; R.ref[w] = ref; R.s[w] = s; R.j[w] = nan; }
+}
+
 // Scan segment [e0, e1) of the row at `row`; the segment's record is complete
-// in thread 0. xs is the row's draft-token index (or -1): if it lies in the
-// segment, thread 0 loads that logit up front (its latency hides behind the
-// stream) and keeps it for the record.
+// in thread 0. tokp points at the row's draft token (or is null): thread 0
+// reads it at once, and once the first batch has arrived (the token with it)
+// loads that logit if it lies in the segment. The unaligned head and tail
+// elements are loaded before the stream too, so no load waits at the end.
+// R is used by this segment only: consecutive segments alternate between two.
 template <class E, int KIND>
-__device__ TileRec tile_scan(const char* row, int e0, int e1, int xs, float ch, float cl, Red& R) {
+__device__ TileRec tile_scan(const char* row, int e0, int e1, const int* tokp, float ch, float cl, Red& R) {
     using vec = typename E::vec;
     constexpr int VE = E::VE;
     const int tid = threadIdx.x;
@@ -459,9 +480,23 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, int xs, float ch, 
     const int nvec = (len - head) / VE;
     const int tail = len - head - nvec * VE;
     const vec* vp = reinterpret_cast<const vec*>(start + static_cast<size_t>(head) * E::ES);
+    int xs = -1;
+    if (tid == 0 && tokp) xs = *tokp;
+    // head / tail elements: at most 2*VE-2 of them, one per thread
+    float sx = -INFINITY;
+    int sidx = 0x7fffffff;
+    const bool has_ht = tid < head + tail;
+    if (has_ht) {
+        const int rel = tid < head ? tid : head + nvec * VE + (tid - head);
+        sx = E::load1(row, static_cast<size_t>(e0) + rel);
+        sidx = e0 + rel;
+    }
     float lx = 0.0f;
-    const bool got = tid == 0 && xs >= e0 && xs < e1;
-    if (got) lx = E::load1(row, static_cast<size_t>(xs));
+    bool got = false;
+    auto fetch_lx = [&]() {
+        got = tid == 0 && xs >= e0 && xs < e1;
+        if (got) lx = E::load1(row, static_cast<size_t>(xs));
+    };
 
     Lane st;
     st.t1 = -INFINITY; st.t2 = -INFINITY; st.mref = -INFINITY; st.ref = 0.0f;
@@ -478,10 +513,11 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, int xs, float ch, 
     const int nb = (nvec + U * NT - 1) / (U * NT);
     auto consume = [&](const vec (&X)[U], int i) {
         const bool full = (i + 1) * U * NT <= nvec;
+        const int rem = nvec - i * U * NT - tid;           // vectors of this batch left at u = 0
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int vi = (i * U + u) * NT + tid;
-            if (full || vi < nvec) {
+            if (full || u * NT < rem) {
                 float x[VE];
                 E::unpack(X[u], x);
                 consume_vec<KIND, VE>(st, x, vi, ch, cl);
@@ -493,12 +529,18 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, int xs, float ch, 
 #pragma unroll
         for (int u = 0; u < U; ++u) A[u] = load_nt<E>(rs, voff, u * BSTRIDE);
     }
+    if constexpr (KIND == K_TARGET || KIND == K_DRAFT) {
+        if (nb == 0) fetch_lx();
+    }
     for (int i = 0; i < nb; i += 2) {
         if (i + 1 < nb) {
 #pragma unroll
             for (int u = 0; u < U; ++u) Bv[u] = load_nt<E>(rs, voff, ((i + 1) * U + u) * BSTRIDE);
         }
         consume(A, i);
+        if constexpr (KIND == K_TARGET || KIND == K_DRAFT) {
+            if (i == 0) fetch_lx();                        // the token arrived before batch 0
+        }
         if (i + 1 >= nb) break;
         if (i + 2 < nb) {
 #pragma unroll
@@ -507,24 +549,17 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, int xs, float ch, 
         consume(Bv, i + 1);
     }
 
-    // head / tail elements: at most 2*VE-2 of them, one per thread
     const float vb = st.t1;
     const int bvec = st.bvec;
-    float sx = -INFINITY;
-    int sidx = 0x7fffffff;
-    if (tid < head + tail) {
-        const int rel = tid < head ? tid : head + nvec * VE + (tid - head);
-        sx = E::load1(row, static_cast<size_t>(e0) + rel);
-        sidx = e0 + rel;
-        consume_one<KIND>(st, sx, ch, cl);
-    }
+    if (has_ht) consume_one<KIND>(st, sx, ch, cl);
 
-    float t1 = st.t1, t2 = st.t2;
-    block_top2(R, t1, t2);
     TileRec out;
-    out.t1 = t1; out.t2 = t2; out.idx = 0x7fffffff; out.ref = 0.0f; out.s = 0.0; out.lx = 0.0f; out.flags = 0;
-
+    out.t1 = -INFINITY; out.t2 = -INFINITY;
+    out.idx = 0x7fffffff; out.ref = 0.0f; out.s = 0.0; out.lx = 0.0f; out.flags = 0;
     if constexpr (KIND == K_GREEDY) {
+        float t1 = st.t1, t2 = st.t2;
+        block_top2(R, t1, t2);
+        out.t1 = t1; out.t2 = t2;
         int cand = 0x7fffffff;
         if (bvec >= 0 && vb == t1) {
             float x[VE];
@@ -538,11 +573,26 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, int xs, float ch, 
         out.idx = block_min(R, cand);
         out.flags = block_max(R, st.nan) ? 1 : 0;
     } else {
-        float ref = st.ref;
-        double s = st.s;
-        block_sref(R, ref, s);
-        out.ref = ref; out.s = s;
-        if (got) { out.lx = lx; out.flags = 2; }
+        wave_rec<KIND>(R, st);
+        lds_sync();
+        if (tid == 0) {
+            float a1 = R.t1[0], a2 = R.t2[0], r = R.ref[0];
+            double sum = R.s[0];
+            int nan = R.j[0];
+            for (int q = 1; q < NWAVE; ++q) {
+                top2_merge(a1, a2, R.t1[q], R.t2[q]);
+                sref_merge(r, sum, R.ref[q], R.s[q]);
+                nan |= R.j[q];
+            }
+            out.t1 = a1;
+            out.t2 = KIND == K_DRAFT ? -INFINITY : a2;
+            if constexpr (KIND == K_TOP2) {
+                out.flags = nan ? 1 : 0;
+            } else {
+                out.ref = r; out.s = sum;
+                if (got) { out.lx = lx; out.flags = 2; }
+            }
+        }
     }
     return out;
 }
@@ -601,8 +651,8 @@ __device__ inline double exp2_lean(double d) {
 
 
 template <class E, int MODE>
-__global__ __launch_bounds__(NT) void scan_kernel(Params P) {
-    __shared__ Red R;
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void scan_kernel(Params P) {
+    __shared__ Red R2[2];
     const int tid = threadIdx.x;
     const int k = P.k, V = P.V;
     // Workgroup w owns the flattened elements [w*L, (w+1)*L) of all B*rpb rows,
@@ -626,7 +676,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(Params P) {
     }
     const long long g0 = w * P.L;
     const long long g1 = g0 + P.L < P.N ? g0 + P.L : P.N;
-    for (long long g = g0; g < g1;) {
+    int seg = 0;
+    for (long long g = g0; g < g1; ++seg) {
+        Red& R = R2[seg & 1];
         const long long row = g / V;
         const int e0 = static_cast<int>(g - row * V);
         const long long rend = (row + 1) * V < g1 ? (row + 1) * V : g1;
@@ -640,13 +692,14 @@ __global__ __launch_bounds__(NT) void scan_kernel(Params P) {
             rowp = static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + (j - k - 1)) * V * E::ES;
         TileRec tr;
         if constexpr (MODE == SPEC_MODE_GREEDY) {
-            tr = tile_scan<E, K_GREEDY>(rowp, e0, e1, -1, P.ch, P.cl, R);
+            tr = tile_scan<E, K_GREEDY>(rowp, e0, e1, nullptr, P.ch, P.cl, R);
         } else {
             // the draft token of this row's position (target rows i < k, draft rows)
             const int pos = is_target ? j : j - k - 1;
-            const int xs = pos < k ? P.tok[static_cast<size_t>(b) * k + pos] : -1;
-            if (is_target) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, xs, P.ch, P.cl, R);
-            else tr = tile_scan<E, K_DRAFT>(rowp, e0, e1, xs, P.ch, P.cl, R);
+            const int* tokp = pos < k ? P.tok + static_cast<size_t>(b) * k + pos : nullptr;
+            if (j == k) tr = tile_scan<E, K_TOP2>(rowp, e0, e1, nullptr, P.ch, P.cl, R);
+            else if (is_target) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, tokp, P.ch, P.cl, R);
+            else tr = tile_scan<E, K_DRAFT>(rowp, e0, e1, tokp, P.ch, P.cl, R);
         }
         if (tid == 0) P.tiles[row + w] = tr;
         g = rend;
@@ -667,7 +720,7 @@ struct Dec {
 // Merge the segment records t[w0..w1] of one row in element order (earlier
 // segments win ties of the greedy argmax); the first four are loaded together.
 template <int MODE>
-__device__ inline RowRec merge_row(const TileRec* t, long long w0, long long w1) {
+__device__ inline RowRec merge_row(const TileRec* t, long long w0, long long w1, bool with_sum) {
     TileRec m = t[w0];
     for (long long q0 = w0 + 1; q0 <= w1; q0 += 4) {
         TileRec o[4];
@@ -678,9 +731,9 @@ __device__ inline RowRec merge_row(const TileRec* t, long long w0, long long w1)
             if (q0 + u > w1) break;
             const float prev = m.t1;
             top2_merge(m.t1, m.t2, o[u].t1, o[u].t2);
+            m.flags |= o[u].flags & 1;
             if constexpr (MODE == SPEC_MODE_GREEDY) {
                 if (o[u].t1 > prev) m.idx = o[u].idx;
-                m.flags |= o[u].flags & 1;
             } else {
                 sref_merge(m.ref, m.s, o[u].ref, o[u].s);
                 if (o[u].flags & 2) { m.lx = o[u].lx; m.flags |= 2; }
@@ -689,7 +742,7 @@ __device__ inline RowRec merge_row(const TileRec* t, long long w0, long long w1)
     }
     RowRec rr;
     rr.m = m.t1; rr.t2 = m.t2; rr.idx = m.idx; rr.lg = 0.0; rr.lx = m.lx; rr.has_lx = (m.flags & 2) != 0;
-    if constexpr (MODE == SPEC_MODE_GREEDY) {
+    if (MODE == SPEC_MODE_GREEDY || !with_sum) {
         rr.valid = !(m.flags & 1) && m.t1 > -INFINITY && m.t1 < INFINITY;
     } else {
         rr.valid = (m.s == m.s) && m.s > 0.0 && m.s < INFINITY && m.t1 > -INFINITY && m.t1 < INFINITY;
@@ -721,7 +774,8 @@ __device__ BatchRec decide_batch(const Params& P, Dec& D, int b, bool write) {
     if (tid < rpb) {
         const size_t row = static_cast<size_t>(b) * rpb + tid;
         const long long r0 = static_cast<long long>(row) * V;
-        const RowRec rr = merge_row<MODE>(P.tiles + row, r0 / P.L, (r0 + V - 1) / P.L);
+        // the bonus target row k of sampling mode carries no sum
+        const RowRec rr = merge_row<MODE>(P.tiles + row, r0 / P.L, (r0 + V - 1) / P.L, tid != k);
         D.rec[tid] = rr;
         if (write && tid <= k) {
             const float g = (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
