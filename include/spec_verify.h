@@ -79,7 +79,7 @@ extern "C" {
 
 #define SPEC_OK 0
 #define SPEC_ERR_NULL (-1)      /* a required pointer is NULL                                   */
-#define SPEC_ERR_SHAPE (-2)     /* B < 1, B > 2^22, k outside [0, SPEC_MAX_K], V < 1,
+#define SPEC_ERR_SHAPE (-2)     /* B < 1, B > 2^21, k outside [0, SPEC_MAX_K], V < 1,
                                    V > SPEC_MAX_V_SAMPLE in SAMPLE mode, V > 2^29, or a size
                                    overflow                                                     */
 #define SPEC_ERR_DTYPE (-3)     /* dtype is not SPEC_DTYPE_F32 / SPEC_DTYPE_BF16                */

@@ -100,7 +100,12 @@ struct EmuWG {
     static constexpr size_t STACK = 512 * 1024;
     ucontext_t sched;
     std::vector<ucontext_t> ctx;
-    std::vector<char> stacks;
+    char* stacks = nullptr;     // fiber stacks, pages committed only as they are touched
+    size_t stacks_bytes = 0;
+    EmuWG() = default;
+    EmuWG(const EmuWG&) = delete;
+    EmuWG& operator=(const EmuWG&) = delete;
+    ~EmuWG() { delete[] stacks; }
     std::vector<char> done;
     unsigned n = 0;
     void (*body)(void*) = nullptr;
@@ -177,10 +182,14 @@ inline void emu_run_wg(EmuWG& w, unsigned wg, unsigned nthreads) {
     w.n = nthreads;
     w.ctx.assign(nthreads, ucontext_t{});
     w.done.assign(nthreads, 0);
-    if (w.stacks.size() < nthreads * EmuWG::STACK) w.stacks.resize(nthreads * EmuWG::STACK);
+    if (w.stacks_bytes < nthreads * EmuWG::STACK) {
+        delete[] w.stacks;
+        w.stacks_bytes = nthreads * EmuWG::STACK;
+        w.stacks = new char[w.stacks_bytes];
+    }
     for (unsigned t = 0; t < nthreads; ++t) {
         getcontext(&w.ctx[t]);
-        w.ctx[t].uc_stack.ss_sp = w.stacks.data() + t * EmuWG::STACK;
+        w.ctx[t].uc_stack.ss_sp = w.stacks + t * EmuWG::STACK;
         w.ctx[t].uc_stack.ss_size = EmuWG::STACK;
         w.ctx[t].uc_link = &w.sched;
         makecontext(&w.ctx[t], reinterpret_cast<void (*)()>(emu_fiber_entry), 2, 0u, 0u);

@@ -56,9 +56,10 @@ namespace {
 constexpr int NT = 256;                 // threads per workgroup (4 wave64)
 constexpr int NWAVE = NT / 64;
 constexpr int MAX_AMB = 4;              // band elements recorded per chunk (the draw sorts 4)
-constexpr int NT2 = 512;                // threads per pass-2 workgroup (8 wave64)
-constexpr int W_CAP = 512;              // most pass-2 workgroups per batch row
-constexpr int MAXS = W_CAP * (NT2 / 64); // most pass-2 segments per row (one per wave)
+constexpr int NT2 = 512;                // threads per draw workgroup (8 wave64)
+constexpr int NTS = 1024;               // threads per pass-2 segment workgroup (16 wave64)
+constexpr int W_CAP = 256;              // most pass-2 workgroups per batch row
+constexpr int MAXS = W_CAP * (NTS / 64); // most pass-2 segments per row (one per wave)
 constexpr int SEG_U = 6;                // vectors per lane and row loaded together in pass 2
 constexpr int SLOTS_CAP = 4096;         // most resident pass-2 workgroups assumed by the workspace
 constexpr int MAX_V = SPEC_MAX_V_SAMPLE; // largest vocabulary of sampling mode
@@ -68,7 +69,6 @@ constexpr int MIN_SLICE = 8192;         // smallest pass-1 slice (elements) wort
 constexpr int EXP_N = 1024;             // entries of the 2^(j/N) table of the fp64 exp
 constexpr unsigned TAB_BASE = 111u << 7;  // bf16 magnitude bits of 2^-16 (start of the value table)
 constexpr unsigned TAB_RANGE = 24u << 7;  // magnitudes per sign: 24 binades, 2^-16 <= |v| < 2^8
-constexpr unsigned TAB_TOP = TAB_BASE + TAB_RANGE - 1u;
 constexpr unsigned TAB_NEG = 4096;      // entry of the first negative value
 constexpr int TAB_MAX = TAB_NEG + TAB_RANGE;  // value-table entries (entries RANGE..NEG-1 unused)
 
@@ -659,18 +659,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void sc
     // so every workgroup streams the same number of bytes and the grid is one
     // resident round. It emits one record per row segment, in slot row + w.
     const long long w = blockIdx.x;
-    if constexpr (MODE == SPEC_MODE_SAMPLE) {
-        // pass 2's tables, spread over the workgroups: 2^(j/N) of the fp64 exp,
-        // and (bf16) exp(v/T - C) of every bf16 value v the table covers
-        const long long gi0 = w * NT + tid, gstride = static_cast<long long>(gridDim.x) * NT;
-        for (long long j = gi0; j < EXP_N; j += gstride) P.exptab[j] = exp2(static_cast<double>(j) / EXP_N);
-        if constexpr (E::ES == 2) {
-            for (long long j = gi0; j < TAB_MAX; j += gstride) {
-                const unsigned sgn = j >= TAB_NEG ? 1u : 0u;
-                const unsigned mi = static_cast<unsigned>(j) - sgn * TAB_NEG;
-                const unsigned bits = (sgn << 15) | (mi + TAB_BASE);
-                const double v = __uint_as_float(bits << 16);
-                P.tautab[j] = mi < TAB_RANGE ? exp(fma(v, P.invT, -P.tab_c)) : 0.0;
+    // pass 2's tables, a few entries per workgroup (entry j in workgroup
+    // j mod G, thread j div G), so no workgroup starts its stream much later
+    // than the others: 2^(j/N) of the fp64 exp, and (bf16) exp(v/T - C) of
+    // every bf16 value v the table covers
+    {
+        if constexpr (MODE == SPEC_MODE_SAMPLE) {
+            const long long ntab = EXP_N + (E::ES == 2 ? TAB_MAX : 0);
+            const long long G = gridDim.x;
+            for (long long j = w + G * tid; j < ntab; j += G * NT) {
+                if (j < EXP_N) {
+                    P.exptab[j] = exp2(static_cast<double>(j) / EXP_N);
+                } else {
+                    const long long t = j - EXP_N;
+                    const unsigned sgn = t >= TAB_NEG ? 1u : 0u;
+                    const unsigned mi = static_cast<unsigned>(t) - sgn * TAB_NEG;
+                    const unsigned bits = (sgn << 15) | (mi + TAB_BASE);
+                    const double v = __uint_as_float(bits << 16);
+                    P.tautab[t] = mi < TAB_RANGE ? exp(fma(v, P.invT, -P.tab_c)) : 0.0;
+                }
             }
         }
     }
@@ -1005,16 +1012,27 @@ __device__ inline void vals_vec(const typename E::vec& w, double off, const Pass
         for (int q = 0; q < 8; ++q) out[q] = val_exp_bf16(w, q, off, Q, TE);
     } else if constexpr (E::ES == 2) {
         if (Q.tab) {
+            // both halves of a word at once with 16-bit lane arithmetic:
+            // key = magnitude bits - TAB_BASE, clamped to the table (a value
+            // outside it reads an edge entry and is replaced below), times 8
+            // for a byte offset, plus the sign bit itself as 32768 bytes =
+            // TAB_NEG entries; a half never carries into the other
+            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+            static_assert(TAB_NEG * sizeof(double) == 0x8000u && TAB_RANGE * sizeof(double) <= 0x8000u,
+                          "sign bit is the negative-table offset");
+            const u16x2 base = {static_cast<unsigned short>(TAB_BASE), static_cast<unsigned short>(TAB_BASE)};
+            const u16x2 last = {static_cast<unsigned short>(TAB_RANGE - 1), static_cast<unsigned short>(TAB_RANGE - 1)};
+            const char* tb = reinterpret_cast<const char*>(TT);
             bool oor = false;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const unsigned word = (q >> 1) == 0 ? w.x : (q >> 1) == 1 ? w.y : (q >> 1) == 2 ? w.z : w.w;
-                // magnitude bits, and TAB_NEG for a negative value
-                const unsigned m = (q & 1) ? (word >> 16) & 0x7fffu : word & 0x7fffu;
-                const unsigned sg = (q & 1) ? (word >> 19) & TAB_NEG : (word & 0x8000u) >> 3;
-                const unsigned mc = min(max(m, TAB_BASE), TAB_TOP);
-                oor |= mc != m;
-                out[q] = TT[mc - TAB_BASE + sg];
+            for (int d = 0; d < 4; ++d) {
+                const unsigned word = d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w;
+                const u16x2 key = __builtin_bit_cast(u16x2, word & 0x7fff7fffu) - base;   // wraps below TAB_BASE
+                const u16x2 kc = __builtin_elementwise_min(key, last);
+                oor |= __builtin_bit_cast(unsigned, kc) != __builtin_bit_cast(unsigned, key);
+                const unsigned off2 = __builtin_bit_cast(unsigned, kc << 3) | (word & 0x80008000u);
+                out[2 * d] = *reinterpret_cast<const double*>(tb + (off2 & 0xffffu));
+                out[2 * d + 1] = *reinterpret_cast<const double*>(tb + (off2 >> 16));
             }
             if (oor) {                                     // rare
 #pragma unroll 1
@@ -1104,45 +1122,49 @@ struct WaveAmb {
 
 template <class E>
 struct SegLds {
-    RedT<NT2 / 64> R;
     alignas(16) double TT[E::ES == 2 ? TAB_MAX : 2];
     alignas(16) double TE[EXP_N];
     Dec D;
-    WaveAmb A[NT2 / 64];
+    WaveAmb A[NTS / 64];
 };
 
 // pass 2's tables held in registers between their loads and the LDS stores,
-// so the loads overlap the decision (NT2 threads: one vector of the exp table
-// and up to six of the value table per thread)
+// so the loads overlap the decision (NTS threads: at most one vector of the
+// exp table and four of the value table per thread)
 template <class E>
 struct TableRegs {
-    static constexpr int NTT = E::ES == 2 ? (TAB_MAX / 2 + NT2 - 1) / NT2 : 0;
-    static_assert(E::ES != 2 || NTT * NT2 * 2 == TAB_MAX, "whole vectors per thread");
+    static constexpr int NTT = E::ES == 2 ? (TAB_MAX / 2 + NTS - 1) / NTS : 0;
     u32x4 te;
     u32x4 tt[NTT > 0 ? NTT : 1];
 };
 
 template <class E>
 __device__ inline void tables_fetch(const Params& P, TableRegs<E>& R) {
-    static_assert(EXP_N / 2 == NT2, "one exp-table vector per thread");
-    R.te = reinterpret_cast<const u32x4*>(P.exptab)[threadIdx.x];
+    static_assert(EXP_N / 2 <= NTS, "at most one exp-table vector per thread");
+    const int tid = threadIdx.x;
+    if (tid < EXP_N / 2) R.te = reinterpret_cast<const u32x4*>(P.exptab)[tid];
     if constexpr (E::ES == 2) {
         if (P.tab_on) {
 #pragma unroll
-            for (int q = 0; q < TableRegs<E>::NTT; ++q)
-                R.tt[q] = reinterpret_cast<const u32x4*>(P.tautab)[q * NT2 + static_cast<int>(threadIdx.x)];
+            for (int q = 0; q < TableRegs<E>::NTT; ++q) {
+                const int i = q * NTS + tid;
+                if (i < TAB_MAX / 2) R.tt[q] = reinterpret_cast<const u32x4*>(P.tautab)[i];
+            }
         }
     }
 }
 
 template <class E>
 __device__ inline void tables_store(const Params& P, const TableRegs<E>& R, double* TT, double* TE) {
-    reinterpret_cast<u32x4*>(TE)[threadIdx.x] = R.te;
+    const int tid = threadIdx.x;
+    if (tid < EXP_N / 2) reinterpret_cast<u32x4*>(TE)[tid] = R.te;
     if constexpr (E::ES == 2) {
         if (P.tab_on) {
 #pragma unroll
-            for (int q = 0; q < TableRegs<E>::NTT; ++q)
-                reinterpret_cast<u32x4*>(TT)[q * NT2 + static_cast<int>(threadIdx.x)] = R.tt[q];
+            for (int q = 0; q < TableRegs<E>::NTT; ++q) {
+                const int i = q * NTS + tid;
+                if (i < TAB_MAX / 2) reinterpret_cast<u32x4*>(TT)[i] = R.tt[q];
+            }
         }
     }
 }
@@ -1252,20 +1274,20 @@ __device__ inline void seg_run(const Params& P, const Pass2& Q, int b, int s, in
     }
 }
 
-// Pass 2, sampling mode. Batch row b has W = P.wpb workgroups of NT2/64 waves
+// Pass 2, sampling mode. Batch row b has W = P.wpb workgroups of NTS/64 waves
 // and its selected row pair (or bonus row) is split into 8W equal segments of
 // whole 16-byte vectors, one per wave. Each workgroup decides b itself (the W
 // copies agree; workgroup 0 writes the outputs and the batch record), issues
 // its waves' loads, and then every wave streams its segment with lane-
 // interleaved vectors and no workgroup barrier, ending with one record.
 template <class E, bool VEC>
-__global__ __launch_bounds__(NT2) __attribute__((amdgpu_waves_per_eu(4))) void seg_kernel(Params P) {
+__global__ __launch_bounds__(NTS) __attribute__((amdgpu_waves_per_eu(4))) void seg_kernel(Params P) {
     __shared__ SegLds<E> S;
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const int W = P.wpb;
     const int b = blockIdx.x / W, w = blockIdx.x % W;
-    const int s = w * (NT2 / 64) + wv;
+    const int s = w * (NTS / 64) + wv;
     const int v0 = min(P.nvec, s * P.vps), v1 = min(P.nvec, v0 + P.vps);
 
     TableRegs<E> TR;
@@ -1514,7 +1536,7 @@ bool make_plan(int32_t B, int32_t k, int32_t V, int mode, int dtype, Plan& p) {
     p.rpb = mode == SPEC_MODE_SAMPLE ? 2 * k + 1 : k + 1;
     p.rows_total = static_cast<size_t>(B) * p.rpb;
     if (p.rows_total > (1u << 26)) return false;
-    if (B > (1 << 22)) return false;                       // grid sizes stay below 2^32 threads
+    if (B > (1 << 21)) return false;                       // grid sizes stay below 2^32 threads
     if (V > (1 << 29)) return false;                       // a row must fit one buffer resource
     const int ve = dtype == SPEC_DTYPE_F32 ? 4 : 8;
     p.nvec = (V + ve - 1) / ve;
@@ -1523,7 +1545,7 @@ bool make_plan(int32_t B, int32_t k, int32_t V, int mode, int dtype, Plan& p) {
         if (V > MAX_V) return false;
         // pass 2: enough workgroups per batch row to fill SLOTS_CAP resident
         // slots, but at least one vector per lane
-        long long w = (p.nvec + NT2 - 1) / NT2;
+        long long w = (p.nvec + NTS - 1) / NTS;
         const long long by_slots = (SLOTS_CAP + B - 1) / B;
         if (w > by_slots) w = by_slots;
         if (w > W_CAP) w = W_CAP;
@@ -1533,7 +1555,7 @@ bool make_plan(int32_t B, int32_t k, int32_t V, int mode, int dtype, Plan& p) {
     size_t o = 0;
     p.o_tiles = o; o = align256(o + (p.rows_total + G_MAX) * sizeof(TileRec));
     p.o_bat = o; o = align256(o + static_cast<size_t>(B) * sizeof(BatchRec));
-    p.o_segs = o; o = align256(o + static_cast<size_t>(B) * p.wmax * (NT2 / 64) * sizeof(SegRec));
+    p.o_segs = o; o = align256(o + static_cast<size_t>(B) * p.wmax * (NTS / 64) * sizeof(SegRec));
     p.o_exp = o; o = align256(o + EXP_N * sizeof(double));
     p.o_tau = o; o = align256(o + TAB_MAX * sizeof(double));
     p.total = o;
@@ -1591,7 +1613,7 @@ int seg_blocks_per_cu(int dev) {
     static int cache[64] = {0};
     if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, seg_kernel<E, VEC>, NT2, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, seg_kernel<E, VEC>, NTS, 0) != hipSuccess || n < 1)
         n = 1;
     if (dev >= 0 && dev < 64) cache[dev] = n;
     return n;
@@ -1621,11 +1643,11 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     if (W > P.wpb) W = P.wpb;                              // the plan's bound (workspace size)
     if (W < 1) W = 1;
     P.wpb = static_cast<int>(W);
-    P.nseg = P.wpb * (NT2 / 64);
+    P.nseg = P.wpb * (NTS / 64);
     P.vps = (P.nvec + P.nseg - 1) / P.nseg;
     const unsigned G2 = static_cast<unsigned>(static_cast<long long>(P.B) * W);
-    if (P.vec_ok) hipLaunchKernelGGL((seg_kernel<E, true>), dim3(G2), dim3(NT2), 0, s, P);
-    else hipLaunchKernelGGL((seg_kernel<E, false>), dim3(G2), dim3(NT2), 0, s, P);
+    if (P.vec_ok) hipLaunchKernelGGL((seg_kernel<E, true>), dim3(G2), dim3(NTS), 0, s, P);
+    else hipLaunchKernelGGL((seg_kernel<E, false>), dim3(G2), dim3(NTS), 0, s, P);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((draw_kernel<E>), dim3(P.B), dim3(NT2), 0, s, P);
