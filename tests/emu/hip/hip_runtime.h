@@ -7,10 +7,12 @@
 // Model: a launch runs its workgroups on a pool of OS threads (emu_set_pool,
 // default 1 = workgroups strictly one after another). Inside a workgroup the
 // lanes are cooperative fibers (ucontext) on that OS thread, so __shared__
-// (mapped to static thread_local) is private to the workgroup. __syncthreads
-// and each half of a lane shuffle are fiber yields; the scheduler runs every
-// live lane up to its next yield in lane order, which is a barrier as long as
-// every lane meets the same sequence of barriers (the kernel's contract).
+// (mapped to static thread_local) is private to the workgroup. The scheduler
+// resumes the lanes round-robin; a workgroup barrier waits for every live lane
+// of the workgroup and each half of a shuffle or vote waits for the 64 lanes
+// of its wave, so waves may diverge between workgroup barriers as they may on
+// the hardware (each wave's lanes must meet the same wave exchanges, and
+// every live lane the same workgroup barriers: the kernel's contract).
 // Global atomics are the GCC __atomic builtins, so workgroups on different OS
 // threads really race, spin-waits included.
 #pragma once
@@ -96,8 +98,14 @@ template <class T> inline T atomicOr(T* p, T v) { return __atomic_fetch_or(p, v,
 inline void __threadfence() { __atomic_thread_fence(__ATOMIC_SEQ_CST); }
 
 // ---------------------------------------------------------------- fibers
+// Lanes are fibers run round-robin. A workgroup barrier releases once every
+// live lane of the workgroup has arrived; a wave-level exchange (shuffle,
+// vote, wave barrier) releases once the 64 lanes of that wave have arrived,
+// so waves may take different paths between workgroup barriers, as on the
+// hardware. Arrival counts use generation numbers.
 struct EmuWG {
     static constexpr size_t STACK = 512 * 1024;
+    static constexpr unsigned MAXW = 1024 / 64;
     ucontext_t sched;
     std::vector<ucontext_t> ctx;
     char* stacks = nullptr;     // fiber stacks, pages committed only as they are touched
@@ -108,6 +116,9 @@ struct EmuWG {
     ~EmuWG() { delete[] stacks; }
     std::vector<char> done;
     unsigned n = 0;
+    unsigned ndone = 0;
+    unsigned blk_arrive = 0, blk_gen = 0;
+    unsigned wave_arrive[MAXW] = {}, wave_gen[MAXW] = {};
     void (*body)(void*) = nullptr;
     void* arg = nullptr;
     alignas(8) unsigned char shfl[1024][8];
@@ -121,10 +132,33 @@ inline void emu_yield() {
     threadIdx.x = me;
 }
 
-inline void __syncthreads() { emu_yield(); }
-// a wave barrier: every lane of the workgroup reaches it (the kernels call it
-// in wave-uniform code), so a yield orders the lanes of each wave as well
-inline void __builtin_amdgcn_wave_barrier() { emu_yield(); }
+// every live lane of the workgroup
+inline void __syncthreads() {
+    EmuWG* w = emu_wg;
+    const unsigned gen = w->blk_gen;
+    if (++w->blk_arrive == w->n - w->ndone) {
+        w->blk_arrive = 0;
+        ++w->blk_gen;
+        return;
+    }
+    while (w->blk_gen == gen) emu_yield();
+}
+
+// the 64 lanes of this thread's wave
+inline void emu_wave_sync() {
+    EmuWG* w = emu_wg;
+    const unsigned wv = threadIdx.x >> 6;
+    const unsigned width = (w->n - wv * 64) < 64 ? (w->n - wv * 64) : 64;
+    const unsigned gen = w->wave_gen[wv];
+    if (++w->wave_arrive[wv] == width) {
+        w->wave_arrive[wv] = 0;
+        ++w->wave_gen[wv];
+        return;
+    }
+    while (w->wave_gen[wv] == gen) emu_yield();
+}
+
+inline void __builtin_amdgcn_wave_barrier() { emu_wave_sync(); }
 
 template <class T>
 inline T __shfl_xor(T v, int mask, int width = 64) {
@@ -133,26 +167,47 @@ inline T __shfl_xor(T v, int mask, int width = 64) {
     const unsigned me = threadIdx.x;
     const unsigned base = me & ~63u, lane = me & 63u;
     memcpy(w->shfl[me], &v, sizeof(T));
-    emu_yield();
+    emu_wave_sync();
     T r;
     memcpy(&r, w->shfl[base + (lane ^ static_cast<unsigned>(mask))], sizeof(T));
-    emu_yield();
+    emu_wave_sync();
     return r;
 }
 
-// wave vote: does any lane of this thread's wave pass a nonzero predicate
-inline int __any(int pred) {
+template <class T>
+inline T __shfl(T v, int src, int width = 64) {
+    (void)width;
+    EmuWG* w = emu_wg;
+    const unsigned me = threadIdx.x;
+    const unsigned base = me & ~63u;
+    memcpy(w->shfl[me], &v, sizeof(T));
+    emu_wave_sync();
+    T r;
+    memcpy(&r, w->shfl[base + (static_cast<unsigned>(src) & 63u)], sizeof(T));
+    emu_wave_sync();
+    return r;
+}
+
+// wave votes over this thread's wave
+inline unsigned long long __ballot(int pred) {
     EmuWG* w = emu_wg;
     const unsigned me = threadIdx.x;
     const unsigned base = me & ~63u;
     const int p = pred != 0;
     memcpy(w->shfl[me], &p, sizeof(int));
-    emu_yield();
-    int r = 0;
-    for (unsigned l = base; l < base + 64 && l < w->n; ++l) { int q; memcpy(&q, w->shfl[l], sizeof(int)); r |= q; }
-    emu_yield();
+    emu_wave_sync();
+    unsigned long long r = 0;
+    for (unsigned l = base; l < base + 64 && l < w->n; ++l) {
+        int q;
+        memcpy(&q, w->shfl[l], sizeof(int));
+        if (q) r |= 1ull << (l - base);
+    }
+    emu_wave_sync();
     return r;
 }
+inline int __any(int pred) { return __ballot(pred) != 0; }
+inline int __ffsll(long long x) { return __builtin_ffsll(x); }
+inline int __clzll(long long x) { return __builtin_clzll(static_cast<unsigned long long>(x)); }
 
 template <class T>
 inline T __shfl_up(T v, unsigned delta, int width = 64) {
@@ -161,10 +216,10 @@ inline T __shfl_up(T v, unsigned delta, int width = 64) {
     const unsigned me = threadIdx.x;
     const unsigned base = me & ~63u, lane = me & 63u;
     memcpy(w->shfl[me], &v, sizeof(T));
-    emu_yield();
+    emu_wave_sync();
     T r;
     memcpy(&r, w->shfl[lane >= delta ? base + lane - delta : me], sizeof(T));
-    emu_yield();
+    emu_wave_sync();
     return r;
 }
 
@@ -174,12 +229,21 @@ inline void emu_fiber_entry(unsigned lo, unsigned hi) {
     const unsigned me = threadIdx.x;
     w->body(w->arg);
     w->done[me] = 1;
+    // a lane that leaves no longer counts for the workgroup barrier
+    ++w->ndone;
+    if (w->blk_arrive > 0 && w->blk_arrive == w->n - w->ndone) {
+        w->blk_arrive = 0;
+        ++w->blk_gen;
+    }
 }
 
 inline void emu_run_wg(EmuWG& w, unsigned wg, unsigned nthreads) {
     emu_wg = &w;
     blockIdx = EmuIdx{wg, 0, 0};
     w.n = nthreads;
+    w.ndone = 0;
+    w.blk_arrive = w.blk_gen = 0;
+    for (unsigned q = 0; q < EmuWG::MAXW; ++q) w.wave_arrive[q] = w.wave_gen[q] = 0;
     w.ctx.assign(nthreads, ucontext_t{});
     w.done.assign(nthreads, 0);
     if (w.stacks_bytes < nthreads * EmuWG::STACK) {

@@ -1313,6 +1313,9 @@ struct DrawLds {
     double mass[MAXS];
     double scan[NT2 / 64];
     double base;
+    // the segment selection of the one-wave path
+    double lam, tgt;
+    int sstar, resid, slow;
 };
 
 // Vectors [v0, v1) of segment s.
@@ -1385,71 +1388,126 @@ __global__ __launch_bounds__(NT2) void draw_kernel(Params P) {
     // as the segment records (for the bf16 table, exp(v/T - C) agrees with the
     // table entry to ~1e-15 relative), so it needs no copy of the table.
     Q.tab = 0;
-    double sums[2] = {tid < NS ? r0.sp : 0.0, tid < NS ? r0.sq : 0.0};
-    for (int s = tid + NT2; s < NS; s += NT2) { sums[0] += recs[s].sp; sums[1] += recs[s].sq; }
-    block_sum<2>(S.R, sums);                               // also publishes the exp table
-    const double lh = Q.lam_hat;
-    Q.lam = Q.resid ? sums[0] / sums[1] : 0.0;
-    const bool band_ok = !Q.resid ||
-        (!P.force_exact && Q.lam >= lh * (1.0 - ETA) && Q.lam <= lh * (1.0 + ETA));
     const double u1 = br.u1;
-
-    double* M = S.mass;
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        if (tid < NS) M[tid] = seg_mass(r0, Q, band_ok);
-        for (int s = tid + NT2; s < NS; s += NT2) M[s] = seg_mass(recs[s], Q, band_ok);
-        lds_sync();
-        // contiguous segment ranges per thread -> ordered scan
-        const int cpt = (NS + NT2 - 1) / NT2;
-        const int c0 = min(NS, tid * cpt), c1 = min(NS, c0 + cpt);
-        double mine = 0.0;
-        for (int c = c0; c < c1; ++c) mine += M[c];
-        double Z;
-        double pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
-        if (Z != Z) {                                      // rare: a segment must be recomputed exactly
-            for (int s = 0; s < NS; ++s) {
-                if (M[s] != M[s]) {
-                    const double m = seg_exact<E>(P, Q, s, S);
-                    if (tid == 0) M[s] = m;
-                    lds_sync();
+    const int lane = tid & 63, wv = tid >> 6;
+    int sstar = 0;
+    double tgt = 0.0;
+    bool selected = false;
+    if (NS <= 64) {
+        // one segment per lane of wave 0: exact lambda, masses, inclusive
+        // scan and the segment holding u*Z with wave operations only
+        if (wv == 0) {
+            const bool has = lane < NS;
+            const double sp = wave_sum(has ? r0.sp : 0.0), sq = wave_sum(has ? r0.sq : 0.0);
+            const double lh = Q.lam_hat;
+            Q.lam = Q.resid ? sp / sq : 0.0;
+            const bool band_ok = !Q.resid ||
+                (!P.force_exact && Q.lam >= lh * (1.0 - ETA) && Q.lam <= lh * (1.0 + ETA));
+            int slow = 0, ss = 0;
+            double base = 0.0, t = 0.0;
+            for (int attempt = 0; attempt < 2; ++attempt) {
+                const double m = has ? seg_mass(r0, Q, band_ok) : 0.0;
+                if (__any(m != m)) { slow = 1; break; }    // a segment needs the exact recompute
+                double x = m;                              // inclusive scan over the lanes
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const double y = __shfl_up(x, off, 64);
+                    if (lane >= off) x += y;
+                }
+                const double Z = __shfl(x, 63, 64);
+                if (Q.resid && !(Z > 0.0)) { Q.resid = false; continue; }   // residual rounded to zero: p_a
+                t = u1 * Z;
+                const unsigned long long hit = __ballot(has && x > t);
+                if (hit) {
+                    ss = __ffsll(static_cast<long long>(hit)) - 1;
+                } else {                                   // rounding: last segment with mass
+                    const unsigned long long pos = __ballot(has && m > 0.0);
+                    ss = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+                }
+                base = __shfl(x, ss > 0 ? ss - 1 : 0, 64);
+                if (ss == 0) base = 0.0;
+                break;
+            }
+            if (lane == 0) {
+                S.slow = slow; S.sstar = ss; S.base = base; S.tgt = t; S.lam = Q.lam; S.resid = Q.resid;
+            }
+        }
+        lds_sync();                                        // also publishes the exp table
+        if (!S.slow) {
+            selected = true;
+            sstar = S.sstar; tgt = S.tgt; Q.lam = S.lam; Q.resid = S.resid != 0;
+        }
+    }
+    if (!selected) {
+        // the block path: many segments, or a segment to recompute exactly
+        double sums[2] = {tid < NS ? r0.sp : 0.0, tid < NS ? r0.sq : 0.0};
+        for (int s = tid + NT2; s < NS; s += NT2) { sums[0] += recs[s].sp; sums[1] += recs[s].sq; }
+        block_sum<2>(S.R, sums);                           // also publishes the exp table
+        const double lh = Q.lam_hat;
+        Q.resid = br.a < k;
+        Q.lam = Q.resid ? sums[0] / sums[1] : 0.0;
+        const bool band_ok = !Q.resid ||
+            (!P.force_exact && Q.lam >= lh * (1.0 - ETA) && Q.lam <= lh * (1.0 + ETA));
+        double* M = S.mass;
+        for (int attempt = 0; attempt < 2; ++attempt) {
+            if (tid < NS) M[tid] = seg_mass(r0, Q, band_ok);
+            for (int s = tid + NT2; s < NS; s += NT2) M[s] = seg_mass(recs[s], Q, band_ok);
+            lds_sync();
+            // contiguous segment ranges per thread -> ordered scan
+            const int cpt = (NS + NT2 - 1) / NT2;
+            const int c0 = min(NS, tid * cpt), c1 = min(NS, c0 + cpt);
+            double mine = 0.0;
+            for (int c = c0; c < c1; ++c) mine += M[c];
+            double Z;
+            double pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
+            if (Z != Z) {                                  // rare: a segment must be recomputed exactly
+                for (int s = 0; s < NS; ++s) {
+                    if (M[s] != M[s]) {
+                        const double m = seg_exact<E>(P, Q, s, S);
+                        if (tid == 0) M[s] = m;
+                        lds_sync();
+                    }
+                }
+                mine = 0.0;
+                for (int c = c0; c < c1; ++c) mine += M[c];
+                pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
+            }
+            if (Q.resid && !(Z > 0.0)) {                  // residual mass rounded to zero: use p_a
+                Q.resid = false;
+                lds_sync();
+                continue;
+            }
+            tgt = u1 * Z;
+            // segment holding the target
+            int cand = 0x7fffffff;
+            {
+                double run = pre;
+                for (int c = c0; c < c1; ++c) {
+                    const double nx = run + M[c];
+                    if (nx > tgt) { cand = c; break; }
+                    run = nx;
                 }
             }
-            mine = 0.0;
-            for (int c = c0; c < c1; ++c) mine += M[c];
-            pre = block_exscan<NT2 / 64>(S.scan, mine, Z);
-        }
-        if (Q.resid && !(Z > 0.0)) {                      // residual mass rounded to zero: use p_a
-            Q.resid = false;
-            lds_sync();
-            continue;
-        }
-        const double tgt = u1 * Z;
-        // segment holding the target
-        int sstar = 0x7fffffff;
-        {
-            double run = pre;
-            for (int c = c0; c < c1; ++c) {
-                const double nx = run + M[c];
-                if (nx > tgt) { sstar = c; break; }
-                run = nx;
+            sstar = block_min(S.R, cand);
+            if (sstar == 0x7fffffff) {                     // rounding: last segment with mass
+                int last = -1;
+                for (int c = tid; c < NS; c += NT2) if (M[c] > 0.0) last = max(last, c);
+                sstar = block_max(S.R, last);
+                if (sstar < 0) sstar = 0;
             }
+            if (c0 <= sstar && sstar < c1) {
+                double run = pre;
+                for (int c = c0; c < sstar; ++c) run += M[c];
+                S.base = run;                               // mass before s*
+            }
+            lds_sync();                                    // S.base visible
+            break;
         }
-        sstar = block_min(S.R, sstar);
-        if (sstar == 0x7fffffff) {                         // rounding: last segment with mass
-            int last = -1;
-            for (int c = tid; c < NS; c += NT2) if (M[c] > 0.0) last = max(last, c);
-            sstar = block_max(S.R, last);
-            if (sstar < 0) sstar = 0;
-        }
-        if (c0 <= sstar && sstar < c1) {
-            double run = pre;
-            for (int c = c0; c < sstar; ++c) run += M[c];
-            S.base = run;                                   // mass before s*
-        }
+    }
+    {
         // rescan s* in element order: round r covers vectors v0 + r*NT2 + [0, NT2)
         int v0, v1;
         seg_range(P, sstar, v0, v1);
-        lds_sync();                                        // S.base visible
         double run0 = S.base;
         int tok = 0x7fffffff, lastpos = -1;
         const __amdgpu_buffer_rsrc_t rsT = make_rsrc(Q.rowT, Q.bytes);
@@ -1502,7 +1560,6 @@ __global__ __launch_bounds__(NT2) void draw_kernel(Params P) {
             if (tok < 0) tok = v0 * VE;
         }
         if (tid == 0) P.out_tok[static_cast<size_t>(b) * (k + 1) + a] = tok;
-        break;
     }
 }
 
