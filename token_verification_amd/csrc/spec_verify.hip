@@ -868,11 +868,114 @@ __device__ BatchRec decide_batch(const Params& P, Dec& D, int b, bool write) {
     return D.br;
 }
 
+
+// The same decision made by one wave when the batch row has at most 64 rows
+// (rpb <= 64): lane r merges row r, and the acceptance tests, validity, the
+// first rejection and the outputs use shuffles and ballots only, with no
+// workgroup barrier. Called by the 64 lanes of one wave; the returned record
+// is complete in every lane.
+template <class E, int MODE>
+__device__ BatchRec decide_wave(const Params& P, int b, bool write) {
+    const int lane = threadIdx.x & 63;
+    const int k = P.k, V = P.V, rpb = P.rpb;
+    constexpr bool sample = MODE == SPEC_MODE_SAMPLE;
+    int x = -1;
+    double u0 = 0.0;
+    float u1 = 0.0f;
+    if (lane < k) {
+        x = P.tok[static_cast<size_t>(b) * k + lane];
+        if constexpr (sample) u0 = P.uni[(static_cast<size_t>(b) * (k + 1) + lane) * 2];
+    }
+    if (sample && lane <= k) u1 = P.uni[(static_cast<size_t>(b) * (k + 1) + lane) * 2 + 1];
+    RowRec rr;
+    rr.m = -INFINITY; rr.t2 = -INFINITY; rr.idx = 0x7fffffff; rr.valid = 0; rr.lg = 0.0; rr.lx = 0.0f; rr.has_lx = 0;
+    if (lane < rpb) {
+        const size_t row = static_cast<size_t>(b) * rpb + lane;
+        const long long r0 = static_cast<long long>(row) * V;
+        // the bonus target row k of sampling mode carries no sum
+        rr = merge_row<MODE>(P.tiles + row, r0 / P.L, (r0 + V - 1) / P.L, lane != k);
+        if (write && lane <= k) {
+            const float g = (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
+            P.gap[static_cast<size_t>(b) * (k + 1) + lane] = g;
+        }
+    }
+    // draft row of position lane (lane < k): lane k + 1 + lane
+    const int dl = lane < k ? k + 1 + lane : lane;
+    const int d_valid = __shfl(rr.valid, dl, 64);
+    const int d_has = __shfl(rr.has_lx, dl, 64);
+    const float d_lx = __shfl(rr.lx, dl, 64);
+    const double d_lg = __shfl(rr.lg, dl, 64);
+    int ok = lane <= k ? rr.valid : 1;                     // target rows 0..k
+    int acc = 0;
+    float pf = __builtin_nanf(""), qf = __builtin_nanf("");
+    if (lane < k) {
+        if (!(x >= 0 && x < V)) ok = 0;
+        if (sample && !d_valid) ok = 0;
+        if (sample && ok && !(rr.has_lx && d_has)) ok = 0;
+        if (ok) {
+            if constexpr (sample) {
+                // log2 p(x) = x*c - lg_p and log2 q(x) = x*c - lg_q, in double
+                const double c = P.c;
+                const double lt = rr.lx, ld = d_lx;
+                const double lp = lt == -INFINITY ? -INFINITY : lt * c - rr.lg;
+                const double lq = ld == -INFINITY ? -INFINITY : ld * c - d_lg;
+                double r;
+                if (lq == -INFINITY) r = (lp == -INFINITY) ? 0.0 : INFINITY;
+                else r = exp2_lean(lp - lq);
+                acc = u0 < r;
+                pf = exp2f(static_cast<float>(lp));
+                qf = exp2f(static_cast<float>(lq));
+            } else {
+                acc = (x == rr.idx);
+            }
+        }
+        if (write && P.tprob) P.tprob[static_cast<size_t>(b) * k + lane] = ok ? pf : __builtin_nanf("");
+        if (write && P.dprob) P.dprob[static_cast<size_t>(b) * k + lane] = ok ? qf : __builtin_nanf("");
+    }
+    const bool valid = __ballot(!ok) == 0;
+    const unsigned long long rej = __ballot(lane < k && !acc);
+    const int a = rej ? __ffsll(static_cast<long long>(rej)) - 1 : k;
+    const int idx_a = __shfl(rr.idx, a, 64);
+    if (write && lane <= k) {
+        int o;
+        if (!valid) o = -1;
+        else if (lane < a) o = x;
+        else if (lane == a) o = sample ? -1 : idx_a;    // sampling: the draw writes it
+        else o = -1;
+        P.out_tok[static_cast<size_t>(b) * (k + 1) + lane] = o;
+    }
+    if (write && lane == 0) P.acc_len[b] = valid ? a : -1;
+    const float mp = __shfl(rr.m, a, 64);
+    const double lgp = __shfl(rr.lg, a, 64);
+    const int ad = a < k ? k + 1 + a : a;
+    const float mq = __shfl(rr.m, ad, 64);
+    const double lgq = __shfl(rr.lg, ad, 64);
+    BatchRec br;
+    br.a = valid ? a : -1;
+    br.u1 = sample ? __shfl(u1, a, 64) : 0.0f;
+    br.mp = mp;
+    br.mq = sample && a < k ? mq : 0.0f;
+    br.lam = 0.0;
+    br.lam_hat = 0.0;
+    if (sample && valid && a < k) {
+        // S_p/S_q in the exp((x - m)/T) normalisation of pass 2 (see decide_batch)
+        const double c = P.c;
+        const double d = (lgp - static_cast<double>(mp) * c) - (lgq - static_cast<double>(mq) * c);
+        const double n = rint(d);
+        br.lam = ldexp(static_cast<double>(exp2f(static_cast<float>(d - n))), static_cast<int>(n));
+    }
+    return br;
+}
+
 // Greedy mode: the decisions are the whole result after pass 1.
 template <class E, int MODE>
 __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     __shared__ Dec D;
-    decide_batch<E, MODE>(P, D, blockIdx.x, true);
+    if (P.rpb <= 64) {                                     // uniform
+        if (threadIdx.x < 64) decide_wave<E, MODE>(P, blockIdx.x, true);
+    } else {
+        decide_batch<E, MODE>(P, D, blockIdx.x, true);
+    }
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -1129,25 +1232,27 @@ struct SegLds {
 };
 
 // pass 2's tables held in registers between their loads and the LDS stores,
-// so the loads overlap the decision (NTS threads: at most one vector of the
-// exp table and four of the value table per thread)
+// so the loads overlap the decision. Threads t0 .. NTS-1 take part (the
+// first wave is left out while it decides): at most one vector of the exp
+// table and four of the value table per thread.
 template <class E>
 struct TableRegs {
-    static constexpr int NTT = E::ES == 2 ? (TAB_MAX / 2 + NTS - 1) / NTS : 0;
+    static constexpr int NTT = E::ES == 2 ? (TAB_MAX / 2 + (NTS - 64) - 1) / (NTS - 64) : 0;
     u32x4 te;
     u32x4 tt[NTT > 0 ? NTT : 1];
 };
 
 template <class E>
-__device__ inline void tables_fetch(const Params& P, TableRegs<E>& R) {
-    static_assert(EXP_N / 2 <= NTS, "at most one exp-table vector per thread");
-    const int tid = threadIdx.x;
-    if (tid < EXP_N / 2) R.te = reinterpret_cast<const u32x4*>(P.exptab)[tid];
+__device__ inline void tables_fetch(const Params& P, TableRegs<E>& R, int t0) {
+    static_assert(EXP_N / 2 <= NTS - 64, "at most one exp-table vector per thread");
+    const int t = static_cast<int>(threadIdx.x) - t0, nt = NTS - t0;
+    if (t < 0) return;
+    if (t < EXP_N / 2) R.te = reinterpret_cast<const u32x4*>(P.exptab)[t];
     if constexpr (E::ES == 2) {
         if (P.tab_on) {
 #pragma unroll
             for (int q = 0; q < TableRegs<E>::NTT; ++q) {
-                const int i = q * NTS + tid;
+                const int i = q * nt + t;
                 if (i < TAB_MAX / 2) R.tt[q] = reinterpret_cast<const u32x4*>(P.tautab)[i];
             }
         }
@@ -1155,14 +1260,15 @@ __device__ inline void tables_fetch(const Params& P, TableRegs<E>& R) {
 }
 
 template <class E>
-__device__ inline void tables_store(const Params& P, const TableRegs<E>& R, double* TT, double* TE) {
-    const int tid = threadIdx.x;
-    if (tid < EXP_N / 2) reinterpret_cast<u32x4*>(TE)[tid] = R.te;
+__device__ inline void tables_store(const Params& P, const TableRegs<E>& R, double* TT, double* TE, int t0) {
+    const int t = static_cast<int>(threadIdx.x) - t0, nt = NTS - t0;
+    if (t < 0) return;
+    if (t < EXP_N / 2) reinterpret_cast<u32x4*>(TE)[t] = R.te;
     if constexpr (E::ES == 2) {
         if (P.tab_on) {
 #pragma unroll
             for (int q = 0; q < TableRegs<E>::NTT; ++q) {
-                const int i = q * NTS + tid;
+                const int i = q * nt + t;
                 if (i < TAB_MAX / 2) reinterpret_cast<u32x4*>(TT)[i] = R.tt[q];
             }
         }
@@ -1291,12 +1397,28 @@ __global__ __launch_bounds__(NTS) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int v0 = min(P.nvec, s * P.vps), v1 = min(P.nvec, v0 + P.vps);
 
     TableRegs<E> TR;
-    tables_fetch<E>(P, TR);                                // in flight during the decision
-    BatchRec br = decide_batch<E, SPEC_MODE_SAMPLE>(P, S.D, b, w == 0);
-    tables_store<E>(P, TR, S.TT, S.TE);                    // arrived before the decision's loads
+    BatchRec br;
+    if (P.rpb <= 64) {                                     // uniform
+        // wave 0 decides (its loads first in its queue) while the other
+        // waves load and store the tables
+        if (wv == 0) {
+            br = decide_wave<E, SPEC_MODE_SAMPLE>(P, b, w == 0);
+            if (tid == 0) S.D.br = br;
+        } else {
+            tables_fetch<E>(P, TR, 64);
+            tables_store<E>(P, TR, S.TT, S.TE, 64);
+        }
+        if ((tid & 63) == 0) S.A[wv].n = 0;
+        lds_sync();                                        // decision, tables and band lists ready
+        br = S.D.br;
+    } else {
+        tables_fetch<E>(P, TR, 64);                        // in flight during the decision
+        br = decide_batch<E, SPEC_MODE_SAMPLE>(P, S.D, b, w == 0);
+        tables_store<E>(P, TR, S.TT, S.TE, 64);
+        if ((tid & 63) == 0) S.A[wv].n = 0;
+        lds_sync();                                        // tables and band lists ready
+    }
     Pass2 Q = pass2_rows<E>(P, b, br);
-    if ((tid & 63) == 0) S.A[wv].n = 0;
-    lds_sync();                                            // tables and band lists ready
     if (Q.tab) Q.lam_hat = br.lam * exp_fast(Q.dm, S.TE);  // into table units
     if (w == 0 && tid == 0) {
         br.lam_hat = Q.lam_hat;
