@@ -60,7 +60,7 @@ constexpr int NT2 = 512;                // threads per draw workgroup (8 wave64)
 constexpr int NTS = 1024;               // threads per pass-2 segment workgroup (16 wave64)
 constexpr int W_CAP = 256;              // most pass-2 workgroups per batch row
 constexpr int MAXS = W_CAP * (NTS / 64); // most pass-2 segments per row (one per wave)
-constexpr int SEG_U = 6;                // vectors per lane and row loaded together in pass 2
+constexpr int SEG_U = 2;                // vectors per lane and row loaded together in pass 2
 constexpr int SLOTS_CAP = 4096;         // most resident pass-2 workgroups assumed by the workspace
 constexpr int MAX_V = SPEC_MAX_V_SAMPLE; // largest vocabulary of sampling mode
 constexpr double ETA = 1e-5;            // relative band around pass 1's lambda estimate
@@ -1303,10 +1303,11 @@ __device__ inline void seg_vector(const typename E::vec& xt, const typename E::v
     }
 }
 
-// Vectors per lane and row loaded together (element loads take more registers).
+// Vectors per lane and row loaded together. Two measured best on MI355X:
+// larger groups hold more registers and leave the first loads exposed longer.
 template <bool VEC>
 struct SegU {
-    static constexpr int U = VEC ? SEG_U : 2;
+    static constexpr int U = SEG_U;
 };
 
 template <class E, bool VEC, bool RESID>
