@@ -58,6 +58,10 @@ def _load():
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.spec_verify_ref.restype = ctypes.c_int
+        lib.spec_verify_ref_ragged.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               P, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.spec_verify_ref_ragged.restype = ctypes.c_int
         lib.spec_verify_ref_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -117,8 +121,12 @@ def _np(x, dt):
 
 
 def spec_verify_ref(target, draft, tokens, uniforms, temperature: float, mode: int,
-                    dtype: Optional[int] = None, threads: int = 0) -> RefResult:
-    """Run the oracle on host arrays shaped [B,k+1,V], [B,k,V], [B,k], [B,k+1,2]."""
+                    dtype: Optional[int] = None, threads: int = 0, draft_len=None) -> RefResult:
+    """Run the oracle on host arrays shaped [B,k+1,V], [B,k,V], [B,k], [B,k+1,2].
+
+    draft_len: optional [B] int32, the number of draft positions each batch row
+    verifies (ragged drafts; None means k for every row).
+    """
     if dtype is None:
         dtype = BF16 if str(getattr(target, "dtype", "")) in ("torch.bfloat16", "uint16") else F32
     tgt = _as_logits(target, dtype)
@@ -147,10 +155,13 @@ def spec_verify_ref(target, draft, tokens, uniforms, temperature: float, mode: i
     def ptr(a):
         return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
-    rc = _load().spec_verify_ref(ptr(tgt), ptr(dft), ptr(tok), ptr(uni),
-                                 ctypes.c_float(temperature), int(mode), int(B), int(k),
-                                 int(V), int(dtype), ptr(acc), ptr(out), ptr(gap), ptr(pt),
-                                 ptr(qt), ptr(ma), ptr(mc), ptr(fl), int(threads))
+    dl = _np(draft_len, np.int32)
+    if dl is not None:
+        assert dl.shape == (B,), dl.shape
+    rc = _load().spec_verify_ref_ragged(ptr(tgt), ptr(dft), ptr(tok), ptr(dl), ptr(uni),
+                                        ctypes.c_float(temperature), int(mode), int(B), int(k),
+                                        int(V), int(dtype), ptr(acc), ptr(out), ptr(gap), ptr(pt),
+                                        ptr(qt), ptr(ma), ptr(mc), ptr(fl), int(threads))
     if rc != 0:
         raise ValueError(f"spec_verify_ref rejected its arguments (rc={rc})")
     return RefResult(acc, out, gap, pt, qt, ma, mc, fl)

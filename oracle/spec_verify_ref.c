@@ -44,6 +44,16 @@
  *
  * Every sum is a Neumaier-compensated sum in vocabulary order.
  *
+ * Ragged drafts (the speculative-decoding design note and "Speculative
+ * Decoding: The Physics of Stolen Time" allow each sequence its own number of
+ * guesses): with draft_len[b] = kb in [0, k], batch row b verifies only
+ * positions 0..kb-1, as the rule above with k = kb: the target rows 0..kb,
+ * the draft rows and tokens 0..kb-1 are read, nothing else of the row; the
+ * bonus comes from target row kb. Outputs keep the [.., k+1] / [.., k] layout:
+ * gap of rows past kb and p/q of positions past kb-1 are NaN (not read), and
+ * out_tokens past the emitted token are -1. A draft_len outside [0, k] makes
+ * the row invalid (gap all NaN). draft_len = NULL means kb = k everywhere.
+ *
  * Margins (for the flagged near-tie policy): margin_acc[b] is the smallest
  * |u - r_i| over the decisions actually taken, margin_cdf[b] the distance of u
  * to the nearest edge of the chosen token's normalized CDF interval
@@ -183,6 +193,7 @@ static void ref_fill_invalid(int k, int32_t* acc_len, int32_t* out)
     for (int i = 0; i <= k; ++i) out[i] = -1;
 }
 
+
 /*
  * Smallest distance, in units of the target distribution's total mass, between
  * the residual draw's point u*Z and a CDF boundary that fp64 can resolve. The
@@ -199,19 +210,22 @@ static void ref_fill_invalid(int k, int32_t* acc_len, int32_t* out)
  * REF_RESID_ABS_MARGIN of a CDF boundary (both are flags).
  */
 static int ref_one_row(const void* target, const void* draft, const int32_t* tokens,
-                       const float* uniforms, double T, int mode, int k, int V, int dtype,
-                       size_t b, int32_t* acc_len, int32_t* out, double* gap,
+                       const float* uniforms, double T, int mode, int kmax, int kb, int V,
+                       int dtype, size_t b, int32_t* acc_len, int32_t* out, double* gap,
                        double* p_tok, double* q_tok, double* m_acc, double* m_cdf,
                        double* work)
 {
-    const size_t rowsT = (size_t)(k + 1), rowsD = (size_t)k;
+    const size_t rowsT = (size_t)(kmax + 1), rowsD = (size_t)kmax;
     int flags = 0;
     *m_acc = INFINITY;
     *m_cdf = INFINITY;
+    for (int i = 0; i <= kmax; ++i) gap[i] = NAN;
+    for (int i = 0; i < kmax; ++i) { p_tok[i] = NAN; q_tok[i] = NAN; }
+    if (kb < 0 || kb > kmax) { ref_fill_invalid(kmax, acc_len, out); return 0; }
+    const int k = kb;                         /* this row's draft length */
     for (int i = 0; i <= k; ++i) {
         gap[i] = ref_gap(target, dtype, (b * rowsT + (size_t)i) * (size_t)V, V);
     }
-    for (int i = 0; i < k; ++i) { p_tok[i] = NAN; q_tok[i] = NAN; }
 
     /* validity of the whole batch row */
     int ok = 1;
@@ -227,7 +241,7 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
             ok = ref_row_ok(draft, dtype, (b * rowsD + (size_t)i) * (size_t)V, V);
         }
     }
-    if (!ok) { ref_fill_invalid(k, acc_len, out); return 0; }
+    if (!ok) { ref_fill_invalid(kmax, acc_len, out); return 0; }
 
     if (mode == REF_GREEDY) {
         int a = k;
@@ -238,7 +252,7 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
         *acc_len = a;
         for (int i = 0; i < a; ++i) out[i] = tokens[b * rowsD + (size_t)i];
         out[a] = ref_argmax(target, dtype, (b * rowsT + (size_t)a) * (size_t)V, V);
-        for (int i = a + 1; i <= k; ++i) out[i] = -1;
+        for (int i = a + 1; i <= kmax; ++i) out[i] = -1;
         return 0;
     }
 
@@ -265,7 +279,7 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
     }
     *acc_len = a;
     for (int i = 0; i < a; ++i) out[i] = tokens[b * rowsD + (size_t)i];
-    for (int i = a + 1; i <= k; ++i) out[i] = -1;
+    for (int i = a + 1; i <= kmax; ++i) out[i] = -1;
 
     double u1 = (double)uniforms[(b * rowsT + (size_t)a) * 2 + 1];
     ref_softmax(target, dtype, (b * rowsT + (size_t)a) * (size_t)V, V, T, p);
@@ -295,18 +309,18 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
 /*
  * Public entry. All buffers are host memory.
  *  target  [B,k+1,V] (float32 or bfloat16 bits), draft [B,k,V] (may be NULL in
- *  greedy mode), tokens [B,k] int32, uniforms [B,k+1,2] float32 (may be NULL
- *  in greedy mode).
+ *  greedy mode), tokens [B,k] int32, draft_len [B] int32 (may be NULL: all k),
+ *  uniforms [B,k+1,2] float32 (may be NULL in greedy mode).
  *  Outputs: acc_len [B], out_tokens [B,k+1], gap [B,k+1], p_tok/q_tok [B,k]
  *  (NaN where not computed), margin_acc [B], margin_cdf [B], flags [B].
  *  threads <= 0 uses the OpenMP default. Returns 0, or -1 on bad arguments.
  */
-int spec_verify_ref(const void* target, const void* draft, const int32_t* tokens,
-                    const float* uniforms, float temperature, int mode,
-                    int B, int k, int V, int dtype,
-                    int32_t* acc_len, int32_t* out_tokens, double* gap,
-                    double* p_tok, double* q_tok, double* margin_acc,
-                    double* margin_cdf, int32_t* flags, int threads)
+int spec_verify_ref_ragged(const void* target, const void* draft, const int32_t* tokens,
+                           const int32_t* draft_len, const float* uniforms, float temperature,
+                           int mode, int B, int k, int V, int dtype,
+                           int32_t* acc_len, int32_t* out_tokens, double* gap,
+                           double* p_tok, double* q_tok, double* margin_acc,
+                           double* margin_cdf, int32_t* flags, int threads)
 {
     if (B < 0 || k < 0 || V < 1) return -1;
     if (dtype != REF_F32 && dtype != REF_BF16) return -1;
@@ -339,7 +353,8 @@ int spec_verify_ref(const void* target, const void* draft, const int32_t* tokens
 #endif
         for (int b = 0; b < B; ++b) {
             if (!work) continue;
-            flags[b] = ref_one_row(target, draft, tokens, uniforms, T, mode, k, V, dtype,
+            const int kb = draft_len ? draft_len[b] : k;
+            flags[b] = ref_one_row(target, draft, tokens, uniforms, T, mode, k, kb, V, dtype,
                                    (size_t)b, &acc_len[b], &out_tokens[(size_t)b * (k + 1)],
                                    &gap[(size_t)b * (k + 1)], &p_tok[(size_t)b * k],
                                    &q_tok[(size_t)b * k], &margin_acc[b], &margin_cdf[b], work);
@@ -347,6 +362,19 @@ int spec_verify_ref(const void* target, const void* draft, const int32_t* tokens
         free(work);
     }
     return failed ? -2 : 0;
+}
+
+/* Fixed-length drafts: every batch row verifies all k positions. */
+int spec_verify_ref(const void* target, const void* draft, const int32_t* tokens,
+                    const float* uniforms, float temperature, int mode,
+                    int B, int k, int V, int dtype,
+                    int32_t* acc_len, int32_t* out_tokens, double* gap,
+                    double* p_tok, double* q_tok, double* margin_acc,
+                    double* margin_cdf, int32_t* flags, int threads)
+{
+    return spec_verify_ref_ragged(target, draft, tokens, NULL, uniforms, temperature, mode, B, k, V,
+                                  dtype, acc_len, out_tokens, gap, p_tok, q_tok, margin_acc,
+                                  margin_cdf, flags, threads);
 }
 
 /* Number of threads the OpenMP runtime would use by default. */

@@ -382,3 +382,87 @@ def test_residual_below_fp64_resolution_is_flagged():
     if r2.accepted_len[0] == 0:
         assert r2.flags[0] == 0
 
+
+
+# ---------------------------------------------------------------- ragged drafts
+# A batch row with draft_len kb is, by definition, the verify rule with k = kb
+# on its first kb positions (the design note and the stolen-time article let
+# each sequence guess its own number of tokens). Pinned by identities with the
+# fixed-length rule (itself pinned above): the equal-length case, truncation to
+# kb, rows past kb that are never read, and out-of-range lengths.
+
+def _ragged_case(rng, B, k, V):
+    t = rng.normal(0, 2, (B, k + 1, V)).astype(np.float32)
+    d = (t[:, :k] + rng.normal(0, 1, (B, k, V))).astype(np.float32)
+    tok = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1, 2)).astype(np.float32)
+    return t, d, tok, u
+
+
+@pytest.mark.parametrize("mode", [oracle.SAMPLE, oracle.GREEDY])
+def test_ragged_full_length_equals_fixed(mode):
+    rng = np.random.default_rng(21)
+    t, d, tok, u = _ragged_case(rng, 40, 4, 30)
+    dd, uu = (d, u) if mode == oracle.SAMPLE else (None, None)
+    a = oracle.spec_verify_ref(t, dd, tok, uu, 0.8, mode, dtype=oracle.F32)
+    r = oracle.spec_verify_ref(t, dd, tok, uu, 0.8, mode, dtype=oracle.F32,
+                               draft_len=np.full(40, 4, np.int32))
+    for f in ("accepted_len", "out_tokens", "flags"):
+        assert (getattr(a, f) == getattr(r, f)).all(), f
+    for f in ("gap", "p_tok", "q_tok", "margin_acc", "margin_cdf"):
+        np.testing.assert_array_equal(getattr(a, f), getattr(r, f))
+
+
+@pytest.mark.parametrize("mode", [oracle.SAMPLE, oracle.GREEDY])
+def test_ragged_row_equals_truncated_fixed_call(mode):
+    rng = np.random.default_rng(22)
+    B, k, V = 30, 5, 24
+    t, d, tok, u = _ragged_case(rng, B, k, V)
+    if mode == oracle.GREEDY:
+        am = np.argmax(t[:, :k], axis=2).astype(np.int32)
+        tok = np.where(rng.random((B, k)) < 0.7, am, tok).astype(np.int32)
+    dl = rng.integers(0, k + 1, B).astype(np.int32)
+    dd, uu = (d, u) if mode == oracle.SAMPLE else (None, None)
+    r = oracle.spec_verify_ref(t, dd, tok, uu, 1.3, mode, dtype=oracle.F32, draft_len=dl)
+    for b in range(B):
+        kb = int(dl[b])
+        f = oracle.spec_verify_ref(t[b:b + 1, :kb + 1].copy(),
+                                   None if dd is None else d[b:b + 1, :kb].copy(),
+                                   tok[b:b + 1, :kb].copy(),
+                                   None if uu is None else u[b:b + 1, :kb + 1].copy(),
+                                   1.3, mode, dtype=oracle.F32)
+        assert r.accepted_len[b] == f.accepted_len[0]
+        assert (r.out_tokens[b, :kb + 1] == f.out_tokens[0]).all()
+        assert (r.out_tokens[b, kb + 1:] == -1).all()
+        np.testing.assert_array_equal(r.gap[b, :kb + 1], f.gap[0])
+        assert np.isnan(r.gap[b, kb + 1:]).all()
+        np.testing.assert_array_equal(r.p_tok[b, :kb], f.p_tok[0])
+        assert np.isnan(r.p_tok[b, kb:]).all() and np.isnan(r.q_tok[b, kb:]).all()
+        assert r.margin_acc[b] == f.margin_acc[0] and r.margin_cdf[b] == f.margin_cdf[0]
+        assert r.flags[b] == f.flags[0]
+
+
+def test_ragged_rows_past_the_length_are_not_read():
+    rng = np.random.default_rng(23)
+    B, k, V = 12, 4, 20
+    t, d, tok, u = _ragged_case(rng, B, k, V)
+    dl = rng.integers(0, k + 1, B).astype(np.int32)
+    r = oracle.spec_verify_ref(t, d, tok, u, 1.0, oracle.SAMPLE, dtype=oracle.F32, draft_len=dl)
+    t2, d2, tok2 = t.copy(), d.copy(), tok.copy()
+    for b in range(B):                 # poison everything the row must not read
+        t2[b, dl[b] + 1:] = np.nan
+        d2[b, dl[b]:] = np.inf
+        tok2[b, dl[b]:] = -5
+    r2 = oracle.spec_verify_ref(t2, d2, tok2, u, 1.0, oracle.SAMPLE, dtype=oracle.F32, draft_len=dl)
+    assert (r.accepted_len == r2.accepted_len).all() and (r.accepted_len >= 0).all()
+    assert (r.out_tokens == r2.out_tokens).all()
+    np.testing.assert_array_equal(r.gap, r2.gap)
+
+
+def test_ragged_length_out_of_range_is_invalid():
+    rng = np.random.default_rng(24)
+    t, d, tok, u = _ragged_case(rng, 3, 2, 10)
+    r = oracle.spec_verify_ref(t, d, tok, u, 1.0, oracle.SAMPLE, dtype=oracle.F32,
+                               draft_len=np.array([-1, 3, 2], np.int32))
+    assert list(r.accepted_len[:2]) == [-1, -1] and r.accepted_len[2] >= 0
+    assert (r.out_tokens[:2] == -1).all() and np.isnan(r.gap[:2]).all()
