@@ -100,7 +100,8 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
                 float* draft_prob, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of workspace spec_verify needs for these sizes (0 if the sizes are invalid).
+ * Bytes of workspace spec_verify and spec_verify_ragged need for these sizes (0 if
+ * the sizes are invalid).
  * Host-only; makes no HIP call.
  */
 size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int dtype, int mode);
@@ -115,6 +116,30 @@ int spec_verify_check_args(const void* target_logits, const void* draft_logits,
                            int mode, int32_t B, int32_t k, int32_t V, int dtype,
                            const int32_t* accepted_len, const int32_t* out_tokens, const float* gap,
                            const void* workspace, size_t workspace_bytes);
+
+/*
+ * Ragged drafts: the same step when every batch row carries its own number of drafts
+ * ("Speculative Decoding: The Physics of Stolen Time", section 6, adaptive k; the
+ * speculative-decoding design note, "The acceptance math", variable-length drafting).
+ * draft_len [B] int32 (DEVICE pointer, not NULL, 4-byte aligned) holds kb for every
+ * batch row; the tensors keep the shapes of spec_verify with k = the largest draft
+ * count the caller allows. Row b is verified exactly as spec_verify verifies a call
+ * with k = kb on its first kb positions: target rows 0..kb, draft rows and tokens
+ * 0..kb-1 and uniforms 0..kb are read, nothing else of the row; the bonus token comes
+ * from target row kb. Outputs keep the [B, k+1] / [B, k] layout: gap of rows past kb
+ * and target_prob/draft_prob of positions past kb-1 are NaN, out_tokens past the
+ * emitted token are -1. A draft_len value outside [0, k] makes the row invalid
+ * (accepted_len -1, out_tokens -1, gap NaN); it is not a synchronous error, since
+ * the values live on the device. Only the rows in use are streamed from HBM. The
+ * workspace, errors and execution are those of spec_verify
+ * (spec_verify_workspace_size covers both entry points).
+ */
+int spec_verify_ragged(const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* draft_len,
+                       const float* uniforms, float temperature, int mode, int32_t B, int32_t k,
+                       int32_t V, int dtype, int32_t* accepted_len, int32_t* out_tokens,
+                       float* gap, float* target_prob, float* draft_prob, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* Thread-local description of the last non-zero return of this library. */
 const char* spec_verify_last_error(void);

@@ -24,6 +24,8 @@ L = ctypes.CDLL(os.path.join(HERE, "libspecverify_emu.so"))
 P, I, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 L.spec_verify.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int, P, P, P, P, P, P, S, P]
 L.spec_verify.restype = ctypes.c_int
+L.spec_verify_ragged.argtypes = [P, P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int, P, P, P, P, P, P, S, P]
+L.spec_verify_ragged.restype = ctypes.c_int
 L.spec_verify_workspace_size.argtypes = [I, I, I, ctypes.c_int, ctypes.c_int]
 L.spec_verify_workspace_size.restype = S
 L.spec_verify_last_error.restype = ctypes.c_char_p
@@ -68,17 +70,27 @@ def run_case(x, cus=1, ws_reuse=None, pool=1):
     off = (-base) % 256
     L.spec_verify_emu_set_cu_count(cus)
     L.spec_verify_emu_set_pool(pool)
-    rc = L.spec_verify(ptr(t), ptr(d), ptr(tok), ptr(u), ctypes.c_float(x["T"]), mode, B, k, V, dtype,
-                       ptr(acc), ptr(out), ptr(gap), ptr(tp) if mode == 0 else None,
-                       ptr(dp) if mode == 0 else None, ctypes.c_void_p(base + off), n, None)
+    dl = x.get("draft_len")
+    dlh = None if dl is None else np.ascontiguousarray(np.asarray(dl, np.int32))
+
+    def call(acc, out, gap, tp, dp):
+        if dlh is None:
+            return L.spec_verify(ptr(t), ptr(d), ptr(tok), ptr(u), ctypes.c_float(x["T"]), mode, B, k, V, dtype,
+                                 ptr(acc), ptr(out), ptr(gap), ptr(tp), ptr(dp), ctypes.c_void_p(base + off), n,
+                                 None)
+        return L.spec_verify_ragged(ptr(t), ptr(d), ptr(tok), ptr(dlh), ptr(u), ctypes.c_float(x["T"]), mode, B,
+                                    k, V, dtype, ptr(acc), ptr(out), ptr(gap), ptr(tp), ptr(dp),
+                                    ctypes.c_void_p(base + off), n, None)
+
+    rc = call(acc, out, gap, tp if mode == 0 else None, dp if mode == 0 else None)
     assert rc == 0, (rc, L.spec_verify_last_error())
     # a second call on the same workspace must reproduce the first bit for bit
     acc2, out2, gap2 = acc.copy(), out.copy(), gap.copy()
-    rc = L.spec_verify(ptr(t), ptr(d), ptr(tok), ptr(u), ctypes.c_float(x["T"]), mode, B, k, V, dtype,
-                       ptr(acc2), ptr(out2), ptr(gap2), None, None, ctypes.c_void_p(base + off), n, None)
+    rc = call(acc2, out2, gap2, None, None)
     assert rc == 0
     assert (acc2 == acc).all() and (out2 == out).all() and (gap2.view(np.uint32) == gap.view(np.uint32)).all()
-    ref = oracle.spec_verify_ref(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], mode)
+    ref = oracle.spec_verify_ref(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], mode,
+                                 draft_len=dlh)
     flagged = ref.flagged(DELTA_ACC, DELTA_CDF) if mode == 0 else np.zeros(B, bool)
     same = (acc == ref.accepted_len) & (out == ref.out_tokens).all(axis=1)
     bad = ~same & ~flagged
@@ -91,8 +103,18 @@ def run_case(x, cus=1, ws_reuse=None, pool=1):
     assert (np.isfinite(g) == fin).all()
     assert np.abs(g[fin] - r[fin]).max(initial=0) <= (1e-5 if dtype == 0 else 2e-3)
     if mode == 0 and k > 0:
-        assert np.abs(tp.astype(np.float64)[valid] - ref.p_tok[valid]).max(initial=0) <= 1e-5
-        assert np.abs(dp.astype(np.float64)[valid] - ref.q_tok[valid]).max(initial=0) <= 1e-5
+        for gg, rr in ((tp, ref.p_tok), (dp, ref.q_tok)):
+            gg = gg.astype(np.float64)[valid]
+            rr = rr[valid]
+            assert (np.isnan(gg) == np.isnan(rr)).all()
+            assert np.abs(gg - rr)[~np.isnan(rr)].max(initial=0) <= 1e-5
+    if dlh is not None:
+        # draft lengths outside [0, k]: invalid, every gap NaN
+        bad_len = (dlh < 0) | (dlh > k)
+        assert (acc[bad_len] == -1).all() and np.isnan(gap[bad_len]).all()
+        # rows past kb: NaN gaps
+        past = np.arange(k + 1)[None, :] > dlh[:, None]
+        assert np.isnan(gap[past & valid[:, None]]).all()
     return int(flagged.sum())
 
 
@@ -174,6 +196,26 @@ def bf16_long_rows():
     rng = np.random.default_rng(5)
     for V in (60000, 60001):
         run_case(rand_case(rng, 8, 2, V, 1, 1.0), cus=1)
+
+
+@case
+def ragged():
+    # per-row draft lengths 0..k, with two out-of-range lengths; sampling and
+    # greedy, one wave deciding (rpb <= 64) and one workgroup (k = 40)
+    rng = np.random.default_rng(6)
+    for dtype, k, V, mode, cus in ((0, 5, 3001, 0, 2), (1, 5, 4100, 0, 1), (1, 4, 2000, 1, 2),
+                                   (0, 40, 97, 0, 1), (1, 40, 130, 1, 1)):
+        B = 9
+        x = rand_case(rng, B, k, V, dtype, 1.1, mode=mode, coarse=mode == 1)
+        dl = rng.integers(0, k + 1, B).astype(np.int32)
+        dl[2], dl[5] = -1, k + 1
+        dl[0], dl[1] = 0, k
+        x["draft_len"] = dl
+        run_case(x, cus=cus)
+    # more batch rows than one chunk of the row-packing scan (greedy: no pass 2)
+    x = rand_case(rng, 1100, 2, 5, 0, 1.0, mode=1, coarse=True)
+    x["draft_len"] = rng.integers(-1, 4, 1100).astype(np.int32)
+    run_case(x, cus=4)
 
 
 @case

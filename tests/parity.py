@@ -69,6 +69,7 @@ def compare(gpu, ref, dtype: str, greedy: bool):
     g_gpu = gap[valid]
     fin = np.isfinite(g_ref)
     assert (np.isfinite(g_gpu) == fin).all(), "gap finiteness differs"
+    assert (np.isnan(g_gpu) == np.isnan(g_ref)).all(), "gap NaN positions differ"
     if fin.any():
         err = np.abs(g_gpu[fin] - g_ref[fin]).max()
         stats["gap_err"] = float(err)
@@ -77,7 +78,10 @@ def compare(gpu, ref, dtype: str, greedy: bool):
         for name, g, r in (("p", gpu.target_prob, ref.p_tok), ("q", gpu.draft_prob, ref.q_tok)):
             gg = g.cpu().numpy().astype(np.float64)[valid]
             rr = r[valid]
-            err = np.abs(gg - rr).max() if rr.size else 0.0
+            # positions a row does not verify (ragged drafts) are NaN on both sides
+            nan = np.isnan(rr)
+            assert (np.isnan(gg) == nan).all(), f"{name}(x) NaN positions differ"
+            err = np.abs(gg[~nan] - rr[~nan]).max() if (~nan).any() else 0.0
             stats[f"{name}_err"] = float(err)
             assert err <= tol, f"{name}(x) error {err} > {tol}"
     return stats

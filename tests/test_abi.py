@@ -27,7 +27,7 @@ def test_exports_match_header():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     exported = {s for s in exported if s.startswith("spec_verify")}
     assert declared() == exported
-    assert len(exported) == 5
+    assert len(exported) == 6
 
 
 def test_version():
@@ -116,3 +116,20 @@ def test_cpu_tensors_rejected():
     with pytest.raises(ValueError):
         tv.spec_verify(t, torch.zeros(1, 1, 4), torch.zeros(1, 1, dtype=torch.int32),
                        torch.zeros(1, 2, 2), 1.0, 0)
+
+
+@pytest.mark.parametrize("kw,dlen,code", [
+    ({}, None, -1),                 # draft_len is required by the ragged entry
+    ({}, FAKE + 2, -7),             # and 4-byte aligned
+    ({"B": 0}, FAKE, -2),
+    ({"tokens": None}, FAKE, -1),
+])
+def test_ragged_entry_rejects_synchronously(kw, dlen, code):
+    # every case fails the host-side checks, so no HIP call is made
+    a = args(**kw)
+    L = tv.lib()
+    rc = L.spec_verify_ragged(a["target"], a["draft"], a["tokens"], dlen, a["uniforms"],
+                              ctypes.c_float(a["T"]), a["mode"], a["B"], a["k"], a["V"], a["dtype"],
+                              a["acc"], a["out"], a["gap"], None, None, a["ws"], a["ws_bytes"], None)
+    assert rc == code
+    assert binding.last_error()

@@ -61,6 +61,10 @@ def test_emulated_bf16_long_rows(emu_lib):
     run_cases("bf16_long_rows")
 
 
+def test_emulated_ragged_drafts(emu_lib):
+    run_cases("ragged")
+
+
 def test_emulated_concurrent_workgroups(emu_lib):
     run_cases("concurrent_b8")
 

@@ -52,6 +52,9 @@ def lib():
                 L.spec_verify.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
                                           P, P, P, P, P, P, S, P]
                 L.spec_verify.restype = ctypes.c_int
+                L.spec_verify_ragged.argtypes = [P, P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
+                                                 P, P, P, P, P, P, S, P]
+                L.spec_verify_ragged.restype = ctypes.c_int
                 L.spec_verify_workspace_size.argtypes = [I, I, I, ctypes.c_int, ctypes.c_int]
                 L.spec_verify_workspace_size.restype = S
                 L.spec_verify_check_args.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
@@ -108,12 +111,15 @@ def _ptr(t: Optional[torch.Tensor]):
 def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
                 uniforms: Optional[torch.Tensor], temperature: float = 1.0, mode: int = SAMPLE, *,
                 workspace: Optional[torch.Tensor] = None, return_probs: bool = False,
-                out: Optional[VerifyResult] = None) -> VerifyResult:
+                out: Optional[VerifyResult] = None,
+                draft_len: Optional[torch.Tensor] = None) -> VerifyResult:
     """Batched verify step on device tensors (see include/spec_verify.h).
 
     target [B,k+1,V] and draft [B,k,V] are float32 or bfloat16 (draft may be
     None in greedy mode), tokens [B,k] int32, uniforms [B,k+1,2] float32 (None
-    allowed in greedy mode). Work is enqueued on the current stream of the
+    allowed in greedy mode). With draft_len (int32 [B] on the same device)
+    every batch row b verifies only its first draft_len[b] positions
+    (spec_verify_ragged). Work is enqueued on the current stream of the
     target's device; the returned tensors are ready once that stream is.
     """
     if not isinstance(target, torch.Tensor) or target.dim() != 3:
@@ -137,7 +143,10 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: tor
     if uniforms is not None:
         if uniforms.shape != (B, k + 1, 2) or uniforms.dtype != torch.float32 or uniforms.device != dev:
             raise ValueError("uniforms must be float32 [B, k+1, 2] on the target's device")
-    for t in (target, draft, tokens, uniforms):
+    if draft_len is not None:
+        if draft_len.shape != (B,) or draft_len.dtype != torch.int32 or draft_len.device != dev:
+            raise ValueError("draft_len must be int32 [B] on the target's device")
+    for t in (target, draft, tokens, uniforms, draft_len):
         if t is not None and not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
 
@@ -154,11 +163,15 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: tor
     if need == 0:
         raise SpecVerifyError(-2, f"unsupported sizes B={B} k={k} V={V}")
     ws = workspace if workspace is not None else _workspace(dev, stream, need)
-    rc = lib().spec_verify(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms),
-                           ctypes.c_float(temperature), int(mode), B, k, V, dtype,
-                           _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
-                           _ptr(out.target_prob), _ptr(out.draft_prob),
-                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+    tail = (ctypes.c_float(temperature), int(mode), B, k, V, dtype,
+            _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
+            _ptr(out.target_prob), _ptr(out.draft_prob),
+            ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+    if draft_len is None:
+        rc = lib().spec_verify(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), *tail)
+    else:
+        rc = lib().spec_verify_ragged(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(draft_len),
+                                      _ptr(uniforms), *tail)
     if rc != 0:
         raise SpecVerifyError(rc, last_error())
     return out

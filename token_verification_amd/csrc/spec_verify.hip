@@ -139,6 +139,7 @@ struct alignas(32) BatchRec {  // what pass 2 and the draw need of one batch row
     float mp, mq;              // max raw logit of target row a and (a < k) draft row a
     double lam;                // pass-1 estimate of S_p/S_q at row a (a < k), max-normalised
     double lam_hat;            // the same in pass 2's units (written by pass 2)
+    int kb;                    // this batch row's draft length (a < kb: residual draw)
 };
 
 struct alignas(64) SegRec {    // one pass-2 segment (one wave's share of a row pair)
@@ -153,6 +154,7 @@ struct Params {
     const void* tgt;
     const void* dft;
     const int* tok;
+    const int* dlen;           // [B] per-row draft lengths (ragged drafts), or null: all k
     const float* uni;
     int* acc_len;
     int* out_tok;
@@ -176,6 +178,11 @@ struct Params {
     SegRec* segs;              // [B*nseg]
     double* exptab;            // [EXP_N] 2^(j/EXP_N), written by pass 1 for pass 2
     double* tautab;            // [TAB_MAX] exp(v/T - tab_c) of bf16 values v, written by pass 1
+    // ragged drafts: only the rows a batch row uses enter pass 1's flattened
+    // space, in batch-row order; written by rows_kernel before pass 1
+    int* rowoff;               // [B] first packed row of each batch row
+    int* rowmap;               // [rows] packed row -> (b << 9) | bonus << 8 | draft << 7 | position
+    long long* rhdr;           // [2] pass 1's slice length L and element count N
     int tab_on;                // the bf16 value table is built and usable
     double tab_lim;            // the table covers 2^-16 <= |v| < tab_lim
     double tab_c;
@@ -681,8 +688,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void sc
             }
         }
     }
-    const long long g0 = w * P.L;
-    const long long g1 = g0 + P.L < P.N ? g0 + P.L : P.N;
+    // ragged drafts: the slice length and element count of the packed rows
+    const long long L = P.dlen ? P.rhdr[0] : P.L, N = P.dlen ? P.rhdr[1] : P.N;
+    const long long g0 = w * L;
+    const long long g1 = g0 + L < N ? g0 + L : N;
     int seg = 0;
     for (long long g = g0; g < g1; ++seg) {
         Red& R = R2[seg & 1];
@@ -690,26 +699,90 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void sc
         const int e0 = static_cast<int>(g - row * V);
         const long long rend = (row + 1) * V < g1 ? (row + 1) * V : g1;
         const int e1 = static_cast<int>(rend - row * V);
-        const int b = static_cast<int>(row / P.rpb), j = static_cast<int>(row % P.rpb);
-        const bool is_target = j <= k;
+        // batch row, target or draft row, its position, and whether it is the
+        // bonus row (the target row after the last draft position)
+        int b, pos;
+        bool draft, bonus;
+        if (P.dlen) {
+            const int code = P.rowmap[row];
+            b = code >> 9; bonus = (code >> 8) & 1; draft = (code >> 7) & 1; pos = code & 127;
+        } else {
+            b = static_cast<int>(row / P.rpb);
+            const int j = static_cast<int>(row % P.rpb);
+            draft = j > k; pos = draft ? j - k - 1 : j; bonus = j == k;
+        }
         const char* rowp;
-        if (is_target)
-            rowp = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + j) * V * E::ES;
+        if (!draft)
+            rowp = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + pos) * V * E::ES;
         else
-            rowp = static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + (j - k - 1)) * V * E::ES;
+            rowp = static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + pos) * V * E::ES;
         TileRec tr;
         if constexpr (MODE == SPEC_MODE_GREEDY) {
             tr = tile_scan<E, K_GREEDY>(rowp, e0, e1, nullptr, P.ch, P.cl, R);
         } else {
-            // the draft token of this row's position (target rows i < k, draft rows)
-            const int pos = is_target ? j : j - k - 1;
-            const int* tokp = pos < k ? P.tok + static_cast<size_t>(b) * k + pos : nullptr;
-            if (j == k) tr = tile_scan<E, K_TOP2>(rowp, e0, e1, nullptr, P.ch, P.cl, R);
-            else if (is_target) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, tokp, P.ch, P.cl, R);
+            // the draft token of this row's position (every row but the bonus row)
+            const int* tokp = P.tok + static_cast<size_t>(b) * k + pos;
+            if (bonus) tr = tile_scan<E, K_TOP2>(rowp, e0, e1, nullptr, P.ch, P.cl, R);
+            else if (!draft) tr = tile_scan<E, K_TARGET>(rowp, e0, e1, tokp, P.ch, P.cl, R);
             else tr = tile_scan<E, K_DRAFT>(rowp, e0, e1, tokp, P.ch, P.cl, R);
         }
         if (tid == 0) P.tiles[row + w] = tr;
         g = rend;
+    }
+}
+
+// Ragged drafts: pack the rows each batch row uses (target rows 0..kb, then,
+// in sampling mode, draft rows 0..kb-1) into pass 1's flattened space, so
+// pass 1 reads only those. One workgroup scans the row counts in chunks of
+// NTR batch rows; a draft length outside [0, k] contributes no rows. Also
+// sets pass 1's slice length for its G workgroups.
+constexpr int NTR = 1024;
+
+__global__ __launch_bounds__(NTR) void rows_kernel(Params P) {
+    __shared__ int wsum[NTR / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const bool sample = P.mode == SPEC_MODE_SAMPLE;
+    int carry = 0;
+    for (int c0 = 0; c0 < P.B; c0 += NTR) {
+        const int b = c0 + tid;
+        int kb = -1, n = 0;
+        if (b < P.B) {
+            kb = P.dlen[b];
+            if (kb >= 0 && kb <= P.k) n = sample ? 2 * kb + 1 : kb + 1;
+        }
+        int x = n;                                         // inclusive scan over the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wv] = x;
+        __syncthreads();
+        int pre = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < NTR / 64; ++i) {
+            const int t = wsum[i];
+            pre += i < wv ? t : 0;
+            tot += t;
+        }
+        const int r0 = carry + pre + x - n;
+        if (b < P.B) {
+            P.rowoff[b] = r0;
+            for (int j = 0; j < n; ++j) {
+                const int dr = j > kb;
+                const int pos = dr ? j - kb - 1 : j;
+                const int bonus = !dr && j == kb;
+                P.rowmap[r0 + j] = (b << 9) | (bonus << 8) | (dr << 7) | pos;
+            }
+        }
+        carry += tot;
+        __syncthreads();                                   // wsum is reused
+    }
+    if (tid == 0) {
+        const long long N = static_cast<long long>(carry) * P.V;
+        const long long L = (N + P.G - 1) / P.G;
+        P.rhdr[0] = L > 0 ? L : 1;
+        P.rhdr[1] = N;
     }
 }
 
@@ -758,78 +831,115 @@ __device__ inline RowRec merge_row(const TileRec* t, long long w0, long long w1,
     return rr;
 }
 
+// Draft length, first row record and pass-1 slice length of batch row b. A
+// draft length outside [0, k] gives kb = -1: the row has no records and is
+// invalid.
+struct RowSpan {
+    int kb;
+    long long row0, L;
+};
+
+__device__ inline RowSpan row_span(const Params& P, int b) {
+    RowSpan r;
+    if (P.dlen) {
+        const int kb = P.dlen[b];
+        r.kb = kb >= 0 && kb <= P.k ? kb : -1;
+        r.row0 = P.rowoff[b];
+        r.L = P.rhdr[0];
+    } else {
+        r.kb = P.k;
+        r.row0 = static_cast<long long>(b) * P.rpb;
+        r.L = P.L;
+    }
+    return r;
+}
+
 // Decide batch row b in one workgroup (any size of at least k + 1 and rpb
 // threads): merge the segment records of its rows, evaluate the acceptance
 // tests, and return (in every thread) what pass 2 needs. With `write`, also
-// write the outputs and the batch record.
+// write the outputs and the batch record. A row with draft length kb < k
+// decides positions 0..kb-1 with the bonus at row kb; its outputs past those
+// are NaN (gap, p, q) and -1 (tokens).
 template <class E, int MODE>
 __device__ BatchRec decide_batch(const Params& P, Dec& D, int b, bool write) {
     const int tid = threadIdx.x;
-    const int k = P.k, V = P.V, rpb = P.rpb;
+    const int k = P.k, V = P.V;
     constexpr bool sample = MODE == SPEC_MODE_SAMPLE;
+    const RowSpan sp = row_span(P, b);
+    const bool kb_ok = sp.kb >= 0;
+    const int kb = kb_ok ? sp.kb : 0;
+    const int nrows = !kb_ok ? 0 : sample ? 2 * kb + 1 : kb + 1;
 
     // One round of independent loads: the draft token and uniform of position
     // tid, and the segment records of row tid (the draft-token logits came with
     // the records).
     int x = -1;
     double u0 = 0.0;
-    if (tid < k) {
+    if (tid < kb) {
         x = P.tok[static_cast<size_t>(b) * k + tid];
         if constexpr (sample) u0 = P.uni[(static_cast<size_t>(b) * (k + 1) + tid) * 2];
     }
-    if (sample && tid <= k) D.u1[tid] = P.uni[(static_cast<size_t>(b) * (k + 1) + tid) * 2 + 1];
-    if (tid < rpb) {
-        const size_t row = static_cast<size_t>(b) * rpb + tid;
-        const long long r0 = static_cast<long long>(row) * V;
-        // the bonus target row k of sampling mode carries no sum
-        const RowRec rr = merge_row<MODE>(P.tiles + row, r0 / P.L, (r0 + V - 1) / P.L, tid != k);
-        D.rec[tid] = rr;
-        if (write && tid <= k) {
-            const float g = (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
-            P.gap[static_cast<size_t>(b) * (k + 1) + tid] = g;
-        }
+    if (sample && tid <= kb) D.u1[tid] = P.uni[(static_cast<size_t>(b) * (k + 1) + tid) * 2 + 1];
+    if (tid < nrows) {
+        const long long row = sp.row0 + tid;
+        const long long r0 = row * V;
+        // the bonus target row kb of sampling mode carries no sum
+        D.rec[tid] = merge_row<MODE>(P.tiles + row, r0 / sp.L, (r0 + V - 1) / sp.L, tid != kb);
+    } else if (tid == 0) {
+        D.rec[0].valid = 0;                                // no records: invalid draft length
     }
-    if (tid == 0) { D.valid = 1; D.a = k; }
+    if (write && tid <= k) {
+        float g = __builtin_nanf("");
+        if (tid < nrows && tid <= kb) {
+            const RowRec& rr = D.rec[tid];
+            g = (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
+        }
+        P.gap[static_cast<size_t>(b) * (k + 1) + tid] = g;
+    }
+    if (tid == 0) { D.valid = 1; D.a = kb; }
     lds_sync();
 
     int ok = 1;
-    if (tid <= k) ok = D.rec[tid].valid;                  // target rows 0..k
+    if (tid <= kb) ok = D.rec[tid].valid;                 // target rows 0..kb
     if (tid < k) {
-        const bool inr = x >= 0 && x < V;
-        if (!inr) ok = 0;
-        if (sample && !D.rec[k + 1 + tid].valid) ok = 0;
-        if (sample && ok && !(D.rec[tid].has_lx && D.rec[k + 1 + tid].has_lx)) ok = 0;
         int acc = 0;
         float pf = __builtin_nanf(""), qf = __builtin_nanf("");
-        if (ok) {
-            const RowRec& rt = D.rec[tid];
-            if constexpr (sample) {
-                // log2 p(x) = x*c - lg_p and log2 q(x) = x*c - lg_q, in double
-                const RowRec& rd = D.rec[k + 1 + tid];
-                const double lt = rt.lx, ld = rd.lx;
-                const double c = P.c;
-                const double lp = lt == -INFINITY ? -INFINITY : lt * c - rt.lg;
-                const double lq = ld == -INFINITY ? -INFINITY : ld * c - rd.lg;
-                double r;
-                if (lq == -INFINITY) r = (lp == -INFINITY) ? 0.0 : INFINITY;
-                else r = exp2_lean(lp - lq);
-                acc = u0 < r;
-                pf = exp2f(static_cast<float>(lp));
-                qf = exp2f(static_cast<float>(lq));
-            } else {
-                acc = (x == rt.idx);
+        if (tid < kb) {
+            const bool inr = x >= 0 && x < V;
+            if (!inr) ok = 0;
+            if (sample && !D.rec[kb + 1 + tid].valid) ok = 0;
+            if (sample && ok && !(D.rec[tid].has_lx && D.rec[kb + 1 + tid].has_lx)) ok = 0;
+            if (ok) {
+                const RowRec& rt = D.rec[tid];
+                if constexpr (sample) {
+                    // log2 p(x) = x*c - lg_p and log2 q(x) = x*c - lg_q, in double
+                    const RowRec& rd = D.rec[kb + 1 + tid];
+                    const double lt = rt.lx, ld = rd.lx;
+                    const double c = P.c;
+                    const double lp = lt == -INFINITY ? -INFINITY : lt * c - rt.lg;
+                    const double lq = ld == -INFINITY ? -INFINITY : ld * c - rd.lg;
+                    double r;
+                    if (lq == -INFINITY) r = (lp == -INFINITY) ? 0.0 : INFINITY;
+                    else r = exp2_lean(lp - lq);
+                    acc = u0 < r;
+                    pf = exp2f(static_cast<float>(lp));
+                    qf = exp2f(static_cast<float>(lq));
+                } else {
+                    acc = (x == rt.idx);
+                }
             }
+            D.acc[tid] = acc;
         }
-        D.acc[tid] = acc;
-        if (write && P.tprob) P.tprob[static_cast<size_t>(b) * k + tid] = ok ? pf : __builtin_nanf("");
-        if (write && P.dprob) P.dprob[static_cast<size_t>(b) * k + tid] = ok ? qf : __builtin_nanf("");
+        const bool pq = tid < kb && ok;
+        if (write && P.tprob) P.tprob[static_cast<size_t>(b) * k + tid] = pq ? pf : __builtin_nanf("");
+        if (write && P.dprob) P.dprob[static_cast<size_t>(b) * k + tid] = pq ? qf : __builtin_nanf("");
     }
     if (!ok) atomicAnd(&D.valid, 0);
     lds_sync();
     const int valid = D.valid;
     if (tid == 0) {
-        int a = k;
-        for (int i = 0; i < k; ++i) if (!D.acc[i]) { a = i; break; }
+        int a = kb;
+        for (int i = 0; i < kb; ++i) if (!D.acc[i]) { a = i; break; }
         D.a = a;
     }
     lds_sync();
@@ -846,17 +956,18 @@ __device__ BatchRec decide_batch(const Params& P, Dec& D, int b, bool write) {
         if (write) P.acc_len[b] = valid ? a : -1;
         BatchRec br;
         br.a = valid ? a : -1;
+        br.kb = kb;
         br.u1 = sample ? D.u1[a] : 0.0f;
         br.mp = D.rec[a].m;
-        br.mq = sample && a < k ? D.rec[k + 1 + a].m : 0.0f;
+        br.mq = sample && a < kb ? D.rec[kb + 1 + a].m : 0.0f;
         br.lam = 0.0;
         br.lam_hat = 0.0;
-        if (sample && valid && a < k) {
+        if (sample && valid && a < kb) {
             // S_p/S_q in the exp((x - m)/T) normalisation of pass 2: only
             // used to place a relative band of ETA, so 2^d is taken as
             // 2^round(d) * exp2f(d - round(d)) (relative error ~1e-7)
             const RowRec& rt = D.rec[a];
-            const RowRec& rd = D.rec[k + 1 + a];
+            const RowRec& rd = D.rec[kb + 1 + a];
             const double c = P.c;
             const double d = (rt.lg - static_cast<double>(rt.m) * c) - (rd.lg - static_cast<double>(rd.m) * c);
             const double n = rint(d);
@@ -877,38 +988,43 @@ __device__ BatchRec decide_batch(const Params& P, Dec& D, int b, bool write) {
 template <class E, int MODE>
 __device__ BatchRec decide_wave(const Params& P, int b, bool write) {
     const int lane = threadIdx.x & 63;
-    const int k = P.k, V = P.V, rpb = P.rpb;
+    const int k = P.k, V = P.V;
     constexpr bool sample = MODE == SPEC_MODE_SAMPLE;
+    const RowSpan sp = row_span(P, b);
+    const bool kb_ok = sp.kb >= 0;
+    const int kb = kb_ok ? sp.kb : 0;
+    const int nrows = !kb_ok ? 0 : sample ? 2 * kb + 1 : kb + 1;
     int x = -1;
     double u0 = 0.0;
     float u1 = 0.0f;
-    if (lane < k) {
+    if (lane < kb) {
         x = P.tok[static_cast<size_t>(b) * k + lane];
         if constexpr (sample) u0 = P.uni[(static_cast<size_t>(b) * (k + 1) + lane) * 2];
     }
-    if (sample && lane <= k) u1 = P.uni[(static_cast<size_t>(b) * (k + 1) + lane) * 2 + 1];
+    if (sample && lane <= kb) u1 = P.uni[(static_cast<size_t>(b) * (k + 1) + lane) * 2 + 1];
     RowRec rr;
     rr.m = -INFINITY; rr.t2 = -INFINITY; rr.idx = 0x7fffffff; rr.valid = 0; rr.lg = 0.0; rr.lx = 0.0f; rr.has_lx = 0;
-    if (lane < rpb) {
-        const size_t row = static_cast<size_t>(b) * rpb + lane;
-        const long long r0 = static_cast<long long>(row) * V;
-        // the bonus target row k of sampling mode carries no sum
-        rr = merge_row<MODE>(P.tiles + row, r0 / P.L, (r0 + V - 1) / P.L, lane != k);
-        if (write && lane <= k) {
-            const float g = (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
-            P.gap[static_cast<size_t>(b) * (k + 1) + lane] = g;
-        }
+    if (lane < nrows) {
+        const long long row = sp.row0 + lane;
+        const long long r0 = row * V;
+        // the bonus target row kb of sampling mode carries no sum
+        rr = merge_row<MODE>(P.tiles + row, r0 / sp.L, (r0 + V - 1) / sp.L, lane != kb);
     }
-    // draft row of position lane (lane < k): lane k + 1 + lane
-    const int dl = lane < k ? k + 1 + lane : lane;
+    if (write && lane <= k) {
+        const float g = lane >= nrows || lane > kb ? __builtin_nanf("")
+                      : (rr.t2 == -INFINITY) ? INFINITY : rr.m - rr.t2;
+        P.gap[static_cast<size_t>(b) * (k + 1) + lane] = g;
+    }
+    // draft row of position lane (lane < kb): lane kb + 1 + lane
+    const int dl = lane < kb ? kb + 1 + lane : lane;
     const int d_valid = __shfl(rr.valid, dl, 64);
     const int d_has = __shfl(rr.has_lx, dl, 64);
     const float d_lx = __shfl(rr.lx, dl, 64);
     const double d_lg = __shfl(rr.lg, dl, 64);
-    int ok = lane <= k ? rr.valid : 1;                     // target rows 0..k
+    int ok = lane <= kb ? rr.valid : 1;                    // target rows 0..kb (none: invalid)
     int acc = 0;
     float pf = __builtin_nanf(""), qf = __builtin_nanf("");
-    if (lane < k) {
+    if (lane < kb) {
         if (!(x >= 0 && x < V)) ok = 0;
         if (sample && !d_valid) ok = 0;
         if (sample && ok && !(rr.has_lx && d_has)) ok = 0;
@@ -929,12 +1045,15 @@ __device__ BatchRec decide_wave(const Params& P, int b, bool write) {
                 acc = (x == rr.idx);
             }
         }
-        if (write && P.tprob) P.tprob[static_cast<size_t>(b) * k + lane] = ok ? pf : __builtin_nanf("");
-        if (write && P.dprob) P.dprob[static_cast<size_t>(b) * k + lane] = ok ? qf : __builtin_nanf("");
+    }
+    if (lane < k) {
+        const bool pq = lane < kb && ok;
+        if (write && P.tprob) P.tprob[static_cast<size_t>(b) * k + lane] = pq ? pf : __builtin_nanf("");
+        if (write && P.dprob) P.dprob[static_cast<size_t>(b) * k + lane] = pq ? qf : __builtin_nanf("");
     }
     const bool valid = __ballot(!ok) == 0;
-    const unsigned long long rej = __ballot(lane < k && !acc);
-    const int a = rej ? __ffsll(static_cast<long long>(rej)) - 1 : k;
+    const unsigned long long rej = __ballot(lane < kb && !acc);
+    const int a = rej ? __ffsll(static_cast<long long>(rej)) - 1 : kb;
     const int idx_a = __shfl(rr.idx, a, 64);
     if (write && lane <= k) {
         int o;
@@ -947,17 +1066,18 @@ __device__ BatchRec decide_wave(const Params& P, int b, bool write) {
     if (write && lane == 0) P.acc_len[b] = valid ? a : -1;
     const float mp = __shfl(rr.m, a, 64);
     const double lgp = __shfl(rr.lg, a, 64);
-    const int ad = a < k ? k + 1 + a : a;
+    const int ad = a < kb ? kb + 1 + a : a;
     const float mq = __shfl(rr.m, ad, 64);
     const double lgq = __shfl(rr.lg, ad, 64);
     BatchRec br;
     br.a = valid ? a : -1;
+    br.kb = kb;
     br.u1 = sample ? __shfl(u1, a, 64) : 0.0f;
     br.mp = mp;
-    br.mq = sample && a < k ? mq : 0.0f;
+    br.mq = sample && a < kb ? mq : 0.0f;
     br.lam = 0.0;
     br.lam_hat = 0.0;
-    if (sample && valid && a < k) {
+    if (sample && valid && a < kb) {
         // S_p/S_q in the exp((x - m)/T) normalisation of pass 2 (see decide_batch)
         const double c = P.c;
         const double d = (lgp - static_cast<double>(mp) * c) - (lgq - static_cast<double>(mq) * c);
@@ -1045,7 +1165,7 @@ template <class E>
 __device__ inline Pass2 pass2_rows(const Params& P, int b, const BatchRec& br) {
     const int k = P.k, V = P.V, a = br.a < 0 ? 0 : br.a;
     Pass2 Q;
-    Q.resid = a < k;
+    Q.resid = a < br.kb;
     Q.rowT = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + a) * V * E::ES;
     Q.rowD = Q.resid ? static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + a) * V * E::ES
                      : Q.rowT;
@@ -1567,7 +1687,7 @@ __global__ __launch_bounds__(NT2) void draw_kernel(Params P) {
         for (int s = tid + NT2; s < NS; s += NT2) { sums[0] += recs[s].sp; sums[1] += recs[s].sq; }
         block_sum<2>(S.R, sums);                           // also publishes the exp table
         const double lh = Q.lam_hat;
-        Q.resid = br.a < k;
+        Q.resid = br.a < br.kb;
         Q.lam = Q.resid ? sums[0] / sums[1] : 0.0;
         const bool band_ok = !Q.resid ||
             (!P.force_exact && Q.lam >= lh * (1.0 - ETA) && Q.lam <= lh * (1.0 + ETA));
@@ -1705,7 +1825,7 @@ struct Plan {
     int wmax;                  // most pass-2 workgroups per batch row (sampling; 0 in greedy mode)
     size_t rows_total;
     // workspace offsets (bytes)
-    size_t o_tiles, o_bat, o_segs, o_exp, o_tau, total;
+    size_t o_tiles, o_bat, o_segs, o_exp, o_tau, o_rowoff, o_rowmap, o_rhdr, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1738,6 +1858,10 @@ bool make_plan(int32_t B, int32_t k, int32_t V, int mode, int dtype, Plan& p) {
     p.o_segs = o; o = align256(o + static_cast<size_t>(B) * p.wmax * (NTS / 64) * sizeof(SegRec));
     p.o_exp = o; o = align256(o + EXP_N * sizeof(double));
     p.o_tau = o; o = align256(o + TAB_MAX * sizeof(double));
+    // ragged drafts (also counted for fixed-length calls: one size serves both)
+    p.o_rowoff = o; o = align256(o + static_cast<size_t>(B) * sizeof(int));
+    p.o_rowmap = o; o = align256(o + p.rows_total * sizeof(int));
+    p.o_rhdr = o; o = align256(o + 2 * sizeof(long long));
     p.total = o;
     return true;
 }
@@ -1746,7 +1870,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int check(const void* tgt, const void* dft, const int32_t* tok, const float* uni, float T, int mode,
           int32_t B, int32_t k, int32_t V, int dtype, const int32_t* acc, const int32_t* out,
-          const float* gap, const void* ws, size_t ws_bytes, Plan& plan) {
+          const float* gap, const void* ws, size_t ws_bytes, Plan& plan, bool ragged = false,
+          const int32_t* dlen = nullptr) {
     if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16)
         return fail(SPEC_ERR_DTYPE, "dtype %d is not SPEC_DTYPE_F32 or SPEC_DTYPE_BF16", dtype);
     if (mode != SPEC_MODE_SAMPLE && mode != SPEC_MODE_GREEDY)
@@ -1760,6 +1885,7 @@ int check(const void* tgt, const void* dft, const int32_t* tok, const float* uni
     const bool sample = mode == SPEC_MODE_SAMPLE;
     if (!tgt) return fail(SPEC_ERR_NULL, "target_logits is NULL");
     if (k > 0 && !tok) return fail(SPEC_ERR_NULL, "draft_tokens is NULL");
+    if (ragged && !dlen) return fail(SPEC_ERR_NULL, "draft_len is NULL");
     if (sample && k > 0 && !dft) return fail(SPEC_ERR_NULL, "draft_logits is NULL in sampling mode");
     if (sample && !uni) return fail(SPEC_ERR_NULL, "uniforms is NULL in sampling mode");
     if (!acc || !out || !gap) return fail(SPEC_ERR_NULL, "an output pointer is NULL");
@@ -1767,7 +1893,8 @@ int check(const void* tgt, const void* dft, const int32_t* tok, const float* uni
         return fail(SPEC_ERR_TEMP, "temperature must be finite and > 0 in sampling mode (got %g)", (double)T);
     const size_t es = dtype == SPEC_DTYPE_F32 ? 4 : 2;
     if (!aligned(tgt, es) || (dft && !aligned(dft, es)) || (tok && !aligned(tok, 4)) ||
-        (uni && !aligned(uni, 4)) || !aligned(acc, 4) || !aligned(out, 4) || !aligned(gap, 4))
+        (uni && !aligned(uni, 4)) || !aligned(acc, 4) || !aligned(out, 4) || !aligned(gap, 4) ||
+        (dlen && !aligned(dlen, 4)))
         return fail(SPEC_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
     if (!ws || ws_bytes < plan.total)
         return fail(SPEC_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", plan.total, ws_bytes,
@@ -1808,8 +1935,16 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     if (G < 1) G = 1;
     P.L = (P.N + G - 1) / G;
     P.G = static_cast<int>((P.N + P.L - 1) / P.L);
+    hipError_t e;
+    if (P.dlen) {
+        // ragged drafts: the packed rows and pass 1's slices over them (at
+        // most P.N elements, so the same G workgroups suffice)
+        hipLaunchKernelGGL(rows_kernel, dim3(1), dim3(NTR), 0, s, P);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((scan_kernel<E, MODE>), dim3(P.G), dim3(NT), 0, s, P);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (MODE == SPEC_MODE_GREEDY) {
         hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
@@ -1834,33 +1969,13 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     return hipGetLastError();
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int dtype, int mode) {
-    if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return 0;
-    Plan p;
-    if (!make_plan(B, k, V, mode, dtype, p)) return 0;
-    return p.total;
-}
-
-int spec_verify_check_args(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
-                           const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V,
-                           int dtype, const int32_t* accepted_len, const int32_t* out_tokens, const float* gap,
-                           const void* workspace, size_t workspace_bytes) {
-    Plan p;
-    return check(target_logits, draft_logits, draft_tokens, uniforms, temperature, mode, B, k, V, dtype,
-                 accepted_len, out_tokens, gap, workspace, workspace_bytes, p);
-}
-
-int spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
-                const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V, int dtype,
-                int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
-                void* workspace, size_t workspace_bytes, void* stream) {
+int run(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens, const int32_t* draft_len,
+        bool ragged, const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V, int dtype,
+        int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
+        void* workspace, size_t workspace_bytes, void* stream) {
     Plan plan;
     const int rc = check(target_logits, draft_logits, draft_tokens, uniforms, temperature, mode, B, k, V,
-                         dtype, accepted_len, out_tokens, gap, workspace, workspace_bytes, plan);
+                         dtype, accepted_len, out_tokens, gap, workspace, workspace_bytes, plan, ragged, draft_len);
     if (rc != SPEC_OK) return rc;
 
     char* ws = static_cast<char*>(workspace);
@@ -1868,6 +1983,7 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
     P.tgt = target_logits;
     P.dft = draft_logits;
     P.tok = draft_tokens;
+    P.dlen = ragged ? draft_len : nullptr;
     P.uni = uniforms;
     P.acc_len = accepted_len;
     P.out_tok = out_tokens;
@@ -1915,6 +2031,9 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
     P.segs = reinterpret_cast<SegRec*>(ws + plan.o_segs);
     P.exptab = reinterpret_cast<double*>(ws + plan.o_exp);
     P.tautab = reinterpret_cast<double*>(ws + plan.o_tau);
+    P.rowoff = reinterpret_cast<int*>(ws + plan.o_rowoff);
+    P.rowmap = reinterpret_cast<int*>(ws + plan.o_rowmap);
+    P.rhdr = reinterpret_cast<long long*>(ws + plan.o_rhdr);
     // bf16 value table: |v| in [2^-16, 2^8), usable for rows whose maxima lie
     // below 2^kmax, kmax <= 8 the largest with 2^kmax / T <= 700, centred by
     // C = 2^kmax/T - 600
@@ -1947,8 +2066,45 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
     return SPEC_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int dtype, int mode) {
+    if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return 0;
+    Plan p;
+    if (!make_plan(B, k, V, mode, dtype, p)) return 0;
+    return p.total;
+}
+
+int spec_verify_check_args(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                           const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V,
+                           int dtype, const int32_t* accepted_len, const int32_t* out_tokens, const float* gap,
+                           const void* workspace, size_t workspace_bytes) {
+    Plan p;
+    return check(target_logits, draft_logits, draft_tokens, uniforms, temperature, mode, B, k, V, dtype,
+                 accepted_len, out_tokens, gap, workspace, workspace_bytes, p);
+}
+
+int spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V, int dtype,
+                int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    return run(target_logits, draft_logits, draft_tokens, nullptr, false, uniforms, temperature, mode, B, k, V,
+               dtype, accepted_len, out_tokens, gap, target_prob, draft_prob, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_ragged(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const int32_t* draft_len, const float* uniforms, float temperature, int mode, int32_t B,
+                       int32_t k, int32_t V, int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                       float* target_prob, float* draft_prob, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    return run(target_logits, draft_logits, draft_tokens, draft_len, true, uniforms, temperature, mode, B, k, V,
+               dtype, accepted_len, out_tokens, gap, target_prob, draft_prob, workspace, workspace_bytes, stream);
+}
+
 const char* spec_verify_last_error(void) { return g_err; }
 
-const char* spec_verify_version(void) { return "specverify 0.3.0 (gfx950)"; }
+const char* spec_verify_version(void) { return "specverify 0.4.0 (gfx950)"; }
 
 }  // extern "C"

@@ -29,6 +29,13 @@ softmax(draft_row / T) of the *stored* (rounded) draft row, by the Gumbel-max
 construction (argmax of d/T plus Gumbel noise), which is an exact sampler for
 that categorical distribution. Uniforms are float32 in [0, 1).
 
+Ragged drafts (``draft_lengths``): per-row draft counts for any workload,
+kb = the number of successes before the first failure of independent trials
+that continue with probability 0.8, capped at k (a drafter that stops when its
+own confidence drops, with a per-step continuation rate near the acceptance
+rates the pages quote), from a generator seeded from (workload, seed,
+"draft_len"). The logits, tokens and uniforms are those of ``make``.
+
 Every batch row b is drawn from its own generator seeded from (workload, seed,
 b), so any subset of rows can be regenerated alone; the global choices (which
 draft rows are replaced, which greedy positions are replaced) come from one
@@ -224,3 +231,17 @@ def make(w: Workload | str, seed: int = 0, device="cpu", rows: Optional[range] =
         tokens[j] = tok
     return {"target": target, "draft": draft, "tokens": tokens, "uniforms": uniforms,
             "T": w.T, "mode": w.mode, "workload": w}
+
+
+RAGGED_CONTINUE = 0.8
+
+
+def draft_lengths(w: Workload | str, seed: int = 0, device="cpu", p: float = RAGGED_CONTINUE):
+    """Per-row draft lengths int32 [B] in [0, k]: successes before the first
+    failure of trials that continue with probability p, capped at k."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    g = _gen("cpu", w.name, seed, "draft_len")
+    trials = torch.rand((w.B, max(w.k, 1)), generator=g, dtype=torch.float64) < p
+    run = torch.cumprod(trials.to(torch.int64), dim=1).sum(dim=1)
+    return run.clamp(max=w.k).to(torch.int32).to(device)
