@@ -63,6 +63,9 @@ def _load():
                                                P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.spec_verify_ref_ragged.restype = ctypes.c_int
         lib.spec_verify_ref_max_threads.restype = ctypes.c_int
+        lib.spec_gate_ref.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_float, P, P, P, P]
+        lib.spec_gate_ref.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -165,3 +168,47 @@ def spec_verify_ref(target, draft, tokens, uniforms, temperature: float, mode: i
     if rc != 0:
         raise ValueError(f"spec_verify_ref rejected its arguments (rc={rc})")
     return RefResult(acc, out, gap, pt, qt, ma, mc, fl)
+
+
+MARGIN, CERTIFIED = 0, 1
+
+
+@dataclass
+class GateResult:
+    argmax: np.ndarray    # [n] int32, -1 for an invalid row
+    gap: np.ndarray       # [n] float64 (NaN for an invalid row)
+    fire: np.ndarray      # [n] bool
+
+
+def spec_gate_ref(logits, rule: int, tau: float, admit=None, dtype: Optional[int] = None) -> GateResult:
+    """Confidence gate over ready distributions logits [n, V] (float32 or bf16).
+
+    admit: optional uint32 [(V + 31) // 32] bit mask of admissible tokens.
+    """
+    if dtype is None:
+        dtype = BF16 if str(getattr(logits, "dtype", "")) in ("torch.bfloat16", "uint16") else F32
+    x = _as_logits(logits, dtype)
+    n, V = x.shape
+    am = _np(admit, np.uint32)
+    if am is not None:
+        assert am.shape == ((V + 31) // 32,), am.shape
+    arg = np.zeros(n, np.int32)
+    gap = np.zeros(n, np.float64)
+    fire = np.zeros(n, np.int32)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = _load().spec_gate_ref(ptr(x), int(n), int(V), int(dtype), int(rule), ctypes.c_float(tau),
+                               ptr(am), ptr(arg), ptr(gap), ptr(fire))
+    if rc != 0:
+        raise ValueError(f"spec_gate_ref rejected its arguments (rc={rc})")
+    return GateResult(arg, gap, fire.astype(bool))
+
+
+def admit_mask(tokens, V: int) -> np.ndarray:
+    """The V-bit admissible-set mask of a list of token ids."""
+    m = np.zeros((V + 31) // 32, np.uint32)
+    for t in tokens:
+        m[int(t) >> 5] |= np.uint32(1) << np.uint32(int(t) & 31)
+    return m

@@ -386,3 +386,56 @@ int spec_verify_ref_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Confidence gate over n ready distributions logits[n, V] ("Speculative
+ * Pre-Positioning", section 2.4, Eqs. 11-12, and the gated serve of
+ * Algorithm 2): gamma = l(1) - l(2), the two largest raw logits counted as a
+ * multiset (so a tie at the top gives 0; +inf when the row has fewer than two
+ * finite entries), a = the lowest index of the maximum, and
+ *   rule 0 (margin):    fire iff gamma > tau and a is admissible;
+ *   rule 1 (certified): fire iff gamma > 0, 2*tau <= gamma and a is admissible
+ * (the speculative-decoding design note, "Axis 1 reuses the gate we already
+ * have": with a strict argmax and every logit moved by less than tau in
+ * sup-norm, 2*tau <= gamma keeps the argmax; tau is then the residual bound Q).
+ * The comparison is made on the gap rounded to float32 (the difference of the
+ * two float logits in single precision) against the float32 tau, the
+ * precision the gap is stored in. admit is a V-bit mask, bit (j & 31) of word
+ * j >> 5 marking token j admissible; NULL admits every token. A row with NaN
+ * or +inf anywhere or with no finite entry is invalid: argmax -1, gap NaN,
+ * fire 0. Returns 0, or -1 on bad arguments (tau NaN; rule 1 with tau < 0).
+ */
+int spec_gate_ref(const void* logits, int n, int V, int dtype, int rule, float tau,
+                  const uint32_t* admit, int32_t* argmax, double* gap, int32_t* fire)
+{
+    if (n < 0 || V < 1 || (dtype != REF_F32 && dtype != REF_BF16)) return -1;
+    if (rule != 0 && rule != 1) return -1;
+    if (isnan(tau) || (rule == 1 && tau < 0.0f)) return -1;
+    for (int r = 0; r < n; ++r) {
+        const size_t off = (size_t)r * (size_t)V;
+        if (!ref_row_ok(logits, dtype, off, V)) {
+            argmax[r] = -1;
+            gap[r] = NAN;
+            fire[r] = 0;
+            continue;
+        }
+        double t1 = -INFINITY, t2 = -INFINITY;
+        int finite = 0;
+        for (int x = 0; x < V; ++x) {
+            const double v = ref_load(logits, dtype, off + (size_t)x);
+            if (isfinite(v)) ++finite;
+            if (v > t1) { t2 = t1; t1 = v; }
+            else if (v > t2) { t2 = v; }
+        }
+        const int a = ref_argmax(logits, dtype, off, V);
+        volatile float g32 = finite < 2 ? INFINITY : (float)t1 - (float)t2;
+        const int ok_a = admit == NULL || ((admit[a >> 5] >> (a & 31)) & 1u);
+        int f;
+        if (rule == 0) f = g32 > tau;
+        else f = g32 > 0.0f && 2.0f * tau <= g32;
+        argmax[r] = a;
+        gap[r] = finite < 2 ? INFINITY : t1 - t2;
+        fire[r] = f && ok_a;
+    }
+    return 0;
+}
