@@ -9,6 +9,15 @@ bfloat16 logits, sampling mode, T=1.0. Inputs rotate over several device copies
 Prints one JSON line: verified draft positions per second (B*k per step), the
 HBM roofline fraction of the kernel (algorithmic bytes / measured kernel time /
 8 TB/s), and the fp64 CPU oracle timed on a bounded sample of the same work.
+
+--ragged times spec_verify_ragged instead, with per-row draft lengths from
+workloads.draft_lengths: positions are sum(draft_len) per step, and the
+algorithmic bytes count only the rows those lengths use.
+
+--gate N times the confidence gate (spec_gate) over N ready distributions of
+workloads.make_gate (V=128256 bf16, margin rule, tau=2, 64 admissible tokens):
+rows per second, the per-call latency (N=1 is the single-distribution fast
+path), the roofline of its logit read, and the coverage c(tau) of the rows.
 """
 from __future__ import annotations
 
@@ -27,12 +36,21 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "verified draft positions/sec + % of HBM roofline, B=64 k=5 V=151936 bf16"
 
 
-def algorithmic_bytes(w) -> int:
-    """Every logit read once plus the small inputs and outputs."""
+def algorithmic_bytes(w, draft_len=None) -> int:
+    """Every logit the step must read, read once, plus the small inputs and
+    outputs. With per-row draft lengths kb: target rows 0..kb, draft rows and
+    tokens 0..kb-1 and uniforms 0..kb of each row, and the lengths."""
     B, k, V, s = w.B, w.k, w.V, w.elem_bytes
-    rows = B * (k + 1) + (B * k if w.mode == 0 else 0)
-    small = 4 * B * k + (8 * B * (k + 1) if w.mode == 0 else 0)
     outs = 4 * B + 4 * B * (k + 1) + 4 * B * (k + 1)
+    if draft_len is None:
+        rows = B * (k + 1) + (B * k if w.mode == 0 else 0)
+        small = 4 * B * k + (8 * B * (k + 1) if w.mode == 0 else 0)
+        return rows * V * s + small + outs
+    kb = [int(v) for v in draft_len]
+    n_t = sum(v + 1 for v in kb)
+    n_d = sum(kb)
+    rows = n_t + (n_d if w.mode == 0 else 0)
+    small = 4 * n_d + (8 * n_t if w.mode == 0 else 0) + 4 * B
     return rows * V * s + small + outs
 
 
@@ -62,6 +80,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--ragged", action="store_true",
+                    help="per-row draft lengths (spec_verify_ragged)")
+    ap.add_argument("--gate", type=int, default=0, metavar="N",
+                    help="time the confidence gate over N ready distributions instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
@@ -81,6 +103,8 @@ def main() -> int:
 
     if args.probe:
         return probe(args, torch, np)
+    if args.gate:
+        return gate_bench(args, torch, np)
 
     import token_verification_amd as tv
     import workloads
@@ -92,6 +116,9 @@ def main() -> int:
 
     print(f"bench: generating {name}", file=sys.stderr, flush=True)
     x = workloads.make(w, 0, device=dev)
+    dlen = workloads.draft_lengths(w, 0) if args.ragged else None
+    if dlen is not None:
+        x["draft_len"] = dlen.to(dev)
     per_copy = x["target"].numel() * w.elem_bytes + (
         x["draft"].numel() * w.elem_bytes if x["draft"] is not None else 0)
     R = max(1, math.ceil(args.rotate_bytes / per_copy))
@@ -106,7 +133,7 @@ def main() -> int:
     def step(i):
         c = copies[i % R]
         tv.spec_verify(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"], c["mode"],
-                       out=outs[i % R])
+                       out=outs[i % R], draft_len=c.get("draft_len"))
 
     for i in range(args.warmup):
         step(i)
@@ -128,13 +155,15 @@ def main() -> int:
     k_avg = float(kms.mean())
     ms_per_step = wall * 1e3 / args.steps
 
-    positions = B * k if w.mode == 0 else B * k
-    alg = algorithmic_bytes(w)
+    positions = B * k if dlen is None else int(dlen.sum())
+    alg = algorithmic_bytes(w, dlen)
+    label = name + ("_ragged" if dlen is not None else "")
     achieved = alg / (k_avg * 1e-3) / 1e9
     value = positions / (ms_per_step * 1e-3)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if dlen is None else
+        f"verified draft positions/sec + % of HBM roofline, ragged drafts, B={B} k<={k} V={w.V} {w.dtype}",
         "value": round(value, 1),
         "unit": "positions/s",
         "n_gpus": 1,
@@ -146,7 +175,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32+f64",
         "data": "synthetic",
-        "config": {"workload": name, "B": B, "k": k, "V": w.V, "logits": w.dtype,
+        "config": {"workload": label, "B": B, "k": k, "V": w.V, "logits": w.dtype,
                    "mode": "sample" if w.mode == 0 else "greedy", "T": w.T,
                    "rotated_copies": R},
         "kernel_us": {"mean": round(k_avg * 1e3, 2), "p10": round(float(np.percentile(kms, 10)) * 1e3, 2),
@@ -154,27 +183,104 @@ def main() -> int:
                       "p90": round(float(np.percentile(kms, 90)) * 1e3, 2)},
         "positions_per_s_kernel": round(positions / (k_avg * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(name),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(label),
                      "algorithmic_bytes_per_launch": alg,
                      "bytes_per_position": round(alg / positions, 1)},
     }
 
+    if dlen is not None:
+        line["config"]["draft_len"] = {"recipe": "successes before the first failure, p=0.8, capped at k",
+                                       "mean": round(positions / B, 3)}
     if args.cpu_seconds > 0:
         import oracle
         host = {key: (v.cpu() if isinstance(v, torch.Tensor) else v) for key, v in x.items()}
+        hl = None if dlen is None else dlen.numpy()
         oracle.spec_verify_ref(host["target"], host["draft"], host["tokens"], host["uniforms"],
-                               host["T"], host["mode"])          # warm (page-in)
+                               host["T"], host["mode"], draft_len=hl)          # warm (page-in)
         n, t_cpu = 0, 0.0
         while t_cpu < args.cpu_seconds:
             c0 = time.perf_counter()
             oracle.spec_verify_ref(host["target"], host["draft"], host["tokens"], host["uniforms"],
-                                   host["T"], host["mode"])
+                                   host["T"], host["mode"], draft_len=hl)
             t_cpu += time.perf_counter() - c0
             n += 1
         line["cpu_baseline"] = {"value": round(positions * n / t_cpu, 1), "unit": "positions/s",
                                 "cores": oracle.max_threads(), "kind": "oracle",
-                                "sample": f"{n} full calls of {name} (B={B}) on host copies, "
+                                "sample": f"{n} full calls of {label} (B={B}) on host copies, "
                                           f"{t_cpu:.1f} s of oracle time"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def gate_bench(args, torch, np) -> int:
+    import token_verification_amd as tv
+    import workloads
+
+    n, V = args.gate, workloads.GATE_V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x, A = workloads.make_gate(n, V, 0, "bf16", device=dev)
+    mask = workloads.admit_bits(A, V).to(dev)
+    per_copy = x.numel() * 2
+    # rotate over copies (>= 1 GiB) so every call reads its rows from HBM
+    R = max(1, min(8192, math.ceil(args.rotate_bytes / per_copy)))
+    pool = x.repeat(R, 1)
+    copies = [pool[i * n:(i + 1) * n] for i in range(R)]
+    out = tv.binding.GateResult(torch.empty(n, dtype=torch.int32, device=dev),
+                                torch.empty(n, dtype=torch.float32, device=dev),
+                                torch.empty(n, dtype=torch.int32, device=dev))
+    for i in range(args.warmup):
+        tv.spec_gate(copies[i % R], 2.0, mask, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        tv.spec_gate(copies[i % R], 2.0, mask, out=out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    k_avg = float(kms.mean())
+    alg = n * V * 2 + mask.numel() * 4 + 12 * n
+    achieved = alg / (k_avg * 1e-3) / 1e9
+    cov = {}
+    for tau in (0.5, 1.0, 2.0, 4.0, 8.0):
+        r = tv.spec_gate(x, tau, mask)
+        cov[str(tau)] = round(float(r.fire.float().mean()), 4)
+    line = {
+        "metric": f"confidence-gate rows/sec, n={n} V={V} bf16",
+        "value": round(n / (wall / args.steps), 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"gate_n{n}_v{V}_bf16", "n": n, "V": V, "rule": "margin", "tau": 2.0,
+                   "admissible": int(A.numel()), "rotated_copies": R},
+        "latency_us": {"mean": round(k_avg * 1e3, 2), "p50": round(float(np.percentile(kms, 50)) * 1e3, 2),
+                       "p90": round(float(np.percentile(kms, 90)) * 1e3, 2)},
+        "coverage": cov,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        xh = x.cpu()
+        mh = mask.cpu().numpy().view(np.uint32)
+        oracle.spec_gate_ref(xh, 0, 2.0, mh)
+        m, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds:
+            c0 = time.perf_counter()
+            oracle.spec_gate_ref(xh, 0, 2.0, mh)
+            t_cpu += time.perf_counter() - c0
+            m += 1
+        line["cpu_baseline"] = {"value": round(n * m / t_cpu, 1), "unit": "rows/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{m} calls over the same {n} rows, {t_cpu:.1f} s of oracle time"}
     print(json.dumps(line), flush=True)
     return 0
 

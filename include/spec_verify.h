@@ -89,6 +89,10 @@ extern "C" {
 #define SPEC_ERR_ALIGN (-7)     /* a pointer is not aligned to its element size (4 B or 2 B),
                                    or the workspace is not 256-B aligned                        */
 #define SPEC_ERR_HIP (-8)       /* the HIP runtime refused the launch                           */
+#define SPEC_ERR_VALUE (-9)     /* spec_gate: tau is NaN, or negative under the certified rule  */
+
+#define SPEC_GATE_MARGIN 0      /* spec_gate fires iff gap > tau                                */
+#define SPEC_GATE_CERTIFIED 1   /* spec_gate fires iff gap > 0 and 2 * tau <= gap               */
 
 /*
  * Enqueue the verify step. See the file comment for the meaning and layout of every
@@ -140,6 +144,38 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits,
                        int32_t V, int dtype, int32_t* accepted_len, int32_t* out_tokens,
                        float* gap, float* target_prob, float* draft_prob, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * Confidence gate over n ready distributions ("Speculative Pre-Positioning", section
+ * 2.4, Eqs. 11-12, and the gated fast-path serve of Algorithm 2; the certified rule
+ * is the argmax-stability bound of the speculative-decoding design note, "Axis 1
+ * reuses the gate we already have").
+ *   logits [n, V] float32 or bfloat16 (dtype), DEVICE, read only; any rows, e.g. the
+ *     cached ready distributions of n sessions, or the target rows [B*(k+1), V] of a
+ *     verify batch.
+ *   For every row r: argmax[r] = lowest index of the largest logit; gap[r] = top-1
+ *     minus top-2 (as spec_verify's gap: 0 on a tie at the top, +inf with fewer than
+ *     two finite entries); fire[r] = 1 iff argmax[r] is admissible and
+ *       SPEC_GATE_MARGIN:    gap > tau (tau: the gate threshold, 2.0 in the pages);
+ *       SPEC_GATE_CERTIFIED: gap > 0 and 2 * tau <= gap (tau: a bound Q on the
+ *                            sup-norm of the logit error, e.g. a calibrated quantile);
+ *     the comparison is made in float32 on the stored gap. A row with NaN or +inf
+ *     anywhere or with no finite entry gives argmax -1, gap NaN, fire 0.
+ *   admit: the admissible set A as a V-bit mask, uint32 [(V+31)/32], bit (j & 31) of
+ *     word j >> 5 set iff token j is admissible; DEVICE, 4-byte aligned; NULL admits
+ *     every token.
+ *   argmax int32 [n], gap float32 [n], fire int32 [n]: DEVICE outputs, fully
+ *     overwritten.
+ * Workspace: at least spec_gate_workspace_size(n, V, dtype) bytes, same rules as
+ * spec_verify's. Execution and errors as spec_verify (n < 1 or V < 1 gives
+ * SPEC_ERR_SHAPE; an unknown rule SPEC_ERR_MODE; a bad tau SPEC_ERR_VALUE).
+ */
+int spec_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, float tau,
+              const uint32_t* admit, int32_t* argmax, float* gap, int32_t* fire, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace spec_gate needs (0 if the sizes are invalid). Host-only. */
+size_t spec_gate_workspace_size(int32_t n, int32_t V, int dtype);
 
 /* Thread-local description of the last non-zero return of this library. */
 const char* spec_verify_last_error(void);

@@ -29,6 +29,10 @@ L.spec_verify_ragged.restype = ctypes.c_int
 L.spec_verify_workspace_size.argtypes = [I, I, I, ctypes.c_int, ctypes.c_int]
 L.spec_verify_workspace_size.restype = S
 L.spec_verify_last_error.restype = ctypes.c_char_p
+L.spec_gate.argtypes = [P, I, I, ctypes.c_int, ctypes.c_int, F, P, P, P, P, P, S, P]
+L.spec_gate.restype = ctypes.c_int
+L.spec_gate_workspace_size.argtypes = [I, I, ctypes.c_int]
+L.spec_gate_workspace_size.restype = S
 L.spec_verify_emu_set_cu_count.argtypes = [ctypes.c_int]
 L.spec_verify_emu_set_pool.argtypes = [ctypes.c_int]
 
@@ -216,6 +220,53 @@ def ragged():
     x = rand_case(rng, 1100, 2, 5, 0, 1.0, mode=1, coarse=True)
     x["draft_len"] = rng.integers(-1, 4, 1100).astype(np.int32)
     run_case(x, cus=4)
+
+
+def run_gate(x, rule, tau, admit=None, cus=1):
+    dtype = 1 if x.dtype == torch.bfloat16 else 0
+    n, V = x.shape
+    h = host(x, dtype)
+    am = None if admit is None else np.ascontiguousarray(np.asarray(admit).view(np.uint32))
+    arg = np.full(n, -7, np.int32)
+    gap = np.zeros(n, np.float32)
+    fire = np.full(n, -7, np.int32)
+    nb = L.spec_gate_workspace_size(n, V, dtype)
+    ws = np.frombuffer(os.urandom(nb + 256), np.uint8).copy()
+    base = ws.ctypes.data
+    off = (-base) % 256
+    L.spec_verify_emu_set_cu_count(cus)
+    L.spec_verify_emu_set_pool(1)
+    rc = L.spec_gate(ptr(h), n, V, dtype, rule, ctypes.c_float(tau), ptr(am), ptr(arg), ptr(gap), ptr(fire),
+                     ctypes.c_void_p(base + off), nb, None)
+    assert rc == 0, (rc, L.spec_verify_last_error())
+    ref = oracle.spec_gate_ref(x, rule, tau, am)
+    assert (arg == ref.argmax).all(), (np.nonzero(arg != ref.argmax)[0][:5])
+    assert (fire.astype(bool) == ref.fire).all()
+    assert (np.isnan(gap) == np.isnan(ref.gap)).all()
+    ok = ~np.isnan(ref.gap)
+    assert (gap[ok] == ref.gap[ok].astype(np.float32)).all()
+
+
+@case
+def gate():
+    # the confidence gate: seeded ready distributions, both rules, with and
+    # without an admissible set, plus ties, single finite entries and invalid rows
+    rng = np.random.default_rng(8)
+    for dtype, n, V, cus in (("bf16", 1, 50000, 2), ("f32", 40, 3001, 2), ("bf16", 300, 97, 1)):
+        x, A = workloads.make_gate(n, V, 1, dtype)
+        x = x.clone()
+        if n >= 40:
+            x[0, :] = -float("inf")
+            x[1, 5] = float("nan")
+            x[2, :] = 1.0                      # all tied
+            x[3, :] = -float("inf")
+            x[3, 7] = 2.0                      # one finite entry
+            x[4, 3] = float("inf")
+        am = workloads.admit_bits(A, V).numpy()
+        for rule, tau in ((0, 2.0), (0, -1.0), (1, 0.75), (1, 0.0)):
+            run_gate(x, rule, tau, am, cus=cus)
+            run_gate(x, rule, tau, None, cus=cus)
+    del rng
 
 
 @case

@@ -18,16 +18,16 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(spec_verify\w*)\s*\(", src))
+    return set(re.findall(r"\b(spec_(?:verify|gate)\w*)\s*\(", src))
 
 
 def test_exports_match_header():
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
-    exported = {s for s in exported if s.startswith("spec_verify")}
+    exported = {s for s in exported if s.startswith("spec_")}
     assert declared() == exported
-    assert len(exported) == 6
+    assert len(exported) == 8
 
 
 def test_version():
@@ -133,3 +133,30 @@ def test_ragged_entry_rejects_synchronously(kw, dlen, code):
                               a["acc"], a["out"], a["gap"], None, None, a["ws"], a["ws_bytes"], None)
     assert rc == code
     assert binding.last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"rule": 2}, -4),
+    ({"n": 0}, -2),
+    ({"V": 0}, -2),
+    ({"tau": float("nan")}, -9),
+    ({"tau": -1.0, "rule": 1}, -9),
+    ({"logits": None}, -1),
+    ({"fire": None}, -1),
+    ({"admit": FAKE + 2}, -7),
+    ({"dtype": 5}, -3),
+    ({"ws": None}, -6),
+])
+def test_gate_rejects_synchronously(kw, code):
+    a = dict(logits=FAKE, n=3, V=100, dtype=1, rule=0, tau=2.0, admit=None, argmax=FAKE, gap=FAKE,
+             fire=FAKE, ws=0x100000, ws_bytes=1 << 20)
+    a.update(kw)
+    rc = tv.lib().spec_gate(a["logits"], a["n"], a["V"], a["dtype"], a["rule"], ctypes.c_float(a["tau"]),
+                            a["admit"], a["argmax"], a["gap"], a["fire"], a["ws"], a["ws_bytes"], None)
+    assert rc == code
+    assert binding.last_error()
+
+
+def test_gate_workspace_size():
+    assert tv.lib().spec_gate_workspace_size(1, 128256, 1) > 0
+    assert tv.lib().spec_gate_workspace_size(0, 128256, 1) == 0

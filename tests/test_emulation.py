@@ -65,6 +65,10 @@ def test_emulated_ragged_drafts(emu_lib):
     run_cases("ragged")
 
 
+def test_emulated_gate(emu_lib):
+    run_cases("gate")
+
+
 def test_emulated_concurrent_workgroups(emu_lib):
     run_cases("concurrent_b8")
 

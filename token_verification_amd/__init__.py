@@ -7,11 +7,14 @@ cached workspace, and passes the current HIP stream. There is no fallback: if
 the library is not built, importing the binding raises.
 """
 from .binding import (  # noqa: F401
+    CERTIFIED,
     GREEDY,
+    MARGIN,
     SAMPLE,
     SpecVerifyError,
     check_args,
     lib,
+    spec_gate,
     spec_verify,
     workspace_size,
 )

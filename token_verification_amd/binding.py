@@ -19,12 +19,15 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SAMPLE = 0
 GREEDY = 1
+MARGIN = 0          # spec_gate: fire iff gap > tau
+CERTIFIED = 1       # spec_gate: fire iff gap > 0 and 2 * tau <= gap
 F32 = 0
 BF16 = 1
 
 _ERRORS = {
     -1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_DTYPE", -4: "SPEC_ERR_MODE",
     -5: "SPEC_ERR_TEMP", -6: "SPEC_ERR_WORKSPACE", -7: "SPEC_ERR_ALIGN", -8: "SPEC_ERR_HIP",
+    -9: "SPEC_ERR_VALUE",
 }
 
 
@@ -60,6 +63,10 @@ def lib():
                 L.spec_verify_check_args.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
                                                      P, P, P, P, S]
                 L.spec_verify_check_args.restype = ctypes.c_int
+                L.spec_gate.argtypes = [P, I, I, ctypes.c_int, ctypes.c_int, F, P, P, P, P, P, S, P]
+                L.spec_gate.restype = ctypes.c_int
+                L.spec_gate_workspace_size.argtypes = [I, I, ctypes.c_int]
+                L.spec_gate_workspace_size.restype = S
                 L.spec_verify_last_error.restype = ctypes.c_char_p
                 L.spec_verify_version.restype = ctypes.c_char_p
                 _lib = L
@@ -172,6 +179,53 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: tor
     else:
         rc = lib().spec_verify_ragged(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(draft_len),
                                       _ptr(uniforms), *tail)
+    if rc != 0:
+        raise SpecVerifyError(rc, last_error())
+    return out
+
+
+class GateResult(NamedTuple):
+    argmax: torch.Tensor   # [n] int32, -1 for an invalid row
+    gap: torch.Tensor      # [n] float32
+    fire: torch.Tensor     # [n] int32 (0/1)
+
+
+def spec_gate(logits: torch.Tensor, tau: float = 2.0, admit: Optional[torch.Tensor] = None,
+              rule: int = MARGIN, *, workspace: Optional[torch.Tensor] = None,
+              out: Optional[GateResult] = None) -> GateResult:
+    """Confidence gate over the rows of logits [n, V] (see include/spec_verify.h).
+
+    admit: optional int32/uint32-sized bit mask [(V + 31) // 32] of admissible
+    tokens on the same device (int32 tensors carry the bits unchanged).
+    """
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2 or not logits.is_cuda:
+        raise ValueError("logits must be a [n, V] device tensor")
+    if logits.dtype == torch.float32:
+        dtype = F32
+    elif logits.dtype == torch.bfloat16:
+        dtype = BF16
+    else:
+        raise ValueError(f"unsupported logit dtype {logits.dtype}")
+    n, V = logits.shape
+    dev = logits.device
+    if admit is not None:
+        if admit.shape != ((V + 31) // 32,) or admit.element_size() != 4 or admit.device != dev:
+            raise ValueError("admit must be a 32-bit [(V+31)//32] mask on the logits' device")
+    for t in (logits, admit):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = GateResult(torch.empty(n, dtype=torch.int32, device=dev),
+                         torch.empty(n, dtype=torch.float32, device=dev),
+                         torch.empty(n, dtype=torch.int32, device=dev))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = int(lib().spec_gate_workspace_size(n, V, dtype))
+    if need == 0:
+        raise SpecVerifyError(-2, f"unsupported sizes n={n} V={V}")
+    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    rc = lib().spec_gate(_ptr(logits), n, V, dtype, int(rule), ctypes.c_float(tau), _ptr(admit),
+                         _ptr(out.argmax), _ptr(out.gap), _ptr(out.fire),
+                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
     if rc != 0:
         raise SpecVerifyError(rc, last_error())
     return out

@@ -183,6 +183,12 @@ struct Params {
     int* rowoff;               // [B] first packed row of each batch row
     int* rowmap;               // [rows] packed row -> (b << 9) | bonus << 8 | draft << 7 | position
     long long* rhdr;           // [2] pass 1's slice length L and element count N
+    // confidence gate (greedy records of n rows): admissible-token mask (or
+    // null: all), fire output (null: not a gate call), rule and threshold
+    const unsigned* admit;
+    int* fire;
+    int gate_rule;
+    float gate_tau;
     int tab_on;                // the bf16 value table is built and usable
     double tab_lim;            // the table covers 2^-16 <= |v| < tab_lim
     double tab_c;
@@ -254,7 +260,8 @@ struct RedT {
 using Red = RedT<NWAVE>;
 
 // Block top-2 of (t1, t2): every thread returns the block's top-2.
-__device__ void block_top2(Red& R, float& t1, float& t2) {
+template <int NW>
+__device__ void block_top2(RedT<NW>& R, float& t1, float& t2) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int m = 32; m >= 1; m >>= 1) {
         const float o1 = __shfl_xor(t1, m, 64), o2 = __shfl_xor(t2, m, 64);
@@ -264,7 +271,7 @@ __device__ void block_top2(Red& R, float& t1, float& t2) {
     lds_sync();
     if (threadIdx.x == 0) {
         float a1 = R.t1[0], a2 = R.t2[0];
-        for (int q = 1; q < NWAVE; ++q) top2_merge(a1, a2, R.t1[q], R.t2[q]);
+        for (int q = 1; q < NW; ++q) top2_merge(a1, a2, R.t1[q], R.t2[q]);
         R.bt1 = a1; R.bt2 = a2;
     }
     lds_sync();
@@ -440,8 +447,8 @@ __device__ inline typename E::vec load_nt(__amdgpu_buffer_rsrc_t r, unsigned vof
 // Wave-level part of a sampling segment's reduction: top-2 (or max), the
 // (ref, s) sum rescaled to the wave's largest reference, the NaN flag; lane 0
 // leaves them in R slot `w`.
-template <int KIND>
-__device__ inline void wave_rec(Red& R, const Lane& st) {
+template <int KIND, int NW>
+__device__ inline void wave_rec(RedT<NW>& R, const Lane& st) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     float t1 = st.t1, t2 = st.t2;
     for (int m = 32; m >= 1; m >>= 1) {
@@ -475,8 +482,9 @@ __device__ inline void wave_rec(Red& R, const Lane& st) {
 // loads that logit if it lies in the segment. The unaligned head and tail
 // elements are loaded before the stream too, so no load waits at the end.
 // R is used by this segment only: consecutive segments alternate between two.
-template <class E, int KIND>
-__device__ TileRec tile_scan(const char* row, int e0, int e1, const int* tokp, float ch, float cl, Red& R) {
+template <class E, int KIND, int NTH = NT>
+__device__ TileRec tile_scan(const char* row, int e0, int e1, const int* tokp, float ch, float cl,
+                             RedT<NTH / 64>& R) {
     using vec = typename E::vec;
     constexpr int VE = E::VE;
     const int tid = threadIdx.x;
@@ -509,22 +517,22 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, const int* tokp, f
     st.t1 = -INFINITY; st.t2 = -INFINITY; st.mref = -INFINITY; st.ref = 0.0f;
     st.s = 0.0; st.bvec = -1; st.nan = 0;
 
-    // Batch i holds vectors (i*U + u)*NT + tid, u < U. Batches are ping-pong
+    // Batch i holds vectors (i*U + u)*NTH + tid, u < U. Batches are ping-pong
     // pipelined (one in flight while the other is consumed); every branch on i
     // is uniform, and only the last batch can hold vectors past nvec, which
     // load as zeros and are skipped.
     constexpr int U = 4;
-    constexpr unsigned BSTRIDE = NT * 16u;                 // bytes between u and u+1
+    constexpr unsigned BSTRIDE = NTH * 16u;                // bytes between u and u+1
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(vp, static_cast<unsigned>(nvec) * 16u);
     const unsigned voff = static_cast<unsigned>(tid) * 16u;
-    const int nb = (nvec + U * NT - 1) / (U * NT);
+    const int nb = (nvec + U * NTH - 1) / (U * NTH);
     auto consume = [&](const vec (&X)[U], int i) {
-        const bool full = (i + 1) * U * NT <= nvec;
-        const int rem = nvec - i * U * NT - tid;           // vectors of this batch left at u = 0
+        const bool full = (i + 1) * U * NTH <= nvec;
+        const int rem = nvec - i * U * NTH - tid;          // vectors of this batch left at u = 0
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int vi = (i * U + u) * NT + tid;
-            if (full || u * NT < rem) {
+            const int vi = (i * U + u) * NTH + tid;
+            if (full || u * NTH < rem) {
                 float x[VE];
                 E::unpack(X[u], x);
                 consume_vec<KIND, VE>(st, x, vi, ch, cl);
@@ -586,7 +594,7 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, const int* tokp, f
             float a1 = R.t1[0], a2 = R.t2[0], r = R.ref[0];
             double sum = R.s[0];
             int nan = R.j[0];
-            for (int q = 1; q < NWAVE; ++q) {
+            for (int q = 1; q < NTH / 64; ++q) {
                 top2_merge(a1, a2, R.t1[q], R.t2[q]);
                 sref_merge(r, sum, R.ref[q], R.s[q]);
                 nan |= R.j[q];
@@ -1096,6 +1104,61 @@ __global__ __launch_bounds__(NT) void decide_kernel(Params P) {
     } else {
         decide_batch<E, MODE>(P, D, blockIdx.x, true);
     }
+}
+
+// The confidence gate over n rows (batch rows with k = 0, after a greedy pass
+// 1), one thread per row: gap and argmax from the merged records, then
+// fire = the rule holds on the float32 gap and the argmax is admissible.
+template <class E>
+__global__ __launch_bounds__(NT) void gate_kernel(Params P) {
+    const int r = static_cast<int>(blockIdx.x) * NT + static_cast<int>(threadIdx.x);
+    if (r >= P.B) return;
+    const long long r0 = static_cast<long long>(r) * P.V;
+    const RowRec rr = merge_row<SPEC_MODE_GREEDY>(P.tiles + r, r0 / P.L, (r0 + P.V - 1) / P.L, false);
+    int a = -1, fire = 0;
+    float g = __builtin_nanf("");
+    if (rr.valid) {
+        a = rr.idx;
+        g = rr.t2 == -INFINITY ? INFINITY : rr.m - rr.t2;
+        const bool adm = !P.admit || ((P.admit[a >> 5] >> (a & 31)) & 1u);
+        const bool pass = P.gate_rule == SPEC_GATE_MARGIN ? g > P.gate_tau
+                                                          : (g > 0.0f && 2.0f * P.gate_tau <= g);
+        fire = adm && pass;
+    }
+    P.out_tok[r] = a;
+    P.gap[r] = g;
+    P.fire[r] = fire;
+}
+
+// The confidence gate with one workgroup per row (NTG threads streaming the
+// whole row): no pass-1 records and no second launch. One CU streams a row at
+// a few tens of GB/s, so this pays once there are enough rows to occupy the
+// chip (GATE_ROW_MIN); fewer rows are split over many workgroups by a greedy
+// pass 1 and merged by gate_kernel.
+constexpr int NTG = 1024;
+constexpr int GATE_ROW_MIN = 128;
+
+template <class E>
+__global__ __launch_bounds__(NTG) void gate_row_kernel(Params P) {
+    __shared__ RedT<NTG / 64> R;
+    const int r = blockIdx.x;
+    const char* rowp = static_cast<const char*>(P.tgt) + static_cast<size_t>(r) * P.V * E::ES;
+    const TileRec t = tile_scan<E, K_GREEDY, NTG>(rowp, 0, P.V, nullptr, 0.0f, 0.0f, R);
+    if (threadIdx.x != 0) return;
+    const bool valid = !(t.flags & 1) && t.t1 > -INFINITY && t.t1 < INFINITY;
+    int a = -1, fire = 0;
+    float g = __builtin_nanf("");
+    if (valid) {
+        a = t.idx;
+        g = t.t2 == -INFINITY ? INFINITY : t.t1 - t.t2;
+        const bool adm = !P.admit || ((P.admit[a >> 5] >> (a & 31)) & 1u);
+        const bool pass = P.gate_rule == SPEC_GATE_MARGIN ? g > P.gate_tau
+                                                          : (g > 0.0f && 2.0f * P.gate_tau <= g);
+        fire = adm && pass;
+    }
+    P.out_tok[r] = a;
+    P.gap[r] = g;
+    P.fire[r] = fire;
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -1936,6 +1999,10 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     P.L = (P.N + G - 1) / G;
     P.G = static_cast<int>((P.N + P.L - 1) / P.L);
     hipError_t e;
+    if (MODE == SPEC_MODE_GREEDY && P.fire && P.B >= GATE_ROW_MIN) {   // gate: one workgroup per row
+        hipLaunchKernelGGL((gate_row_kernel<E>), dim3(P.B), dim3(NTG), 0, s, P);
+        return hipGetLastError();
+    }
     if (P.dlen) {
         // ragged drafts: the packed rows and pass 1's slices over them (at
         // most P.N elements, so the same G workgroups suffice)
@@ -1947,7 +2014,10 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (MODE == SPEC_MODE_GREEDY) {
-        hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
+        if (P.fire)
+            hipLaunchKernelGGL((gate_kernel<E>), dim3((P.B + NT - 1) / NT), dim3(NT), 0, s, P);
+        else
+            hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
         return hipGetLastError();
     }
     // pass 2: one resident round of workgroups, split evenly over the batch rows
@@ -1969,21 +2039,28 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     return hipGetLastError();
 }
 
-int run(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens, const int32_t* draft_len,
-        bool ragged, const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V, int dtype,
-        int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
-        void* workspace, size_t workspace_bytes, void* stream) {
-    Plan plan;
-    const int rc = check(target_logits, draft_logits, draft_tokens, uniforms, temperature, mode, B, k, V,
-                         dtype, accepted_len, out_tokens, gap, workspace, workspace_bytes, plan, ragged, draft_len);
-    if (rc != SPEC_OK) return rc;
+struct GateOut {
+    const uint32_t* admit;
+    int32_t* fire;
+    int rule;
+    float tau;
+};
 
+// Fill the launch parameters of checked arguments and enqueue the kernels.
+int enqueue(const Plan& plan, const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+            const int32_t* draft_len, const float* uniforms, float temperature, int mode, int32_t B, int32_t k,
+            int32_t V, int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
+            float* draft_prob, const GateOut* gate, void* workspace, void* stream) {
     char* ws = static_cast<char*>(workspace);
     Params P;
     P.tgt = target_logits;
     P.dft = draft_logits;
     P.tok = draft_tokens;
-    P.dlen = ragged ? draft_len : nullptr;
+    P.dlen = draft_len;
+    P.admit = gate ? reinterpret_cast<const unsigned*>(gate->admit) : nullptr;
+    P.fire = gate ? gate->fire : nullptr;
+    P.gate_rule = gate ? gate->rule : 0;
+    P.gate_tau = gate ? gate->tau : 0.0f;
     P.uni = uniforms;
     P.acc_len = accepted_len;
     P.out_tok = out_tokens;
@@ -2066,6 +2143,45 @@ int run(const void* target_logits, const void* draft_logits, const int32_t* draf
     return SPEC_OK;
 }
 
+int run(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens, const int32_t* draft_len,
+        bool ragged, const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V, int dtype,
+        int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
+        void* workspace, size_t workspace_bytes, void* stream) {
+    Plan plan;
+    const int rc = check(target_logits, draft_logits, draft_tokens, uniforms, temperature, mode, B, k, V,
+                         dtype, accepted_len, out_tokens, gap, workspace, workspace_bytes, plan, ragged, draft_len);
+    if (rc != SPEC_OK) return rc;
+    return enqueue(plan, target_logits, draft_logits, draft_tokens, ragged ? draft_len : nullptr, uniforms,
+                   temperature, mode, B, k, V, dtype, accepted_len, out_tokens, gap, target_prob, draft_prob,
+                   nullptr, workspace, stream);
+}
+
+int check_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, float tau, const uint32_t* admit,
+               const int32_t* argmax, const float* gap, const int32_t* fire, const void* ws, size_t ws_bytes,
+               Plan& plan) {
+    if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16)
+        return fail(SPEC_ERR_DTYPE, "dtype %d is not SPEC_DTYPE_F32 or SPEC_DTYPE_BF16", dtype);
+    if (rule != SPEC_GATE_MARGIN && rule != SPEC_GATE_CERTIFIED)
+        return fail(SPEC_ERR_MODE, "rule %d is not SPEC_GATE_MARGIN or SPEC_GATE_CERTIFIED", rule);
+    if (n < 1 || V < 1) return fail(SPEC_ERR_SHAPE, "need n >= 1 and V >= 1 (got n=%d V=%d)", n, V);
+    if (!make_plan(n, 0, V, SPEC_MODE_GREEDY, dtype, plan))
+        return fail(SPEC_ERR_SHAPE, "sizes n=%d V=%d exceed the supported range", n, V);
+    if (tau != tau || (rule == SPEC_GATE_CERTIFIED && tau < 0.0f))
+        return fail(SPEC_ERR_VALUE, "tau must not be NaN, and must be >= 0 for the certified rule (got %g)",
+                    (double)tau);
+    if (!logits) return fail(SPEC_ERR_NULL, "logits is NULL");
+    if (!argmax || !gap || !fire) return fail(SPEC_ERR_NULL, "an output pointer is NULL");
+    const size_t es = dtype == SPEC_DTYPE_F32 ? 4 : 2;
+    if (!aligned(logits, es) || (admit && !aligned(admit, 4)) || !aligned(argmax, 4) || !aligned(gap, 4) ||
+        !aligned(fire, 4))
+        return fail(SPEC_ERR_ALIGN, "a pointer is not aligned to its element size");
+    if (!ws || ws_bytes < plan.total)
+        return fail(SPEC_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", plan.total, ws_bytes,
+                    ws ? "" : ", NULL");
+    if (!aligned(ws, 256)) return fail(SPEC_ERR_ALIGN, "workspace must be 256-byte aligned");
+    return SPEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2101,6 +2217,21 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, cons
                        void* stream) {
     return run(target_logits, draft_logits, draft_tokens, draft_len, true, uniforms, temperature, mode, B, k, V,
                dtype, accepted_len, out_tokens, gap, target_prob, draft_prob, workspace, workspace_bytes, stream);
+}
+
+size_t spec_gate_workspace_size(int32_t n, int32_t V, int dtype) {
+    return spec_verify_workspace_size(n, 0, V, dtype, SPEC_MODE_GREEDY);
+}
+
+int spec_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, float tau, const uint32_t* admit,
+              int32_t* argmax, float* gap, int32_t* fire, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan plan;
+    const int rc = check_gate(logits, n, V, dtype, rule, tau, admit, argmax, gap, fire, workspace,
+                              workspace_bytes, plan);
+    if (rc != SPEC_OK) return rc;
+    const GateOut g{admit, fire, rule, tau};
+    return enqueue(plan, logits, nullptr, nullptr, nullptr, nullptr, 1.0f, SPEC_MODE_GREEDY, n, 0, V, dtype,
+                   nullptr, argmax, gap, nullptr, nullptr, &g, workspace, stream);
 }
 
 const char* spec_verify_last_error(void) { return g_err; }

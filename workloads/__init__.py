@@ -36,6 +36,14 @@ own confidence drops, with a per-step continuation rate near the acceptance
 rates the pages quote), from a generator seeded from (workload, seed,
 "draft_len"). The logits, tokens and uniforms are those of ``make``.
 
+Confidence-gate rows (``make_gate``): n ready distributions of V logits, iid
+N(0, 2^2), then one token t per row set to the row maximum plus U(0, 20) (the
+70B-class model in the pre-positioning paper shows decision-point gaps from
+below 2 to about 20), with t drawn from the admissible set A with probability
+0.9 and uniformly otherwise; A is 64 distinct token ids drawn once per
+(n, V, seed). Rounded to bfloat16 for bf16 rows. ``admit_bits`` packs a token
+list into the V-bit mask the gate reads (bit j & 31 of word j >> 5).
+
 Every batch row b is drawn from its own generator seeded from (workload, seed,
 b), so any subset of rows can be regenerated alone; the global choices (which
 draft rows are replaced, which greedy positions are replaced) come from one
@@ -245,3 +253,30 @@ def draft_lengths(w: Workload | str, seed: int = 0, device="cpu", p: float = RAG
     trials = torch.rand((w.B, max(w.k, 1)), generator=g, dtype=torch.float64) < p
     run = torch.cumprod(trials.to(torch.int64), dim=1).sum(dim=1)
     return run.clamp(max=w.k).to(torch.int32).to(device)
+
+
+GATE_V = 128256            # a 70B-class model's vocabulary
+GATE_A = 64                # admissible single-token answers
+
+
+def make_gate(n: int, V: int = GATE_V, seed: int = 0, dtype: str = "bf16", device="cpu"):
+    """Ready distributions logits [n, V] and the admissible token ids (int64 [GATE_A])."""
+    g = _gen("cpu", "gate", n, V, seed)
+    A = torch.randperm(V, generator=g)[:min(GATE_A, V)]
+    x = torch.randn((n, V), generator=g, dtype=torch.float32) * 2.0
+    inA = torch.rand(n, generator=g) < 0.9
+    pick_a = A[torch.randint(0, A.numel(), (n,), generator=g)]
+    pick_u = torch.randint(0, V, (n,), generator=g)
+    t = torch.where(inA, pick_a, pick_u)
+    s = torch.rand(n, generator=g) * 20.0
+    x[torch.arange(n), t] = x.max(dim=1).values + s
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    return x.to(td).to(device), A
+
+
+def admit_bits(tokens, V: int) -> torch.Tensor:
+    """int32 [(V + 31) // 32] mask with bit (j & 31) of word j >> 5 set for each token j."""
+    words = [0] * ((V + 31) // 32)
+    for j in (int(t) for t in tokens):
+        words[j >> 5] |= 1 << (j & 31)
+    return torch.tensor([w - (1 << 32) if w >= (1 << 31) else w for w in words], dtype=torch.int32)
