@@ -18,6 +18,8 @@ Inference Wall" part 7, "Why it inverts, mechanism 2"):
   slot a. The emitted (resampled or bonus) token is the next pending token:
   its KV and state come with the next forward.
 * An invalid row (a = -1) commits nothing: kv_len and the state are unchanged.
+  Nor does a row whose accepted_len lies outside [0, k] (no such slot exists;
+  a verify step never produces one).
 
 Parity: pinned in tests/test_oracle_commit.py against a model whose state is a
 closed form of the committed tokens.
@@ -27,15 +29,18 @@ from __future__ import annotations
 import numpy as np
 
 
-def commit_ref(accepted_len, kv_len, slots=None, state=None):
+def commit_ref(accepted_len, kv_len, slots=None, state=None, k=None):
     """Return (new kv_len, new state) for accepted_len [B], kv_len [B] and,
-    optionally, slots [B, k+1, ...] and state [B, ...] (any dtype: a copy)."""
+    optionally, slots [B, k+1, ...] and state [B, ...] (any dtype: a copy).
+    k defaults to slots.shape[1] - 1 (required without slots)."""
     a = np.asarray(accepted_len, np.int64)
+    if k is None:
+        k = slots.shape[1] - 1
     kv = np.asarray(kv_len, np.int64).copy()
     B = a.shape[0]
     new_state = None if state is None else np.array(state, copy=True)
     for b in range(B):
-        if a[b] < 0:
+        if a[b] < 0 or a[b] > k:
             continue
         kv[b] = kv[b] + 1 + a[b]
         if new_state is not None:

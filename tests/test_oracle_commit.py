@@ -55,5 +55,13 @@ def test_commit_is_the_state_of_the_committed_prefix():
 def test_inputs_are_not_modified_and_state_is_optional():
     acc = np.array([2, -1], np.int32)
     kv = np.array([5, 7], np.int32)
-    new_kv, st = commit_ref(acc, kv)
+    new_kv, st = commit_ref(acc, kv, k=3)
     assert list(new_kv) == [8, 7] and st is None and list(kv) == [5, 7]
+
+
+def test_lengths_outside_the_slots_commit_nothing():
+    slots = np.arange(2 * 3 * 2).reshape(2, 3, 2)
+    state = np.full((2, 2), -1)
+    new_kv, st = commit_ref(np.array([3, 2]), np.array([0, 0]), slots, state)
+    assert list(new_kv) == [0, 3]
+    assert (st[0] == -1).all() and (st[1] == slots[1, 2]).all()
