@@ -18,6 +18,10 @@ algorithmic bytes count only the rows those lengths use.
 workloads.make_gate (V=128256 bf16, margin rule, tau=2, 64 admissible tokens):
 rows per second, the per-call latency (N=1 is the single-distribution fast
 path), the roofline of its logit read, and the coverage c(tau) of the rows.
+
+--commit times the commit / rollback step (spec_commit) after the headline
+verify call: B=64 rows, k=5, 4 MiB of recurrent state per row and k+1
+checkpoint slots, accepted lengths from the verify call itself.
 """
 from __future__ import annotations
 
@@ -84,6 +88,8 @@ def main() -> int:
                     help="per-row draft lengths (spec_verify_ragged)")
     ap.add_argument("--gate", type=int, default=0, metavar="N",
                     help="time the confidence gate over N ready distributions instead")
+    ap.add_argument("--commit", action="store_true",
+                    help="time the commit / rollback step after the headline verify instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
@@ -105,6 +111,8 @@ def main() -> int:
         return probe(args, torch, np)
     if args.gate:
         return gate_bench(args, torch, np)
+    if args.commit:
+        return commit_bench(args, torch, np)
 
     import token_verification_amd as tv
     import workloads
@@ -281,6 +289,70 @@ def gate_bench(args, torch, np) -> int:
         line["cpu_baseline"] = {"value": round(n * m / t_cpu, 1), "unit": "rows/s", "cores": 1,
                                 "kind": "oracle",
                                 "sample": f"{m} calls over the same {n} rows, {t_cpu:.1f} s of oracle time"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def commit_bench(args, torch, np) -> int:
+    import token_verification_amd as tv
+    import workloads
+
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = workloads.make(w, 0, device=dev)
+    acc = tv.spec_verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"], 0).accepted_len
+    del x
+    row = 4 << 20
+    B, k = w.B, w.k
+    g = torch.Generator(device=dev).manual_seed(5)
+    slots = torch.randint(-2 ** 31, 2 ** 31 - 1, (B, k + 1, row // 4), generator=g, dtype=torch.int32, device=dev)
+    state = torch.zeros((B, row // 4), dtype=torch.int32, device=dev)
+    kv = torch.zeros(B, dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        tv.spec_commit(acc, k, kv, slots, state)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        tv.spec_commit(acc, k, kv, slots, state)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    k_avg = float(kms.mean())
+    nvalid = int((acc >= 0).sum())
+    alg = 2 * nvalid * row + 4 * B + 8 * nvalid
+    achieved = alg / (k_avg * 1e-3) / 1e9
+    line = {
+        "metric": f"committed rows/sec (KV truncation + {row >> 20} MiB state-slot copy), B={B} k={k}",
+        "value": round(B / (wall / args.steps), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bytes", "data": "synthetic",
+        "config": {"workload": f"commit_b{B}_k{k}_state{row >> 20}mib", "B": B, "k": k,
+                   "state_bytes": row, "accepted_from": workloads.HEADLINE},
+        "kernel_us": {"mean": round(k_avg * 1e3, 2), "p50": round(float(np.percentile(kms, 50)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if args.cpu_seconds > 0:
+        from oracle.commit import commit_ref
+        a_h, kv_h = acc.cpu().numpy(), kv.cpu().numpy()
+        sl_h, st_h = slots.cpu().numpy(), state.cpu().numpy()
+        m, t_cpu = 0, 0.0
+        while t_cpu < min(args.cpu_seconds, 5.0):
+            c0 = time.perf_counter()
+            commit_ref(a_h, kv_h, sl_h, st_h, k=k)
+            t_cpu += time.perf_counter() - c0
+            m += 1
+        line["cpu_baseline"] = {"value": round(B * m / t_cpu, 1), "unit": "rows/s", "cores": 1,
+                                "kind": "oracle", "sample": f"{m} commits of the same {B} rows"}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -177,6 +177,32 @@ int spec_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, flo
 /* Bytes of workspace spec_gate needs (0 if the sizes are invalid). Host-only. */
 size_t spec_gate_workspace_size(int32_t n, int32_t V, int dtype);
 
+/*
+ * Commit / rollback after a verify step (KV truncation on rejection: "Speculative
+ * Decoding: The Physics of Stolen Time", section 6, "KV-cache management", and the
+ * speculative-decoding design note's KV rollback; per-position recurrent-state
+ * checkpoints of hybrid models: "The Inference Wall" part 7, "Why it inverts,
+ * mechanism 2").
+ * The verify forward of batch row b consumed k+1 tokens (the pending token, then the
+ * k drafts), appended their KV entries at kv_len[b]..kv_len[b]+k, and wrote
+ * checkpoint slot j = the recurrent state after the pending token and drafts 0..j-1.
+ * With a = accepted_len[b] in [0, k]:
+ *   kv_len[b] += 1 + a                (the entries of rejected drafts are dropped),
+ *   state[b, :] = slots[b, a, :]      (the state of the committed prefix).
+ * Rows with a outside [0, k] (e.g. -1, an invalid verify row) are left unchanged.
+ *   accepted_len [B] int32: DEVICE, read only (spec_verify's output).
+ *   kv_len [B] int32: DEVICE, updated in place; NULL skips the KV lengths.
+ *   slots [B, k+1, state_bytes] and state [B, state_bytes]: DEVICE raw bytes (any
+ *     element type), state_bytes a multiple of 4, pointers 4-byte aligned (16-byte
+ *     alignment and a 16-byte multiple use 16-byte copies); state_bytes = 0 skips
+ *     the state (slots and state may then be NULL). slots and state must not overlap.
+ * Needs no workspace. Enqueues one kernel on `stream` (nothing when kv_len is NULL
+ * and state_bytes is 0). Errors: SPEC_ERR_SHAPE (B < 1, B > 2^21, k outside
+ * [0, SPEC_MAX_K], sizes too large), SPEC_ERR_NULL, SPEC_ERR_ALIGN, SPEC_ERR_HIP.
+ */
+int spec_commit(const int32_t* accepted_len, int32_t B, int32_t k, int32_t* kv_len,
+                const void* slots, void* state, size_t state_bytes, void* stream);
+
 /* Thread-local description of the last non-zero return of this library. */
 const char* spec_verify_last_error(void);
 

@@ -33,6 +33,8 @@ L.spec_gate.argtypes = [P, I, I, ctypes.c_int, ctypes.c_int, F, P, P, P, P, P, S
 L.spec_gate.restype = ctypes.c_int
 L.spec_gate_workspace_size.argtypes = [I, I, ctypes.c_int]
 L.spec_gate_workspace_size.restype = S
+L.spec_commit.argtypes = [P, I, I, P, P, P, S, P]
+L.spec_commit.restype = ctypes.c_int
 L.spec_verify_emu_set_cu_count.argtypes = [ctypes.c_int]
 L.spec_verify_emu_set_pool.argtypes = [ctypes.c_int]
 
@@ -267,6 +269,31 @@ def gate():
             run_gate(x, rule, tau, am, cus=cus)
             run_gate(x, rule, tau, None, cus=cus)
     del rng
+
+
+@case
+def commit():
+    # commit / rollback: 16-byte and 4-byte copies, several chunks per row,
+    # invalid and out-of-range accepted lengths, no KV lengths, no state
+    from oracle.commit import commit_ref
+    rng = np.random.default_rng(9)
+    L.spec_verify_emu_set_cu_count(2)
+    L.spec_verify_emu_set_pool(1)
+    for B, k, words in ((5, 3, 3 * 8192 + 100), (7, 0, 333), (4, 5, 0), (3, 2, 4096)):
+        acc = rng.integers(-1, k + 2, B).astype(np.int32)
+        acc[0] = k
+        kv = rng.integers(0, 1000, B).astype(np.int32)
+        slots = rng.integers(0, 2 ** 31, (B, k + 1, words)).astype(np.int32)
+        state = rng.integers(0, 2 ** 31, (B, words)).astype(np.int32)
+        ref_kv, ref_state = commit_ref(acc, kv, slots, state, k=k)
+        kv2, st2 = kv.copy(), state.copy()
+        rc = L.spec_commit(ptr(acc), B, k, ptr(kv2), ptr(slots) if words else None,
+                           ptr(st2) if words else None, 4 * words, None)
+        assert rc == 0, L.spec_verify_last_error()
+        assert (kv2 == ref_kv).all() and (st2 == ref_state).all()
+        kv3 = kv.copy()
+        assert L.spec_commit(ptr(acc), B, k, ptr(kv3), None, None, 0, None) == 0
+        assert (kv3 == ref_kv).all()
 
 
 @case

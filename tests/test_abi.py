@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(spec_(?:verify|gate)\w*)\s*\(", src))
+    return set(re.findall(r"\b(spec_(?:verify|gate|commit)\w*)\s*\(", src))
 
 
 def test_exports_match_header():
@@ -27,7 +27,7 @@ def test_exports_match_header():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     exported = {s for s in exported if s.startswith("spec_")}
     assert declared() == exported
-    assert len(exported) == 8
+    assert len(exported) == 9
 
 
 def test_version():
@@ -160,3 +160,19 @@ def test_gate_rejects_synchronously(kw, code):
 def test_gate_workspace_size():
     assert tv.lib().spec_gate_workspace_size(1, 128256, 1) > 0
     assert tv.lib().spec_gate_workspace_size(0, 128256, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"B": 0}, -2),
+    ({"k": 65}, -2),
+    ({"acc": None}, -1),
+    ({"slots": None}, -1),
+    ({"row": 6}, -7),
+    ({"state": FAKE + 2}, -7),
+])
+def test_commit_rejects_synchronously(kw, code):
+    a = dict(acc=FAKE, B=4, k=3, kv=FAKE, slots=FAKE, state=0x200000, row=64)
+    a.update(kw)
+    rc = tv.lib().spec_commit(a["acc"], a["B"], a["k"], a["kv"], a["slots"], a["state"], a["row"], None)
+    assert rc == code
+    assert binding.last_error()

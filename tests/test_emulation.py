@@ -69,6 +69,10 @@ def test_emulated_gate(emu_lib):
     run_cases("gate")
 
 
+def test_emulated_commit(emu_lib):
+    run_cases("commit")
+
+
 def test_emulated_concurrent_workgroups(emu_lib):
     run_cases("concurrent_b8")
 

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     SpecVerifyError,
     check_args,
     lib,
+    spec_commit,
     spec_gate,
     spec_verify,
     workspace_size,

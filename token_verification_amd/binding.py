@@ -67,6 +67,8 @@ def lib():
                 L.spec_gate.restype = ctypes.c_int
                 L.spec_gate_workspace_size.argtypes = [I, I, ctypes.c_int]
                 L.spec_gate_workspace_size.restype = S
+                L.spec_commit.argtypes = [P, I, I, P, P, P, S, P]
+                L.spec_commit.restype = ctypes.c_int
                 L.spec_verify_last_error.restype = ctypes.c_char_p
                 L.spec_verify_version.restype = ctypes.c_char_p
                 _lib = L
@@ -229,3 +231,37 @@ def spec_gate(logits: torch.Tensor, tau: float = 2.0, admit: Optional[torch.Tens
     if rc != 0:
         raise SpecVerifyError(rc, last_error())
     return out
+
+
+def spec_commit(accepted_len: torch.Tensor, k: int, kv_len: Optional[torch.Tensor] = None,
+                slots: Optional[torch.Tensor] = None, state: Optional[torch.Tensor] = None) -> None:
+    """Commit a verify step in place (see include/spec_verify.h): kv_len[b] += 1 + a
+    and state[b] = slots[b, a] for every row with a = accepted_len[b] in [0, k].
+
+    accepted_len int32 [B]; kv_len int32 [B] or None; slots [B, k+1, ...] and
+    state [B, ...] of one dtype (any), or both None.
+    """
+    if accepted_len.dim() != 1 or accepted_len.dtype != torch.int32 or not accepted_len.is_cuda:
+        raise ValueError("accepted_len must be an int32 [B] device tensor")
+    B = accepted_len.shape[0]
+    dev = accepted_len.device
+    if kv_len is not None:
+        if kv_len.shape != (B,) or kv_len.dtype != torch.int32 or kv_len.device != dev:
+            raise ValueError("kv_len must be int32 [B] on accepted_len's device")
+    if (slots is None) != (state is None):
+        raise ValueError("slots and state go together")
+    row = 0
+    if state is not None:
+        if state.shape[0] != B or slots.shape[:2] != (B, k + 1) or slots.shape[2:] != state.shape[1:]:
+            raise ValueError("slots must be [B, k+1, *S] and state [B, *S]")
+        if slots.dtype != state.dtype or slots.device != dev or state.device != dev:
+            raise ValueError("slots and state must share a dtype and accepted_len's device")
+        row = state[0].numel() * state.element_size() if B else 0
+    for t in (accepted_len, kv_len, slots, state):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().spec_commit(_ptr(accepted_len), B, int(k), _ptr(kv_len), _ptr(slots), _ptr(state), row,
+                           ctypes.c_void_p(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, last_error())

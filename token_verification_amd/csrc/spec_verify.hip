@@ -1869,6 +1869,63 @@ __global__ __launch_bounds__(NT2) void draw_kernel(Params P) {
     }
 }
 
+// ------------------------------------------------------------------ commit / rollback
+
+// After a verify step: every batch row with a = accepted_len in [0, k] keeps
+// the KV entries of the pending token and its a accepted drafts (kv_len +=
+// 1 + a) and takes recurrent-state checkpoint slot a as its live state; other
+// rows are left alone. The state copy is a plain stream: each workgroup moves
+// one chunk of one row with 16-byte vectors (4-byte words when the buffers or
+// the row size are not 16-byte multiples), every thread holding CPV loads in
+// flight.
+constexpr int NTC = 256;
+constexpr int CPV = 8;
+constexpr size_t COMMIT_CHUNK = static_cast<size_t>(NTC) * CPV * 16;   // bytes per workgroup
+
+struct CommitParams {
+    const int* acc;
+    int* kv_len;               // may be null
+    const char* slots;         // [B, k+1, row] bytes, may be null (with state)
+    char* state;               // [B, row] bytes
+    size_t row;                // state bytes per batch row
+    int B, k;
+    int chunks;                // workgroups per batch row
+    int vec16;                 // 16-byte vectors usable
+};
+
+__global__ __launch_bounds__(NTC) void commit_kernel(CommitParams C) {
+    const int b = static_cast<int>(blockIdx.x) / C.chunks, c = static_cast<int>(blockIdx.x) % C.chunks;
+    const int a = C.acc[b];
+    if (a < 0 || a > C.k) return;                          // uniform: nothing to commit
+    if (c == 0 && threadIdx.x == 0 && C.kv_len) C.kv_len[b] += 1 + a;
+    if (!C.state) return;
+    const char* src = C.slots + (static_cast<size_t>(b) * (C.k + 1) + a) * C.row;
+    char* dst = C.state + static_cast<size_t>(b) * C.row;
+    const size_t lo = static_cast<size_t>(c) * COMMIT_CHUNK;
+    const size_t hi = lo + COMMIT_CHUNK < C.row ? lo + COMMIT_CHUNK : C.row;
+    if (C.vec16) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src + lo);
+        u32x4* d4 = reinterpret_cast<u32x4*>(dst + lo);
+        const int n = static_cast<int>((hi - lo) / 16);
+        u32x4 v[CPV];
+#pragma unroll
+        for (int u = 0; u < CPV; ++u) {
+            const int i = u * NTC + static_cast<int>(threadIdx.x);
+            if (i < n) v[u] = s4[i];
+        }
+#pragma unroll
+        for (int u = 0; u < CPV; ++u) {
+            const int i = u * NTC + static_cast<int>(threadIdx.x);
+            if (i < n) __builtin_nontemporal_store(v[u], d4 + i);
+        }
+    } else {
+        const unsigned* s1 = reinterpret_cast<const unsigned*>(src + lo);
+        unsigned* d1 = reinterpret_cast<unsigned*>(dst + lo);
+        const int n = static_cast<int>((hi - lo) / 4);
+        for (int i = static_cast<int>(threadIdx.x); i < n; i += NTC) d1[i] = s1[i];
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 thread_local char g_err[512] = "";
@@ -2232,6 +2289,40 @@ int spec_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, flo
     const GateOut g{admit, fire, rule, tau};
     return enqueue(plan, logits, nullptr, nullptr, nullptr, nullptr, 1.0f, SPEC_MODE_GREEDY, n, 0, V, dtype,
                    nullptr, argmax, gap, nullptr, nullptr, &g, workspace, stream);
+}
+
+int spec_commit(const int32_t* accepted_len, int32_t B, int32_t k, int32_t* kv_len, const void* slots,
+                void* state, size_t state_bytes, void* stream) {
+    if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K)
+        return fail(SPEC_ERR_SHAPE, "need 1 <= B <= 2^21 and 0 <= k <= %d (got B=%d k=%d)", SPEC_MAX_K, B, k);
+    if (!accepted_len) return fail(SPEC_ERR_NULL, "accepted_len is NULL");
+    const bool has_state = state_bytes > 0;
+    if (has_state && (!slots || !state))
+        return fail(SPEC_ERR_NULL, "slots and state are required when state_bytes > 0");
+    if (state_bytes % 4 != 0 || !aligned(accepted_len, 4) || (kv_len && !aligned(kv_len, 4)) ||
+        (has_state && (!aligned(slots, 4) || !aligned(state, 4))))
+        return fail(SPEC_ERR_ALIGN, "pointers must be 4-byte aligned and state_bytes a multiple of 4");
+    if (has_state && state_bytes > (static_cast<size_t>(1) << 40))
+        return fail(SPEC_ERR_SHAPE, "state_bytes %zu is too large", state_bytes);
+    CommitParams C;
+    C.acc = accepted_len;
+    C.kv_len = kv_len;
+    C.slots = static_cast<const char*>(has_state ? slots : nullptr);
+    C.state = static_cast<char*>(has_state ? state : nullptr);
+    C.row = state_bytes;
+    C.B = B;
+    C.k = k;
+    const size_t chunks = has_state ? (state_bytes + COMMIT_CHUNK - 1) / COMMIT_CHUNK : 1;
+    if (static_cast<double>(chunks) * B >= 2147483647.0)
+        return fail(SPEC_ERR_SHAPE, "B * state_bytes is too large");
+    C.chunks = static_cast<int>(chunks);
+    C.vec16 = has_state && state_bytes % 16 == 0 && aligned(slots, 16) && aligned(state, 16);
+    if (!kv_len && !has_state) return SPEC_OK;             // nothing to do
+    hipLaunchKernelGGL(commit_kernel, dim3(static_cast<unsigned>(chunks * B)), dim3(NTC), 0,
+                       static_cast<hipStream_t>(stream), C);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SPEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return SPEC_OK;
 }
 
 const char* spec_verify_last_error(void) { return g_err; }
