@@ -179,7 +179,8 @@ struct Params {
     double* exptab;            // [EXP_N] 2^(j/EXP_N), written by pass 1 for pass 2
     double* tautab;            // [TAB_MAX] exp(v/T - tab_c) of bf16 values v, written by pass 1
     // ragged drafts: only the rows a batch row uses enter pass 1's flattened
-    // space, in batch-row order; written by rows_kernel before pass 1
+    // space, in batch-row order; written by rows_kernel before pass 1 (many
+    // batch rows) or by pass 1's first workgroup (rowoff, rhdr)
     int* rowoff;               // [B] first packed row of each batch row
     int* rowmap;               // [rows] packed row -> (b << 9) | bonus << 8 | draft << 7 | position
     long long* rhdr;           // [2] pass 1's slice length L and element count N
@@ -665,9 +666,15 @@ __device__ inline double exp2_lean(double d) {
 }
 
 
+// Ragged drafts with at most RAG_INLINE batch rows: pass 1 packs the rows
+// itself (four batch rows per thread, a workgroup scan into LDS) instead of
+// waiting for rows_kernel.
+constexpr int RAG_INLINE = 4 * NT;
+
 template <class E, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void scan_kernel(Params P) {
     __shared__ Red R2[2];
+    __shared__ int RO[RAG_INLINE + 1];                     // ragged: first packed row of each batch row
     const int tid = threadIdx.x;
     const int k = P.k, V = P.V;
     // Workgroup w owns the flattened elements [w*L, (w+1)*L) of all B*rpb rows,
@@ -696,8 +703,57 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void sc
             }
         }
     }
-    // ragged drafts: the slice length and element count of the packed rows
-    const long long L = P.dlen ? P.rhdr[0] : P.L, N = P.dlen ? P.rhdr[1] : P.N;
+    // ragged drafts: the packed rows, their slice length and element count
+    long long L = P.L, N = P.N;
+    const bool inl = P.dlen && P.B <= RAG_INLINE;          // uniform
+    if (inl) {
+        int n[4], loc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int b = tid * 4 + q;
+            int c = 0;
+            if (b < P.B) {
+                const int kb = P.dlen[b];
+                if (kb >= 0 && kb <= k) c = MODE == SPEC_MODE_SAMPLE ? 2 * kb + 1 : kb + 1;
+            }
+            n[q] = c;
+            loc += c;
+        }
+        const int lane = tid & 63, wv = tid >> 6;
+        int x = loc;                                       // inclusive scan over the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) R2[0].i[wv] = x;
+        lds_sync();
+        int pre = x - loc, tot = 0;
+#pragma unroll
+        for (int q = 0; q < NWAVE; ++q) {
+            const int t = R2[0].i[q];
+            pre += q < wv ? t : 0;
+            tot += t;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int b = tid * 4 + q;
+            if (b < P.B) {
+                RO[b] = pre;
+                if (w == 0) P.rowoff[b] = pre;
+            }
+            pre += n[q];
+        }
+        if (tid == 0) RO[P.B] = tot;
+        N = static_cast<long long>(tot) * V;
+        L = (N + gridDim.x - 1) / gridDim.x;
+        if (L < 1) L = 1;
+        if (w == 0 && tid == 0) { P.rhdr[0] = L; P.rhdr[1] = N; }
+        lds_sync();                                        // RO complete; R2[0] free again
+    } else if (P.dlen) {
+        L = P.rhdr[0];
+        N = P.rhdr[1];
+    }
     const long long g0 = w * L;
     const long long g1 = g0 + L < N ? g0 + L : N;
     int seg = 0;
@@ -711,7 +767,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void sc
         // bonus row (the target row after the last draft position)
         int b, pos;
         bool draft, bonus;
-        if (P.dlen) {
+        if (inl) {
+            // the batch row holding packed row `row`: the largest b with RO[b] <= row
+            int lo = 0, hi = P.B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (RO[mid] <= row) lo = mid;
+                else hi = mid - 1;
+            }
+            b = lo;
+            const int j = static_cast<int>(row) - RO[b], nb = RO[b + 1] - RO[b];
+            const int kb = MODE == SPEC_MODE_SAMPLE ? (nb - 1) >> 1 : nb - 1;
+            draft = j > kb; pos = draft ? j - kb - 1 : j; bonus = j == kb;
+        } else if (P.dlen) {
             const int code = P.rowmap[row];
             b = code >> 9; bonus = (code >> 8) & 1; draft = (code >> 7) & 1; pos = code & 127;
         } else {
@@ -2060,9 +2128,10 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
         hipLaunchKernelGGL((gate_row_kernel<E>), dim3(P.B), dim3(NTG), 0, s, P);
         return hipGetLastError();
     }
-    if (P.dlen) {
-        // ragged drafts: the packed rows and pass 1's slices over them (at
-        // most P.N elements, so the same G workgroups suffice)
+    if (P.dlen && P.B > RAG_INLINE) {
+        // ragged drafts with many batch rows: the packed rows and pass 1's
+        // slices over them (at most P.N elements, so the same G workgroups
+        // suffice); fewer batch rows are packed by pass 1 itself
         hipLaunchKernelGGL(rows_kernel, dim3(1), dim3(NTR), 0, s, P);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
