@@ -483,7 +483,7 @@ __device__ inline void wave_rec(RedT<NW>& R, const Lane& st) {
 // loads that logit if it lies in the segment. The unaligned head and tail
 // elements are loaded before the stream too, so no load waits at the end.
 // R is used by this segment only: consecutive segments alternate between two.
-template <class E, int KIND, int NTH = NT>
+template <class E, int KIND, int NTH = NT, int U = 4>
 __device__ TileRec tile_scan(const char* row, int e0, int e1, const int* tokp, float ch, float cl,
                              RedT<NTH / 64>& R) {
     using vec = typename E::vec;
@@ -522,7 +522,6 @@ __device__ TileRec tile_scan(const char* row, int e0, int e1, const int* tokp, f
     // pipelined (one in flight while the other is consumed); every branch on i
     // is uniform, and only the last batch can hold vectors past nvec, which
     // load as zeros and are skipped.
-    constexpr int U = 4;
     constexpr unsigned BSTRIDE = NTH * 16u;                // bytes between u and u+1
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(vp, static_cast<unsigned>(nvec) * 16u);
     const unsigned voff = static_cast<unsigned>(tid) * 16u;
@@ -1200,18 +1199,21 @@ __global__ __launch_bounds__(NT) void gate_kernel(Params P) {
 
 // The confidence gate with one workgroup per row (NTG threads streaming the
 // whole row): no pass-1 records and no second launch. One CU streams a row at
-// a few tens of GB/s, so this pays once there are enough rows to occupy the
-// chip (GATE_ROW_MIN); fewer rows are split over many workgroups by a greedy
-// pass 1 and merged by gate_kernel.
+// only ~28 GB/s whatever the load depth (measured: 4, 8 or 16 vectors in
+// flight per thread give 9.9, 9.8 and 9.2 us for one row of 128256 bf16), so
+// below GATE_ROW_MIN rows a greedy pass 1 splits the rows over many
+// workgroups and gate_kernel merges them (8.1 us for one row); from 16 rows on
+// the per-row kernel is as fast or faster (46 us for 1024 rows, against 53).
 constexpr int NTG = 1024;
-constexpr int GATE_ROW_MIN = 128;
+constexpr int GATE_U = 4;                  // vectors per thread in each load batch
+constexpr int GATE_ROW_MIN = 16;
 
 template <class E>
 __global__ __launch_bounds__(NTG) void gate_row_kernel(Params P) {
     __shared__ RedT<NTG / 64> R;
     const int r = blockIdx.x;
     const char* rowp = static_cast<const char*>(P.tgt) + static_cast<size_t>(r) * P.V * E::ES;
-    const TileRec t = tile_scan<E, K_GREEDY, NTG>(rowp, 0, P.V, nullptr, 0.0f, 0.0f, R);
+    const TileRec t = tile_scan<E, K_GREEDY, NTG, GATE_U>(rowp, 0, P.V, nullptr, 0.0f, 0.0f, R);
     if (threadIdx.x != 0) return;
     const bool valid = !(t.flags & 1) && t.t1 > -INFINITY && t.t1 < INFINITY;
     int a = -1, fire = 0;
