@@ -59,11 +59,11 @@ def algorithmic_bytes(w, draft_len=None) -> int:
 
 
 def counter_traffic(name: str):
-    """HBM bytes per call from the committed rocprofv3 counter summary of this
-    workload (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None
-    when there is none or the kernel source changed since it was taken."""
+    """HBM bytes per call from the committed rocprofv3 counter summary
+    profiles/<name>.md (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
+    copy), or None when there is none or the kernel source changed since."""
     import hashlib
-    summary = os.path.join(ROOT, "profiles", f"spec_verify_{name}.md")
+    summary = os.path.join(ROOT, "profiles", f"{name}.md")
     src = os.path.join(ROOT, "token_verification_amd", "csrc", "spec_verify.hip")
     if not os.path.exists(summary):
         return None
@@ -191,7 +191,7 @@ def main() -> int:
                       "p90": round(float(np.percentile(kms, 90)) * 1e3, 2)},
         "positions_per_s_kernel": round(positions / (k_avg * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(label),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic("spec_verify_" + label),
                      "algorithmic_bytes_per_launch": alg,
                      "bytes_per_position": round(alg / positions, 1)},
     }
@@ -272,7 +272,8 @@ def gate_bench(args, torch, np) -> int:
                        "p90": round(float(np.percentile(kms, 90)) * 1e3, 2)},
         "coverage": cov,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": counter_traffic(f"spec_gate_n{n}_v{V}_bf16"),
                      "algorithmic_bytes_per_launch": alg},
     }
     if args.cpu_seconds > 0:
@@ -338,7 +339,8 @@ def commit_bench(args, torch, np) -> int:
                    "state_bytes": row, "accepted_from": workloads.HEADLINE},
         "kernel_us": {"mean": round(k_avg * 1e3, 2), "p50": round(float(np.percentile(kms, 50)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": counter_traffic(f"spec_commit_b{B}_k{k}_state{row >> 20}mib"),
                      "algorithmic_bytes_per_launch": alg},
     }
     if args.cpu_seconds > 0:
