@@ -231,3 +231,38 @@ def test_noncontiguous_rejected_and_errors():
     with pytest.raises(tv.SpecVerifyError) as e:
         tv.spec_verify(x["target"], None, x["tokens"], x["uniforms"], 1.0, 0)
     assert e.value.code == -1
+
+
+def _band_case(rng, B, k, V, clusters):
+    """Draft rows equal to the target except a few low-mass entries: the exact
+    lambda is within 1e-5 of 1, so elements with x_t == x_d (and, with
+    clusters, tiny-magnitude elements one or two bf16 ulps apart) fall inside
+    pass 2's band around it."""
+    t = torch.from_numpy(rng.normal(0, 2.0, (B, k + 1, V)).astype(np.float32)).to(torch.bfloat16)
+    d = t[:, :k].clone()
+    for b in range(B):
+        for i in range(k):
+            low = torch.argsort(t[b, i].float())[:5]
+            d[b, i, low] = (t[b, i, low].float() - 4.0).to(torch.bfloat16)
+            if clusters:
+                # tiny magnitudes: x_t - x_d of +-1 and +-2 ulps at 2^-10
+                idx = torch.from_numpy(rng.choice(V, 64, replace=False))
+                base = torch.full((64,), 2.0 ** -10)
+                t[b, i, idx] = base.to(torch.bfloat16)
+                steps = torch.tensor([0, 1, -1, 2, -2] * 13)[:64].float() * 2.0 ** -17
+                d[b, i, idx] = (base + steps).to(torch.bfloat16)
+    tok = torch.from_numpy(rng.integers(0, V, (B, k)).astype(np.int32))
+    uni = torch.from_numpy(rng.random((B, k + 1, 2)).astype(np.float32))
+    uni[:, :, 0] = 0.999                     # reject at the first position: a residual draw
+    return {"target": t, "draft": d, "tokens": tok, "uniforms": uni, "T": 1.0, "mode": 0}
+
+
+@pytest.mark.parametrize("clusters", [False, True])
+def test_band_groups(clusters):
+    # one band group per segment (x_t == x_d), or more distinct keys than the
+    # groups a segment records (the draw then recomputes those segments)
+    rng = np.random.default_rng(71 + clusters)
+    for V in (20000, 151936):
+        x = _band_case(rng, 6, 2, V, clusters)
+        st = run_pair(to_dev(x), "bf16", False)
+        say("band groups", clusters, V, st)

@@ -55,7 +55,7 @@ namespace {
 
 constexpr int NT = 256;                 // threads per workgroup (4 wave64)
 constexpr int NWAVE = NT / 64;
-constexpr int MAX_AMB = 4;              // band elements recorded per chunk (the draw sorts 4)
+constexpr int MAX_AMB = 4;              // groups of band elements recorded per pass-2 segment
 constexpr int NT2 = 512;                // threads per draw workgroup (8 wave64)
 constexpr int NTS = 1024;               // threads per pass-2 segment workgroup (16 wave64)
 constexpr int W_CAP = 256;              // most pass-2 workgroups per batch row
@@ -144,10 +144,9 @@ struct alignas(32) BatchRec {  // what pass 2 and the draw need of one batch row
 
 struct alignas(64) SegRec {    // one pass-2 segment (one wave's share of a row pair)
     double sp, sq, e, f;       // sum e, sum f, sums over the certain-positive set
-    double ae[MAX_AMB], af[MAX_AMB];  // e and f of the recorded band elements
-    int namb;                  // band elements seen (> MAX_AMB: overflow)
-    int amb[MAX_AMB];          // their indices
-    int pad[3];
+    double ae[MAX_AMB], af[MAX_AMB];  // sums of e and f over each group of band elements
+    int namb;                  // groups (> MAX_AMB: overflow, the draw recomputes the segment)
+    int pad[7];
 };
 
 struct Params {
@@ -1314,27 +1313,6 @@ __device__ inline Pass2 pass2_rows(const Params& P, int b, const BatchRec& br) {
     return Q;
 }
 
-// Value of one element: bits of a bf16 logit, or an fp32 logit.
-__device__ inline double val_bf16(unsigned bits, double off, const Pass2& Q, const double* TT, const double* TE) {
-    if (Q.tab) {
-        const unsigned key = (bits & 0x7fffu) - TAB_BASE;
-        if (key < TAB_RANGE) return TT[key + (bits >> 15) * TAB_NEG];
-    }
-    return exp_fast(fma(static_cast<double>(__uint_as_float(bits << 16)), Q.invT, off), TE);
-}
-
-__device__ inline double val_f32(float x, double off, const Pass2& Q, const double* TE) {
-    return exp_fast(fma(static_cast<double>(x), Q.invT, off), TE);
-}
-
-template <class E>
-__device__ inline double val_at(const void* row, int j, double off, const Pass2& Q, const double* TT, const double* TE) {
-    if constexpr (E::ES == 2)
-        return val_bf16(reinterpret_cast<const unsigned short*>(row)[j], off, Q, TT, TE);
-    else
-        return val_f32(reinterpret_cast<const float*>(row)[j], off, Q, TE);
-}
-
 // Bits of element q of a 16-byte bf16 vector.
 __device__ inline unsigned bf16_bits(const u32x4& w, int q) {
     const unsigned word = (q >> 1) == 0 ? w.x : (q >> 1) == 1 ? w.y : (q >> 1) == 2 ? w.z : w.w;
@@ -1408,15 +1386,6 @@ __device__ inline void vals_vec(const typename E::vec& w, double off, const Pass
     }
 }
 
-// Residual weight e - lambda f (clamped at 0), or e for the bonus draw, of element j.
-template <class E>
-__device__ inline double weight_at(const Pass2& Q, int j, const double* TT, const double* TE) {
-    const double e = val_at<E>(Q.rowT, j, Q.offT, Q, TT, TE);
-    if (!Q.resid) return e;
-    const double w = e - Q.lam * val_at<E>(Q.rowD, j, Q.offD, Q, TT, TE);
-    return w > 0.0 ? w : 0.0;
-}
-
 // Elements q >= n of a vector set to -inf (weight 0): the row's last vector
 // when V is not a multiple of VE.
 template <class E>
@@ -1469,11 +1438,16 @@ __device__ inline typename E::vec load_vec(__amdgpu_buffer_rsrc_t rs, const void
     }
 }
 
-// Band elements seen by one wave (pass 2): index and both values.
-struct WaveAmb {
-    int n;
-    int idx[MAX_AMB];
-    double e[MAX_AMB], f[MAX_AMB];
+// Band elements of one lane's share of a segment (pass 2), grouped by their
+// exact logit difference x_t - x_d: every element of a group has the same
+// ratio e/f, so the group lies on one side of the exact lambda and its
+// residual is max(0, sum e - lambda sum f). A lane keeps one group (its first
+// band key); a second key marks the lane as conflicting, and the segment is
+// then recomputed by the draw. At the end of the segment the lanes' groups
+// are merged by key, in the order of the lowest lane holding each key.
+struct LaneBand {
+    double key, se, sf;
+    int state;                 // 0: no band element, 1: one key, 2: several keys
 };
 
 template <class E>
@@ -1481,7 +1455,6 @@ struct SegLds {
     alignas(16) double TT[E::ES == 2 ? TAB_MAX : 2];
     alignas(16) double TE[EXP_N];
     Dec D;
-    WaveAmb A[NTS / 64];
 };
 
 // pass 2's tables held in registers between their loads and the LDS stores,
@@ -1531,9 +1504,25 @@ __device__ inline void tables_store(const Params& P, const TableRegs<E>& R, doub
 // Sums of one wave's segment: S_p, S_q and, over the elements that are
 // certainly positive for every lambda in the band around lam_hat, E and F;
 // band elements go to the wave's list.
+// Logit difference x_t - x_d of element q (exact in double).
+template <class E>
+__device__ inline double band_key(const typename E::vec& xt, const typename E::vec& xd, int q) {
+    if constexpr (E::ES == 2) {
+        return static_cast<double>(__uint_as_float(bf16_bits(xt, q) << 16)) -
+               static_cast<double>(__uint_as_float(bf16_bits(xd, q) << 16));
+    } else {
+        const float a = q == 0 ? xt.x : q == 1 ? xt.y : q == 2 ? xt.z : xt.w;
+        const float d = q == 0 ? xd.x : q == 1 ? xd.y : q == 2 ? xd.z : xd.w;
+        return static_cast<double>(a) - static_cast<double>(d);
+    }
+}
+
+// Sums of one vector pair: S_p, S_q and, over the elements that are
+// certainly positive for every lambda in the band around lam_hat, E and F;
+// band elements go to the lane's group.
 template <class E, bool RESID>
-__device__ inline void seg_vector(const typename E::vec& xt, const typename E::vec& xd, int j0, const Pass2& Q,
-                                  double hi_b, double lo_b, const double* TT, const double* TE, WaveAmb& A,
+__device__ inline void seg_vector(const typename E::vec& xt, const typename E::vec& xd, const Pass2& Q,
+                                  double hi_b, double lo_b, const double* TT, const double* TE, LaneBand& L,
                                   double (&acc)[4]) {
     constexpr int VE = E::VE;
     double e[VE], f[VE];
@@ -1549,8 +1538,10 @@ __device__ inline void seg_vector(const typename E::vec& xt, const typename E::v
             acc[2] = fma(e[q], pd, acc[2]);
             acc[3] = fma(f[q], pd, acc[3]);
             if (!pos && e[q] > lo_b * f[q]) {              // rare: inside the band
-                const int slot = atomicAdd(&A.n, 1);
-                if (slot < MAX_AMB) { A.idx[slot] = j0 + q; A.e[slot] = e[q]; A.f[slot] = f[q]; }
+                const double k = band_key<E>(xt, xd, q);
+                if (L.state == 0) { L.key = k; L.state = 1; }
+                if (k == L.key) { L.se += e[q]; L.sf += f[q]; }
+                else L.state = 2;
             }
         }
     }
@@ -1566,7 +1557,7 @@ struct SegU {
 template <class E, bool VEC, bool RESID>
 __device__ inline void seg_group(const Params& P, const Pass2& Q, __amdgpu_buffer_rsrc_t rsT,
                                  __amdgpu_buffer_rsrc_t rsD, int v0, int v1, int t0, int T, double hi_b,
-                                 double lo_b, const double* TT, const double* TE, WaveAmb& A, double (&acc)[4],
+                                 double lo_b, const double* TT, const double* TE, LaneBand& L, double (&acc)[4],
                                  const typename E::vec (&xt)[SegU<VEC>::U], const typename E::vec (&xd)[SegU<VEC>::U]) {
     const int lane = threadIdx.x & 63;
     const int tailn = P.V - (P.nvec - 1) * E::VE;          // elements of the row's last vector
@@ -1579,7 +1570,7 @@ __device__ inline void seg_group(const Params& P, const Pass2& Q, __amdgpu_buffe
                 mask_tail<E>(a, tailn);
                 if constexpr (RESID) mask_tail<E>(d, tailn);
             }
-            seg_vector<E, RESID>(a, d, vi * E::VE, Q, hi_b, lo_b, TT, TE, A, acc);
+            seg_vector<E, RESID>(a, d, Q, hi_b, lo_b, TT, TE, L, acc);
         }
     }
 }
@@ -1601,35 +1592,58 @@ __device__ inline void seg_issue(const Pass2& Q, __amdgpu_buffer_rsrc_t rsT, __a
 // One wave's segment of a batch row, then its record.
 template <class E, bool VEC, bool RESID>
 __device__ inline void seg_run(const Params& P, const Pass2& Q, int b, int s, int v0, int v1, SegLds<E>& S) {
-    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const __amdgpu_buffer_rsrc_t rsT = make_rsrc(Q.rowT, Q.bytes);
     const __amdgpu_buffer_rsrc_t rsD = make_rsrc(Q.rowD, RESID ? Q.bytes : 0u);
     const int T = (v1 - v0 + 63) >> 6;
     const double hi_b = Q.lam_hat * (1.0 + ETA), lo_b = Q.lam_hat * (1.0 - ETA);
-    WaveAmb& A = S.A[wv];
+    LaneBand L;
+    L.key = 0.0; L.se = 0.0; L.sf = 0.0; L.state = 0;
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     for (int t0 = 0; t0 < T; t0 += SegU<VEC>::U) {
         typename E::vec xt[SegU<VEC>::U], xd[SegU<VEC>::U];
         seg_issue<E, VEC, RESID>(Q, rsT, rsD, P.V, v0, v1, t0, T, xt, xd);
-        seg_group<E, VEC, RESID>(P, Q, rsT, rsD, v0, v1, t0, T, hi_b, lo_b, S.TT, S.TE, A, acc, xt, xd);
+        seg_group<E, VEC, RESID>(P, Q, rsT, rsD, v0, v1, t0, T, hi_b, lo_b, S.TT, S.TE, L, acc, xt, xd);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = wave_sum(acc[q]);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    // merge the lanes' band groups by key (uniform; rare)
+    int n = 0;
+    double se[MAX_AMB] = {0.0, 0.0, 0.0, 0.0}, sf[MAX_AMB] = {0.0, 0.0, 0.0, 0.0};
+    if (__any(L.state != 0)) {
+        if (__any(L.state == 2)) {
+            n = MAX_AMB + 1;                               // a lane met two keys: recompute
+        } else {
+            bool pend = L.state == 1;
+            while (__any(pend)) {                          // one round per distinct key
+                const int l = __ffsll(static_cast<long long>(__ballot(pend))) - 1;
+                const double k = __shfl(L.key, l, 64);
+                const bool m = pend && L.key == k;
+                const double a = wave_sum(m ? L.se : 0.0), c = wave_sum(m ? L.sf : 0.0);
+                if (n < MAX_AMB) {
+#pragma unroll
+                    for (int g = 0; g < MAX_AMB; ++g) { se[g] = g == n ? a : se[g]; sf[g] = g == n ? c : sf[g]; }
+                    ++n;
+                } else {
+                    n = MAX_AMB + 1;
+                    break;
+                }
+                pend = pend && !m && lane != l;            // lane l always leaves
+            }
+        }
+    }
     if (lane == 0) {
         SegRec r;
         r.sp = acc[0]; r.sq = acc[1]; r.e = acc[2]; r.f = acc[3];
-        const int n = A.n;
-        r.namb = n < MAX_AMB + 1 ? n : MAX_AMB + 1;
+        r.namb = n;
 #pragma unroll
-        for (int q = 0; q < MAX_AMB; ++q) {
-            const bool h = q < n;
-            r.amb[q] = h ? A.idx[q] : 0;
-            r.ae[q] = h ? A.e[q] : 0.0;
-            r.af[q] = h ? A.f[q] : 0.0;
+        for (int g = 0; g < MAX_AMB; ++g) {
+            const bool h = g < n;
+            r.ae[g] = h ? se[g] : 0.0;
+            r.af[g] = h ? sf[g] : 0.0;
         }
-        r.pad[0] = r.pad[1] = r.pad[2] = 0;
+#pragma unroll
+        for (int q = 0; q < 7; ++q) r.pad[q] = 0;
         P.segs[static_cast<size_t>(b) * P.nseg + s] = r;
     }
 }
@@ -1662,15 +1676,13 @@ __global__ __launch_bounds__(NTS) __attribute__((amdgpu_waves_per_eu(4))) void s
             tables_fetch<E>(P, TR, 64);
             tables_store<E>(P, TR, S.TT, S.TE, 64);
         }
-        if ((tid & 63) == 0) S.A[wv].n = 0;
-        lds_sync();                                        // decision, tables and band lists ready
+        lds_sync();                                        // decision and tables ready
         br = S.D.br;
     } else {
         tables_fetch<E>(P, TR, 64);                        // in flight during the decision
         br = decide_batch<E, SPEC_MODE_SAMPLE>(P, S.D, b, w == 0);
         tables_store<E>(P, TR, S.TT, S.TE, 64);
-        if ((tid & 63) == 0) S.A[wv].n = 0;
-        lds_sync();                                        // tables and band lists ready
+        lds_sync();                                        // tables ready
     }
     Pass2 Q = pass2_rows<E>(P, b, br);
     if (Q.tab) Q.lam_hat = br.lam * exp_fast(Q.dm, S.TE);  // into table units
@@ -1700,39 +1712,62 @@ __device__ inline void seg_range(const Params& P, int s, int& v0, int& v1) {
     v1 = min(P.nvec, v0 + P.vps);
 }
 
-// Mass of segment s recomputed element by element (whole block, ordered).
+// Mass of segment s recomputed element by element with the values of the
+// rescan (whole block: 16-byte vectors, thread-sequential sums, then a fixed
+// block reduction).
 template <class E>
 __device__ double seg_exact(const Params& P, const Pass2& Q, int s, DrawLds& S) {
+    constexpr int VE = E::VE;
     int v0, v1;
     seg_range(P, s, v0, v1);
-    const int lo = v0 * E::VE, hi = min(P.V, v1 * E::VE);
+    const __amdgpu_buffer_rsrc_t rsT = make_rsrc(Q.rowT, Q.bytes);
+    const __amdgpu_buffer_rsrc_t rsD = make_rsrc(Q.rowD, Q.resid ? Q.bytes : 0u);
+    const int tailn = P.V - (P.nvec - 1) * VE;
     double acc[1] = {0.0};
-    for (int j = lo + static_cast<int>(threadIdx.x); j < hi; j += NT2) acc[0] += weight_at<E>(Q, j, nullptr, S.TE);
+#pragma unroll 1
+    for (int vb = v0; vb < v1; vb += NT2) {
+        const int vi = vb + static_cast<int>(threadIdx.x);
+        const bool in = vi < v1;
+        typename E::vec xt, xd;
+        if (P.vec_ok) {
+            xt = load_vec<E, true>(rsT, Q.rowT, Q.bytes, vi, P.V, in);
+            xd = load_vec<E, true>(rsD, Q.rowD, Q.bytes, vi, P.V, in && Q.resid);
+        } else {
+            xt = load_vec<E, false>(rsT, Q.rowT, Q.bytes, vi, P.V, in);
+            xd = load_vec<E, false>(rsD, Q.rowD, Q.bytes, vi, P.V, in && Q.resid);
+        }
+        if (vi == P.nvec - 1 && tailn < VE) { mask_tail<E>(xt, tailn); mask_tail<E>(xd, tailn); }
+        // one element at a time (few registers: this is the rare path)
+#pragma unroll 1
+        for (int q = 0; q < VE; ++q) {
+            double e, f = 0.0;
+            if constexpr (E::ES == 2) {
+                e = val_exp_bf16(xt, q, Q.offT, Q, S.TE);
+                if (Q.resid) f = val_exp_bf16(xd, q, Q.offD, Q, S.TE);
+            } else {
+                const float xs[4] = {xt.x, xt.y, xt.z, xt.w}, ds[4] = {xd.x, xd.y, xd.z, xd.w};
+                e = exp_fast(fma(static_cast<double>(xs[q]), Q.invT, Q.offT), S.TE);
+                if (Q.resid) f = exp_fast(fma(static_cast<double>(ds[q]), Q.invT, Q.offD), S.TE);
+            }
+            const double x = Q.resid ? e - Q.lam * f : e;
+            if (x > 0.0 && in) acc[0] += x;
+        }
+    }
     block_sum<1>(S.R, acc);
     return acc[0];
 }
 
-// Mass of one segment from its record (NaN: must be recomputed exactly).
+// Mass of one segment from its record (NaN: must be recomputed exactly):
+// the certain-positive sums, then each band group in the order it was met.
 __device__ inline double seg_mass(const SegRec& r, const Pass2& Q, bool band_ok) {
     if (!Q.resid) return r.sp;
     if (!band_ok || r.namb > MAX_AMB) return __builtin_nan("");
     double m = r.e - Q.lam * r.f;
     if (!(m > 0.0)) m = 0.0;
-    // band elements in index order (fixed summation order): a sorting network
-    // on four (index, slot) keys, unused slots last
-    const int n = r.namb;
-    int k0 = n > 0 ? r.amb[0] * 4 + 0 : 0x7fffffff, k1 = n > 1 ? r.amb[1] * 4 + 1 : 0x7fffffff;
-    int k2 = n > 2 ? r.amb[2] * 4 + 2 : 0x7fffffff, k3 = n > 3 ? r.amb[3] * 4 + 3 : 0x7fffffff;
-    auto cswap = [](int& x, int& y) { const int lo = min(x, y), hi = max(x, y); x = lo; y = hi; };
-    cswap(k0, k1); cswap(k2, k3); cswap(k0, k2); cswap(k1, k3); cswap(k1, k2);
-    const int ks[4] = {k0, k1, k2, k3};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (q < n) {
-            const int sl = ks[q] & 3;
-            const double ae = sl == 0 ? r.ae[0] : sl == 1 ? r.ae[1] : sl == 2 ? r.ae[2] : r.ae[3];
-            const double af = sl == 0 ? r.af[0] : sl == 1 ? r.af[1] : sl == 2 ? r.af[2] : r.af[3];
-            const double w = ae - Q.lam * af;
+    for (int g = 0; g < MAX_AMB; ++g) {
+        if (g < r.namb) {
+            const double w = r.ae[g] - Q.lam * r.af[g];
             m += w > 0.0 ? w : 0.0;
         }
     }
