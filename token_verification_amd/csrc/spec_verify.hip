@@ -2156,7 +2156,12 @@ int seg_blocks_per_cu(int dev) {
 template <class E, int MODE>
 hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     long long G = static_cast<long long>(ncu) * scan_blocks_per_cu<E, MODE>(dev);
-    const long long by_size = (P.N + MIN_SLICE - 1) / MIN_SLICE;
+    // slices of at least MIN_SLICE elements, but at least one workgroup per
+    // row while the rows fit the round: a workgroup walks its row segments
+    // one after another, so small calls are bound by segments per workgroup
+    long long by_size = (P.N + MIN_SLICE - 1) / MIN_SLICE;
+    const long long rows = P.N / P.V;
+    if (by_size < rows) by_size = rows;
     if (G > by_size) G = by_size;
     if (G > G_MAX) G = G_MAX;
     if (G < 1) G = 1;
