@@ -45,7 +45,7 @@
  * entries, probability 0).
  *
  * Workspace: caller-owned device memory of at least spec_verify_workspace_size() bytes
- * (256-byte aligned). It carries the per-segment, per-batch-row and per-chunk records
+ * (256-byte aligned). It carries the per-segment and per-batch-row records
  * that one kernel of the call hands to the next; every record is written before it is
  * read, so the workspace needs no initialisation and may be reused freely. One
  * workspace serves one call at a time: calls that overlap in time (e.g. on two

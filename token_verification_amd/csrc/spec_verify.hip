@@ -5,9 +5,11 @@
 // greedy argmax matching of "The Inference Wall" part 7; the top-1 minus top-2
 // logit gap of "Speculative Pre-Positioning", Eq. 11).
 //
-// Three stream-ordered kernels per call in sampling mode (two in greedy mode);
-// no workgroup ever waits on another (every hand-over between them is a kernel
-// boundary).
+// Three stream-ordered kernels per call in sampling mode (two in greedy mode;
+// ragged drafts over more than 1024 batch rows add rows_kernel first); no
+// workgroup ever waits on another (every hand-over between them is a kernel
+// boundary). The same file holds the confidence gate (gate_kernel,
+// gate_row_kernel) and the commit step (commit_kernel).
 //
 //  1. scan_kernel -- one resident round of workgroups, each streaming an equal
 //     slice of the flattened (row, element) space (a slice may span row
@@ -19,7 +21,7 @@
 //     ref = ceil(max*c), so rescaling when the running max grows is an exact
 //     power-of-two ldexp. The lane whose vector holds the row's draft token
 //     keeps that logit. Greedy mode also finds the first index of the max.
-//  2. The decision of a batch row (decide_batch): merges the segments of its
+//  2. The decision of a batch row (decide_wave / decide_batch): merges the segments of its
 //     rows, writes the gaps, evaluates every acceptance test
 //     r_i = p_i(x_i)/q_i(x_i) in the log2 domain in fp64, finds the first
 //     rejection a and writes every output except the token the sampling draw
@@ -33,7 +35,8 @@
 //     with lambda = S_p/S_q, so a single read gives S_p, S_q and, over the
 //     elements whose sign is certain under pass 1's estimate of lambda
 //     (relative band ETA), the sums E, F; elements inside the band are
-//     recorded with their values and settled once lambda is exact.
+//     grouped by their exact logit difference (one ratio e/f per group) and
+//     settled once lambda is exact.
 //  4. draw_kernel (sampling) -- one workgroup per batch row: exact lambda,
 //     segment masses, ordered scan to the segment holding u*Z, fp64 rescan of
 //     that segment in vocabulary order.
@@ -1649,7 +1652,7 @@ __device__ inline void seg_run(const Params& P, const Pass2& Q, int b, int s, in
 }
 
 // Pass 2, sampling mode. Batch row b has W = P.wpb workgroups of NTS/64 waves
-// and its selected row pair (or bonus row) is split into 8W equal segments of
+// and its selected row pair (or bonus row) is split into 16W equal segments of
 // whole 16-byte vectors, one per wave. Each workgroup decides b itself (the W
 // copies agree; workgroup 0 writes the outputs and the batch record), issues
 // its waves' loads, and then every wave streams its segment with lane-
