@@ -58,10 +58,11 @@ def algorithmic_bytes(w, draft_len=None) -> int:
     return rows * V * s + small + outs
 
 
-def counter_traffic(name: str):
-    """HBM bytes per call from the committed rocprofv3 counter summary
-    profiles/<name>.md (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
-    copy), or None when there is none or the kernel source changed since."""
+def counter_traffic(name: str, key: str = "traffic_bytes_per_call"):
+    """HBM bytes per call (or, with key="traffic_bytes_pass1", of pass 1 alone)
+    from the committed rocprofv3 counter summary profiles/<name>.md
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when
+    there is none or the kernel source changed since."""
     import hashlib
     summary = os.path.join(ROOT, "profiles", f"{name}.md")
     src = os.path.join(ROOT, "token_verification_amd", "csrc", "spec_verify.hip")
@@ -69,13 +70,13 @@ def counter_traffic(name: str):
         return None
     fields = {}
     for line in open(summary):
-        if ":" in line and line.split(":")[0] in ("source_sha256", "traffic_bytes_per_call"):
+        if ":" in line and line.split(":")[0] in ("source_sha256", key):
             key, val = line.split(":", 1)
             fields[key] = val.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != sha or "traffic_bytes_per_call" not in fields:
+    if fields.get("source_sha256") != sha or key not in fields:
         return None
-    return int(fields["traffic_bytes_per_call"])
+    return int(fields[key])
 
 
 def main() -> int:
@@ -166,6 +167,24 @@ def main() -> int:
     positions = B * k if dlen is None else int(dlen.sum())
     alg = algorithmic_bytes(w, dlen)
     label = name + ("_ragged" if dlen is not None else "")
+
+    # the dominant kernel, pass 1 (every logit streamed once), timed live with
+    # events the library records between its kernels (spec_verify_timed)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        c = copies[i % R]
+        tv.spec_verify(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"], c["mode"],
+                       out=outs[i % R], draft_len=c.get("draft_len"), phase_events=pev[i])
+    torch.cuda.synchronize()
+    ph = np.array([[a[j].elapsed_time(a[j + 1]) for j in range(3)] for a in pev])
+    p1_ms = float(ph[:, 0].mean())
+    if dlen is None:
+        logit_rows = B * (k + 1) + (B * k if w.mode == 0 else 0)
+    else:
+        logit_rows = int((dlen + 1).sum()) + (int(dlen.sum()) if w.mode == 0 else 0)
+    p1_bytes = logit_rows * w.V * w.elem_bytes
+    p1_gbs = p1_bytes / (p1_ms * 1e-3) / 1e9
     achieved = alg / (k_avg * 1e-3) / 1e9
     value = positions / (ms_per_step * 1e-3)
 
@@ -190,10 +209,19 @@ def main() -> int:
                       "p50": round(float(np.percentile(kms, 50)) * 1e3, 2),
                       "p90": round(float(np.percentile(kms, 90)) * 1e3, 2)},
         "positions_per_s_kernel": round(positions / (k_avg * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic("spec_verify_" + label),
-                     "algorithmic_bytes_per_launch": alg,
-                     "bytes_per_position": round(alg / positions, 1)},
+        "phase_us": {"pass1": round(p1_ms * 1e3, 2), "pass2": round(float(ph[:, 1].mean()) * 1e3, 2),
+                     "draw": round(float(ph[:, 2].mean()) * 1e3, 2)},
+        # the dominant kernel: pass 1 reads every logit once
+        "roofline": {"bound": "hbm", "kernel": "scan_kernel (pass 1)", "achieved": round(p1_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(p1_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": counter_traffic("spec_verify_" + label, "traffic_bytes_pass1"),
+                     "algorithmic_bytes_per_launch": p1_bytes},
+        # the whole call (all kernels) against the same bytes plus the small tensors
+        "roofline_call": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(achieved / PEAK_HBM_GBS, 4),
+                          "traffic": counter_traffic("spec_verify_" + label),
+                          "algorithmic_bytes_per_launch": alg,
+                          "bytes_per_position": round(alg / positions, 1)},
     }
 
     if dlen is not None:

@@ -146,6 +146,23 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits,
                        size_t workspace_bytes, void* stream);
 
 /*
+ * spec_verify (draft_len NULL) or spec_verify_ragged (draft_len set) with phase timing:
+ * events points to four hipEvent_t the caller created (timing enabled), recorded on
+ * `stream` before the first kernel (events[0]), after pass 1, the scan of every logit
+ * (events[1]), after the decisions and pass 2 (events[2]) and after the draw (events[3];
+ * greedy mode records events[2] and events[3] together). hipEventElapsedTime between
+ * them gives each phase's duration on the device, e.g. the streaming pass alone. Errors
+ * as spec_verify, plus SPEC_ERR_NULL when an event is missing. For profiling tools; the
+ * results equal spec_verify's.
+ */
+int spec_verify_timed(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const int32_t* draft_len, const float* uniforms,
+                      float temperature, int mode, int32_t B, int32_t k, int32_t V, int dtype,
+                      int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
+                      float* draft_prob, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* events);
+
+/*
  * Confidence gate over n ready distributions ("Speculative Pre-Positioning", section
  * 2.4, Eqs. 11-12, and the gated fast-path serve of Algorithm 2; the certified rule
  * is the argmax-stability bound of the speculative-decoding design note, "Axis 1

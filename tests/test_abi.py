@@ -27,7 +27,7 @@ def test_exports_match_header():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     exported = {s for s in exported if s.startswith("spec_")}
     assert declared() == exported
-    assert len(exported) == 9
+    assert len(exported) == 10
 
 
 def test_version():

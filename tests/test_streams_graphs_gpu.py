@@ -128,3 +128,22 @@ def test_two_streams_with_own_workspaces():
         torch.cuda.synchronize()
         for i in (0, 1):
             same(ref[i], outs[i][:3])
+
+
+@pytest.mark.parametrize("ragged,mode", [(False, 0), (True, 0), (False, 1)])
+def test_timed_entry_matches_and_orders_its_events(ragged, mode):
+    w = workloads.WORKLOADS["b64_k5_v151936_bf16"]
+    x = workloads.make(w, 2, device=DEV)
+    dl = workloads.draft_lengths(w, 2).to(DEV) if ragged else None
+    d, u = (x["draft"], x["uniforms"]) if mode == 0 else (None, None)
+    a = tv.spec_verify(x["target"], d, x["tokens"], u, x["T"], mode, draft_len=dl)
+    torch.cuda.synchronize()
+    a = [t.clone() for t in a[:3]]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    b = tv.spec_verify(x["target"], d, x["tokens"], u, x["T"], mode, draft_len=dl, phase_events=evs)
+    torch.cuda.synchronize()
+    same(a, b[:3])
+    t = [evs[i].elapsed_time(evs[i + 1]) for i in range(3)]
+    say("phases ms", [round(v, 4) for v in t])
+    assert t[0] > 0 and t[1] >= 0 and t[2] >= 0
+    assert t[0] < 1.0                          # pass 1 of this shape takes tens of microseconds

@@ -58,6 +58,9 @@ def lib():
                 L.spec_verify_ragged.argtypes = [P, P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
                                                  P, P, P, P, P, P, S, P]
                 L.spec_verify_ragged.restype = ctypes.c_int
+                L.spec_verify_timed.argtypes = [P, P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
+                                                P, P, P, P, P, P, S, P, P]
+                L.spec_verify_timed.restype = ctypes.c_int
                 L.spec_verify_workspace_size.argtypes = [I, I, I, ctypes.c_int, ctypes.c_int]
                 L.spec_verify_workspace_size.restype = S
                 L.spec_verify_check_args.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
@@ -121,15 +124,19 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: tor
                 uniforms: Optional[torch.Tensor], temperature: float = 1.0, mode: int = SAMPLE, *,
                 workspace: Optional[torch.Tensor] = None, return_probs: bool = False,
                 out: Optional[VerifyResult] = None,
-                draft_len: Optional[torch.Tensor] = None) -> VerifyResult:
+                draft_len: Optional[torch.Tensor] = None,
+                phase_events=None) -> VerifyResult:
     """Batched verify step on device tensors (see include/spec_verify.h).
 
     target [B,k+1,V] and draft [B,k,V] are float32 or bfloat16 (draft may be
     None in greedy mode), tokens [B,k] int32, uniforms [B,k+1,2] float32 (None
     allowed in greedy mode). With draft_len (int32 [B] on the same device)
     every batch row b verifies only its first draft_len[b] positions
-    (spec_verify_ragged). Work is enqueued on the current stream of the
-    target's device; the returned tensors are ready once that stream is.
+    (spec_verify_ragged). With phase_events (four torch.cuda.Event created
+    with enable_timing=True) the call goes through spec_verify_timed, which
+    records them before pass 1, after pass 1, after pass 2 and after the draw.
+    Work is enqueued on the current stream of the target's device; the
+    returned tensors are ready once that stream is.
     """
     if not isinstance(target, torch.Tensor) or target.dim() != 3:
         raise ValueError("target must be a [B, k+1, V] tensor")
@@ -176,7 +183,18 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: tor
             _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
             _ptr(out.target_prob), _ptr(out.draft_prob),
             ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
-    if draft_len is None:
+    if phase_events is not None:
+        if len(phase_events) != 4:
+            raise ValueError("phase_events must hold four events")
+        handles = []
+        for ev in phase_events:
+            if not ev.cuda_event:                         # torch creates events lazily
+                ev.record(torch.cuda.current_stream(dev))
+            handles.append(ev.cuda_event)
+        arr = (ctypes.c_void_p * 4)(*handles)
+        rc = lib().spec_verify_timed(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(draft_len), _ptr(uniforms),
+                                     *tail, ctypes.cast(arr, ctypes.c_void_p))
+    elif draft_len is None:
         rc = lib().spec_verify(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), *tail)
     else:
         rc = lib().spec_verify_ragged(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(draft_len),

@@ -2156,8 +2156,12 @@ int seg_blocks_per_cu(int dev) {
     return n;
 }
 
+// Phase events of spec_verify_timed (null otherwise): ev[0] before the first
+// kernel, ev[1] after pass 1, ev[2] after the decisions and pass 2, ev[3] after
+// the draw (greedy mode records ev[2] and ev[3] together).
 template <class E, int MODE>
-hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
+hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s, hipEvent_t const* ev = nullptr) {
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
     long long G = static_cast<long long>(ncu) * scan_blocks_per_cu<E, MODE>(dev);
     // slices of at least MIN_SLICE elements, but at least one workgroup per
     // row while the rows fit the round: a workgroup walks its row segments
@@ -2175,6 +2179,8 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
         hipLaunchKernelGGL((gate_row_kernel<E>), dim3(P.B), dim3(NTG), 0, s, P);
         return hipGetLastError();
     }
+    e = mark(0);
+    if (e != hipSuccess) return e;
     if (P.dlen && P.B > RAG_INLINE) {
         // ragged drafts with many batch rows: the packed rows and pass 1's
         // slices over them (at most P.N elements, so the same G workgroups
@@ -2185,13 +2191,17 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     }
     hipLaunchKernelGGL((scan_kernel<E, MODE>), dim3(P.G), dim3(NT), 0, s, P);
     e = hipGetLastError();
+    if (e == hipSuccess) e = mark(1);
     if (e != hipSuccess) return e;
     if constexpr (MODE == SPEC_MODE_GREEDY) {
         if (P.fire)
             hipLaunchKernelGGL((gate_kernel<E>), dim3((P.B + NT - 1) / NT), dim3(NT), 0, s, P);
         else
             hipLaunchKernelGGL((decide_kernel<E, MODE>), dim3(P.B), dim3(NT), 0, s, P);
-        return hipGetLastError();
+        e = hipGetLastError();
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess) e = mark(3);
+        return e;
     }
     // pass 2: one resident round of workgroups, split evenly over the batch rows
     long long slots = static_cast<long long>(ncu) *
@@ -2207,9 +2217,12 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s) {
     if (P.vec_ok) hipLaunchKernelGGL((seg_kernel<E, true>), dim3(G2), dim3(NTS), 0, s, P);
     else hipLaunchKernelGGL((seg_kernel<E, false>), dim3(G2), dim3(NTS), 0, s, P);
     e = hipGetLastError();
+    if (e == hipSuccess) e = mark(2);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((draw_kernel<E>), dim3(P.B), dim3(NT2), 0, s, P);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(3);
+    return e;
 }
 
 struct GateOut {
@@ -2223,7 +2236,8 @@ struct GateOut {
 int enqueue(const Plan& plan, const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
             const int32_t* draft_len, const float* uniforms, float temperature, int mode, int32_t B, int32_t k,
             int32_t V, int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
-            float* draft_prob, const GateOut* gate, void* workspace, void* stream) {
+            float* draft_prob, const GateOut* gate, void* workspace, void* stream,
+            void* const* events = nullptr) {
     char* ws = static_cast<char*>(workspace);
     Params P;
     P.tgt = target_logits;
@@ -2305,13 +2319,14 @@ int enqueue(const Plan& plan, const void* target_logits, const void* draft_logit
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
         return fail(SPEC_ERR_HIP, "cannot query the current HIP device");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
     hipError_t e;
     if (dtype == SPEC_DTYPE_BF16)
-        e = mode == SPEC_MODE_SAMPLE ? launch_all<Bf16, SPEC_MODE_SAMPLE>(P, dev, ncu, s)
-                                     : launch_all<Bf16, SPEC_MODE_GREEDY>(P, dev, ncu, s);
+        e = mode == SPEC_MODE_SAMPLE ? launch_all<Bf16, SPEC_MODE_SAMPLE>(P, dev, ncu, s, ev)
+                                     : launch_all<Bf16, SPEC_MODE_GREEDY>(P, dev, ncu, s, ev);
     else
-        e = mode == SPEC_MODE_SAMPLE ? launch_all<F32, SPEC_MODE_SAMPLE>(P, dev, ncu, s)
-                                     : launch_all<F32, SPEC_MODE_GREEDY>(P, dev, ncu, s);
+        e = mode == SPEC_MODE_SAMPLE ? launch_all<F32, SPEC_MODE_SAMPLE>(P, dev, ncu, s, ev)
+                                     : launch_all<F32, SPEC_MODE_GREEDY>(P, dev, ncu, s, ev);
     if (e != hipSuccess) return fail(SPEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return SPEC_OK;
 }
@@ -2319,14 +2334,14 @@ int enqueue(const Plan& plan, const void* target_logits, const void* draft_logit
 int run(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens, const int32_t* draft_len,
         bool ragged, const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V, int dtype,
         int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
-        void* workspace, size_t workspace_bytes, void* stream) {
+        void* workspace, size_t workspace_bytes, void* stream, void* const* events = nullptr) {
     Plan plan;
     const int rc = check(target_logits, draft_logits, draft_tokens, uniforms, temperature, mode, B, k, V,
                          dtype, accepted_len, out_tokens, gap, workspace, workspace_bytes, plan, ragged, draft_len);
     if (rc != SPEC_OK) return rc;
     return enqueue(plan, target_logits, draft_logits, draft_tokens, ragged ? draft_len : nullptr, uniforms,
                    temperature, mode, B, k, V, dtype, accepted_len, out_tokens, gap, target_prob, draft_prob,
-                   nullptr, workspace, stream);
+                   nullptr, workspace, stream, events);
 }
 
 int check_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, float tau, const uint32_t* admit,
@@ -2390,6 +2405,18 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, cons
                        void* stream) {
     return run(target_logits, draft_logits, draft_tokens, draft_len, true, uniforms, temperature, mode, B, k, V,
                dtype, accepted_len, out_tokens, gap, target_prob, draft_prob, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_timed(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                      const int32_t* draft_len, const float* uniforms, float temperature, int mode, int32_t B,
+                      int32_t k, int32_t V, int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                      float* target_prob, float* draft_prob, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* events) {
+    if (!events || !events[0] || !events[1] || !events[2] || !events[3])
+        return fail(SPEC_ERR_NULL, "spec_verify_timed needs four events");
+    return run(target_logits, draft_logits, draft_tokens, draft_len, draft_len != nullptr, uniforms, temperature,
+               mode, B, k, V, dtype, accepted_len, out_tokens, gap, target_prob, draft_prob, workspace,
+               workspace_bytes, stream, events);
 }
 
 size_t spec_gate_workspace_size(int32_t n, int32_t V, int dtype) {
