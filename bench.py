@@ -71,8 +71,8 @@ def counter_traffic(name: str, key: str = "traffic_bytes_per_call"):
     fields = {}
     for line in open(summary):
         if ":" in line and line.split(":")[0] in ("source_sha256", key):
-            key, val = line.split(":", 1)
-            fields[key] = val.strip()
+            name_, val = line.split(":", 1)
+            fields[name_] = val.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if fields.get("source_sha256") != sha or key not in fields:
         return None
