@@ -94,6 +94,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
+    ap.add_argument("--lmhead", action="store_true",
+                    help="time greedy verification fused with an int8 LM head instead "
+                         "(B=256 k=3 V=128256 d=4096 unless --lmhead-shape)")
+    ap.add_argument("--lmhead-shape", default="256,3,128256,4096", metavar="B,k,V,d")
     ap.add_argument("--probe", choices=["copy", "sum"], default=None,
                     help="instead of the verify step, time a plain 1 GiB device copy (or a "
                          "read-only sum): achievable-bandwidth context and the known-size "
@@ -114,6 +118,8 @@ def main() -> int:
         return gate_bench(args, torch, np)
     if args.commit:
         return commit_bench(args, torch, np)
+    if args.lmhead:
+        return lmhead_bench(args, torch, np)
 
     import token_verification_amd as tv
     import workloads
@@ -383,6 +389,83 @@ def commit_bench(args, torch, np) -> int:
             m += 1
         line["cpu_baseline"] = {"value": round(B * m / t_cpu, 1), "unit": "rows/s", "cores": 1,
                                 "kind": "oracle", "sample": f"{m} commits of the same {B} rows"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+PEAK_INT8_TOPS = 5000.0    # MI355X dense int8 matrix peak, TOP/s
+
+
+def lmhead_bench(args, torch, np) -> int:
+    import token_verification_amd as tv
+    import workloads
+
+    B, k, V, d = (int(v) for v in args.lmhead_shape.split(","))
+    M = B * (k + 1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: generating the int8 LM head B={B} k={k} V={V} d={d}", file=sys.stderr, flush=True)
+    x = workloads.make_lmhead(B, k, V, d, seed=0, device=dev)
+    a = (x["hidden"], x["hidden_scale"], x["weight"], x["weight_scale"], x["tokens"])
+    out = tv.binding.VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                                  torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                                  torch.empty((B, k + 1), dtype=torch.float32, device=dev), None, None)
+    for _ in range(args.warmup):
+        tv.spec_verify_lmhead(*a, out=out)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        tv.spec_verify_lmhead(*a, out=out, phase_events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    head = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    tail = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    call = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    ops = 2.0 * M * V * d                                  # int8 multiply-adds, counted as two ops
+    achieved = ops / (float(head.mean()) * 1e-3) / 1e12
+    wbytes = V * d + M * d + 4 * (V + M)
+    positions = B * k
+    acc = out.accepted_len.cpu().numpy()
+    line = {
+        "metric": f"verified draft positions/sec, greedy verify fused with an int8 LM head, "
+                  f"B={B} k={k} V={V} d={d}",
+        "value": round(positions / (wall / args.steps), 1),
+        "unit": "positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"lmhead_b{B}_k{k}_v{V}_d{d}_int8", "B": B, "k": k, "V": V, "d": d,
+                   "hidden_rows": M},
+        "phase_us": {"lmhead_kernel": round(float(head.mean()) * 1e3, 2),
+                     "merge_and_decide": round(float(tail.mean()) * 1e3, 2),
+                     "call": round(float(call.mean()) * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": counter_traffic(f"spec_verify_lmhead_b{B}_k{k}_v{V}_d{d}_int8",
+                                                "traffic_bytes_lmhead_kernel"),
+                     "algorithmic_ops_per_launch": ops},
+        "hbm_context": {"weight_and_hidden_bytes": wbytes,
+                        "GB_per_s": round(wbytes / (float(head.mean()) * 1e-3) / 1e9, 1)},
+        "accepted_mean": round(float(acc[acc >= 0].mean()), 3) if (acc >= 0).any() else None,
+    }
+    if args.cpu_seconds > 0:
+        from oracle.lmhead import lmhead_greedy_ref
+        hh, hs, ww, wsc = (t.cpu().numpy() for t in a[:4])
+        tok = a[4].cpu().numpy()
+        n, t_cpu, b = 0, 0.0, 0
+        while t_cpu < args.cpu_seconds:
+            rows = np.arange(b * (k + 1), (b + 1) * (k + 1))
+            c0 = time.perf_counter()
+            lmhead_greedy_ref(hh[rows], hs[rows], ww, wsc, tok[b:b + 1], 1, k)
+            t_cpu += time.perf_counter() - c0
+            n += 1
+            b = (b + 1) % B
+        line["cpu_baseline"] = {"value": round(n * k / t_cpu, 1), "unit": "positions/s",
+                                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "sample": f"{n} batch rows one at a time (k+1 hidden rows against the "
+                                          f"whole head), {t_cpu:.1f} s of oracle time"}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -220,6 +220,49 @@ size_t spec_gate_workspace_size(int32_t n, int32_t V, int dtype);
 int spec_commit(const int32_t* accepted_len, int32_t B, int32_t k, int32_t* kv_len,
                 const void* slots, void* state, size_t state_bytes, void* stream);
 
+/*
+ * Greedy verification fused with an int8 LM head (the verify forward's batched
+ * LM-head projection: the speculative-decoding design note, "Cost / correctness
+ * constraints", batched verify forward; "Speculative Decoding: The Physics of Stolen
+ * Time", section 1, the target's parallel pass; quantized heads as in the 4-bit and
+ * GGUF deployments those pages run). The logits are never stored:
+ *   logit[m, v] = fl32( fl32( float32(acc[m, v]) * hidden_scale[m] ) * weight_scale[v] ),
+ *   acc[m, v]   = sum_j hidden[m, j] * weight[v, j]   (exact integer; float32() rounds
+ *                                                      to nearest even),
+ * with hidden row m = b*(k+1) + i the target's final hidden state at position i of
+ * batch row b. The outputs are exactly spec_verify's GREEDY outputs on those float32
+ * logits (argmax with the lowest index on ties, first mismatch, gap; invalid rows as
+ * there: a NaN or +inf logit, a row without a finite entry, a draft token outside
+ * [0, V)).
+ *   hidden [B*(k+1), d] int8, weight [V, d] int8: DEVICE, 16-byte aligned.
+ *   hidden_scale [B*(k+1)], weight_scale [V] float32: DEVICE.
+ *   draft_tokens [B, k] int32, accepted_len [B], out_tokens [B, k+1], gap [B, k+1]:
+ *     DEVICE, as in spec_verify (GREEDY mode).
+ * d must be a multiple of 128 in [128, 65536] (so |acc| < 2^31); 1 <= B <= 2^21,
+ * 0 <= k <= SPEC_MAX_K, 1 <= V <= 2^29, B*(k+1) <= 2^26. Workspace: at least
+ * spec_lmhead_workspace_size() bytes, 256-byte aligned, no initialisation needed,
+ * one call at a time. Enqueues three kernels on `stream`; no allocation, no host
+ * synchronisation. Errors: SPEC_ERR_SHAPE, SPEC_ERR_NULL, SPEC_ERR_ALIGN,
+ * SPEC_ERR_WORKSPACE, SPEC_ERR_HIP (nothing enqueued).
+ */
+int spec_verify_lmhead(const int8_t* hidden, const float* hidden_scale, const int8_t* weight,
+                       const float* weight_scale, const int32_t* draft_tokens, int32_t B, int32_t k,
+                       int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace spec_verify_lmhead needs (0 if the sizes are invalid). Host-only. */
+size_t spec_lmhead_workspace_size(int32_t B, int32_t k, int32_t V, int32_t d);
+
+/*
+ * spec_verify_lmhead that also records events[0] before the LM-head kernel,
+ * events[1] after it and events[2] after the decisions, on `stream` (three
+ * hipEvent_t created by the caller). Same results.
+ */
+int spec_verify_lmhead_timed(const int8_t* hidden, const float* hidden_scale, const int8_t* weight,
+                             const float* weight_scale, const int32_t* draft_tokens, int32_t B, int32_t k,
+                             int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
 /* Thread-local description of the last non-zero return of this library. */
 const char* spec_verify_last_error(void);
 

@@ -5,9 +5,10 @@ TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``.
 The verify forward ends with the LM-head projection of the hidden states of
 the k+1 verified positions ("Speculative Decoding: The Physics of Stolen Time",
 section 1, the target's parallel verification pass; the speculative-decoding
-design note, "Batched verify forward"). With an int8 LM head (weights and
-activations quantised with one fp32 scale per vocabulary row and per hidden
-row, as the 4-bit and 8-bit deployments the pages describe do):
+design note, "Cost / correctness constraints", batched verify forward). The
+pages run quantized targets (a 4-bit 70B-class model in "Speculative
+Pre-Positioning", section 4; quantized GGUF weights in the design note); the
+head here is int8 with one fp32 scale per vocabulary row and per hidden row:
 
     acc[m, v]    = sum_d h[m, d] * w[v, d]                 (exact integer)
     logit[m, v]  = fl32( fl32( float32(acc) * h_scale[m] ) * w_scale[v] )

@@ -132,6 +132,7 @@ struct EmuWG {
     void (*body)(void*) = nullptr;
     void* arg = nullptr;
     alignas(8) unsigned char shfl[1024][8];
+    alignas(16) unsigned char mfa[1024][16], mfb[1024][16];
 };
 inline thread_local EmuWG* emu_wg = nullptr;
 
@@ -233,6 +234,34 @@ inline T __shfl_up(T v, unsigned delta, int width = 64) {
     return r;
 }
 
+// v_mfma_i32_32x32x32_i8 over the 64 lanes of this thread's wave (the lane
+// layout of the gfx950 instruction): A(i, k) is byte k % 16 of lane
+// i + 32 (k / 16)'s a, B(k, j) byte k % 16 of lane j + 32 (k / 16)'s b, and
+// D(i, j) = C(i, j) + sum_k A(i, k) B(k, j) is register 4 (i / 8) + i % 4 of
+// lane j + 32 ((i / 4) % 2).
+typedef int emu_i32x4 __attribute__((ext_vector_type(4)));
+typedef int emu_i32x16 __attribute__((ext_vector_type(16)));
+inline emu_i32x16 emu_mfma_i32_32x32x32_i8(emu_i32x4 a, emu_i32x4 b, emu_i32x16 c, int, int, int) {
+    EmuWG* w = emu_wg;
+    const unsigned me = threadIdx.x, base = me & ~63u, lane = me & 63u;
+    memcpy(w->mfa[me], &a, 16);
+    memcpy(w->mfb[me], &b, 16);
+    emu_wave_sync();
+    const unsigned j = lane & 31, h = lane >> 5;
+    emu_i32x16 d = c;
+    for (int q = 0; q < 16; ++q) {
+        const unsigned i = 8 * (q / 4) + 4 * h + q % 4;
+        long long s = 0;
+        for (int kk = 0; kk < 32; ++kk)
+            s += static_cast<long long>(static_cast<signed char>(w->mfa[base + i + 32 * (kk / 16)][kk % 16])) *
+                 static_cast<signed char>(w->mfb[base + j + 32 * (kk / 16)][kk % 16]);
+        d[q] = static_cast<int>(static_cast<long long>(d[q]) + s);
+    }
+    emu_wave_sync();
+    return d;
+}
+#define __builtin_amdgcn_mfma_i32_32x32x32_i8 emu_mfma_i32_32x32x32_i8
+
 inline void emu_fiber_entry(unsigned lo, unsigned hi) {
     (void)lo; (void)hi;
     EmuWG* w = emu_wg;
@@ -317,6 +346,8 @@ inline void emu_launch(void (*kernel)(P), dim3 grid, dim3 block, P params) {
 // ---------------------------------------------------------------- host API
 typedef int hipError_t;
 typedef void* hipStream_t;
+typedef void* hipEvent_t;
+inline hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return 0; }
 enum { hipSuccess = 0, hipErrorInvalidValue = 1 };
 enum hipMemcpyKind { hipMemcpyDeviceToHost = 2 };
 enum hipDeviceAttribute_t { hipDeviceAttributeMultiprocessorCount = 0 };

@@ -35,6 +35,10 @@ L.spec_gate_workspace_size.argtypes = [I, I, ctypes.c_int]
 L.spec_gate_workspace_size.restype = S
 L.spec_commit.argtypes = [P, I, I, P, P, P, S, P]
 L.spec_commit.restype = ctypes.c_int
+L.spec_verify_lmhead.argtypes = [P, P, P, P, P, I, I, I, I, P, P, P, P, S, P]
+L.spec_verify_lmhead.restype = ctypes.c_int
+L.spec_lmhead_workspace_size.argtypes = [I, I, I, I]
+L.spec_lmhead_workspace_size.restype = S
 L.spec_verify_emu_set_cu_count.argtypes = [ctypes.c_int]
 L.spec_verify_emu_set_pool.argtypes = [ctypes.c_int]
 
@@ -308,6 +312,52 @@ def exact_path():
     rng = np.random.default_rng(3)
     run_case(rand_case(rng, 4, 3, 9000, 0, 0.9))
     del os.environ["SPEC_VERIFY_FORCE_EXACT_PATH"]
+
+
+def run_lmhead(x, pool=1):
+    from oracle.lmhead import lmhead_greedy_ref
+    B, k, V, d = x["B"], x["k"], x["V"], x["d"]
+    h, hs, w, ws = (np.ascontiguousarray(x[n].numpy()) for n in ("hidden", "hidden_scale", "weight", "weight_scale"))
+    tok = np.ascontiguousarray(x["tokens"].numpy().astype(np.int32))
+    acc = np.full(B, -7, np.int32)
+    out = np.full((B, k + 1), -7, np.int32)
+    gap = np.zeros((B, k + 1), np.float32)
+    nb = L.spec_lmhead_workspace_size(B, k, V, d)
+    assert nb > 0
+    wsp = np.frombuffer(os.urandom(nb + 256), np.uint8).copy()
+    base = wsp.ctypes.data
+    off = (-base) % 256
+    L.spec_verify_emu_set_pool(pool)
+    rc = L.spec_verify_lmhead(ptr(h), ptr(hs), ptr(w), ptr(ws), ptr(tok), B, k, V, d, ptr(acc), ptr(out),
+                              ptr(gap), ctypes.c_void_p(base + off), nb, None)
+    assert rc == 0, (rc, L.spec_verify_last_error())
+    ref = lmhead_greedy_ref(h, hs, w, ws, tok, B, k)
+    assert (acc == ref.accepted_len).all(), (acc, ref.accepted_len)
+    assert (out == ref.out_tokens).all()
+    valid = ref.accepted_len >= 0                           # gaps are compared on valid rows
+    g, r = gap.astype(np.float64)[valid], ref.gap[valid]
+    assert (np.isnan(g) == np.isnan(r)).all() and (np.isinf(g) == np.isinf(r)).all()
+    fin = np.isfinite(r)
+    assert np.abs(g[fin] - r[fin]).max(initial=0.0) <= 1e-5
+    return acc
+
+
+@case
+def lmhead():
+    # int8 LM head fused with greedy verification: partial vocabulary and
+    # hidden-row tiles, several LDS stages, k = 0, NaN / inf scales, a token
+    # outside [0, V), ties at the top
+    for B, k, V, d, pool in ((3, 2, 700, 256, 1), (50, 3, 300, 128, 2), (4, 0, 257, 128, 1)):
+        x = workloads.make_lmhead(B, k, V, d, seed=1)
+        if B >= 50:
+            x["hidden_scale"][0] = float("nan")            # batch row 0: NaN logits
+            x["hidden_scale"][5] = float("inf")            # batch row 1: +-inf / NaN logits
+            x["tokens"][2, 1] = V                          # batch row 2: token out of range
+            x["hidden"][12:16] = 0                         # batch row 3: all logits 0, a tie at 0
+            x["tokens"][3, :] = 0
+        acc = run_lmhead(x, pool=pool)
+        if B >= 50:
+            assert acc[0] == -1 and acc[1] == -1 and acc[2] == -1 and acc[3] == 3
 
 
 if __name__ == "__main__":

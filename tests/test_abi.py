@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(spec_(?:verify|gate|commit)\w*)\s*\(", src))
+    return set(re.findall(r"\b(spec_(?:verify|gate|commit|lmhead)\w*)\s*\(", src))
 
 
 def test_exports_match_header():
@@ -27,7 +27,7 @@ def test_exports_match_header():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     exported = {s for s in exported if s.startswith("spec_")}
     assert declared() == exported
-    assert len(exported) == 10
+    assert len(exported) == 13
 
 
 def test_version():
@@ -176,3 +176,45 @@ def test_commit_rejects_synchronously(kw, code):
     rc = tv.lib().spec_commit(a["acc"], a["B"], a["k"], a["kv"], a["slots"], a["state"], a["row"], None)
     assert rc == code
     assert binding.last_error()
+
+
+def test_lmhead_workspace_size():
+    L = tv.lib()
+    assert L.spec_lmhead_workspace_size(256, 3, 128256, 4096) > 0
+    assert L.spec_lmhead_workspace_size(256, 3, 128256, 4096) % 256 == 0
+    assert L.spec_lmhead_workspace_size(0, 3, 100, 128) == 0
+    assert L.spec_lmhead_workspace_size(1, 65, 100, 128) == 0
+    assert L.spec_lmhead_workspace_size(1, 3, 100, 100) == 0       # d not a multiple of 128
+    assert L.spec_lmhead_workspace_size(1, 3, 100, 65536 + 128) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"B": 0}, -2),
+    ({"k": 65}, -2),
+    ({"d": 192}, -2),
+    ({"d": 0}, -2),
+    ({"hidden": None}, -1),
+    ({"w_scale": None}, -1),
+    ({"tokens": None}, -1),
+    ({"gap": None}, -1),
+    ({"hidden": FAKE + 4}, -7),
+    ({"weight": FAKE + 8}, -7),
+    ({"h_scale": FAKE + 2}, -7),
+    ({"ws": None}, -6),
+    ({"ws_bytes": 256}, -6),
+    ({"ws": 0x100010}, -7),
+])
+def test_lmhead_rejects_synchronously(kw, code):
+    a = dict(hidden=FAKE, h_scale=FAKE, weight=FAKE, w_scale=FAKE, tokens=FAKE, B=4, k=3, V=1000, d=256,
+             acc=FAKE, out=FAKE, gap=FAKE, ws=0x100000, ws_bytes=1 << 24)
+    a.update(kw)
+    rc = tv.lib().spec_verify_lmhead(a["hidden"], a["h_scale"], a["weight"], a["w_scale"], a["tokens"], a["B"],
+                                     a["k"], a["V"], a["d"], a["acc"], a["out"], a["gap"], a["ws"],
+                                     a["ws_bytes"], None)
+    assert rc == code
+    assert binding.last_error()
+    ev = (ctypes.c_void_p * 3)(None, None, None)
+    rc = tv.lib().spec_verify_lmhead_timed(a["hidden"], a["h_scale"], a["weight"], a["w_scale"], a["tokens"],
+                                           a["B"], a["k"], a["V"], a["d"], a["acc"], a["out"], a["gap"],
+                                           a["ws"], a["ws_bytes"], None, ctypes.cast(ev, ctypes.c_void_p))
+    assert rc in (code, -1)

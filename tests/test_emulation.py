@@ -25,7 +25,7 @@ def emu_lib():
     out = os.path.join(EMU, "libspecverify_emu.so")
     cmd = [CLANG, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
            "-I", EMU, "-I", os.path.join(ROOT, "include"), "-Wno-unknown-pragmas",
-           "-Wno-pass-failed",
+           "-Wno-pass-failed", "-Wno-psabi",
            "-o", out, os.path.join(EMU, "spec_verify_emu.cpp"), "-lpthread"]
     if ASAN:
         cmd[5:5] = ["-fsanitize=address,undefined"]
@@ -71,6 +71,10 @@ def test_emulated_gate(emu_lib):
 
 def test_emulated_commit(emu_lib):
     run_cases("commit")
+
+
+def test_emulated_lmhead(emu_lib):
+    run_cases("lmhead")
 
 
 def test_emulated_concurrent_workgroups(emu_lib):

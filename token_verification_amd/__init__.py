@@ -17,5 +17,6 @@ from .binding import (  # noqa: F401
     spec_commit,
     spec_gate,
     spec_verify,
+    spec_verify_lmhead,
     workspace_size,
 )

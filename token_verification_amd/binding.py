@@ -72,6 +72,12 @@ def lib():
                 L.spec_gate_workspace_size.restype = S
                 L.spec_commit.argtypes = [P, I, I, P, P, P, S, P]
                 L.spec_commit.restype = ctypes.c_int
+                L.spec_verify_lmhead.argtypes = [P, P, P, P, P, I, I, I, I, P, P, P, P, S, P]
+                L.spec_verify_lmhead.restype = ctypes.c_int
+                L.spec_verify_lmhead_timed.argtypes = [P, P, P, P, P, I, I, I, I, P, P, P, P, S, P, P]
+                L.spec_verify_lmhead_timed.restype = ctypes.c_int
+                L.spec_lmhead_workspace_size.argtypes = [I, I, I, I]
+                L.spec_lmhead_workspace_size.restype = S
                 L.spec_verify_last_error.restype = ctypes.c_char_p
                 L.spec_verify_version.restype = ctypes.c_char_p
                 _lib = L
@@ -283,3 +289,65 @@ def spec_commit(accepted_len: torch.Tensor, k: int, kv_len: Optional[torch.Tenso
                            ctypes.c_void_p(stream))
     if rc != 0:
         raise SpecVerifyError(rc, last_error())
+
+
+def spec_verify_lmhead(hidden: torch.Tensor, hidden_scale: torch.Tensor, weight: torch.Tensor,
+                       weight_scale: torch.Tensor, tokens: torch.Tensor, *,
+                       workspace: Optional[torch.Tensor] = None, out: Optional[VerifyResult] = None,
+                       phase_events=None) -> VerifyResult:
+    """Greedy verification fused with an int8 LM head (see include/spec_verify.h).
+
+    hidden int8 [B*(k+1), d] (row b*(k+1)+i: position i of batch row b),
+    hidden_scale float32 [B*(k+1)], weight int8 [V, d], weight_scale float32
+    [V], tokens int32 [B, k], all on one device. With phase_events (three
+    torch.cuda.Event created with enable_timing=True) the call records them
+    before the LM-head kernel, after it and after the decisions.
+    """
+    for t, nm in ((hidden, "hidden"), (weight, "weight")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != torch.int8 or not t.is_cuda:
+            raise ValueError(f"{nm} must be an int8 2-D device tensor")
+    M, d = hidden.shape
+    V = weight.shape[0]
+    if weight.shape[1] != d:
+        raise ValueError("hidden and weight must share d")
+    if tokens.dim() != 2 or tokens.dtype != torch.int32:
+        raise ValueError("tokens must be int32 [B, k]")
+    B, k = tokens.shape
+    dev = hidden.device
+    if M != B * (k + 1):
+        raise ValueError("hidden must hold B*(k+1) rows")
+    if hidden_scale.shape != (M,) or weight_scale.shape != (V,) or hidden_scale.dtype != torch.float32 \
+            or weight_scale.dtype != torch.float32:
+        raise ValueError("hidden_scale [B*(k+1)] and weight_scale [V] must be float32")
+    for t in (hidden, hidden_scale, weight, weight_scale, tokens):
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                           torch.empty((B, k + 1), dtype=torch.float32, device=dev), None, None)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = int(lib().spec_lmhead_workspace_size(B, k, V, d))
+    if need == 0:
+        raise SpecVerifyError(-2, f"unsupported sizes B={B} k={k} V={V} d={d}")
+    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    args = (_ptr(hidden), _ptr(hidden_scale), _ptr(weight), _ptr(weight_scale), _ptr(tokens), B, k, V, d,
+            _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
+            ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+    if phase_events is not None:
+        if len(phase_events) != 3:
+            raise ValueError("phase_events must hold three events")
+        handles = []
+        for ev in phase_events:
+            if not ev.cuda_event:                         # torch creates events lazily
+                ev.record(torch.cuda.current_stream(dev))
+            handles.append(ev.cuda_event)
+        arr = (ctypes.c_void_p * 3)(*handles)
+        rc = lib().spec_verify_lmhead_timed(*args, ctypes.cast(arr, ctypes.c_void_p))
+    else:
+        rc = lib().spec_verify_lmhead(*args)
+    if rc != 0:
+        raise SpecVerifyError(rc, last_error())
+    return out

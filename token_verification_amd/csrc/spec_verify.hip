@@ -2036,6 +2036,228 @@ __global__ __launch_bounds__(NTC) void commit_kernel(CommitParams C) {
     }
 }
 
+// ------------------------------------------------------------------ int8 LM head + greedy verification
+//
+// The verify forward's last step, the LM-head projection of the k + 1 hidden
+// states of every batch row, fused with greedy verification: with an int8
+// head (per-row fp32 scales of the hidden states and of the vocabulary rows)
+//     acc[m, v]   = sum_j h[m, j] * w[v, j]                       (int32, exact)
+//     logit[m, v] = fl32(fl32(float(acc[m, v]) * h_scale[m]) * w_scale[v]),
+// and the greedy decision needs of every row only its first argmax and its
+// top-2 values. head_kernel computes the logits tile by tile on the matrix
+// cores and reduces them in registers, so they never reach memory:
+//   * one workgroup per 256-vocabulary x 128-hidden-row tile, 2 x 2 waves of
+//     128 x 64; the vocabulary rows are the MFMA's A operand, so each lane's
+//     accumulators hold 16 vocabulary entries of ONE hidden row and the row
+//     reduction is per lane (then one exchange with lane ^ 32 and one through
+//     LDS between the two vocabulary waves);
+//   * d (a multiple of 128) is staged through LDS 128 bytes at a time (32 KB of weights, 16 KB of
+//     hidden states), the 16-byte chunk index XOR-swizzled with the row so
+//     that the MFMA operand reads of any 8 consecutive lanes hit distinct
+//     banks; the next stage's global loads are in flight during the MFMAs;
+//   * since the products are exact integers, the order of the d-sum is free:
+//     the K layout of the MFMA only has to be the same for both operands;
+//   * workgroups are numbered so that the hidden-row tiles of one vocabulary
+//     tile run on one XCD and share its weights through that XCD's L2.
+// Each workgroup writes one record (top-2, first argmax, NaN flag) per hidden
+// row; head_merge_kernel merges the vocabulary tiles of every row into one
+// pass-1 record (slot 2m: pass 1's slot rule with one slice per row), and
+// decide_kernel makes the greedy decisions exactly as after pass 1.
+
+constexpr int HV = 256;                 // vocabulary rows per head tile
+constexpr int HM = 128;                 // hidden rows per head tile
+constexpr int HK = 128;                 // bytes of d per LDS stage
+constexpr int NTH = 256;                // threads per head workgroup
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+struct HeadRec {                        // one hidden row over one vocabulary tile
+    float t1, t2;
+    int idx;                            // first index of t1 (INT_MAX if none)
+    int flags;                          // bit 0: a NaN logit
+};
+
+struct HeadParams {
+    const signed char* h;               // [M, d]
+    const float* hs;                    // [M]
+    const signed char* w;               // [V, d]
+    const float* ws;                    // [V]
+    HeadRec* rec;                       // [M, nvt]
+    TileRec* tiles;                     // [2M], row m's merged record at 2m
+    int M, V, d;
+    int nvt, nmt;                       // vocabulary and hidden-row tiles
+    int nks;                            // LDS stages: d / HK
+};
+
+// Fold logit x of vocabulary index v (ascending within a lane) into a top-2
+// and first argmax; NaN never enters.
+__device__ inline void head_take(float x, int v, float& t1, float& t2, int& i1) {
+    const bool up = x > t1;
+    t2 = up ? t1 : fmaxf(t2, x);
+    i1 = up ? v : i1;
+    t1 = up ? x : t1;
+}
+
+// Merge two top-2 records; the lower index wins a tie of the maxima.
+__device__ inline void head_merge(float& t1, float& t2, int& i1, int& fl, float u1, float u2, int j1, int g) {
+    const bool take = u1 > t1 || (u1 == t1 && j1 < i1);
+    t2 = fmaxf(fmaxf(t2, u2), fminf(t1, u1));
+    i1 = take ? j1 : i1;
+    t1 = take ? u1 : t1;
+    fl |= g;
+}
+
+// Scale the accumulators of one lane to logits and reduce them to a top-2
+// per hidden row (EDGE: the tile reaches past V, so entries past it are skipped).
+template <bool EDGE>
+__device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4][2], int v0, int m0, int vw,
+                                     int mw, int r, int hi, float (&T1)[2], float (&T2)[2], int (&I1)[2],
+                                     int (&FL)[2]) {
+    float hsv[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int m = m0 + 64 * mw + 32 * mb + r;
+        hsv[mb] = m < H.M ? H.hs[m] : 0.0f;
+        T1[mb] = -INFINITY; T2[mb] = -INFINITY; I1[mb] = 0x7fffffff; FL[mb] = 0;
+    }
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+        const int vbase = v0 + 128 * vw + 32 * vb + 4 * hi;
+        float wsv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int v = vbase + 8 * (q >> 2) + (q & 3);
+            wsv[q] = !EDGE || v < H.V ? H.ws[v] : 0.0f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int v = vbase + 8 * (q >> 2) + (q & 3);
+                float x = (static_cast<float>(acc[vb][mb][q]) * hsv[mb]) * wsv[q];
+                FL[mb] |= x != x;
+                if (EDGE) x = v < H.V ? x : -INFINITY;
+                head_take(x, v, T1[mb], T2[mb], I1[mb]);
+            }
+    }
+}
+
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel(HeadParams H) {
+    __shared__ __attribute__((aligned(16))) unsigned char S[(HV + HM) * HK];
+    const int t = static_cast<int>(threadIdx.x), lane = t & 63, wv = t >> 6;
+    const int vw = wv & 1, mw = wv >> 1, r = lane & 31, hi = lane >> 5;
+    // tile of this workgroup: workgroup b runs on XCD b % 8, so tiles are
+    // dealt out in 8 contiguous runs, one per XCD
+    const unsigned nb = gridDim.x, b = blockIdx.x, per = nb / 8;
+    const unsigned tix = b < per * 8 ? (b % 8) * per + b / 8 : b;
+    const int vt = static_cast<int>(tix) / H.nmt, mt = static_cast<int>(tix) % H.nmt;
+    const int v0 = vt * HV, m0 = mt * HM;
+    const int nv = min(HV, H.V - v0), nm = min(HM, H.M - m0);
+    const unsigned d = static_cast<unsigned>(H.d);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(v0) * d, static_cast<unsigned>(nv) * d);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(m0) * d, static_cast<unsigned>(nm) * d);
+
+    // staging: thread t moves chunk t & 7 of rows (t >> 3) + 32 j (d is a
+    // multiple of HK); rows past the tile's end load zeros (out of the resource)
+    const int lr = t >> 3, lc = t & 7;
+    const int pc = (lc ^ (lr & 7)) << 4;                    // swizzled chunk of that row
+    u32x4 gw[HV / 32], gh[HM / 32];
+    auto fetch = [&](int k0) {
+        const unsigned o0 = static_cast<unsigned>(lr) * d + static_cast<unsigned>(k0 + lc * 16);
+#pragma unroll
+        for (int j = 0; j < HV / 32; ++j)
+            gw[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, static_cast<int>(o0 + 32u * j * d), 0, 0);
+#pragma unroll
+        for (int j = 0; j < HM / 32; ++j)
+            gh[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(o0 + 32u * j * d), 0, 0);
+    };
+
+    i32x16 acc[4][2];
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[vb][mb][q] = 0;
+    // operand rows of this lane: A (weights) 128*vw + 32*vb + r, B (hidden)
+    // 64*mw + 32*mb + r; K step s reads chunk 2s + hi of them
+    const int ra = (128 * vw + r) * HK, rb = HV * HK + (64 * mw + r) * HK, sw = r & 7;
+    fetch(0);
+    for (int ks = 0; ks < H.nks; ++ks) {
+        __syncthreads();                                   // the last stage's reads are done
+#pragma unroll
+        for (int j = 0; j < HV / 32; ++j) *reinterpret_cast<u32x4*>(S + (lr + 32 * j) * HK + pc) = gw[j];
+#pragma unroll
+        for (int j = 0; j < HM / 32; ++j) *reinterpret_cast<u32x4*>(S + HV * HK + (lr + 32 * j) * HK + pc) = gh[j];
+        __syncthreads();
+        if (ks + 1 < H.nks) fetch((ks + 1) * HK);
+#pragma unroll
+        for (int s = 0; s < HK / 32; ++s) {
+            const int co = ((2 * s + hi) ^ sw) << 4;
+            i32x4 a[4], q[2];
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb) a[vb] = *reinterpret_cast<const i32x4*>(S + ra + vb * 32 * HK + co);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) q[mb] = *reinterpret_cast<const i32x4*>(S + rb + mb * 32 * HK + co);
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    acc[vb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[vb], q[mb], acc[vb][mb], 0, 0, 0);
+        }
+    }
+
+    // epilogue: lane holds hidden row 64*mw + 32*mb + r and, in register q of
+    // block vb, vocabulary row 128*vw + 32*vb + 8*(q/4) + 4*hi + q%4
+    float T1[2], T2[2];
+    int I1[2], FL[2];
+    if (v0 + HV <= H.V) head_epilogue<false>(H, acc, v0, m0, vw, mw, r, hi, T1, T2, I1, FL);
+    else head_epilogue<true>(H, acc, v0, m0, vw, mw, r, hi, T1, T2, I1, FL);
+    __syncthreads();                                       // the staging tiles are free
+    HeadRec* L = reinterpret_cast<HeadRec*>(S);            // [2][HM]: per vocabulary wave
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const float u1 = __shfl_xor(T1[mb], 32, 64), u2 = __shfl_xor(T2[mb], 32, 64);
+        const int j1 = __shfl_xor(I1[mb], 32, 64), g = __shfl_xor(FL[mb], 32, 64);
+        head_merge(T1[mb], T2[mb], I1[mb], FL[mb], u1, u2, j1, g);
+        if (hi == 0) L[vw * HM + 64 * mw + 32 * mb + r] = HeadRec{T1[mb], T2[mb], I1[mb], FL[mb]};
+    }
+    __syncthreads();
+    if (t < nm) {
+        HeadRec o = L[t];
+        const HeadRec p = L[HM + t];
+        head_merge(o.t1, o.t2, o.idx, o.flags, p.t1, p.t2, p.idx, p.flags);
+        H.rec[static_cast<size_t>(m0 + t) * H.nvt + vt] = o;
+    }
+}
+
+// One wave per hidden row: merge its vocabulary-tile records into the row's
+// pass-1 record.
+__global__ __launch_bounds__(NT) void head_merge_kernel(HeadParams H) {
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int m = static_cast<int>(blockIdx.x) * NWAVE + (static_cast<int>(threadIdx.x) >> 6);
+    if (m >= H.M) return;                                  // uniform per wave
+    float t1 = -INFINITY, t2 = -INFINITY;
+    int i1 = 0x7fffffff, fl = 0;
+    const HeadRec* R = H.rec + static_cast<size_t>(m) * H.nvt;
+    for (int j = lane; j < H.nvt; j += 64) {
+        const HeadRec o = R[j];
+        head_merge(t1, t2, i1, fl, o.t1, o.t2, o.idx, o.flags);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float u1 = __shfl_xor(t1, off, 64), u2 = __shfl_xor(t2, off, 64);
+        const int j1 = __shfl_xor(i1, off, 64), g = __shfl_xor(fl, off, 64);
+        head_merge(t1, t2, i1, fl, u1, u2, j1, g);
+    }
+    if (lane == 0) {
+        TileRec tr;
+        tr.t1 = t1; tr.t2 = t2; tr.ref = 0.0f; tr.idx = i1; tr.s = 0.0; tr.lx = 0.0f; tr.flags = fl & 1;
+        H.tiles[2 * static_cast<size_t>(m)] = tr;
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 thread_local char g_err[512] = "";
@@ -2370,6 +2592,109 @@ int check_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, fl
     return SPEC_OK;
 }
 
+// ---- int8 LM head + greedy verification
+
+constexpr int HEAD_MAX_D = 65536;       // |acc| <= 2^14 * d stays inside int32
+
+struct HeadPlan {
+    int M, nvt, nmt;
+    size_t o_rec, o_tiles, total;
+};
+
+bool make_head_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadPlan& p) {
+    if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K || V < 1 || V > (1 << 29)) return false;
+    if (d < HK || d > HEAD_MAX_D || d % HK != 0) return false;
+    const long long M = static_cast<long long>(B) * (k + 1);
+    if (M > (1 << 26)) return false;
+    const long long nvt = (V + HV - 1) / HV, nmt = (M + HM - 1) / HM;
+    if (nvt * nmt >= (1ll << 31)) return false;
+    p.M = static_cast<int>(M);
+    p.nvt = static_cast<int>(nvt);
+    p.nmt = static_cast<int>(nmt);
+    size_t o = 0;
+    p.o_rec = o; o = align256(o + static_cast<size_t>(M) * nvt * sizeof(HeadRec));
+    p.o_tiles = o; o = align256(o + 2 * static_cast<size_t>(M) * sizeof(TileRec));
+    p.total = o;
+    return true;
+}
+
+int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weight, const float* weight_scale,
+             const int32_t* draft_tokens, int32_t B, int32_t k, int32_t V, int32_t d, int32_t* accepted_len,
+             int32_t* out_tokens, float* gap, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* events) {
+    if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K || V < 1 || V > (1 << 29))
+        return fail(SPEC_ERR_SHAPE, "need 1 <= B <= 2^21, 0 <= k <= %d, 1 <= V <= 2^29 (got B=%d k=%d V=%d)",
+                    SPEC_MAX_K, B, k, V);
+    if (d < HK || d > HEAD_MAX_D || d % HK != 0)
+        return fail(SPEC_ERR_SHAPE, "d must be a multiple of %d in [%d, %d] (got %d)", HK, HK, HEAD_MAX_D, d);
+    HeadPlan plan;
+    if (!make_head_plan(B, k, V, d, plan))
+        return fail(SPEC_ERR_SHAPE, "sizes B=%d k=%d V=%d d=%d exceed the supported range", B, k, V, d);
+    if (!hidden || !hidden_scale || !weight || !weight_scale)
+        return fail(SPEC_ERR_NULL, "hidden, hidden_scale, weight and weight_scale are required");
+    if (k > 0 && !draft_tokens) return fail(SPEC_ERR_NULL, "draft_tokens is NULL");
+    if (!accepted_len || !out_tokens || !gap) return fail(SPEC_ERR_NULL, "an output pointer is NULL");
+    if (!aligned(hidden, 16) || !aligned(weight, 16))
+        return fail(SPEC_ERR_ALIGN, "hidden and weight must be 16-byte aligned");
+    if (!aligned(hidden_scale, 4) || !aligned(weight_scale, 4) || (draft_tokens && !aligned(draft_tokens, 4)) ||
+        !aligned(accepted_len, 4) || !aligned(out_tokens, 4) || !aligned(gap, 4))
+        return fail(SPEC_ERR_ALIGN, "a pointer is not aligned to its element size");
+    if (!workspace || workspace_bytes < plan.total)
+        return fail(SPEC_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", plan.total, workspace_bytes,
+                    workspace ? "" : ", NULL");
+    if (!aligned(workspace, 256)) return fail(SPEC_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (events && (!events[0] || !events[1] || !events[2]))
+        return fail(SPEC_ERR_NULL, "spec_verify_lmhead_timed needs three events");
+
+    char* ws = static_cast<char*>(workspace);
+    HeadParams H;
+    H.h = reinterpret_cast<const signed char*>(hidden);
+    H.hs = hidden_scale;
+    H.w = reinterpret_cast<const signed char*>(weight);
+    H.ws = weight_scale;
+    H.rec = reinterpret_cast<HeadRec*>(ws + plan.o_rec);
+    H.tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
+    H.M = plan.M; H.V = V; H.d = d;
+    H.nvt = plan.nvt; H.nmt = plan.nmt;
+    H.nks = d / HK;
+    // the greedy decisions read the merged records as pass 1's, one slice per row
+    Params P;
+    memset(&P, 0, sizeof P);
+    P.tok = draft_tokens;
+    P.acc_len = accepted_len;
+    P.out_tok = out_tokens;
+    P.gap = gap;
+    P.B = B; P.k = k; P.V = V;
+    P.rpb = k + 1;
+    P.N = static_cast<long long>(plan.M) * V;
+    P.L = V;
+    P.G = plan.M;
+    P.mode = SPEC_MODE_GREEDY;
+    P.c = 1.4426950408889634;
+    P.tiles = H.tiles;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(head_kernel, dim3(static_cast<unsigned>(plan.nvt) * plan.nmt), dim3(NTH), 0, s, H);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(head_merge_kernel, dim3(static_cast<unsigned>((plan.M + NWAVE - 1) / NWAVE)), dim3(NT),
+                           0, s, H);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL((decide_kernel<F32, SPEC_MODE_GREEDY>), dim3(B), dim3(NT), 0, s, P);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
+    if (e != hipSuccess) return fail(SPEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return SPEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2468,8 +2793,31 @@ int spec_commit(const int32_t* accepted_len, int32_t B, int32_t k, int32_t* kv_l
     return SPEC_OK;
 }
 
+size_t spec_lmhead_workspace_size(int32_t B, int32_t k, int32_t V, int32_t d) {
+    HeadPlan p;
+    if (!make_head_plan(B, k, V, d, p)) return 0;
+    return p.total;
+}
+
+int spec_verify_lmhead(const int8_t* hidden, const float* hidden_scale, const int8_t* weight,
+                       const float* weight_scale, const int32_t* draft_tokens, int32_t B, int32_t k, int32_t V,
+                       int32_t d, int32_t* accepted_len, int32_t* out_tokens, float* gap, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return run_head(hidden, hidden_scale, weight, weight_scale, draft_tokens, B, k, V, d, accepted_len,
+                    out_tokens, gap, workspace, workspace_bytes, stream, nullptr);
+}
+
+int spec_verify_lmhead_timed(const int8_t* hidden, const float* hidden_scale, const int8_t* weight,
+                             const float* weight_scale, const int32_t* draft_tokens, int32_t B, int32_t k,
+                             int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    if (!events) return fail(SPEC_ERR_NULL, "spec_verify_lmhead_timed needs three events");
+    return run_head(hidden, hidden_scale, weight, weight_scale, draft_tokens, B, k, V, d, accepted_len,
+                    out_tokens, gap, workspace, workspace_bytes, stream, events);
+}
+
 const char* spec_verify_last_error(void) { return g_err; }
 
-const char* spec_verify_version(void) { return "specverify 0.4.0 (gfx950)"; }
+const char* spec_verify_version(void) { return "specverify 0.5.0 (gfx950)"; }
 
 }  // extern "C"

@@ -280,3 +280,35 @@ def admit_bits(tokens, V: int) -> torch.Tensor:
     for j in (int(t) for t in tokens):
         words[j >> 5] |= 1 << (j & 31)
     return torch.tensor([w - (1 << 32) if w >= (1 << 31) else w for w in words], dtype=torch.int32)
+
+
+LMHEAD_D = 4096            # hidden size of the 8B-class models with these vocabularies
+
+
+def make_lmhead(B: int, k: int, V: int, d: int = LMHEAD_D, seed: int = 0, device="cpu"):
+    """An int8 LM head and the k + 1 hidden states of B batch rows.
+
+    weight [V, d] int8 ~ round(N(0, 30^2)) clipped to [-127, 127]; hidden row m
+    (= b*(k+1) + i) leans towards a planted vocabulary row: round(N(0, 30^2) +
+    beta * weight[planted]) clipped, beta ~ U(0.055, 0.094), which lifts the
+    planted logit by about 3.5 to 6 standard deviations of the others (at
+    d = 4096), so it is
+    the argmax of most rows but not all. Scales: hidden U(0.5, 1.5) / 2^7,
+    weight U(0.9, 1.1) / 2^7 (float32). Draft tokens are the planted rows of
+    positions 0..k-1 with 30% replaced by uniform random ids.
+    """
+    g = _gen(device, "lmhead", B, k, V, d, seed)
+    M = B * (k + 1)
+    w = torch.randn((V, d), generator=g, device=device).mul_(30.0).round_().clamp_(-127, 127)
+    planted = torch.randint(0, V, (M,), generator=g, device=device)
+    beta = torch.rand((M, 1), generator=g, device=device) * 0.039 + 0.055
+    h = torch.randn((M, d), generator=g, device=device).mul_(30.0)
+    h.add_(beta * w[planted]).round_().clamp_(-127, 127)
+    hs = (torch.rand(M, generator=g, device=device) + 0.5) / 128.0
+    ws = (torch.rand(V, generator=g, device=device) * 0.2 + 0.9) / 128.0
+    tok = planted.view(B, k + 1)[:, :k].clone()
+    swap = torch.rand((B, k), generator=g, device=device) < 0.3
+    rnd = torch.randint(0, V, (B, k), generator=g, device=device)
+    tok = torch.where(swap, rnd, tok).to(torch.int32)
+    return {"hidden": h.to(torch.int8), "hidden_scale": hs.float(), "weight": w.to(torch.int8),
+            "weight_scale": ws.float(), "tokens": tok, "B": B, "k": k, "V": V, "d": d}
