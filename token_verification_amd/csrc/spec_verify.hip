@@ -2065,7 +2065,6 @@ __global__ __launch_bounds__(NTC) void commit_kernel(CommitParams C) {
 // decide_kernel makes the greedy decisions exactly as after pass 1.
 
 constexpr int HV = 256;                 // vocabulary rows per head tile
-constexpr int HM = 128;                 // hidden rows per head tile
 constexpr int HK = 128;                 // bytes of d per LDS stage
 constexpr int NTH = 256;                // threads per head workgroup
 
@@ -2110,14 +2109,13 @@ __device__ inline void head_merge(float& t1, float& t2, int& i1, int& fl, float 
 
 // Scale the accumulators of one lane to logits and reduce them to a top-2
 // per hidden row (EDGE: the tile reaches past V, so entries past it are skipped).
-template <bool EDGE>
-__device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4][2], int v0, int m0, int vw,
-                                     int mw, int r, int hi, float (&T1)[2], float (&T2)[2], int (&I1)[2],
-                                     int (&FL)[2]) {
-    float hsv[2];
+template <int MB, bool EDGE>
+__device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4][MB], int v0, int mrow, int vw,
+                                     int hi, float (&T1)[MB], float (&T2)[MB], int (&I1)[MB], int (&FL)[MB]) {
+    float hsv[MB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + 64 * mw + 32 * mb + r;
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = mrow + 32 * mb;
         hsv[mb] = m < H.M ? H.hs[m] : 0.0f;
         T1[mb] = -INFINITY; T2[mb] = -INFINITY; I1[mb] = 0x7fffffff; FL[mb] = 0;
     }
@@ -2131,7 +2129,7 @@ __device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4]
             wsv[q] = !EDGE || v < H.V ? H.ws[v] : 0.0f;
         }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int v = vbase + 8 * (q >> 2) + (q & 3);
@@ -2143,93 +2141,176 @@ __device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4]
     }
 }
 
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel(HeadParams H) {
-    __shared__ __attribute__((aligned(16))) unsigned char S[(HV + HM) * HK];
-    const int t = static_cast<int>(threadIdx.x), lane = t & 63, wv = t >> 6;
-    const int vw = wv & 1, mw = wv >> 1, r = lane & 31, hi = lane >> 5;
-    // tile of this workgroup: workgroup b runs on XCD b % 8, so tiles are
-    // dealt out in 8 contiguous runs, one per XCD
-    const unsigned nb = gridDim.x, b = blockIdx.x, per = nb / 8;
-    const unsigned tix = b < per * 8 ? (b % 8) * per + b / 8 : b;
-    const int vt = static_cast<int>(tix) / H.nmt, mt = static_cast<int>(tix) % H.nmt;
-    const int v0 = vt * HV, m0 = mt * HM;
-    const int nv = min(HV, H.V - v0), nm = min(HM, H.M - m0);
-    const unsigned d = static_cast<unsigned>(H.d);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(v0) * d, static_cast<unsigned>(nv) * d);
-    const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(m0) * d, static_cast<unsigned>(nm) * d);
+// The part of a head workgroup shared by both pipelines: its tile, the
+// staging of d-slices (global loads into registers, stores into a swizzled
+// LDS stage: chunk c of row q at chunk c ^ ((q >> 1) & 7), so that the MFMA
+// operand reads of 16 consecutive lanes, rows r..r+15 at one chunk, spread
+// over all LDS banks), the operand reads and the epilogue.
+template <int MB>
+struct HeadTile {
+    static constexpr int BM = 64 * MB;                     // hidden rows per tile
+    static constexpr int ST = (HV + BM) * HK;              // bytes per LDS stage
+    static constexpr int NW = HV / 32, NH = BM / 32;       // staged chunks per thread
+    int t, vw, mw, r, hi, vt, v0, m0, nm;
+    unsigned d;
+    __amdgpu_buffer_rsrc_t rw, rh;
+    int lr, pc, o_lane, ra, rb, sw;
+    u32x4 gw[NW], gh[NH];
+    i32x4 fa[2][4], fb[2][MB];
 
-    // staging: thread t moves chunk t & 7 of rows (t >> 3) + 32 j (d is a
-    // multiple of HK); rows past the tile's end load zeros (out of the resource)
-    const int lr = t >> 3, lc = t & 7;
-    const int pc = (lc ^ (lr & 7)) << 4;                    // swizzled chunk of that row
-    u32x4 gw[HV / 32], gh[HM / 32];
-    auto fetch = [&](int k0) {
-        const unsigned o0 = static_cast<unsigned>(lr) * d + static_cast<unsigned>(k0 + lc * 16);
+    __device__ HeadTile(const HeadParams& H) {
+        t = static_cast<int>(threadIdx.x);
+        const int lane = t & 63, wv = t >> 6;
+        vw = wv & 1; mw = wv >> 1; r = lane & 31; hi = lane >> 5;
+        // workgroup b runs on XCD b % 8, so tiles are dealt out in 8
+        // contiguous runs, one per XCD: the hidden-row tiles of a vocabulary
+        // tile run together and share its weights through that XCD's L2
+        const unsigned nb = gridDim.x, b = blockIdx.x, per = nb / 8;
+        const unsigned tix = b < per * 8 ? (b % 8) * per + b / 8 : b;
+        vt = static_cast<int>(tix) / H.nmt;
+        const int mt = static_cast<int>(tix) % H.nmt;
+        v0 = vt * HV; m0 = mt * BM;
+        const int nv = min(HV, H.V - v0);
+        nm = min(BM, H.M - m0);
+        d = static_cast<unsigned>(H.d);
+        rw = make_rsrc(H.w + static_cast<size_t>(v0) * d, static_cast<unsigned>(nv) * d);
+        rh = make_rsrc(H.h + static_cast<size_t>(m0) * d, static_cast<unsigned>(nm) * d);
+        // thread t stages chunk t & 7 of rows (t >> 3) + 32 j; rows past the
+        // tile's end load zeros (out of the resource)
+        lr = t >> 3;
+        const int lc = t & 7;
+        pc = (lc ^ ((lr >> 1) & 7)) << 4;
+        o_lane = lr * static_cast<int>(d) + lc * 16;
+        // operand rows of this lane: A (weights) 128*vw + 32*vb + r, B
+        // (hidden) 32*MB*mw + 32*mb + r; K step s reads chunk 2s + hi of them
+        ra = (128 * vw + r) * HK;
+        rb = HV * HK + (32 * MB * mw + r) * HK;
+        sw = (r >> 1) & 7;
+    }
+    __device__ void fetch(int k0) {
+        const unsigned o0 = static_cast<unsigned>(o_lane + k0);
 #pragma unroll
-        for (int j = 0; j < HV / 32; ++j)
+        for (int j = 0; j < NW; ++j)
             gw[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, static_cast<int>(o0 + 32u * j * d), 0, 0);
 #pragma unroll
-        for (int j = 0; j < HM / 32; ++j)
+        for (int j = 0; j < NH; ++j)
             gh[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(o0 + 32u * j * d), 0, 0);
-    };
+    }
+    __device__ void stash(unsigned char* B) const {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) *reinterpret_cast<u32x4*>(B + (lr + 32 * j) * HK + pc) = gw[j];
+#pragma unroll
+        for (int j = 0; j < NH; ++j) *reinterpret_cast<u32x4*>(B + HV * HK + (lr + 32 * j) * HK + pc) = gh[j];
+    }
+    __device__ void frag(const unsigned char* B, int s, int slot) {
+        const int co = ((2 * s + hi) ^ sw) << 4;
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) fa[slot][vb] = *reinterpret_cast<const i32x4*>(B + ra + vb * 32 * HK + co);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) fb[slot][mb] = *reinterpret_cast<const i32x4*>(B + rb + mb * 32 * HK + co);
+    }
+    __device__ void mma(i32x16 (&acc)[4][MB], int slot) const {
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[vb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][vb], fb[slot][mb], acc[vb][mb], 0, 0, 0);
+    }
+    // lane holds hidden row 32*MB*mw + 32*mb + r and, in register q of block
+    // vb, vocabulary row 128*vw + 32*vb + 8*(q/4) + 4*hi + q%4; S (the LDS
+    // stages, free again) carries the exchange between the vocabulary waves
+    __device__ void finish(const HeadParams& H, const i32x16 (&acc)[4][MB], unsigned char* S) const {
+        float T1[MB], T2[MB];
+        int I1[MB], FL[MB];
+        const int mrow = m0 + 32 * MB * mw + r;
+        if (v0 + HV <= H.V) head_epilogue<MB, false>(H, acc, v0, mrow, vw, hi, T1, T2, I1, FL);
+        else head_epilogue<MB, true>(H, acc, v0, mrow, vw, hi, T1, T2, I1, FL);
+        HeadRec* L = reinterpret_cast<HeadRec*>(S);        // [2][BM]: per vocabulary wave
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const float u1 = __shfl_xor(T1[mb], 32, 64), u2 = __shfl_xor(T2[mb], 32, 64);
+            const int j1 = __shfl_xor(I1[mb], 32, 64), g = __shfl_xor(FL[mb], 32, 64);
+            head_merge(T1[mb], T2[mb], I1[mb], FL[mb], u1, u2, j1, g);
+            if (hi == 0) L[vw * BM + 32 * MB * mw + 32 * mb + r] = HeadRec{T1[mb], T2[mb], I1[mb], FL[mb]};
+        }
+        __syncthreads();
+        if (t < nm) {
+            HeadRec o = L[t];
+            const HeadRec p = L[BM + t];
+            head_merge(o.t1, o.t2, o.idx, o.flags, p.t1, p.t2, p.idx, p.flags);
+            H.rec[static_cast<size_t>(m0 + t) * H.nvt + vt] = o;
+        }
+    }
+};
 
-    i32x16 acc[4][2];
+template <int MB>
+__device__ inline void acc_zero(i32x16 (&acc)[4][MB]) {
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[vb][mb][q] = 0;
-    // operand rows of this lane: A (weights) 128*vw + 32*vb + r, B (hidden)
-    // 64*mw + 32*mb + r; K step s reads chunk 2s + hi of them
-    const int ra = (128 * vw + r) * HK, rb = HV * HK + (64 * mw + r) * HK, sw = r & 7;
-    fetch(0);
-    for (int ks = 0; ks < H.nks; ++ks) {
-        __syncthreads();                                   // the last stage's reads are done
-#pragma unroll
-        for (int j = 0; j < HV / 32; ++j) *reinterpret_cast<u32x4*>(S + (lr + 32 * j) * HK + pc) = gw[j];
-#pragma unroll
-        for (int j = 0; j < HM / 32; ++j) *reinterpret_cast<u32x4*>(S + HV * HK + (lr + 32 * j) * HK + pc) = gh[j];
-        __syncthreads();
-        if (ks + 1 < H.nks) fetch((ks + 1) * HK);
+}
+
+// 256-row tiles: 2 x 2 waves of 128 x 128, one wave per SIMD. The
+// accumulators (256 registers) sit in AGPRs, which leaves room to read the
+// operands of the next K step while the MFMAs of this one run and to stage
+// the next d-slice into the other LDS buffer half-way through the stage, so
+// each stage needs a single barrier.
+__global__ __launch_bounds__(NTH) void head_kernel_wide(HeadParams H) {
+    using T = HeadTile<4>;
+    __shared__ __attribute__((aligned(16))) unsigned char S[2 * T::ST];
+    T w(H);
+    i32x16 acc[4][4];
+    acc_zero<4>(acc);
+    const int nks = H.nks;
+    w.fetch(0);
+    w.stash(S);
+    __syncthreads();
+    if (nks > 1) w.fetch(HK);
+    for (int ks = 0; ks < nks; ++ks) {
+        const unsigned char* cur = S + (ks & 1) * T::ST;
+        unsigned char* nxt = S + ((ks + 1) & 1) * T::ST;   // read in stage ks - 1, free since its barrier
+        w.frag(cur, 0, 0);
 #pragma unroll
         for (int s = 0; s < HK / 32; ++s) {
-            const int co = ((2 * s + hi) ^ sw) << 4;
-            i32x4 a[4], q[2];
+            if (s + 1 < HK / 32) w.frag(cur, s + 1, (s + 1) & 1);
+            w.mma(acc, s & 1);
+            if (s == 1 && ks + 1 < nks) {
+                w.stash(nxt);
+                if (ks + 2 < nks) w.fetch((ks + 2) * HK);
+            }
+        }
+        __syncthreads();
+    }
+    w.finish(H, acc, S);
+}
+
+// 128-row tiles: 2 x 2 waves of 128 x 64 at two waves per SIMD (two
+// workgroups per CU interleave), one LDS stage, the next d-slice in flight
+// during the MFMAs.
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_narrow(HeadParams H) {
+    using T = HeadTile<2>;
+    __shared__ __attribute__((aligned(16))) unsigned char S[T::ST];
+    T w(H);
+    i32x16 acc[4][2];
+    acc_zero<2>(acc);
+    const int nks = H.nks;
+    w.fetch(0);
+    for (int ks = 0; ks < nks; ++ks) {
+        __syncthreads();                                   // the last stage's reads are done
+        w.stash(S);
+        __syncthreads();
+        if (ks + 1 < nks) w.fetch((ks + 1) * HK);
 #pragma unroll
-            for (int vb = 0; vb < 4; ++vb) a[vb] = *reinterpret_cast<const i32x4*>(S + ra + vb * 32 * HK + co);
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) q[mb] = *reinterpret_cast<const i32x4*>(S + rb + mb * 32 * HK + co);
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    acc[vb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[vb], q[mb], acc[vb][mb], 0, 0, 0);
+        for (int s = 0; s < HK / 32; ++s) {
+            w.frag(S, s, 0);
+            w.mma(acc, 0);
         }
     }
-
-    // epilogue: lane holds hidden row 64*mw + 32*mb + r and, in register q of
-    // block vb, vocabulary row 128*vw + 32*vb + 8*(q/4) + 4*hi + q%4
-    float T1[2], T2[2];
-    int I1[2], FL[2];
-    if (v0 + HV <= H.V) head_epilogue<false>(H, acc, v0, m0, vw, mw, r, hi, T1, T2, I1, FL);
-    else head_epilogue<true>(H, acc, v0, m0, vw, mw, r, hi, T1, T2, I1, FL);
-    __syncthreads();                                       // the staging tiles are free
-    HeadRec* L = reinterpret_cast<HeadRec*>(S);            // [2][HM]: per vocabulary wave
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const float u1 = __shfl_xor(T1[mb], 32, 64), u2 = __shfl_xor(T2[mb], 32, 64);
-        const int j1 = __shfl_xor(I1[mb], 32, 64), g = __shfl_xor(FL[mb], 32, 64);
-        head_merge(T1[mb], T2[mb], I1[mb], FL[mb], u1, u2, j1, g);
-        if (hi == 0) L[vw * HM + 64 * mw + 32 * mb + r] = HeadRec{T1[mb], T2[mb], I1[mb], FL[mb]};
-    }
-    __syncthreads();
-    if (t < nm) {
-        HeadRec o = L[t];
-        const HeadRec p = L[HM + t];
-        head_merge(o.t1, o.t2, o.idx, o.flags, p.t1, p.t2, p.idx, p.flags);
-        H.rec[static_cast<size_t>(m0 + t) * H.nvt + vt] = o;
-    }
+    __syncthreads();                                       // the staging tile is free
+    w.finish(H, acc, S);
 }
 
 // One wave per hidden row: merge its vocabulary-tile records into the row's
@@ -2597,7 +2678,8 @@ int check_gate(const void* logits, int32_t n, int32_t V, int dtype, int rule, fl
 constexpr int HEAD_MAX_D = 65536;       // |acc| <= 2^14 * d stays inside int32
 
 struct HeadPlan {
-    int M, nvt, nmt;
+    int M, nvt;
+    int mb;                             // hidden-row blocks per wave: tiles of 64*mb rows
     size_t o_rec, o_tiles, total;
 };
 
@@ -2606,11 +2688,15 @@ bool make_head_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadPlan& p) {
     if (d < HK || d > HEAD_MAX_D || d % HK != 0) return false;
     const long long M = static_cast<long long>(B) * (k + 1);
     if (M > (1 << 26)) return false;
-    const long long nvt = (V + HV - 1) / HV, nmt = (M + HM - 1) / HM;
+    const long long nvt = (V + HV - 1) / HV;
+    // 256-row tiles reuse each staged operand more; 128-row tiles when they
+    // pad the hidden rows clearly less (e.g. 384 rows: 3 x 128, not 2 x 256)
+    const long long pad4 = (M + 255) / 256 * 256, pad2 = (M + 127) / 128 * 128;
+    p.mb = pad4 * 10 <= pad2 * 11 ? 4 : 2;
+    const long long nmt = (M + 64 * p.mb - 1) / (64 * p.mb);
     if (nvt * nmt >= (1ll << 31)) return false;
     p.M = static_cast<int>(M);
     p.nvt = static_cast<int>(nvt);
-    p.nmt = static_cast<int>(nmt);
     size_t o = 0;
     p.o_rec = o; o = align256(o + static_cast<size_t>(M) * nvt * sizeof(HeadRec));
     p.o_tiles = o; o = align256(o + 2 * static_cast<size_t>(M) * sizeof(TileRec));
@@ -2655,7 +2741,8 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     H.rec = reinterpret_cast<HeadRec*>(ws + plan.o_rec);
     H.tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
     H.M = plan.M; H.V = V; H.d = d;
-    H.nvt = plan.nvt; H.nmt = plan.nmt;
+    H.nvt = plan.nvt;
+    H.nmt = (plan.M + 64 * plan.mb - 1) / (64 * plan.mb);
     H.nks = d / HK;
     // the greedy decisions read the merged records as pass 1's, one slice per row
     Params P;
@@ -2677,7 +2764,9 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(head_kernel, dim3(static_cast<unsigned>(plan.nvt) * plan.nmt), dim3(NTH), 0, s, H);
+        const dim3 grid(static_cast<unsigned>(plan.nvt) * static_cast<unsigned>(H.nmt));
+        if (plan.mb == 4) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(NTH), 0, s, H);
+        else hipLaunchKernelGGL(head_kernel_narrow, grid, dim3(NTH), 0, s, H);
         e = hipGetLastError();
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
