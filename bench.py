@@ -450,6 +450,24 @@ def lmhead_bench(args, torch, np) -> int:
                         "GB_per_s": round(wbytes / (float(head.mean()) * 1e-3) / 1e9, 1)},
         "accepted_mean": round(float(acc[acc >= 0].mean()), 3) if (acc >= 0).any() else None,
     }
+    # context: the library int8 GEMM alone (hipBLASLt through torch._int_mm, int32
+    # logits written out), which an unfused path would follow with scaling and a verify
+    try:
+        wt = x["weight"].t()
+        for _ in range(3):
+            torch._int_mm(x["hidden"], wt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch._int_mm(x["hidden"], wt)
+        e1.record()
+        torch.cuda.synchronize()
+        lib_us = e0.elapsed_time(e1) / 10 * 1e3
+        line["library_gemm_context"] = {"op": "torch._int_mm(hidden, weight.t()) -> int32 [M, V]",
+                                        "us": round(lib_us, 1), "TOP/s": round(ops / lib_us / 1e6, 1)}
+    except Exception as ex:                                # context only; never fails the bench
+        line["library_gemm_context"] = {"error": f"{type(ex).__name__}: {str(ex)[:120]}"}
     if args.cpu_seconds > 0:
         from oracle.lmhead import lmhead_greedy_ref
         hh, hs, ww, wsc = (t.cpu().numpy() for t in a[:4])
