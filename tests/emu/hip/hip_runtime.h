@@ -73,6 +73,17 @@ inline emu_u32x4 emu_raw_load_b128(EmuRsrc r, int voff, int soff, int) {
 }
 #define __builtin_amdgcn_make_buffer_rsrc emu_make_rsrc
 #define __builtin_amdgcn_raw_buffer_load_b128 emu_raw_load_b128
+// 16-byte buffer load with the LDS as destination: lane l's bytes land at
+// the (wave-uniform) LDS address + 16*l; past the range they are zeros
+template <class LdsPtr>
+inline void emu_raw_load_lds(EmuRsrc r, LdsPtr lds, unsigned size, int voff, int soff, unsigned off, unsigned) {
+    const unsigned lane = threadIdx.x & 63u;
+    unsigned char* dst = (unsigned char*)(lds) + static_cast<size_t>(lane) * size;
+    const unsigned o = static_cast<unsigned>(voff) + static_cast<unsigned>(soff) + off;
+    if (static_cast<unsigned long long>(o) + size <= r.bytes) memcpy(dst, r.base + o, size);
+    else memset(dst, 0, size);
+}
+#define __builtin_amdgcn_raw_ptr_buffer_load_lds emu_raw_load_lds
 
 inline int __double2loint(double d) { uint64_t u; memcpy(&u, &d, 8); return static_cast<int>(static_cast<uint32_t>(u)); }
 inline int __double2hiint(double d) { uint64_t u; memcpy(&u, &d, 8); return static_cast<int>(static_cast<uint32_t>(u >> 32)); }

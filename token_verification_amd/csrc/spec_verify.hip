@@ -2253,37 +2253,102 @@ __device__ inline void acc_zero(i32x16 (&acc)[4][MB]) {
             for (int q = 0; q < 16; ++q) acc[vb][mb][q] = 0;
 }
 
-// 256-row tiles: 2 x 2 waves of 128 x 128, one wave per SIMD. The
-// accumulators (256 registers) sit in AGPRs, which leaves room to read the
-// operands of the next K step while the MFMAs of this one run and to stage
-// the next d-slice into the other LDS buffer half-way through the stage, so
-// each stage needs a single barrier.
+// 256-row tiles: 2 x 2 waves of 128 x 128, one wave per SIMD, the 256
+// accumulator registers in AGPRs. The d-slices go from memory straight into
+// LDS (16-byte buffer loads with the LDS as destination, no staging
+// registers): 64 bytes of d per stage, four 32 KB stage buffers, the loads of
+// three stages in flight. Stage layout: row q (256 weight rows, then 256
+// hidden rows) at q*64, its 16-byte chunk c at c ^ ((q >> 2) & 3), so the
+// operand reads of 16 consecutive lanes (rows r..r+15, one chunk) cover all
+// banks. One load instruction of a wave fills 16 rows (1 KB, lane l at
+// 16*l), so each lane fetches the chunk that lands at its position. Half-way
+// through stage ks each wave waits for its loads of stage ks + 1, a barrier
+// makes them visible (and certifies that stage ks - 1 is read by everyone),
+// the loads of stage ks + 3 go into that free buffer, and the first operands
+// of stage ks + 1 are read while the MFMAs of stage ks finish.
+constexpr int HKW = 64;                 // bytes of d per stage of the wide head kernel
+constexpr int WST = 2 * HV * HKW;       // bytes per stage: 256 weight rows + 256 hidden rows
+constexpr int WBUF = 4;                 // stage buffers
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __global__ __launch_bounds__(NTH) void head_kernel_wide(HeadParams H) {
-    using T = HeadTile<4>;
-    __shared__ __attribute__((aligned(16))) unsigned char S[2 * T::ST];
-    T w(H);
+    __shared__ __attribute__((aligned(16))) unsigned char S[WBUF * WST];
+    const int t = static_cast<int>(threadIdx.x), lane = t & 63, wv = t >> 6;
+    const int vw = wv & 1, mw = wv >> 1, r = lane & 31, hi = lane >> 5;
+    const unsigned nb = gridDim.x, b = blockIdx.x, per = nb / 8;
+    const unsigned tix = b < per * 8 ? (b % 8) * per + b / 8 : b;
+    const int vt = static_cast<int>(tix) / H.nmt, mt = static_cast<int>(tix) % H.nmt;
+    const int v0 = vt * HV, m0 = mt * HV;
+    const int nv = min(HV, H.V - v0), nm = min(HV, H.M - m0);
+    const unsigned d = static_cast<unsigned>(H.d);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(v0) * d, static_cast<unsigned>(nv) * d);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(m0) * d, static_cast<unsigned>(nm) * d);
+    // loads: instruction j of wave wv fills rows wv*64 + 16j .. +15 of each
+    // half; lane l lands on row + l/4, physical chunk l % 4, which holds
+    // logical chunk (l % 4) ^ ((l >> 4) & 3); rows past the tile load zeros
+    const unsigned lo = static_cast<unsigned>(wv * 64 + (lane >> 2)) * d +
+                        static_cast<unsigned>(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+    auto issue = [&](int ks) {
+        unsigned char* B = S + (ks % WBUF) * WST + wv * 64 * HKW;
+        const unsigned o = lo + static_cast<unsigned>(ks * HKW);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(B + j * 16 * HKW), 16,
+                                                     static_cast<int>(o + 16u * j * d), 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(B + HV * HKW + j * 16 * HKW), 16,
+                                                     static_cast<int>(o + 16u * j * d), 0, 0, 0);
+    };
+    // operands: A row 128*vw + 32*vb + r, B row 256 + 128*mw + 32*mb + r;
+    // K step s (two per stage) reads logical chunk 2s + hi
+    const int ra = (128 * vw + r) * HKW, rb = (HV + 128 * mw + r) * HKW, sw = (r >> 2) & 3;
+    i32x4 fa[2][4], fb[2][4];
+    auto frag = [&](int ks, int s, int slot) {
+        const unsigned char* B = S + (ks % WBUF) * WST;
+        const int co = ((2 * s + hi) ^ sw) << 4;
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) fa[slot][vb] = *reinterpret_cast<const i32x4*>(B + ra + vb * 32 * HKW + co);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) fb[slot][mb] = *reinterpret_cast<const i32x4*>(B + rb + mb * 32 * HKW + co);
+    };
     i32x16 acc[4][4];
     acc_zero<4>(acc);
-    const int nks = H.nks;
-    w.fetch(0);
-    w.stash(S);
-    __syncthreads();
-    if (nks > 1) w.fetch(HK);
-    for (int ks = 0; ks < nks; ++ks) {
-        const unsigned char* cur = S + (ks & 1) * T::ST;
-        unsigned char* nxt = S + ((ks + 1) & 1) * T::ST;   // read in stage ks - 1, free since its barrier
-        w.frag(cur, 0, 0);
+    auto mma = [&](int slot) {
 #pragma unroll
-        for (int s = 0; s < HK / 32; ++s) {
-            if (s + 1 < HK / 32) w.frag(cur, s + 1, (s + 1) & 1);
-            w.mma(acc, s & 1);
-            if (s == 1 && ks + 1 < nks) {
-                w.stash(nxt);
-                if (ks + 2 < nks) w.fetch((ks + 2) * HK);
-            }
+        for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                acc[vb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][vb], fb[slot][mb], acc[vb][mb], 0, 0, 0);
+    };
+    const int nks = H.d / HKW;
+    // s_waitcnt immediates: vmcnt <= n, expcnt and lgkmcnt unconstrained
+    constexpr int WAIT_VM16 = (1 << 14) | (7 << 4) | (15 << 8);   // vmcnt bits 5:4 live in 15:14
+    constexpr int WAIT_VM8 = 8 | (7 << 4) | (15 << 8), WAIT_VM0 = (7 << 4) | (15 << 8);
+    for (int q = 0; q < 3 && q < nks; ++q) issue(q);
+    // stage 0 done: this wave's later stages (8 loads each) may stay in flight
+    if (nks >= 3) __builtin_amdgcn_s_waitcnt(WAIT_VM16);
+    else if (nks == 2) __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+    else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    __syncthreads();
+    frag(0, 0, 0);
+    for (int ks = 0; ks < nks; ++ks) {
+        frag(ks, 1, 1);
+        mma(0);
+        if (ks + 1 < nks) {
+            // this wave's loads of stage ks + 1 are done once at most those of
+            // stage ks + 2 remain
+            if (ks + 2 < nks) __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+            else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+            __syncthreads();
+            if (ks + 3 < nks) issue(ks + 3);
+            frag(ks + 1, 0, 0);
         }
-        __syncthreads();
+        mma(1);
     }
+    __syncthreads();                                       // every wave is done with the stages
+    HeadTile<4> w(H);
     w.finish(H, acc, S);
 }
 
