@@ -2065,7 +2065,7 @@ __global__ __launch_bounds__(NTC) void commit_kernel(CommitParams C) {
 // decide_kernel makes the greedy decisions exactly as after pass 1.
 
 constexpr int HV = 256;                 // vocabulary rows per head tile
-constexpr int HK = 128;                 // bytes of d per LDS stage
+constexpr int HK = 128;                 // d must be a multiple of this
 constexpr int NTH = 256;                // threads per head workgroup
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -2086,7 +2086,6 @@ struct HeadParams {
     TileRec* tiles;                     // [2M], row m's merged record at 2m
     int M, V, d;
     int nvt, nmt;                       // vocabulary and hidden-row tiles
-    int nks;                            // LDS stages: d / HK
 };
 
 // Fold logit x of vocabulary index v (ascending within a lane) into a top-2
@@ -2141,80 +2140,26 @@ __device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4]
     }
 }
 
-// The part of a head workgroup shared by both pipelines: its tile, the
-// staging of d-slices (global loads into registers, stores into a swizzled
-// LDS stage: chunk c of row q at chunk c ^ ((q >> 1) & 7), so that the MFMA
-// operand reads of 16 consecutive lanes, rows r..r+15 at one chunk, spread
-// over all LDS banks), the operand reads and the epilogue.
+// What a head workgroup needs besides its main loop: its tile (workgroup b
+// runs on XCD b % 8, so tiles are dealt out in 8 contiguous runs, one per
+// XCD: the hidden-row tiles of a vocabulary tile run together and share its
+// weights through that XCD's L2) and the epilogue.
 template <int MB>
 struct HeadTile {
     static constexpr int BM = 64 * MB;                     // hidden rows per tile
-    static constexpr int ST = (HV + BM) * HK;              // bytes per LDS stage
-    static constexpr int NW = HV / 32, NH = BM / 32;       // staged chunks per thread
-    int t, vw, mw, r, hi, vt, v0, m0, nm;
-    unsigned d;
-    __amdgpu_buffer_rsrc_t rw, rh;
-    int lr, pc, o_lane, ra, rb, sw;
-    u32x4 gw[NW], gh[NH];
-    i32x4 fa[2][4], fb[2][MB];
+    int t, vw, mw, r, hi, vt, v0, m0, nv, nm;
 
-    __device__ HeadTile(const HeadParams& H) {
+    __device__ explicit HeadTile(const HeadParams& H) {
         t = static_cast<int>(threadIdx.x);
         const int lane = t & 63, wv = t >> 6;
         vw = wv & 1; mw = wv >> 1; r = lane & 31; hi = lane >> 5;
-        // workgroup b runs on XCD b % 8, so tiles are dealt out in 8
-        // contiguous runs, one per XCD: the hidden-row tiles of a vocabulary
-        // tile run together and share its weights through that XCD's L2
         const unsigned nb = gridDim.x, b = blockIdx.x, per = nb / 8;
         const unsigned tix = b < per * 8 ? (b % 8) * per + b / 8 : b;
         vt = static_cast<int>(tix) / H.nmt;
         const int mt = static_cast<int>(tix) % H.nmt;
         v0 = vt * HV; m0 = mt * BM;
-        const int nv = min(HV, H.V - v0);
+        nv = min(HV, H.V - v0);
         nm = min(BM, H.M - m0);
-        d = static_cast<unsigned>(H.d);
-        rw = make_rsrc(H.w + static_cast<size_t>(v0) * d, static_cast<unsigned>(nv) * d);
-        rh = make_rsrc(H.h + static_cast<size_t>(m0) * d, static_cast<unsigned>(nm) * d);
-        // thread t stages chunk t & 7 of rows (t >> 3) + 32 j; rows past the
-        // tile's end load zeros (out of the resource)
-        lr = t >> 3;
-        const int lc = t & 7;
-        pc = (lc ^ ((lr >> 1) & 7)) << 4;
-        o_lane = lr * static_cast<int>(d) + lc * 16;
-        // operand rows of this lane: A (weights) 128*vw + 32*vb + r, B
-        // (hidden) 32*MB*mw + 32*mb + r; K step s reads chunk 2s + hi of them
-        ra = (128 * vw + r) * HK;
-        rb = HV * HK + (32 * MB * mw + r) * HK;
-        sw = (r >> 1) & 7;
-    }
-    __device__ void fetch(int k0) {
-        const unsigned o0 = static_cast<unsigned>(o_lane + k0);
-#pragma unroll
-        for (int j = 0; j < NW; ++j)
-            gw[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, static_cast<int>(o0 + 32u * j * d), 0, 0);
-#pragma unroll
-        for (int j = 0; j < NH; ++j)
-            gh[j] = __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(o0 + 32u * j * d), 0, 0);
-    }
-    __device__ void stash(unsigned char* B) const {
-#pragma unroll
-        for (int j = 0; j < NW; ++j) *reinterpret_cast<u32x4*>(B + (lr + 32 * j) * HK + pc) = gw[j];
-#pragma unroll
-        for (int j = 0; j < NH; ++j) *reinterpret_cast<u32x4*>(B + HV * HK + (lr + 32 * j) * HK + pc) = gh[j];
-    }
-    __device__ void frag(const unsigned char* B, int s, int slot) {
-        const int co = ((2 * s + hi) ^ sw) << 4;
-#pragma unroll
-        for (int vb = 0; vb < 4; ++vb) fa[slot][vb] = *reinterpret_cast<const i32x4*>(B + ra + vb * 32 * HK + co);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fb[slot][mb] = *reinterpret_cast<const i32x4*>(B + rb + mb * 32 * HK + co);
-    }
-    __device__ void mma(i32x16 (&acc)[4][MB], int slot) const {
-#pragma unroll
-        for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[vb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][vb], fb[slot][mb], acc[vb][mb], 0, 0, 0);
     }
     // lane holds hidden row 32*MB*mw + 32*mb + r and, in register q of block
     // vb, vocabulary row 128*vw + 32*vb + 8*(q/4) + 4*hi + q%4; S (the LDS
@@ -2253,129 +2198,115 @@ __device__ inline void acc_zero(i32x16 (&acc)[4][MB]) {
             for (int q = 0; q < 16; ++q) acc[vb][mb][q] = 0;
 }
 
-// 256-row tiles: 2 x 2 waves of 128 x 128, one wave per SIMD, the 256
-// accumulator registers in AGPRs. The d-slices go from memory straight into
-// LDS (16-byte buffer loads with the LDS as destination, no staging
-// registers): 64 bytes of d per stage, four 32 KB stage buffers, the loads of
-// three stages in flight. Stage layout: row q (256 weight rows, then 256
-// hidden rows) at q*64, its 16-byte chunk c at c ^ ((q >> 2) & 3), so the
-// operand reads of 16 consecutive lanes (rows r..r+15, one chunk) cover all
-// banks. One load instruction of a wave fills 16 rows (1 KB, lane l at
+// The main loop: 2 x 2 waves of 128 x 32*MB. The d-slices go from memory
+// straight into LDS (16-byte buffer loads with the LDS as destination, no
+// staging registers): 64 bytes of d per stage, NBUF stage buffers, the loads
+// of NBUF - 1 stages in flight. Stage layout: row q (256 weight rows, then
+// 64*MB hidden rows) at q*64, its 16-byte chunk c at c ^ ((q >> 2) & 3), so
+// the operand reads of 16 consecutive lanes (rows r..r+15, one chunk) cover
+// all banks. One load instruction of a wave fills 16 rows (1 KB, lane l at
 // 16*l), so each lane fetches the chunk that lands at its position. Half-way
-// through stage ks each wave waits for its loads of stage ks + 1, a barrier
-// makes them visible (and certifies that stage ks - 1 is read by everyone),
-// the loads of stage ks + 3 go into that free buffer, and the first operands
-// of stage ks + 1 are read while the MFMAs of stage ks finish.
-constexpr int HKW = 64;                 // bytes of d per stage of the wide head kernel
-constexpr int WST = 2 * HV * HKW;       // bytes per stage: 256 weight rows + 256 hidden rows
-constexpr int WBUF = 4;                 // stage buffers
+// through stage ks each wave waits for its own loads of stage ks + 1, a
+// barrier makes everyone's visible (and certifies that stage ks - 1 has been
+// read by all waves), the loads of stage ks + NBUF - 1 go into that free
+// buffer, and the first operands of stage ks + 1 are read while the MFMAs of
+// stage ks finish.
+constexpr int HKW = 64;                 // bytes of d per stage
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__global__ __launch_bounds__(NTH) void head_kernel_wide(HeadParams H) {
-    __shared__ __attribute__((aligned(16))) unsigned char S[WBUF * WST];
-    const int t = static_cast<int>(threadIdx.x), lane = t & 63, wv = t >> 6;
-    const int vw = wv & 1, mw = wv >> 1, r = lane & 31, hi = lane >> 5;
-    const unsigned nb = gridDim.x, b = blockIdx.x, per = nb / 8;
-    const unsigned tix = b < per * 8 ? (b % 8) * per + b / 8 : b;
-    const int vt = static_cast<int>(tix) / H.nmt, mt = static_cast<int>(tix) % H.nmt;
-    const int v0 = vt * HV, m0 = mt * HV;
-    const int nv = min(HV, H.V - v0), nm = min(HV, H.M - m0);
+// s_waitcnt immediate: vmcnt <= n (bits 3:0 and 15:14), expcnt and lgkmcnt unconstrained
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// wait until at most `stages` later stages (LPW loads each) of this wave are in flight
+template <int LPW>
+__device__ inline void wait_stages(int stages) {
+    if (stages >= 2) __builtin_amdgcn_s_waitcnt(vm_wait(2 * LPW));
+    else if (stages == 1) __builtin_amdgcn_s_waitcnt(vm_wait(LPW));
+    else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+}
+
+template <int MB, int NBUF>
+__device__ __attribute__((always_inline)) inline void head_main(const HeadParams& H) {
+    constexpr int BM = 64 * MB;
+    constexpr int ST = (HV + BM) * HKW;                    // bytes per stage
+    constexpr int LPW = 4 + MB;                            // load instructions per wave and stage
+    constexpr int P = NBUF - 1;                            // stages in flight
+    static_assert(2 * LPW <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) unsigned char S[NBUF * ST];
+    const HeadTile<MB> w(H);
+    const int lane = w.t & 63, wv = w.t >> 6;
     const unsigned d = static_cast<unsigned>(H.d);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(v0) * d, static_cast<unsigned>(nv) * d);
-    const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(m0) * d, static_cast<unsigned>(nm) * d);
-    // loads: instruction j of wave wv fills rows wv*64 + 16j .. +15 of each
-    // half; lane l lands on row + l/4, physical chunk l % 4, which holds
-    // logical chunk (l % 4) ^ ((l >> 4) & 3); rows past the tile load zeros
-    const unsigned lo = static_cast<unsigned>(wv * 64 + (lane >> 2)) * d +
-                        static_cast<unsigned>(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(w.v0) * d, static_cast<unsigned>(w.nv) * d);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(w.m0) * d, static_cast<unsigned>(w.nm) * d);
+    // loads: weight instruction j of wave wv fills rows wv*64 + 16j .. +15,
+    // hidden instruction j rows wv*16*MB + 16j .. +15; lane l lands on row
+    // + l/4, physical chunk l % 4, which holds logical chunk
+    // (l % 4) ^ ((l >> 4) & 3); rows past the tile load zeros
+    const unsigned cl = static_cast<unsigned>(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+    const unsigned low = static_cast<unsigned>(wv * 64 + (lane >> 2)) * d + cl;
+    const unsigned loh = static_cast<unsigned>(wv * 16 * MB + (lane >> 2)) * d + cl;
     auto issue = [&](int ks) {
-        unsigned char* B = S + (ks % WBUF) * WST + wv * 64 * HKW;
-        const unsigned o = lo + static_cast<unsigned>(ks * HKW);
+        unsigned char* B = S + (ks % NBUF) * ST;
+        const unsigned k0 = static_cast<unsigned>(ks * HKW);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(B + j * 16 * HKW), 16,
-                                                     static_cast<int>(o + 16u * j * d), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(B + (wv * 64 + 16 * j) * HKW), 16,
+                                                     static_cast<int>(low + k0 + 16u * j * d), 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(B + HV * HKW + j * 16 * HKW), 16,
-                                                     static_cast<int>(o + 16u * j * d), 0, 0, 0);
+        for (int j = 0; j < MB; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(B + (HV + wv * 16 * MB + 16 * j) * HKW), 16,
+                                                     static_cast<int>(loh + k0 + 16u * j * d), 0, 0, 0);
     };
-    // operands: A row 128*vw + 32*vb + r, B row 256 + 128*mw + 32*mb + r;
+    // operands: A row 128*vw + 32*vb + r, B row 256 + 32*MB*mw + 32*mb + r;
     // K step s (two per stage) reads logical chunk 2s + hi
-    const int ra = (128 * vw + r) * HKW, rb = (HV + 128 * mw + r) * HKW, sw = (r >> 2) & 3;
-    i32x4 fa[2][4], fb[2][4];
+    const int ra = (128 * w.vw + w.r) * HKW, rb = (HV + 32 * MB * w.mw + w.r) * HKW, sw = (w.r >> 2) & 3;
+    i32x4 fa[2][4], fb[2][MB];
     auto frag = [&](int ks, int s, int slot) {
-        const unsigned char* B = S + (ks % WBUF) * WST;
-        const int co = ((2 * s + hi) ^ sw) << 4;
+        const unsigned char* B = S + (ks % NBUF) * ST;
+        const int co = ((2 * s + w.hi) ^ sw) << 4;
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb) fa[slot][vb] = *reinterpret_cast<const i32x4*>(B + ra + vb * 32 * HKW + co);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) fb[slot][mb] = *reinterpret_cast<const i32x4*>(B + rb + mb * 32 * HKW + co);
+        for (int mb = 0; mb < MB; ++mb) fb[slot][mb] = *reinterpret_cast<const i32x4*>(B + rb + mb * 32 * HKW + co);
     };
-    i32x16 acc[4][4];
-    acc_zero<4>(acc);
+    i32x16 acc[4][MB];
+    acc_zero<MB>(acc);
     auto mma = [&](int slot) {
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
                 acc[vb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][vb], fb[slot][mb], acc[vb][mb], 0, 0, 0);
     };
-    const int nks = H.d / HKW;
-    // s_waitcnt immediates: vmcnt <= n, expcnt and lgkmcnt unconstrained
-    constexpr int WAIT_VM16 = (1 << 14) | (7 << 4) | (15 << 8);   // vmcnt bits 5:4 live in 15:14
-    constexpr int WAIT_VM8 = 8 | (7 << 4) | (15 << 8), WAIT_VM0 = (7 << 4) | (15 << 8);
-    for (int q = 0; q < 3 && q < nks; ++q) issue(q);
-    // stage 0 done: this wave's later stages (8 loads each) may stay in flight
-    if (nks >= 3) __builtin_amdgcn_s_waitcnt(WAIT_VM16);
-    else if (nks == 2) __builtin_amdgcn_s_waitcnt(WAIT_VM8);
-    else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    const int nks = H.d / HKW;                             // >= 2
+    for (int q = 0; q < P && q < nks; ++q) issue(q);
+    wait_stages<LPW>(min(P, nks) - 1);                     // stage 0 is in
     __syncthreads();
     frag(0, 0, 0);
     for (int ks = 0; ks < nks; ++ks) {
         frag(ks, 1, 1);
         mma(0);
         if (ks + 1 < nks) {
-            // this wave's loads of stage ks + 1 are done once at most those of
-            // stage ks + 2 remain
-            if (ks + 2 < nks) __builtin_amdgcn_s_waitcnt(WAIT_VM8);
-            else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+            wait_stages<LPW>(min(P - 2, nks - 2 - ks));    // stage ks + 1 is in
             __syncthreads();
-            if (ks + 3 < nks) issue(ks + 3);
+            if (ks + P < nks) issue(ks + P);
             frag(ks + 1, 0, 0);
         }
         mma(1);
     }
     __syncthreads();                                       // every wave is done with the stages
-    HeadTile<4> w(H);
     w.finish(H, acc, S);
 }
 
-// 128-row tiles: 2 x 2 waves of 128 x 64 at two waves per SIMD (two
-// workgroups per CU interleave), one LDS stage, the next d-slice in flight
-// during the MFMAs.
+// 256-row tiles: 128 x 128 per wave, one wave per SIMD (256 accumulator
+// registers in AGPRs), four 32 KB stage buffers.
+__global__ __launch_bounds__(NTH) void head_kernel_wide(HeadParams H) { head_main<4, 4>(H); }
+
+// 128-row tiles: 128 x 64 per wave, two waves per SIMD (two workgroups per
+// CU interleave), three 24 KB stage buffers.
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_narrow(HeadParams H) {
-    using T = HeadTile<2>;
-    __shared__ __attribute__((aligned(16))) unsigned char S[T::ST];
-    T w(H);
-    i32x16 acc[4][2];
-    acc_zero<2>(acc);
-    const int nks = H.nks;
-    w.fetch(0);
-    for (int ks = 0; ks < nks; ++ks) {
-        __syncthreads();                                   // the last stage's reads are done
-        w.stash(S);
-        __syncthreads();
-        if (ks + 1 < nks) w.fetch((ks + 1) * HK);
-#pragma unroll
-        for (int s = 0; s < HK / 32; ++s) {
-            w.frag(S, s, 0);
-            w.mma(acc, 0);
-        }
-    }
-    __syncthreads();                                       // the staging tile is free
-    w.finish(H, acc, S);
+    head_main<2, 3>(H);
 }
 
 // One wave per hidden row: merge its vocabulary-tile records into the row's
@@ -2808,7 +2739,6 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     H.M = plan.M; H.V = V; H.d = d;
     H.nvt = plan.nvt;
     H.nmt = (plan.M + 64 * plan.mb - 1) / (64 * plan.mb);
-    H.nks = d / HK;
     // the greedy decisions read the merged records as pass 1's, one slice per row
     Params P;
     memset(&P, 0, sizeof P);
