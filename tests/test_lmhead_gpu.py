@@ -71,6 +71,9 @@ def oracle_of(x, rows=None):
     (7, 0, 257, 128),           # k = 0: only the bonus argmax
     (2, 64, 300, 384),          # the largest k (decision over more than 64 rows)
     (40, 5, 32000, 1024),       # 8 XCD runs of tiles and a remainder
+    (64, 3, 1000, 128),         # 256-row tiles with the fewest stages (two)
+    (64, 3, 2000, 256),         # 256-row tiles, four stages (the prologue fills three)
+    (96, 3, 3000, 640),         # 384 rows: 128-row tiles, ten stages
 ])
 def test_lmhead_matches_oracle(B, k, V, d):
     say("lmhead", B, k, V, d)

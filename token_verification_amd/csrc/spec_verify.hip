@@ -9,7 +9,10 @@
 // ragged drafts over more than 1024 batch rows add rows_kernel first); no
 // workgroup ever waits on another (every hand-over between them is a kernel
 // boundary). The same file holds the confidence gate (gate_kernel,
-// gate_row_kernel) and the commit step (commit_kernel).
+// gate_row_kernel), the commit step (commit_kernel) and greedy verification
+// fused with an int8 LM head on the matrix cores (head_kernel_wide /
+// head_kernel_narrow, head_merge_kernel, then decide_kernel; described at
+// those kernels).
 //
 //  1. scan_kernel -- one resident round of workgroups, each streaming an equal
 //     slice of the flattened (row, element) space (a slice may span row
