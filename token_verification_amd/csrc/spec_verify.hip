@@ -2047,17 +2047,15 @@ __global__ __launch_bounds__(NTC) void commit_kernel(CommitParams C) {
 //     acc[m, v]   = sum_j h[m, j] * w[v, j]                       (int32, exact)
 //     logit[m, v] = fl32(fl32(float(acc[m, v]) * h_scale[m]) * w_scale[v]),
 // and the greedy decision needs of every row only its first argmax and its
-// top-2 values. head_kernel computes the logits tile by tile on the matrix
-// cores and reduces them in registers, so they never reach memory:
-//   * one workgroup per 256-vocabulary x 128-hidden-row tile, 2 x 2 waves of
-//     128 x 64; the vocabulary rows are the MFMA's A operand, so each lane's
-//     accumulators hold 16 vocabulary entries of ONE hidden row and the row
-//     reduction is per lane (then one exchange with lane ^ 32 and one through
-//     LDS between the two vocabulary waves);
-//   * d (a multiple of 128) is staged through LDS 128 bytes at a time (32 KB of weights, 16 KB of
-//     hidden states), the 16-byte chunk index XOR-swizzled with the row so
-//     that the MFMA operand reads of any 8 consecutive lanes hit distinct
-//     banks; the next stage's global loads are in flight during the MFMAs;
+// top-2 values. The head kernels compute the logits tile by tile on the matrix
+// cores and reduce them in registers, so they never reach memory:
+//   * one workgroup per 256-vocabulary x (64*MB)-hidden-row tile (MB = 4 or
+//     2), 2 x 2 waves; the vocabulary rows are the MFMA's A operand, so each
+//     lane's accumulators hold 16 vocabulary entries of ONE hidden row and
+//     the row reduction is per lane (then one exchange with lane ^ 32 and one
+//     through LDS between the two vocabulary waves);
+//   * d (a multiple of 128) streams through LDS in 64-byte stages loaded
+//     straight into LDS, several stages in flight (head_main);
 //   * since the products are exact integers, the order of the d-sum is free:
 //     the K layout of the MFMA only has to be the same for both operands;
 //   * workgroups are numbered so that the hidden-row tiles of one vocabulary
