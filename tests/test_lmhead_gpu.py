@@ -157,3 +157,33 @@ def test_lmhead_graph_replays_and_timed_entry():
     t = [evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2])]
     say("phases ms", [round(v, 4) for v in t])
     assert t[0] > 0 and t[1] >= 0
+
+
+@pytest.mark.parametrize("B,k", [(1, 0), (64, 3)])     # 128-row and 256-row tiles
+def test_lmhead_float32_order_decides_the_argmax(B, k):
+    # Vocabulary rows 0 and 1 share their int8 weights; every hidden row gives
+    # acc = 680962 against them. With hs = 0.006459721829742193 the two float32
+    # products give 5408.34033203125 for row 0 (ws 1.2294964790344238) and
+    # 5408.3408203125 for row 1 (ws 1.2294965982437134), one ulp apart; one
+    # rounding of the exact product, or the swapped order, would give row 1
+    # 5408.34033203125 too, and the tie would go to row 0.
+    V, d = 300, 128
+    pairs = [(127, 127)] * 42 + [(127, 27), (115, 1)]
+    M = B * (k + 1)
+    h = torch.zeros((M, d), dtype=torch.int8)
+    w = torch.zeros((V, d), dtype=torch.int8)
+    for j, (x, y) in enumerate(pairs):
+        h[:, j] = x
+        w[0, j] = w[1, j] = y
+    hs = torch.full((M,), 0.006459721829742193, dtype=torch.float32)
+    ws = torch.full((V,), 1.0, dtype=torch.float32)
+    ws[0], ws[1] = 1.2294964790344238, 1.2294965982437134
+    tok = torch.ones((B, k), dtype=torch.int32)
+    x = {"hidden": h, "hidden_scale": hs, "weight": w, "weight_scale": ws, "tokens": tok, "B": B, "k": k,
+         "V": V, "d": d}
+    r = run(x)
+    torch.cuda.synchronize()
+    check(r, oracle_of(x))
+    assert r.accepted_len.tolist() == [k] * B
+    assert (r.out_tokens.cpu() == 1).all()
+    assert (r.gap.cpu() == 0.00048828125).all()

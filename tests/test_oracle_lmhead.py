@@ -47,6 +47,23 @@ def test_scaling_worked_example():
     assert got[0, 0] == (np.float32(7.0) * hs) * ws
 
 
+def test_two_float32_roundings_not_one():
+    # acc = 680962: the oracle rounds after each product,
+    # fl32(fl32(acc * hs) * ws) = 5408.3408203125, where one rounding of the
+    # exact product gives 5408.34033203125, and so does the swapped order.
+    hs = np.float32(0.006459721829742193)
+    ws = np.float32(1.2294965982437134)
+    pairs = [(127, 127)] * 42 + [(127, 27), (115, 1)]      # 42 * 16129 + 3429 + 115
+    d = 128
+    h = np.zeros((1, d), np.int8)
+    w = np.zeros((1, d), np.int8)
+    for j, (x, y) in enumerate(pairs):
+        h[0, j], w[0, j] = x, y
+    assert int((h.astype(np.int64) @ w.astype(np.int64).T)[0, 0]) == 680962
+    got = lmhead_logits_ref(h, np.array([hs]), w, np.array([ws]))[0, 0]
+    assert float(got) == 5408.3408203125
+
+
 def test_greedy_on_the_logits():
     rng = np.random.default_rng(1)
     B, k, V, d = 4, 3, 50, 32
