@@ -2304,6 +2304,9 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
 // registers in AGPRs), four 32 KB stage buffers.
 __global__ __launch_bounds__(NTH) void head_kernel_wide(HeadParams H) { head_main<4, 4>(H); }
 
+// 192-row tiles: 128 x 96 per wave, one wave per SIMD, four 28 KB stage buffers.
+__global__ __launch_bounds__(NTH) void head_kernel_mid(HeadParams H) { head_main<3, 4>(H); }
+
 // 128-row tiles: 128 x 64 per wave, two waves per SIMD (two workgroups per
 // CU interleave), three 24 KB stage buffers.
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_narrow(HeadParams H) {
@@ -2686,10 +2689,12 @@ bool make_head_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadPlan& p) {
     const long long M = static_cast<long long>(B) * (k + 1);
     if (M > (1 << 26)) return false;
     const long long nvt = (V + HV - 1) / HV;
-    // 256-row tiles reuse each staged operand more; 128-row tiles when they
-    // pad the hidden rows clearly less (e.g. 384 rows: 3 x 128, not 2 x 256)
-    const long long pad4 = (M + 255) / 256 * 256, pad2 = (M + 127) / 128 * 128;
-    p.mb = pad4 * 10 <= pad2 * 11 ? 4 : 2;
+    // wider tiles reuse each staged operand more; a narrower one when it pads
+    // the hidden rows clearly less (e.g. 384 rows: 2 x 192, not 2 x 256)
+    const long long pad4 = (M + 255) / 256 * 256, pad3 = (M + 191) / 192 * 192, pad2 = (M + 127) / 128 * 128;
+    if (pad4 * 10 <= (pad3 < pad2 ? pad3 : pad2) * 11) p.mb = 4;
+    else if (pad3 * 10 <= pad2 * 11) p.mb = 3;
+    else p.mb = 2;
     const long long nmt = (M + 64 * p.mb - 1) / (64 * p.mb);
     if (nvt * nmt >= (1ll << 31)) return false;
     p.M = static_cast<int>(M);
@@ -2762,6 +2767,7 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     if (e == hipSuccess) {
         const dim3 grid(static_cast<unsigned>(plan.nvt) * static_cast<unsigned>(H.nmt));
         if (plan.mb == 4) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(NTH), 0, s, H);
+        else if (plan.mb == 3) hipLaunchKernelGGL(head_kernel_mid, grid, dim3(NTH), 0, s, H);
         else hipLaunchKernelGGL(head_kernel_narrow, grid, dim3(NTH), 0, s, H);
         e = hipGetLastError();
     }
