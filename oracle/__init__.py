@@ -62,6 +62,10 @@ def _load():
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.spec_verify_ref_ragged.restype = ctypes.c_int
+        lib.spec_verify_ref_full.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             P, P, P, P, P, P, P, P, ctypes.c_double, P, P, P, ctypes.c_int]
+        lib.spec_verify_ref_full.restype = ctypes.c_int
         lib.spec_verify_ref_max_threads.restype = ctypes.c_int
         lib.spec_gate_ref.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_float, P, P, P, P]
@@ -86,6 +90,14 @@ class RefResult:
     flags: np.ndarray          # [B] int32, bit 0: residual mass was zero; bit 1: the
                                # residual draw is within 1e-13 (of p's total mass) of a
                                # CDF boundary, below what fp64 resolves
+    # Alternatives (only with flip_delta > 0; else None): the outcome with the
+    # acceptance test nearest its boundary decided the other way (rows whose
+    # smallest margin is below flip_delta; other rows repeat the outcome), and
+    # the token the final draw gives with its uniform across the nearest CDF
+    # edge.
+    alt_accepted_len: Optional[np.ndarray] = None   # [B] int32
+    alt_out_tokens: Optional[np.ndarray] = None     # [B,k+1] int32
+    alt_token: Optional[np.ndarray] = None          # [B] int32
 
     def flagged(self, delta_acc: float, delta_cdf: float) -> np.ndarray:
         return (self.margin_acc < delta_acc) | (self.margin_cdf < delta_cdf) | (self.flags != 0)
@@ -124,11 +136,13 @@ def _np(x, dt):
 
 
 def spec_verify_ref(target, draft, tokens, uniforms, temperature: float, mode: int,
-                    dtype: Optional[int] = None, threads: int = 0, draft_len=None) -> RefResult:
+                    dtype: Optional[int] = None, threads: int = 0, draft_len=None,
+                    flip_delta: float = 0.0) -> RefResult:
     """Run the oracle on host arrays shaped [B,k+1,V], [B,k,V], [B,k], [B,k+1,2].
 
     draft_len: optional [B] int32, the number of draft positions each batch row
-    verifies (ragged drafts; None means k for every row).
+    verifies (ragged drafts; None means k for every row). flip_delta > 0 also
+    returns the alternative outcomes of near-tie rows (see RefResult).
     """
     if dtype is None:
         dtype = BF16 if str(getattr(target, "dtype", "")) in ("torch.bfloat16", "uint16") else F32
@@ -161,13 +175,18 @@ def spec_verify_ref(target, draft, tokens, uniforms, temperature: float, mode: i
     dl = _np(draft_len, np.int32)
     if dl is not None:
         assert dl.shape == (B,), dl.shape
-    rc = _load().spec_verify_ref_ragged(ptr(tgt), ptr(dft), ptr(tok), ptr(dl), ptr(uni),
-                                        ctypes.c_float(temperature), int(mode), int(B), int(k),
-                                        int(V), int(dtype), ptr(acc), ptr(out), ptr(gap), ptr(pt),
-                                        ptr(qt), ptr(ma), ptr(mc), ptr(fl), int(threads))
+    alts = flip_delta > 0
+    aa = np.zeros(B, np.int32) if alts else None
+    ao = np.zeros((B, k + 1), np.int32) if alts else None
+    at = np.zeros(B, np.int32) if alts else None
+    rc = _load().spec_verify_ref_full(ptr(tgt), ptr(dft), ptr(tok), ptr(dl), ptr(uni),
+                                      ctypes.c_float(temperature), int(mode), int(B), int(k),
+                                      int(V), int(dtype), ptr(acc), ptr(out), ptr(gap), ptr(pt),
+                                      ptr(qt), ptr(ma), ptr(mc), ptr(fl), float(flip_delta),
+                                      ptr(aa), ptr(ao), ptr(at), int(threads))
     if rc != 0:
         raise ValueError(f"spec_verify_ref rejected its arguments (rc={rc})")
-    return RefResult(acc, out, gap, pt, qt, ma, mc, fl)
+    return RefResult(acc, out, gap, pt, qt, ma, mc, fl, aa, ao, at)
 
 
 MARGIN, CERTIFIED = 0, 1

@@ -45,11 +45,14 @@ def _cdf_breaks(w):
     return list(c / c[-1]) if c[-1] > 0 else []
 
 
-def enumerate_k1(target, draft, T):
-    """Exact distribution of (out0, out1) of the oracle for k = 1.
+def cells_k1(target, draft, T):
+    """The enumeration's inputs for k = 1: one batch row per cell.
 
-    target: float32 [2, V] logits; draft: float32 [1, V]. Returns
-    (dist0 [V], dist1_accepted [V], accept_prob) as float64 arrays.
+    target: float32 [2, V] logits; draft: float32 [1, V]. Returns (target
+    [n,2,V], draft [n,1,V], tokens [n,1] int32, uniforms [n,2,2] float32,
+    weights [n] float64): every draft token x~ with q(x~) > 0 times every cell
+    of the uniforms' partition that matters on its branch, each probed at its
+    float32 midpoint and weighted by q(x~) times the cell lengths.
     """
     target = np.asarray(target, np.float32)
     draft = np.asarray(draft, np.float32)
@@ -83,16 +86,31 @@ def enumerate_k1(target, draft, T):
     uni = np.zeros((n, 2, 2), np.float32)
     for j, (_, u00, u01, u11) in enumerate(rows):
         uni[j, 0, 0], uni[j, 0, 1], uni[j, 1, 1] = u00, u01, u11
-    res = oracle.spec_verify_ref(tgt, dft, tok, uni, T, oracle.SAMPLE, dtype=oracle.F32)
+    return tgt, dft, tok, uni, np.array(weights, np.float64)
+
+
+def distribution(out_tokens, accepted_len, weights, V):
+    """(dist0, dist1_accepted, accept_prob) of weighted outcomes of cells_k1 rows."""
     dist0 = np.zeros(V)
     dist1 = np.zeros(V)
     acc = 0.0
-    for j in range(n):
-        dist0[res.out_tokens[j, 0]] += weights[j]
-        if res.accepted_len[j] == 1:
-            dist1[res.out_tokens[j, 1]] += weights[j]
+    for j in range(len(weights)):
+        dist0[out_tokens[j, 0]] += weights[j]
+        if accepted_len[j] == 1:
+            dist1[out_tokens[j, 1]] += weights[j]
             acc += weights[j]
     return dist0, dist1, acc
+
+
+def enumerate_k1(target, draft, T):
+    """Exact distribution of (out0, out1) of the oracle for k = 1.
+
+    target: float32 [2, V] logits; draft: float32 [1, V]. Returns
+    (dist0 [V], dist1_accepted [V], accept_prob) as float64 arrays.
+    """
+    tgt, dft, tok, uni, weights = cells_k1(target, draft, T)
+    res = oracle.spec_verify_ref(tgt, dft, tok, uni, T, oracle.SAMPLE, dtype=oracle.F32)
+    return distribution(res.out_tokens, res.accepted_len, weights, tgt.shape[2])
 
 
 def closed_form(target, draft, T):

@@ -160,14 +160,18 @@ static int ref_argmax(const void* base, int dtype, size_t off, int V)
 /*
  * Inverse-CDF draw from the non-negative weights w[0..V-1] with uniform u:
  * the smallest j with C_j > u*Z. Returns -1 when Z <= 0. *margin receives the
- * normalized distance of u to the chosen interval's nearest edge.
+ * normalized distance of u to the chosen interval's nearest edge, *alt the
+ * token on the other side of that edge (the nearest index with positive
+ * weight below j when the lower edge is nearer, above j otherwise; j itself
+ * when there is none): what the draw gives when u moves across that edge.
  */
-static int ref_inverse_cdf(const double* w, int V, double u, double* margin, double* Zout)
+static int ref_inverse_cdf(const double* w, int V, double u, double* margin, double* Zout, int* alt)
 {
     ref_sum_t acc = {0.0, 0.0};
     for (int x = 0; x < V; ++x) ref_sum_add(&acc, w[x]);
     double Z = ref_sum_value(&acc);
     *Zout = Z;
+    *alt = -1;
     if (!(Z > 0.0)) return -1;
     double t = u * Z;
     ref_sum_t C = {0.0, 0.0};
@@ -179,11 +183,19 @@ static int ref_inverse_cdf(const double* w, int V, double u, double* margin, dou
         if (cj > t) {
             double lo = u - prev / Z, hi = cj / Z - u;
             *margin = lo < hi ? lo : hi;
+            int nb = j;
+            if (lo < hi) {
+                for (int x = j - 1; x >= 0; --x) if (w[x] > 0.0) { nb = x; break; }
+            } else {
+                for (int x = j + 1; x < V; ++x) if (w[x] > 0.0) { nb = x; break; }
+            }
+            *alt = nb;
             return j;
         }
         prev = cj;
     }
     *margin = 0.0;                           /* unreachable for u < 1 */
+    *alt = V - 1;
     return V - 1;
 }
 
@@ -205,14 +217,65 @@ static void ref_fill_invalid(int k, int32_t* acc_len, int32_t* out)
 #define REF_RESID_ABS_MARGIN 1e-13
 
 /*
+ * The draw at position a of batch row b (0-based, a <= k): a < k samples the
+ * residual norm(max(0, p_a - q_a)), a = k the bonus from p_k, both with the
+ * uniform u[b,a,1]. Sets *tok, *alt (the token across the nearest CDF edge,
+ * see ref_inverse_cdf) and *m_cdf; returns the flag bits (1: the residual mass
+ * was zero and p_a was used; 2: the residual draw lies within
+ * REF_RESID_ABS_MARGIN of a boundary). work holds 3*V doubles.
+ */
+static int ref_draw(const void* target, const void* draft, const float* uniforms, double T,
+                    int kmax, int k, int a, int V, int dtype, size_t b, int32_t* tok, int32_t* alt,
+                    double* m_cdf, double* work)
+{
+    const size_t rowsT = (size_t)(kmax + 1), rowsD = (size_t)kmax;
+    double* p = work;
+    double* q = work + V;
+    double* w = work + 2 * (size_t)V;
+    int flags = 0, t, nb;
+    double Z;
+    double u1 = (double)uniforms[(b * rowsT + (size_t)a) * 2 + 1];
+    ref_softmax(target, dtype, (b * rowsT + (size_t)a) * (size_t)V, V, T, p);
+    if (a < k) {
+        ref_softmax(draft, dtype, (b * rowsD + (size_t)a) * (size_t)V, V, T, q);
+        for (int x = 0; x < V; ++x) {
+            double d = p[x] - q[x];
+            w[x] = d > 0.0 ? d : 0.0;
+        }
+        t = ref_inverse_cdf(w, V, u1, m_cdf, &Z, &nb);
+        if (t < 0) {                          /* Z = 0: draw from p_a, flag */
+            flags |= 1;
+            t = ref_inverse_cdf(p, V, u1, m_cdf, &Z, &nb);
+            *m_cdf = 0.0;
+        } else if (*m_cdf * Z < REF_RESID_ABS_MARGIN) {
+            flags |= 2;
+        }
+    } else {
+        t = ref_inverse_cdf(p, V, u1, m_cdf, &Z, &nb);
+    }
+    *tok = t;
+    *alt = nb;
+    return flags;
+}
+
+/*
  * One batch row. work must hold 3*V doubles.
  * Returns a bit set: 1 = Z fell back to p_a, 2 = the residual draw is within
  * REF_RESID_ABS_MARGIN of a CDF boundary (both are flags).
+ *
+ * Alternatives (sampling mode; NULL pointers skip them): alt_tok receives the
+ * token the final draw gives with its uniform moved across the nearest CDF
+ * edge. When the smallest acceptance margin |u - r_i| of the tests taken is
+ * below flip_delta, alt_acc/alt_out receive the whole outcome with that one
+ * test decided the other way (an accept becomes the first rejection, a
+ * rejection an accept, after which the later tests run as usual); otherwise
+ * they repeat acc_len/out.
  */
 static int ref_one_row(const void* target, const void* draft, const int32_t* tokens,
                        const float* uniforms, double T, int mode, int kmax, int kb, int V,
                        int dtype, size_t b, int32_t* acc_len, int32_t* out, double* gap,
                        double* p_tok, double* q_tok, double* m_acc, double* m_cdf,
+                       double flip_delta, int32_t* alt_acc, int32_t* alt_out, int32_t* alt_tok,
                        double* work)
 {
     const size_t rowsT = (size_t)(kmax + 1), rowsD = (size_t)kmax;
@@ -221,6 +284,8 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
     *m_cdf = INFINITY;
     for (int i = 0; i <= kmax; ++i) gap[i] = NAN;
     for (int i = 0; i < kmax; ++i) { p_tok[i] = NAN; q_tok[i] = NAN; }
+    if (alt_acc) { *alt_acc = -1; for (int i = 0; i <= kmax; ++i) alt_out[i] = -1; }
+    if (alt_tok) *alt_tok = -1;
     if (kb < 0 || kb > kmax) { ref_fill_invalid(kmax, acc_len, out); return 0; }
     const int k = kb;                         /* this row's draft length */
     for (int i = 0; i <= k; ++i) {
@@ -258,10 +323,8 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
 
     double* p = work;
     double* q = work + V;
-    double* w = work + 2 * (size_t)V;
 
-    /* acceptance tests, in order, up to the first rejection */
-    int a = k;
+    /* p_i(x_i) and q_i(x_i) for every position */
     for (int i = 0; i < k; ++i) {
         ref_softmax(target, dtype, (b * rowsT + (size_t)i) * (size_t)V, V, T, p);
         ref_softmax(draft, dtype, (b * rowsD + (size_t)i) * (size_t)V, V, T, q);
@@ -269,40 +332,45 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
         p_tok[i] = p[x];
         q_tok[i] = q[x];
     }
-    for (int i = 0; i < k; ++i) {
-        double P = p_tok[i], Q = q_tok[i];
-        double r = (Q > 0.0) ? P / Q : (P > 0.0 ? INFINITY : 0.0);
-        double u0 = (double)uniforms[(b * rowsT + (size_t)i) * 2 + 0];
-        double mg = fabs(u0 - r);
-        if (mg < *m_acc) *m_acc = mg;
-        if (!(u0 < r)) { a = i; break; }
-    }
-    *acc_len = a;
-    for (int i = 0; i < a; ++i) out[i] = tokens[b * rowsD + (size_t)i];
-    for (int i = a + 1; i <= kmax; ++i) out[i] = -1;
-
-    double u1 = (double)uniforms[(b * rowsT + (size_t)a) * 2 + 1];
-    ref_softmax(target, dtype, (b * rowsT + (size_t)a) * (size_t)V, V, T, p);
-    int tok;
-    double Z;
-    if (a < k) {
-        ref_softmax(draft, dtype, (b * rowsD + (size_t)a) * (size_t)V, V, T, q);
-        for (int x = 0; x < V; ++x) {
-            double d = p[x] - q[x];
-            w[x] = d > 0.0 ? d : 0.0;
+    /* acceptance tests, in order, up to the first rejection; `flip` decides
+       the test at that position the other way (-1: none) */
+    int a = k, amin = -1;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int flip = pass == 0 ? -1 : amin;
+        if (pass == 1 && !(alt_acc && amin >= 0 && *m_acc < flip_delta)) break;
+        int aa = k;
+        for (int i = 0; i < k; ++i) {
+            double P = p_tok[i], Q = q_tok[i];
+            double r = (Q > 0.0) ? P / Q : (P > 0.0 ? INFINITY : 0.0);
+            double u0 = (double)uniforms[(b * rowsT + (size_t)i) * 2 + 0];
+            int accept = u0 < r;
+            if (pass == 0) {
+                double mg = fabs(u0 - r);
+                if (mg < *m_acc) { *m_acc = mg; amin = i; }
+            }
+            if (i == flip) accept = !accept;
+            if (!accept) { aa = i; break; }
         }
-        tok = ref_inverse_cdf(w, V, u1, m_cdf, &Z);
-        if (tok < 0) {                        /* Z = 0: draw from p_a, flag */
-            flags |= 1;
-            tok = ref_inverse_cdf(p, V, u1, m_cdf, &Z);
-            *m_cdf = 0.0;
-        } else if (*m_cdf * Z < REF_RESID_ABS_MARGIN) {
-            flags |= 2;
+        if (pass == 0) {
+            a = aa;
+            *acc_len = a;
+            for (int i = 0; i < a; ++i) out[i] = tokens[b * rowsD + (size_t)i];
+            for (int i = a + 1; i <= kmax; ++i) out[i] = -1;
+            int32_t tok, nb;
+            flags = ref_draw(target, draft, uniforms, T, kmax, k, a, V, dtype, b, &tok, &nb, m_cdf, work);
+            out[a] = tok;
+            if (alt_tok) *alt_tok = nb;
+            if (alt_acc) { *alt_acc = a; for (int i = 0; i <= kmax; ++i) alt_out[i] = out[i]; }
+        } else {
+            int32_t tok, nb;
+            double mc;
+            *alt_acc = aa;
+            for (int i = 0; i < aa; ++i) alt_out[i] = tokens[b * rowsD + (size_t)i];
+            for (int i = aa + 1; i <= kmax; ++i) alt_out[i] = -1;
+            ref_draw(target, draft, uniforms, T, kmax, k, aa, V, dtype, b, &tok, &nb, &mc, work);
+            alt_out[aa] = tok;
         }
-    } else {
-        tok = ref_inverse_cdf(p, V, u1, m_cdf, &Z);
     }
-    out[a] = tok;
     return flags;
 }
 
@@ -313,20 +381,25 @@ static int ref_one_row(const void* target, const void* draft, const int32_t* tok
  *  uniforms [B,k+1,2] float32 (may be NULL in greedy mode).
  *  Outputs: acc_len [B], out_tokens [B,k+1], gap [B,k+1], p_tok/q_tok [B,k]
  *  (NaN where not computed), margin_acc [B], margin_cdf [B], flags [B].
+ *  Optional alternatives (sampling mode; all three NULL to skip): alt_acc [B],
+ *  alt_out [B,k+1] and alt_tok [B], see ref_one_row; flip_delta chooses the
+ *  rows whose nearest acceptance test is flipped.
  *  threads <= 0 uses the OpenMP default. Returns 0, or -1 on bad arguments.
  */
-int spec_verify_ref_ragged(const void* target, const void* draft, const int32_t* tokens,
-                           const int32_t* draft_len, const float* uniforms, float temperature,
-                           int mode, int B, int k, int V, int dtype,
-                           int32_t* acc_len, int32_t* out_tokens, double* gap,
-                           double* p_tok, double* q_tok, double* margin_acc,
-                           double* margin_cdf, int32_t* flags, int threads)
+int spec_verify_ref_full(const void* target, const void* draft, const int32_t* tokens,
+                         const int32_t* draft_len, const float* uniforms, float temperature,
+                         int mode, int B, int k, int V, int dtype,
+                         int32_t* acc_len, int32_t* out_tokens, double* gap,
+                         double* p_tok, double* q_tok, double* margin_acc,
+                         double* margin_cdf, int32_t* flags, double flip_delta,
+                         int32_t* alt_acc, int32_t* alt_out, int32_t* alt_tok, int threads)
 {
     if (B < 0 || k < 0 || V < 1) return -1;
     if (dtype != REF_F32 && dtype != REF_BF16) return -1;
     if (mode != REF_SAMPLE && mode != REF_GREEDY) return -1;
     if (!target || (k > 0 && !tokens)) return -1;
     if (mode == REF_SAMPLE && (!uniforms || (k > 0 && !draft))) return -1;
+    if ((alt_acc == NULL) != (alt_out == NULL)) return -1;
     double T = (double)temperature;
     if (mode == REF_SAMPLE && !(T > 0.0 && isfinite(T))) return -1;
 
@@ -357,11 +430,27 @@ int spec_verify_ref_ragged(const void* target, const void* draft, const int32_t*
             flags[b] = ref_one_row(target, draft, tokens, uniforms, T, mode, k, kb, V, dtype,
                                    (size_t)b, &acc_len[b], &out_tokens[(size_t)b * (k + 1)],
                                    &gap[(size_t)b * (k + 1)], &p_tok[(size_t)b * k],
-                                   &q_tok[(size_t)b * k], &margin_acc[b], &margin_cdf[b], work);
+                                   &q_tok[(size_t)b * k], &margin_acc[b], &margin_cdf[b],
+                                   flip_delta, alt_acc ? &alt_acc[b] : NULL,
+                                   alt_out ? &alt_out[(size_t)b * (k + 1)] : NULL,
+                                   alt_tok ? &alt_tok[b] : NULL, work);
         }
         free(work);
     }
     return failed ? -2 : 0;
+}
+
+/* Per-row draft lengths, no alternatives. */
+int spec_verify_ref_ragged(const void* target, const void* draft, const int32_t* tokens,
+                           const int32_t* draft_len, const float* uniforms, float temperature,
+                           int mode, int B, int k, int V, int dtype,
+                           int32_t* acc_len, int32_t* out_tokens, double* gap,
+                           double* p_tok, double* q_tok, double* margin_acc,
+                           double* margin_cdf, int32_t* flags, int threads)
+{
+    return spec_verify_ref_full(target, draft, tokens, draft_len, uniforms, temperature, mode, B, k,
+                                V, dtype, acc_len, out_tokens, gap, p_tok, q_tok, margin_acc,
+                                margin_cdf, flags, 0.0, NULL, NULL, NULL, threads);
 }
 
 /* Fixed-length drafts: every batch row verifies all k positions. */

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import token_verification_amd as tv
-from parity import compare
+from parity import DELTA_ACC, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,8 @@ def check(t, d, tok, uni, T, mode, dtype, threads=0, draft_len=None):
     torch.cuda.synchronize()
     ref = oracle.spec_verify_ref(t.cpu(), None if greedy else d.cpu(), tok.cpu(),
                                  None if greedy else uni.cpu(), T, mode, threads=threads,
-                                 draft_len=None if draft_len is None else draft_len.cpu().numpy())
+                                 draft_len=None if draft_len is None else draft_len.cpu().numpy(),
+                                 flip_delta=DELTA_ACC)
     return compare(res, ref, dtype, greedy)
 
 

@@ -378,9 +378,97 @@ def test_residual_below_fp64_resolution_is_flagged():
     t2 = rng.normal(0, 2, (1, 2, 50)).astype(np.float32)
     d2 = (t2[:, :1] + rng.normal(0, 1, (1, 1, 50))).astype(np.float32)
     u2 = np.array([[[0.999, 0.3], [0.5, 0.5]]], np.float32)   # u = 0.999 rejects
-    r2 = oracle.spec_verify_ref(t2, d2, np.array([[int(np.argmax(d2[0, 0]))]], np.int32), u2, 1.0, oracle.SAMPLE)
-    if r2.accepted_len[0] == 0:
-        assert r2.flags[0] == 0
+    # the draft token's target logit is -inf, so p(x) = 0 and the test rejects
+    # for every u: the ordinary residual draw always happens and is not flagged
+    x2 = int(np.argmax(d2[0, 0]))
+    t2[0, 0, x2] = NEG
+    r2 = oracle.spec_verify_ref(t2, d2, np.array([[x2]], np.int32), u2, 1.0, oracle.SAMPLE)
+    assert r2.accepted_len[0] == 0
+    assert r2.flags[0] == 0
+    p = softmax(t2[0, 0].astype(np.float64))
+    q = softmax(d2[0, 0].astype(np.float64))
+    w = np.maximum(0.0, p - q)
+    assert r2.out_tokens[0, 0] == np.searchsorted(np.cumsum(w) / w.sum(), np.float64(np.float32(0.3)),
+                                                  side="right")
+
+
+def test_zero_residual_mass_falls_back_to_target():
+    # R12: target and draft rows agree exactly and both give the draft token
+    # probability 0 (-inf logit), so r = 0 rejects at position 0 and the
+    # residual max(0, p - q) is identically zero: the draw falls back to p_0
+    # itself (its inverse CDF at u[0,1]) and the row is flagged (bit 0). A
+    # mistake that draws from the next target row, or forgets the flag, fails.
+    rng = np.random.default_rng(13)
+    V = 9
+    row = rng.normal(0, 1.5, V).astype(np.float32)
+    row[4] = NEG
+    nxt = rng.normal(0, 1.5, V).astype(np.float32)
+    t = np.stack([row, nxt])[None]
+    d = row[None, None].copy()
+    for u1 in (0.05, 0.37, 0.81, 0.999):
+        u = np.array([[[0.5, u1], [0.5, 0.5]]], np.float32)
+        r = run(t, d, [[4]], u)
+        assert r.accepted_len[0] == 0
+        assert r.flags[0] & 1
+        assert r.flagged(1e-6, 1e-12)[0]
+        p = softmax(row.astype(np.float64))
+        assert r.out_tokens[0, 0] == np.searchsorted(np.cumsum(p), np.float64(np.float32(u1)), side="right")
+        assert r.out_tokens[0, 1] == -1
+
+
+# ---------------------------------------------------------------- alternatives of near-tie rows
+# A flagged row may legitimately differ across implementations, but only by
+# taking its nearest decision the other way. The oracle reports that outcome;
+# these pins tie it to the oracle itself re-run with the uniform moved across
+# the boundary.
+
+
+def test_alternative_of_a_near_tie_acceptance():
+    P, Q = [0.1, 0.2, 0.3, 0.4], [0.4, 0.3, 0.2, 0.1]
+    t = np.array([[logits_of(P), np.zeros(4)]], np.float32)
+    d = np.array([[logits_of(Q)]], np.float32)
+    r_true = float(np.float64(softmax(t[0, 0].astype(np.float64))[1] / softmax(d[0, 0].astype(np.float64))[1]))
+    f = np.float32(r_true)
+    if float(f) < r_true:                                        # float32 neighbours of r
+        below, above = f, np.nextafter(f, np.float32(1))
+    else:
+        below, above = np.nextafter(f, np.float32(0)), f
+    assert float(below) < r_true <= float(above)                 # below accepts, above rejects
+    for u0, other in ((below, above), (above, below)):
+        u = np.array([[[u0, 0.6], [0.3, 0.7]]], np.float32)
+        r = oracle.spec_verify_ref(t, d, np.array([[1]], np.int32), u, 1.0, oracle.SAMPLE,
+                                   dtype=oracle.F32, flip_delta=1e-6)
+        assert r.margin_acc[0] < 1e-6
+        u2 = u.copy()
+        u2[0, 0, 0] = other
+        f = oracle.spec_verify_ref(t, d, np.array([[1]], np.int32), u2, 1.0, oracle.SAMPLE, dtype=oracle.F32)
+        assert f.accepted_len[0] != r.accepted_len[0]
+        assert r.alt_accepted_len[0] == f.accepted_len[0]
+        assert (r.alt_out_tokens[0] == f.out_tokens[0]).all()
+    # a row far from every boundary repeats its own outcome
+    u = np.array([[[0.9, 0.6], [0.3, 0.7]]], np.float32)
+    r = oracle.spec_verify_ref(t, d, np.array([[1]], np.int32), u, 1.0, oracle.SAMPLE, dtype=oracle.F32,
+                               flip_delta=1e-6)
+    assert r.alt_accepted_len[0] == r.accepted_len[0] and (r.alt_out_tokens[0] == r.out_tokens[0]).all()
+
+
+def test_alternative_token_across_the_nearest_cdf_edge():
+    # k = 0: the draw is textbook sampling from p (cumsum + searchsorted). With
+    # u just below / above the edge C_2, the draw gives 2 / 3, and the
+    # alternative is the token on the other side (a zero-mass token between is
+    # skipped: token 3 has p = 0, so above the edge comes token 4).
+    p = np.array([0.1, 0.2, 0.3, 0.0, 0.4])
+    t = logits_of(p)[None, None]
+    c = np.cumsum(softmax(t[0, 0].astype(np.float64)))
+    edge = np.float32(c[2])
+    lo = edge if float(edge) < c[2] else np.nextafter(edge, np.float32(0))
+    hi = np.nextafter(lo, np.float32(1))
+    for u1, tok, alt in ((lo, 2, 4), (hi, 4, 2)):
+        assert np.searchsorted(c, np.float64(u1), side="right") == tok
+        r = oracle.spec_verify_ref(t, None, np.zeros((1, 0), np.int32), np.array([[[0.5, u1]]], np.float32),
+                                   1.0, oracle.SAMPLE, dtype=oracle.F32, flip_delta=1e-6)
+        assert r.out_tokens[0, 0] == tok and r.alt_token[0] == alt
+        assert r.margin_cdf[0] < 1e-7
 
 
 

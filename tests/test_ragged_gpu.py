@@ -15,7 +15,7 @@ import torch
 import oracle
 import token_verification_amd as tv
 import workloads
-from parity import compare
+from parity import DELTA_ACC, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ def run_ragged(x, dl, dtype, greedy, rows=None):
             for key in ("target", "draft", "tokens", "uniforms")}
     dlh = dl[sel.cpu() if isinstance(sel, torch.Tensor) else sel].numpy()
     ref = oracle.spec_verify_ref(host["target"], host["draft"], host["tokens"], host["uniforms"],
-                                 x["T"], x["mode"], draft_len=dlh)
+                                 x["T"], x["mode"], draft_len=dlh, flip_delta=DELTA_ACC)
     if rows is not None:
         res = tv.binding.VerifyResult(res.accepted_len[sel], res.out_tokens[sel], res.gap[sel],
                                       None if res.target_prob is None else res.target_prob[sel],

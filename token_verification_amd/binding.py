@@ -1,9 +1,11 @@
 """ctypes binding of libspecverify.so (argument marshalling only).
 
 Every step of the verify computation runs in the HIP library; this module
-checks tensor dtypes/shapes/devices, allocates outputs, keeps one workspace
-per (device, stream), and passes raw device pointers plus the
-current stream to the C ABI declared in ``include/spec_verify.h``.
+checks the dtypes, shapes, devices and layout of every input and of any
+caller-supplied output or workspace tensor (ValueError on a mismatch),
+allocates outputs, keeps one workspace per (device, stream), and passes raw
+device pointers plus the current stream to the C ABI declared in
+``include/spec_verify.h``.
 """
 from __future__ import annotations
 
@@ -109,6 +111,7 @@ class VerifyResult(NamedTuple):
 
 
 _ws_cache: dict = {}
+_need_cache: dict = {}
 
 
 def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
@@ -120,6 +123,38 @@ def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
+
+
+def _user_workspace(ws: torch.Tensor, device: torch.device, nbytes: int) -> torch.Tensor:
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
+    return ws
+
+
+def _check_out_tensor(t, name: str, shape, dtype, device: torch.device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"out.{name} must be a tensor")
+    if tuple(t.shape) != shape or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"out.{name} must be a contiguous {dtype} tensor of shape {list(shape)} on {device} "
+                         f"(got {t.dtype} {list(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ', not contiguous'})")
+
+
+def _check_out(out, B: int, k: int, device: torch.device, probs: bool) -> None:
+    """Every output tensor the library will write: shape, dtype, device, layout."""
+    if not isinstance(out, VerifyResult):
+        raise ValueError("out must be a VerifyResult")
+    _check_out_tensor(out.accepted_len, "accepted_len", (B,), torch.int32, device)
+    _check_out_tensor(out.out_tokens, "out_tokens", (B, k + 1), torch.int32, device)
+    _check_out_tensor(out.gap, "gap", (B, k + 1), torch.float32, device)
+    if probs and (out.target_prob is None or out.draft_prob is None):
+        raise ValueError("return_probs=True needs out.target_prob and out.draft_prob")
+    for name in ("target_prob", "draft_prob"):
+        t = getattr(out, name)
+        if t is not None:
+            _check_out_tensor(t, name, (B, k), torch.float32, device)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -179,16 +214,22 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: tor
         tp = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
         dp = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
         out = VerifyResult(acc, otok, gap, tp, dp)
+    else:
+        _check_out(out, B, k, dev, return_probs)
 
     stream = torch.cuda.current_stream(dev).cuda_stream
-    need = workspace_size(B, k, V, dtype, mode)
-    if need == 0:
-        raise SpecVerifyError(-2, f"unsupported sizes B={B} k={k} V={V}")
-    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    nkey = (B, k, V, dtype, int(mode))
+    need = _need_cache.get(nkey)
+    if need is None:
+        need = workspace_size(B, k, V, dtype, mode)
+        if need == 0:
+            raise SpecVerifyError(-2, f"unsupported sizes B={B} k={k} V={V}")
+        _need_cache[nkey] = need
+    ws = _workspace(dev, stream, need) if workspace is None else _user_workspace(workspace, dev, need)
     tail = (ctypes.c_float(temperature), int(mode), B, k, V, dtype,
             _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
             _ptr(out.target_prob), _ptr(out.draft_prob),
-            ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+            ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), ctypes.c_void_p(stream))
     if phase_events is not None:
         if len(phase_events) != 4:
             raise ValueError("phase_events must hold four events")
@@ -244,14 +285,20 @@ def spec_gate(logits: torch.Tensor, tau: float = 2.0, admit: Optional[torch.Tens
         out = GateResult(torch.empty(n, dtype=torch.int32, device=dev),
                          torch.empty(n, dtype=torch.float32, device=dev),
                          torch.empty(n, dtype=torch.int32, device=dev))
+    else:
+        if not isinstance(out, GateResult):
+            raise ValueError("out must be a GateResult")
+        _check_out_tensor(out.argmax, "argmax", (n,), torch.int32, dev)
+        _check_out_tensor(out.gap, "gap", (n,), torch.float32, dev)
+        _check_out_tensor(out.fire, "fire", (n,), torch.int32, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     need = int(lib().spec_gate_workspace_size(n, V, dtype))
     if need == 0:
         raise SpecVerifyError(-2, f"unsupported sizes n={n} V={V}")
-    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    ws = _workspace(dev, stream, need) if workspace is None else _user_workspace(workspace, dev, need)
     rc = lib().spec_gate(_ptr(logits), n, V, dtype, int(rule), ctypes.c_float(tau), _ptr(admit),
                          _ptr(out.argmax), _ptr(out.gap), _ptr(out.fire),
-                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+                         ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), ctypes.c_void_p(stream))
     if rc != 0:
         raise SpecVerifyError(rc, last_error())
     return out
@@ -328,14 +375,16 @@ def spec_verify_lmhead(hidden: torch.Tensor, hidden_scale: torch.Tensor, weight:
         out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
                            torch.empty((B, k + 1), dtype=torch.int32, device=dev),
                            torch.empty((B, k + 1), dtype=torch.float32, device=dev), None, None)
+    else:
+        _check_out(out, B, k, dev, False)
     stream = torch.cuda.current_stream(dev).cuda_stream
     need = int(lib().spec_lmhead_workspace_size(B, k, V, d))
     if need == 0:
         raise SpecVerifyError(-2, f"unsupported sizes B={B} k={k} V={V} d={d}")
-    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    ws = _workspace(dev, stream, need) if workspace is None else _user_workspace(workspace, dev, need)
     args = (_ptr(hidden), _ptr(hidden_scale), _ptr(weight), _ptr(weight_scale), _ptr(tokens), B, k, V, d,
             _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
-            ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+            ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), ctypes.c_void_p(stream))
     if phase_events is not None:
         if len(phase_events) != 3:
             raise ValueError("phase_events must hold three events")
