@@ -263,6 +263,28 @@ int spec_verify_lmhead_timed(const int8_t* hidden, const float* hidden_scale, co
                              int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens, float* gap,
                              void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): spec_verify with the
+ * library's own device scratch buffer in place of a caller workspace. Every other
+ * argument, the outputs, the errors and the execution are those of spec_verify.
+ * The scratch is a static device array of SPEC_NOALLOC_SCRATCH_BYTES on each GPU
+ * the library runs on, held until the process ends; its device address is looked
+ * up once per device on the first call there (hipGetSymbolAddress), and no call
+ * allocates or frees anything. Sizes whose workspace
+ * (spec_verify_workspace_size) exceeds the scratch return SPEC_ERR_WORKSPACE and
+ * enqueue nothing. Every call on one GPU shares that GPU's scratch, which keeps
+ * the last call's contents (each call writes every record before reading it):
+ * calls that overlap in time on one GPU (e.g. on two streams) race and must be
+ * serialised by the caller.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V,
+                        int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                        float* target_prob, float* draft_prob, void* stream);
+
 /* Thread-local description of the last non-zero return of this library. */
 const char* spec_verify_last_error(void);
 

@@ -27,7 +27,7 @@ def test_exports_match_header():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     exported = {s for s in exported if s.startswith("spec_")}
     assert declared() == exported
-    assert len(exported) == 13
+    assert len(exported) == 14
 
 
 def test_version():
@@ -218,3 +218,12 @@ def test_lmhead_rejects_synchronously(kw, code):
                                            a["B"], a["k"], a["V"], a["d"], a["acc"], a["out"], a["gap"],
                                            a["ws"], a["ws_bytes"], None, ctypes.cast(ev, ctypes.c_void_p))
     assert rc in (code, -1)
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_on_the_host():
+    # the size check comes before any HIP call, so it runs without a GPU
+    need = tv.workspace_size(8192, 4, 151936, 1, 0)
+    assert need > (16 << 20)
+    rc = tv.lib().spec_verify_noalloc(FAKE, FAKE, FAKE, FAKE, 1.0, 0, 8192, 4, 151936, 1, FAKE, FAKE, FAKE,
+                                      None, None, None)
+    assert rc == -6 and "scratch" in binding.last_error()

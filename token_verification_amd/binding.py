@@ -63,6 +63,9 @@ def lib():
                 L.spec_verify_timed.argtypes = [P, P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
                                                 P, P, P, P, P, P, S, P, P]
                 L.spec_verify_timed.restype = ctypes.c_int
+                L.spec_verify_noalloc.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
+                                                  P, P, P, P, P, P]
+                L.spec_verify_noalloc.restype = ctypes.c_int
                 L.spec_verify_workspace_size.argtypes = [I, I, I, ctypes.c_int, ctypes.c_int]
                 L.spec_verify_workspace_size.restype = S
                 L.spec_verify_check_args.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int,
@@ -246,6 +249,51 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: tor
     else:
         rc = lib().spec_verify_ragged(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(draft_len),
                                       _ptr(uniforms), *tail)
+    if rc != 0:
+        raise SpecVerifyError(rc, last_error())
+    return out
+
+
+def spec_verify_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor], tokens: torch.Tensor,
+                        uniforms: Optional[torch.Tensor], temperature: float = 1.0, mode: int = SAMPLE, *,
+                        return_probs: bool = False, out: Optional[VerifyResult] = None) -> VerifyResult:
+    """spec_verify through spec_verify_noalloc: the library's own device scratch
+    serves as the workspace, so the call allocates nothing when ``out`` is
+    given (see include/spec_verify.h; calls that overlap on one GPU race)."""
+    if not isinstance(target, torch.Tensor) or target.dim() != 3 or not target.is_cuda:
+        raise ValueError("target must be a [B, k+1, V] device tensor")
+    if target.dtype == torch.float32:
+        dtype = F32
+    elif target.dtype == torch.bfloat16:
+        dtype = BF16
+    else:
+        raise ValueError(f"unsupported logit dtype {target.dtype}")
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if draft is not None and (draft.shape != (B, k, V) or draft.dtype != target.dtype or draft.device != dev):
+        raise ValueError("draft must match target's dtype/device with shape [B, k, V]")
+    if tokens.shape != (B, k) or tokens.dtype != torch.int32 or tokens.device != dev:
+        raise ValueError("tokens must be int32 [B, k] on the target's device")
+    if uniforms is not None and (uniforms.shape != (B, k + 1, 2) or uniforms.dtype != torch.float32
+                                 or uniforms.device != dev):
+        raise ValueError("uniforms must be float32 [B, k+1, 2] on the target's device")
+    for t in (target, draft, tokens, uniforms):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                           torch.empty((B, k + 1), dtype=torch.float32, device=dev),
+                           torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None,
+                           torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None)
+    else:
+        _check_out(out, B, k, dev, return_probs)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().spec_verify_noalloc(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms),
+                                   ctypes.c_float(temperature), int(mode), B, k, V, dtype,
+                                   _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
+                                   _ptr(out.target_prob), _ptr(out.draft_prob), ctypes.c_void_p(stream))
     if rc != 0:
         raise SpecVerifyError(rc, last_error())
     return out

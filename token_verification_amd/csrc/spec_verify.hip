@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -2788,6 +2789,38 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
 
 }  // namespace
 
+// Device scratch of spec_verify_noalloc, in place of a caller workspace: one
+// copy on every GPU the library runs on, held until the process ends. Host
+// code never uses this name as an address (on the host it is only a stand-in
+// for the symbol); it uses the device address that hipGetSymbolAddress
+// returned for the current device.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// The device address of `scratch` on device dev (the current device), looked
+// up once per device.
+int scratch_ptr(int dev, void** out) {
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(SPEC_ERR_HIP, "device %d is out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SPEC_ERR_HIP, "cannot resolve the scratch buffer on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPEC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int dtype, int mode) {
@@ -2833,6 +2866,27 @@ int spec_verify_timed(const void* target_logits, const void* draft_logits, const
     return run(target_logits, draft_logits, draft_tokens, draft_len, draft_len != nullptr, uniforms, temperature,
                mode, B, k, V, dtype, accepted_len, out_tokens, gap, target_prob, draft_prob, workspace,
                workspace_bytes, stream, events);
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const float* uniforms, float temperature, int mode, int32_t B, int32_t k, int32_t V,
+                        int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
+                        float* draft_prob, void* stream) {
+    Plan plan;
+    if ((dtype == SPEC_DTYPE_F32 || dtype == SPEC_DTYPE_BF16) && make_plan(B, k, V, mode, dtype, plan) &&
+        plan.total > SPEC_NOALLOC_SCRATCH_BYTES)
+        return fail(SPEC_ERR_WORKSPACE,
+                    "spec_verify_noalloc: B=%d k=%d V=%d need %zu bytes of scratch, more than its %u-byte "
+                    "maximum (use spec_verify with a caller workspace)", B, k, V, plan.total,
+                    static_cast<unsigned>(SPEC_NOALLOC_SCRATCH_BYTES));
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_ERR_HIP, "cannot query the current HIP device");
+    void* ws = nullptr;
+    const int rc = scratch_ptr(dev, &ws);
+    if (rc != SPEC_OK) return rc;
+    return run(target_logits, draft_logits, draft_tokens, nullptr, false, uniforms, temperature, mode, B, k, V,
+               dtype, accepted_len, out_tokens, gap, target_prob, draft_prob, ws, SPEC_NOALLOC_SCRATCH_BYTES,
+               stream);
 }
 
 size_t spec_gate_workspace_size(int32_t n, int32_t V, int dtype) {
