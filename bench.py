@@ -79,6 +79,41 @@ def counter_traffic(name: str, key: str = "traffic_bytes_per_call"):
     return int(fields[key])
 
 
+def metric_name(w, ragged: bool) -> str:
+    """The headline metric's wording, with the sizes of the workload actually run."""
+    kind = "" if w.mode == 0 else "greedy, "
+    if ragged:
+        return (f"verified draft positions/sec + % of HBM roofline, {kind}ragged drafts, "
+                f"B={w.B} k<={w.k} V={w.V} {w.dtype}")
+    return f"verified draft positions/sec + % of HBM roofline, {kind}B={w.B} k={w.k} V={w.V} {w.dtype}"
+
+
+def inputs_sha256(x) -> str:
+    """SHA-256 over the bytes of the input tensors, in argument order."""
+    import hashlib
+    import torch
+    h = hashlib.sha256()
+    for key in ("target", "draft", "tokens", "uniforms", "draft_len"):
+        v = x.get(key)
+        if isinstance(v, torch.Tensor):
+            t = v.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                t = t.view(torch.int16)
+            h.update(t.numpy().tobytes())
+    return h.hexdigest()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,21 +189,32 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # per-launch kernel time: event pairs on the stream the kernel runs on
+    # The timed region: K calls back to back, bracketed by one event pair on
+    # the stream the kernels run on (events between the calls would add their
+    # own gaps to the stream), so the GPU time per step includes every kernel
+    # and every gap between them.
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_avg = g0.elapsed_time(g1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    # spread of single calls: event pairs around each call, in a loop of its own
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     kms = np.array([a.elapsed_time(b) for a, b in ev])
-    k_avg = float(kms.mean())
-    ms_per_step = wall * 1e3 / args.steps
 
     positions = B * k if dlen is None else int(dlen.sum())
     alg = algorithmic_bytes(w, dlen)
@@ -194,9 +240,11 @@ def main() -> int:
     achieved = alg / (k_avg * 1e-3) / 1e9
     value = positions / (ms_per_step * 1e-3)
 
+    acc = outs[0].accepted_len.cpu().numpy()
+    valid = (acc >= 0) & (acc <= k)
+    kb = np.full(B, k) if dlen is None else dlen.cpu().numpy()
     line = {
-        "metric": METRIC if dlen is None else
-        f"verified draft positions/sec + % of HBM roofline, ragged drafts, B={B} k<={k} V={w.V} {w.dtype}",
+        "metric": metric_name(w, dlen is not None),
         "value": round(value, 1),
         "unit": "positions/s",
         "n_gpus": 1,
@@ -211,9 +259,14 @@ def main() -> int:
         "config": {"workload": label, "B": B, "k": k, "V": w.V, "logits": w.dtype,
                    "mode": "sample" if w.mode == 0 else "greedy", "T": w.T,
                    "rotated_copies": R},
+        # mean: GPU time per step over the timed region; the percentiles: single calls
         "kernel_us": {"mean": round(k_avg * 1e3, 2), "p10": round(float(np.percentile(kms, 10)) * 1e3, 2),
                       "p50": round(float(np.percentile(kms, 50)) * 1e3, 2),
                       "p90": round(float(np.percentile(kms, 90)) * 1e3, 2)},
+        "acceptance": {"mean_accepted_len": round(float(acc[valid].mean()), 4),
+                       "acceptance_rate": round(float(acc[valid].sum() / max(1, kb[valid].sum())), 4),
+                       "invalid_rows": int((~valid).sum())},
+        "inputs_sha256": inputs_sha256(x),
         "positions_per_s_kernel": round(positions / (k_avg * 1e-3), 1),
         "phase_us": {"pass1": round(p1_ms * 1e3, 2), "pass2": round(float(ph[:, 1].mean()) * 1e3, 2),
                      "draw": round(float(ph[:, 2].mean()) * 1e3, 2)},
@@ -237,8 +290,20 @@ def main() -> int:
         import oracle
         host = {key: (v.cpu() if isinstance(v, torch.Tensor) else v) for key, v in x.items()}
         hl = None if dlen is None else dlen.numpy()
-        oracle.spec_verify_ref(host["target"], host["draft"], host["tokens"], host["uniforms"],
-                               host["T"], host["mode"], draft_len=hl)          # warm (page-in)
+        ref = oracle.spec_verify_ref(host["target"], host["draft"], host["tokens"], host["uniforms"],
+                                     host["T"], host["mode"], draft_len=hl)    # also warms (page-in)
+        # this call's outputs against the oracle's, row by row (flagged: near-ties)
+        out0 = outs[0].out_tokens.cpu().numpy()
+        same = (acc == ref.accepted_len) & (out0 == ref.out_tokens).all(axis=1)
+        if w.mode == 0:
+            fl12 = ref.flagged(1e-6, 1e-12)
+            fl6 = ref.flagged(1e-6, 1e-6)
+        else:
+            fl12 = fl6 = np.zeros(B, bool)
+        line["parity"] = {"rows": B, "mismatch_unflagged": int((~same & ~fl12).sum()),
+                          "mismatch_flagged": int((~same & fl12).sum()),
+                          "flagged_1e-12": int(fl12.sum()), "flagged_literal_1e-6": int(fl6.sum()),
+                          "flag_bits": int((ref.flags != 0).sum())}
         n, t_cpu = 0, 0.0
         while t_cpu < args.cpu_seconds:
             c0 = time.perf_counter()
@@ -246,10 +311,26 @@ def main() -> int:
                                    host["T"], host["mode"], draft_len=hl)
             t_cpu += time.perf_counter() - c0
             n += 1
+        cores = len(os.sched_getaffinity(0))
         line["cpu_baseline"] = {"value": round(positions * n / t_cpu, 1), "unit": "positions/s",
-                                "cores": oracle.max_threads(), "kind": "oracle",
+                                "cores": min(cores, oracle.max_threads()), "kind": "oracle",
                                 "sample": f"{n} full calls of {label} (B={B}) on host copies, "
-                                          f"{t_cpu:.1f} s of oracle time"}
+                                          f"{t_cpu:.1f} s of oracle time",
+                                "cpu_model": cpu_model(), "affinity_cores": cores}
+        # one thread, on the first batch rows (rows are independent)
+        bs = max(1, B // 16)
+        sub = {key: (v[:bs] if isinstance(v, torch.Tensor) else v) for key, v in host.items()}
+        hs = None if hl is None else hl[:bs]
+        n1, t1 = 0, 0.0
+        while t1 < args.cpu_seconds / 4:
+            c0 = time.perf_counter()
+            oracle.spec_verify_ref(sub["target"], sub["draft"], sub["tokens"], sub["uniforms"],
+                                   sub["T"], sub["mode"], draft_len=hs, threads=1)
+            t1 += time.perf_counter() - c0
+            n1 += 1
+        pos1 = bs * k if hs is None else int(hs.sum())
+        line["cpu_baseline_1thread"] = {"value": round(pos1 * n1 / t1, 1), "unit": "positions/s", "cores": 1,
+                                        "sample": f"{n1} calls on the first {bs} batch rows, {t1:.1f} s"}
     print(json.dumps(line), flush=True)
     return 0
 

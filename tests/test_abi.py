@@ -56,7 +56,7 @@ FAKE = 0x10000          # aligned fake device address (never dereferenced)
 
 def args(**kw):
     a = dict(target=FAKE, draft=FAKE, tokens=FAKE, uniforms=FAKE, T=1.0, mode=0, B=4, k=3, V=100,
-             dtype=0, acc=FAKE, out=FAKE, gap=FAKE, ws=0x100000, ws_bytes=1 << 20)
+             dtype=0, acc=FAKE, out=FAKE, gap=FAKE, ws=0x100000, ws_bytes=tv.workspace_size(4, 3, 100, 0, 0))
     a.update(kw)
     return a
 

@@ -51,3 +51,20 @@ def test_profile_summaries_carry_hash_command_and_traffic():
         assert keys, nm
         for _, v in keys:
             assert int(v) > 0
+
+
+def test_metric_names_the_workload_run():
+    assert bench.metric_name(workloads.WORKLOADS[workloads.HEADLINE], False) == bench.METRIC
+    assert "B=512 k=8 V=262144 bf16" in bench.metric_name(workloads.WORKLOADS["b512_k8_v262144_bf16"], False)
+    g = bench.metric_name(workloads.WORKLOADS["b256_k3_v128256_bf16_greedy"], False)
+    assert "greedy" in g and "B=256 k=3 V=128256 bf16" in g
+    assert "ragged" in bench.metric_name(workloads.WORKLOADS[workloads.HEADLINE], True)
+
+
+def test_inputs_hash_follows_the_bytes():
+    w = workloads.WORKLOADS["b1_k4_v1000_f32"]
+    a, b = workloads.make(w, 0), workloads.make(w, 0)
+    assert bench.inputs_sha256(a) == bench.inputs_sha256(b)
+    b["uniforms"] = b["uniforms"].clone()
+    b["uniforms"][0, 0, 0] += 0.25
+    assert bench.inputs_sha256(a) != bench.inputs_sha256(b)
