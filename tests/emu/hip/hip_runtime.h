@@ -19,10 +19,12 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <ucontext.h>
 
 #include <atomic>
+#include <chrono>
 #include <thread>
 #include <vector>
 
@@ -99,10 +101,33 @@ inline double __hiloint2double(int hi, int lo) {
 // the occupancy hint of a kernel means nothing here
 #define amdgpu_waves_per_eu(...) unused
 
+// Optional random delays at every device-scope atomic (EMU_JITTER=1), so that
+// concurrent workgroups interleave in many different orders.
+inline int emu_jitter_on() {
+    static const int on = [] { const char* e = getenv("EMU_JITTER"); return e && e[0] == '1'; }();
+    return on;
+}
+inline void emu_jitter() {
+    if (!emu_jitter_on()) return;
+    thread_local unsigned long long x = 0x9E3779B97F4A7C15ull ^ reinterpret_cast<uintptr_t>(&x);
+    x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+    const unsigned r = static_cast<unsigned>(x % 1000);
+    if (r < 30) std::this_thread::sleep_for(std::chrono::microseconds(r));
+    else if (r < 200) std::this_thread::yield();
+}
+template <class T, class V> inline T emu_atomic_add(T* p, V v, int o) {
+    emu_jitter(); T r = __atomic_fetch_add(p, static_cast<T>(v), o); emu_jitter(); return r;
+}
+template <class T, class V> inline void emu_atomic_store(T* p, V v, int o) {
+    emu_jitter(); __atomic_store_n(p, static_cast<T>(v), o); emu_jitter();
+}
+template <class T> inline T emu_atomic_load(const T* p, int o) {
+    emu_jitter(); T r = __atomic_load_n(p, o); emu_jitter(); return r;
+}
 #define __HIP_MEMORY_SCOPE_AGENT 0
-#define __hip_atomic_fetch_add(p, v, o, s) __atomic_fetch_add((p), (v), (o))
-#define __hip_atomic_store(p, v, o, s) __atomic_store_n((p), (v), (o))
-#define __hip_atomic_load(p, o, s) __atomic_load_n((p), (o))
+#define __hip_atomic_fetch_add(p, v, o, s) emu_atomic_add((p), (v), (o))
+#define __hip_atomic_store(p, v, o, s) emu_atomic_store((p), (v), (o))
+#define __hip_atomic_load(p, o, s) emu_atomic_load((p), (o))
 template <class T> inline T atomicAdd(T* p, T v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
 template <class T> inline T atomicAnd(T* p, T v) { return __atomic_fetch_and(p, v, __ATOMIC_SEQ_CST); }
 template <class T> inline T atomicOr(T* p, T v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
@@ -117,6 +142,10 @@ template <class T> inline T atomicMax(T* p, T v) {
     return old;
 }
 inline void __threadfence() { __atomic_thread_fence(__ATOMIC_SEQ_CST); }
+
+// static device arrays are host arrays; a symbol's address is its own
+#define __align__(n) __attribute__((aligned(n)))
+#define HIP_SYMBOL(x) (&(x))
 
 // ---------------------------------------------------------------- fibers
 // Lanes are fibers run round-robin. A workgroup barrier releases once every
@@ -366,6 +395,7 @@ enum hipDeviceAttribute_t { hipDeviceAttributeMultiprocessorCount = 0 };
 inline int& emu_cu_count() { static int n = 1; return n; }
 inline hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
 inline hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = emu_cu_count(); return hipSuccess; }
+inline hipError_t hipGetSymbolAddress(void** p, const void* sym) { *p = const_cast<void*>(sym); return hipSuccess; }
 inline hipError_t hipGetLastError() { return hipSuccess; }
 inline int& emu_blocks_per_cu() { static int n = 8; return n; }
 template <class K>
