@@ -171,7 +171,9 @@ def main() -> int:
         x["draft_len"] = dlen.to(dev)
     per_copy = x["target"].numel() * w.elem_bytes + (
         x["draft"].numel() * w.elem_bytes if x["draft"] is not None else 0)
-    R = max(1, math.ceil(args.rotate_bytes / per_copy))
+    # enough copies that the 256 MB Infinity Cache cannot hold them, at most 64
+    # (tiny workloads stay cache-resident whatever the count)
+    R = min(64, max(1, math.ceil(args.rotate_bytes / per_copy)))
     copies = [x] + [{key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in x.items()}
                     for _ in range(R - 1)]
     B, k = w.B, w.k
