@@ -73,7 +73,8 @@ def oracle_of(x, rows=None):
     (40, 5, 32000, 1024),       # 8 XCD runs of tiles and a remainder
     (64, 3, 1000, 128),         # 256-row tiles with the fewest stages (two)
     (64, 3, 2000, 256),         # 256-row tiles, four stages (the prologue fills three)
-    (96, 3, 3000, 640),         # 384 rows: 128-row tiles, ten stages
+    (96, 3, 3000, 640),         # 384 rows: two 192-row tiles, ten stages
+    (160, 3, 3000, 640),        # 640 rows: five 128-row tiles (the narrow kernel), ten stages
 ])
 def test_lmhead_matches_oracle(B, k, V, d):
     say("lmhead", B, k, V, d)

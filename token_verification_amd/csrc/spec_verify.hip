@@ -2111,8 +2111,9 @@ __device__ inline void head_merge(float& t1, float& t2, int& i1, int& fl, float 
 // Scale the accumulators of one lane to logits and reduce them to a top-2
 // per hidden row (EDGE: the tile reaches past V, so entries past it are skipped).
 template <int MB, bool EDGE>
-__device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4][MB], int v0, int mrow, int vw,
-                                     int hi, float (&T1)[MB], float (&T2)[MB], int (&I1)[MB], int (&FL)[MB]) {
+__device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4][MB], const float* WS, int v0,
+                                     int mrow, int vw, int hi, float (&T1)[MB], float (&T2)[MB], int (&I1)[MB],
+                                     int (&FL)[MB]) {
     float hsv[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -2125,10 +2126,7 @@ __device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4]
         const int vbase = v0 + 128 * vw + 32 * vb + 4 * hi;
         float wsv[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int v = vbase + 8 * (q >> 2) + (q & 3);
-            wsv[q] = !EDGE || v < H.V ? H.ws[v] : 0.0f;
-        }
+        for (int q = 0; q < 16; ++q) wsv[q] = WS[vbase - v0 + 8 * (q >> 2) + (q & 3)];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -2170,8 +2168,15 @@ struct HeadTile {
         float T1[MB], T2[MB];
         int I1[MB], FL[MB];
         const int mrow = m0 + 32 * MB * mw + r;
-        if (v0 + HV <= H.V) head_epilogue<MB, false>(H, acc, v0, mrow, vw, hi, T1, T2, I1, FL);
-        else head_epilogue<MB, true>(H, acc, v0, mrow, vw, hi, T1, T2, I1, FL);
+        // the tile's weight scales go through LDS (one per thread), so the
+        // epilogue reads them with short LDS loads instead of holding many
+        // global loads in flight beside the accumulators
+        float* WS = reinterpret_cast<float*>(S + 2 * BM * sizeof(HeadRec));
+        static_assert(NTH == HV, "one weight scale per thread");
+        WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+        __syncthreads();
+        if (v0 + HV <= H.V) head_epilogue<MB, false>(H, acc, WS, v0, mrow, vw, hi, T1, T2, I1, FL);
+        else head_epilogue<MB, true>(H, acc, WS, v0, mrow, vw, hi, T1, T2, I1, FL);
         HeadRec* L = reinterpret_cast<HeadRec*>(S);        // [2][BM]: per vocabulary wave
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
