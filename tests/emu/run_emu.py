@@ -20,7 +20,7 @@ import oracle  # noqa: E402
 import workloads  # noqa: E402
 from parity import DELTA_ACC, DELTA_CDF  # noqa: E402
 
-L = ctypes.CDLL(os.path.join(HERE, "libspecverify_emu.so"))
+L = ctypes.CDLL(os.path.join(HERE, os.environ.get("SPEC_EMU_LIB", "libspecverify_emu.so")))
 P, I, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 L.spec_verify.argtypes = [P, P, P, P, F, ctypes.c_int, I, I, I, ctypes.c_int, P, P, P, P, P, P, S, P]
 L.spec_verify.restype = ctypes.c_int

@@ -3,7 +3,10 @@
 tests/emu/hip/hip_runtime.h maps the HIP subset the kernels use onto host C++
 (fibers per workgroup), so these tests execute the product kernels on the CPU
 and compare them with the oracle, with a random (uninitialised) workspace.
-SPEC_EMU_ASAN=1 rebuilds the harness with AddressSanitizer (slow, ~10 min).
+SPEC_EMU_ASAN=1 builds the harness with AddressSanitizer and UndefinedBehavior-
+Sanitizer into a library of its own and runs every case under it (slow: the
+whole set took about two hours on 8 cores; the per-case time limits grow to
+match).
 """
 import ctypes
 import os
@@ -17,12 +20,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 EMU = os.path.join(HERE, "emu")
 ROOT = os.path.dirname(HERE)
 ASAN = os.environ.get("SPEC_EMU_ASAN") == "1"
+LIBNAME = "libspecverify_emu_asan.so" if ASAN else "libspecverify_emu.so"
 CLANG = "/opt/rocm/llvm/bin/clang++"   # host clang: native vector types as in the device code
 
 
 @pytest.fixture(scope="module")
 def emu_lib():
-    out = os.path.join(EMU, "libspecverify_emu.so")
+    out = os.path.join(EMU, LIBNAME)
     cmd = [CLANG, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
            "-I", EMU, "-I", os.path.join(ROOT, "include"), "-Wno-unknown-pragmas",
            "-Wno-pass-failed", "-Wno-psabi",
@@ -35,6 +39,9 @@ def emu_lib():
 
 def run_cases(*names, timeout=1200):
     env = dict(os.environ)
+    env["SPEC_EMU_LIB"] = LIBNAME
+    if ASAN:
+        timeout *= 8
     if ASAN:
         asan = subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"],
                               capture_output=True, text=True).stdout.strip()
