@@ -1,4 +1,4 @@
-"""Oracle of greedy verification fused with an int8 LM head (plain numpy).
+"""Oracle of verification fused with int8 LM heads, greedy and sampling (plain numpy).
 
 TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``.
 
@@ -16,7 +16,9 @@ head here is int8 with one fp32 scale per vocabulary row and per hidden row:
 where float32(acc) rounds the integer to nearest even and fl32 is one
 float32 multiplication. The greedy rule ("The Inference Wall" part 7) and the
 gap ("Speculative Pre-Positioning", Eq. 11) then apply to these logits exactly
-as in oracle.spec_verify_ref.
+as in oracle.spec_verify_ref; so does modified rejection sampling, with the
+draft's logits from its own hidden rows and head (or the target's head, when
+the draft shares it).
 
 Each product of two int8 values is at most 2^14 in magnitude, so for d up to
 2^38 every partial sum is an integer below 2^53: a float64 matrix product is
@@ -46,3 +48,26 @@ def lmhead_greedy_ref(h, h_scale, w, w_scale, tokens, B: int, k: int):
     logits = lmhead_logits_ref(h, h_scale, w, w_scale).reshape(B, k + 1, -1)
     return oracle.spec_verify_ref(np.ascontiguousarray(logits), None, np.asarray(tokens, np.int32), None,
                                   1.0, oracle.GREEDY, dtype=oracle.F32)
+
+
+def lmhead_sample_ref(th, ths, tw, tws, dh, dhs, dw, dws, tokens, uniforms, temperature: float, B: int, k: int,
+                      flip_delta: float = 0.0):
+    """Sampling-mode verify of B batch rows through two int8 heads.
+
+    Target rows th[b*(k+1)+i] (i = 0..k) and draft rows dh[b*k+i] (i < k) are
+    projected by their heads as in lmhead_logits_ref (dw / dws None: the draft
+    shares the target's head); modified rejection sampling ("Speculative
+    Decoding: The Physics of Stolen Time", section 2) then runs on those
+    float32 logits as in oracle.spec_verify_ref.
+    """
+    t = lmhead_logits_ref(th, ths, tw, tws).reshape(B, k + 1, -1)
+    V = t.shape[2]
+    if dw is None:
+        dw, dws = tw, tws
+    if k > 0:
+        q = lmhead_logits_ref(dh, dhs, dw, dws).reshape(B, k, V)
+    else:
+        q = np.zeros((B, 0, V), np.float32)
+    return oracle.spec_verify_ref(np.ascontiguousarray(t), np.ascontiguousarray(q),
+                                  np.asarray(tokens, np.int32).reshape(B, k), np.asarray(uniforms, np.float32),
+                                  float(temperature), oracle.SAMPLE, dtype=oracle.F32, flip_delta=flip_delta)
