@@ -133,6 +133,11 @@ def main() -> int:
                     help="time greedy verification fused with an int8 LM head instead "
                          "(B=256 k=3 V=128256 d=4096 unless --lmhead-shape)")
     ap.add_argument("--lmhead-shape", default="256,3,128256,4096", metavar="B,k,V,d")
+    ap.add_argument("--lmhead-sample", action="store_true",
+                    help="time sampling-mode verification fused with int8 LM heads (target and draft "
+                         "hidden rows; the draft shares the head unless --draft-head)")
+    ap.add_argument("--draft-head", action="store_true",
+                    help="with --lmhead-sample: the draft has an int8 head of its own")
     ap.add_argument("--probe", choices=["copy", "sum"], default=None,
                     help="instead of the verify step, time a plain 1 GiB device copy (or a "
                          "read-only sum): achievable-bandwidth context and the known-size "
@@ -153,6 +158,8 @@ def main() -> int:
         return gate_bench(args, torch, np)
     if args.commit:
         return commit_bench(args, torch, np)
+    if args.lmhead_sample:
+        return lmhead_sample_bench(args, torch, np)
     if args.lmhead:
         return lmhead_bench(args, torch, np)
 
@@ -567,6 +574,126 @@ def lmhead_bench(args, torch, np) -> int:
                                 "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
                                 "sample": f"{n} batch rows one at a time (k+1 hidden rows against the "
                                           f"whole head), {t_cpu:.1f} s of oracle time"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def lmhead_sample_bench(args, torch, np) -> int:
+    import token_verification_amd as tv
+    import workloads
+
+    B, k, V, d = (int(v) for v in args.lmhead_shape.split(","))
+    MT, MD = B * (k + 1), B * k
+    own = args.draft_head
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: generating int8 heads and hidden rows B={B} k={k} V={V} d={d} draft_head={own}",
+          file=sys.stderr, flush=True)
+    x = workloads.make_lmhead_sample(B, k, V, d, seed=0, device=dev, draft_head=own)
+    T = 1.0
+    out = tv.binding.VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                                  torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                                  torch.empty((B, k + 1), dtype=torch.float32, device=dev),
+                                  torch.empty((B, k), dtype=torch.float32, device=dev),
+                                  torch.empty((B, k), dtype=torch.float32, device=dev))
+
+    def call(**kw):
+        tv.spec_verify_lmhead_sample(x["hidden"], x["hidden_scale"], x["weight"], x["weight_scale"],
+                                     x["draft_hidden"], x["draft_hidden_scale"], x["tokens"], x["uniforms"], T,
+                                     draft_weight=x["draft_weight"], draft_weight_scale=x["draft_weight_scale"],
+                                     out=out, **kw)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(phase_events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    callt = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    heads = ph[:, 0]
+    ops = 2.0 * (MT + MD) * V * d                          # int8 multiply-adds of both heads, two ops each
+    achieved = ops / (float(heads.mean()) * 1e-3) / 1e12
+    wbytes = (2 if own else 1) * (V * d + 4 * V) + (MT + MD) * (d + 4)
+    positions = B * k
+    acc = out.accepted_len.cpu().numpy()
+    tag = f"lmhead_sample_b{B}_k{k}_v{V}_d{d}_int8" + ("_drafthead" if own else "")
+    line = {
+        "metric": f"verified draft positions/sec, sampling verify fused with int8 LM heads, "
+                  f"B={B} k={k} V={V} d={d}" + (", separate draft head" if own else ", shared head"),
+        "value": round(positions / (wall / args.steps), 1),
+        "unit": "positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": tag, "B": B, "k": k, "V": V, "d": d, "T": T,
+                   "target_rows": MT, "draft_rows": MD, "draft_head": "own" if own else "shared"},
+        "phase_us": {"head_passes": round(float(heads.mean()) * 1e3, 2),
+                     "merges": round(float(ph[:, 1].mean()) * 1e3, 2),
+                     "decide_and_draw": round(float(ph[:, 2].mean()) * 1e3, 2),
+                     "call": round(float(callt.mean()) * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": counter_traffic(f"spec_verify_{tag}", "traffic_bytes_head_passes"),
+                     "algorithmic_ops_per_launch": ops},
+        "hbm_context": {"weight_and_hidden_bytes": wbytes,
+                        "GB_per_s": round(wbytes / (float(heads.mean()) * 1e-3) / 1e9, 1)},
+        "accepted_mean": round(float(acc[acc >= 0].mean()), 3) if (acc >= 0).any() else None,
+    }
+    # context: the unfused path on this GPU -- the library int8 GEMMs (hipBLASLt
+    # through torch._int_mm) writing int32 logits, float32 scaling by torch, and
+    # spec_verify over the stored [B, k+1, V] and [B, k, V] logits
+    try:
+        wt = x["weight"].t()
+        wd = wt if not own else x["draft_weight"].t()
+        wsd = x["weight_scale"] if not own else x["draft_weight_scale"]
+
+        def unfused():
+            tl = (torch._int_mm(x["hidden"], wt).float() * x["hidden_scale"][:, None]) * x["weight_scale"][None, :]
+            dl = (torch._int_mm(x["draft_hidden"], wd).float() * x["draft_hidden_scale"][:, None]) * wsd[None, :]
+            return tv.spec_verify(tl.view(B, k + 1, V), dl.view(B, k, V), x["tokens"], x["uniforms"], T, tv.SAMPLE,
+                                  return_probs=True)
+
+        for _ in range(3):
+            ref = unfused()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(ref[:3], out[:3]))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            unfused()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 10 * 1e3
+        line["unfused_context"] = {"op": "torch._int_mm x2 -> int32 logits, float32 scaling, spec_verify (SAMPLE)",
+                                   "us": round(us, 1), "fused_speedup": round(us / (float(callt.mean()) * 1e3), 3),
+                                   "same_outputs": bool(same)}
+    except Exception as ex:                                # context only; never fails the bench
+        line["unfused_context"] = {"error": f"{type(ex).__name__}: {str(ex)[:120]}"}
+    if args.cpu_seconds > 0:
+        from oracle.lmhead import lmhead_sample_ref
+        a = {n: (None if x[n] is None else x[n].cpu().numpy())
+             for n in ("hidden", "hidden_scale", "weight", "weight_scale", "draft_hidden", "draft_hidden_scale",
+                       "draft_weight", "draft_weight_scale", "tokens", "uniforms")}
+        n, t_cpu, b = 0, 0.0, 0
+        while t_cpu < args.cpu_seconds:
+            rt = np.arange(b * (k + 1), (b + 1) * (k + 1))
+            rd = np.arange(b * k, (b + 1) * k)
+            c0 = time.perf_counter()
+            lmhead_sample_ref(a["hidden"][rt], a["hidden_scale"][rt], a["weight"], a["weight_scale"],
+                              a["draft_hidden"][rd], a["draft_hidden_scale"][rd], a["draft_weight"],
+                              a["draft_weight_scale"], a["tokens"][b:b + 1], a["uniforms"][b:b + 1], T, 1, k)
+            t_cpu += time.perf_counter() - c0
+            n += 1
+            b = (b + 1) % B
+        line["cpu_baseline"] = {"value": round(n * k / t_cpu, 1), "unit": "positions/s",
+                                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "sample": f"{n} batch rows one at a time (2k+1 hidden rows against the "
+                                          f"whole heads), {t_cpu:.1f} s of oracle time"}
     print(json.dumps(line), flush=True)
     return 0
 

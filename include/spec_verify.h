@@ -264,6 +264,66 @@ int spec_verify_lmhead_timed(const int8_t* hidden, const float* hidden_scale, co
                              void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
 /*
+ * Sampling-mode verification fused with int8 LM heads (modified rejection
+ * sampling: "Speculative Decoding: The Physics of Stolen Time", section 2, the
+ * acceptance test and the residual; the speculative-decoding design note, "Cost /
+ * correctness constraints"; the heads as in spec_verify_lmhead). Target logits
+ *   t[m, v] = fl32( fl32( float32(acc_t[m, v]) * target_hidden_scale[m] ) * target_weight_scale[v] ),
+ *   acc_t[m, v] = sum_j target_hidden[m, j] * target_weight[v, j]   (exact integer),
+ * for target hidden row m = b*(k+1) + i, and draft logits likewise from draft
+ * hidden row m = b*k + i and the draft head. The outputs are exactly spec_verify's
+ * SAMPLE outputs on those float32 logits (same near-tie rules, same invalid rows).
+ * One pass of each head (an MFMA tile per 256 vocabulary rows and up to 256 hidden
+ * rows) folds its logits into per-row sums, top-2 and flags, and stores them into
+ * the workspace, where the draw of pass 2 reads the two rows each batch row draws
+ * from (target row a, and draft row a when a < k); the draft token's logit comes
+ * from an exact int8 dot product of its hidden row and head row.
+ *   target_hidden [B*(k+1), d] int8, target_weight [V, d] int8: DEVICE, 16-byte aligned.
+ *   target_hidden_scale [B*(k+1)], target_weight_scale [V] float32: DEVICE.
+ *   draft_hidden [B*k, d] int8 (16-byte aligned), draft_hidden_scale [B*k] float32:
+ *     DEVICE; may be NULL when k = 0.
+ *   draft_weight [V, d] int8, draft_weight_scale [V] float32: DEVICE, or both NULL
+ *     when the draft shares the target's head.
+ *   draft_tokens [B, k] int32, uniforms [B, k+1, 2] float32, accepted_len [B],
+ *     out_tokens [B, k+1], gap [B, k+1], target_prob [B, k], draft_prob [B, k]
+ *     (the last two may be NULL): DEVICE, as in spec_verify (SAMPLE mode).
+ * d must be a multiple of 128 in [128, 65536]; 1 <= B <= 2^21, 0 <= k <= SPEC_MAX_K,
+ * 1 <= V <= SPEC_MAX_V_SAMPLE, B*(k+1) <= 2^26; temperature finite and > 0.
+ * Workspace: at least spec_lmhead_sample_workspace_size() bytes (about
+ * B*(2k+1)*V*4 for the logits, plus per-tile records), 256-byte aligned, no
+ * initialisation needed, one call at a time. Enqueues six kernels (four when k = 0) on
+ * `stream`; no allocation, no host synchronisation. Errors: SPEC_ERR_SHAPE,
+ * SPEC_ERR_TEMP, SPEC_ERR_NULL, SPEC_ERR_ALIGN, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP
+ * (nothing enqueued).
+ */
+int spec_verify_lmhead_sample(const int8_t* target_hidden, const float* target_hidden_scale,
+                              const int8_t* target_weight, const float* target_weight_scale,
+                              const int8_t* draft_hidden, const float* draft_hidden_scale,
+                              const int8_t* draft_weight, const float* draft_weight_scale,
+                              const int32_t* draft_tokens, const float* uniforms, float temperature, int32_t B,
+                              int32_t k, int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens,
+                              float* gap, float* target_prob, float* draft_prob, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace spec_verify_lmhead_sample needs (0 if the sizes are invalid). Host-only. */
+size_t spec_lmhead_sample_workspace_size(int32_t B, int32_t k, int32_t V, int32_t d);
+
+/*
+ * spec_verify_lmhead_sample that also records, on `stream` (four hipEvent_t
+ * created by the caller), events[0] before the first head kernel, events[1] after
+ * the head passes, events[2] after the merges of their records, and events[3]
+ * after the decisions and the draw. Same results.
+ */
+int spec_verify_lmhead_sample_timed(const int8_t* target_hidden, const float* target_hidden_scale,
+                                    const int8_t* target_weight, const float* target_weight_scale,
+                                    const int8_t* draft_hidden, const float* draft_hidden_scale,
+                                    const int8_t* draft_weight, const float* draft_weight_scale,
+                                    const int32_t* draft_tokens, const float* uniforms, float temperature,
+                                    int32_t B, int32_t k, int32_t V, int32_t d, int32_t* accepted_len,
+                                    int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
+                                    void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation): spec_verify with the
  * library's own device scratch buffer in place of a caller workspace. Every other

@@ -360,6 +360,73 @@ def lmhead():
             assert acc[0] == -1 and acc[1] == -1 and acc[2] == -1 and acc[3] == 3
 
 
+def run_lmhead_sample(x, T, pool=1):
+    # set here, not at import: libraries built from older sources lack the symbol
+    from oracle.lmhead import lmhead_sample_ref
+    L.spec_verify_lmhead_sample.argtypes = [P, P, P, P, P, P, P, P, P, P, F, I, I, I, I, P, P, P, P, P, P, S, P]
+    L.spec_verify_lmhead_sample.restype = ctypes.c_int
+    L.spec_lmhead_sample_workspace_size.argtypes = [I, I, I, I]
+    L.spec_lmhead_sample_workspace_size.restype = S
+    B, k, V, d = x["B"], x["k"], x["V"], x["d"]
+    arr = {n: (None if x[n] is None else np.ascontiguousarray(x[n].numpy()))
+           for n in ("hidden", "hidden_scale", "weight", "weight_scale", "draft_hidden", "draft_hidden_scale",
+                     "draft_weight", "draft_weight_scale", "uniforms")}
+    tok = np.ascontiguousarray(x["tokens"].numpy().astype(np.int32))
+    acc = np.full(B, -7, np.int32)
+    out = np.full((B, k + 1), -7, np.int32)
+    gap = np.zeros((B, k + 1), np.float32)
+    tp = np.zeros((B, k), np.float32)
+    dp = np.zeros((B, k), np.float32)
+    nb = L.spec_lmhead_sample_workspace_size(B, k, V, d)
+    assert nb > 0
+    wsp = np.frombuffer(os.urandom(nb + 256), np.uint8).copy()
+    base = wsp.ctypes.data
+    off = (-base) % 256
+    L.spec_verify_emu_set_pool(pool)
+    rc = L.spec_verify_lmhead_sample(
+        ptr(arr["hidden"]), ptr(arr["hidden_scale"]), ptr(arr["weight"]), ptr(arr["weight_scale"]),
+        ptr(arr["draft_hidden"]), ptr(arr["draft_hidden_scale"]), ptr(arr["draft_weight"]),
+        ptr(arr["draft_weight_scale"]), ptr(tok), ptr(arr["uniforms"]), ctypes.c_float(T), B, k, V, d,
+        ptr(acc), ptr(out), ptr(gap), ptr(tp), ptr(dp), ctypes.c_void_p(base + off), nb, None)
+    assert rc == 0, (rc, L.spec_verify_last_error())
+    ref = lmhead_sample_ref(arr["hidden"], arr["hidden_scale"], arr["weight"], arr["weight_scale"],
+                            arr["draft_hidden"], arr["draft_hidden_scale"], arr["draft_weight"],
+                            arr["draft_weight_scale"], tok, arr["uniforms"], T, B, k)
+    flagged = ref.flagged(DELTA_ACC, DELTA_CDF)
+    same = (acc == ref.accepted_len) & (out == ref.out_tokens).all(axis=1)
+    bad = ~same & ~flagged
+    assert not bad.any(), (np.nonzero(bad)[0][:5], acc[bad][:3], ref.accepted_len[bad][:3],
+                           out[bad][:3], ref.out_tokens[bad][:3])
+    valid = ref.accepted_len >= 0
+    g, r = gap.astype(np.float64)[valid], ref.gap[valid]
+    assert (np.isnan(g) == np.isnan(r)).all() and (np.isinf(g) == np.isinf(r)).all()
+    fin = np.isfinite(r)
+    assert np.abs(g[fin] - r[fin]).max(initial=0.0) <= 1e-5
+    for gg, rr in ((tp, ref.p_tok), (dp, ref.q_tok)):
+        gg, rr = gg.astype(np.float64)[valid], rr[valid]
+        assert (np.isnan(gg) == np.isnan(rr)).all()
+        assert np.abs(gg - rr)[~np.isnan(rr)].max(initial=0) <= 1e-5
+    return acc
+
+
+@case
+def lmhead_sample():
+    # sampling-mode verify fused with int8 heads: shared and separate draft
+    # heads, partial tiles, k = 0, NaN / inf scales, a token outside [0, V)
+    for B, k, V, d, T, own, pool in ((3, 2, 700, 256, 1.0, False, 1), (50, 3, 300, 128, 0.7, True, 2),
+                                     (4, 0, 257, 128, 1.3, False, 1), (48, 3, 500, 128, 1.0, False, 2),
+                                     (16, 5, 1500, 384, 0.3, True, 2)):
+        x = workloads.make_lmhead_sample(B, k, V, d, seed=1, draft_head=own)
+        if B >= 48:
+            x["hidden_scale"][0] = float("nan")            # batch row 0: NaN target logits
+            x["draft_hidden_scale"][3] = float("inf")      # batch row 1: +-inf / NaN draft logits
+            x["tokens"][2, 1] = V                          # batch row 2: token out of range
+        acc = run_lmhead_sample(x, T, pool=pool)
+        if B >= 48:
+            assert acc[0] == -1 and acc[1] == -1 and acc[2] == -1
+        print("  accepted", np.bincount(acc[acc >= 0], minlength=k + 1).tolist(), flush=True)
+
+
 if __name__ == "__main__":
     names = sys.argv[1:] or list(CASES)
     for nm in names:

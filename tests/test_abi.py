@@ -27,7 +27,7 @@ def test_exports_match_header():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     exported = {s for s in exported if s.startswith("spec_")}
     assert declared() == exported
-    assert len(exported) == 14
+    assert len(exported) == 17
 
 
 def test_version():
@@ -217,6 +217,55 @@ def test_lmhead_rejects_synchronously(kw, code):
     rc = tv.lib().spec_verify_lmhead_timed(a["hidden"], a["h_scale"], a["weight"], a["w_scale"], a["tokens"],
                                            a["B"], a["k"], a["V"], a["d"], a["acc"], a["out"], a["gap"],
                                            a["ws"], a["ws_bytes"], None, ctypes.cast(ev, ctypes.c_void_p))
+    assert rc in (code, -1)
+
+
+def test_lmhead_sample_workspace_size():
+    L = tv.lib()
+    n = L.spec_lmhead_sample_workspace_size(256, 3, 128256, 4096)
+    assert n > 0 and n % 256 == 0
+    # per-tile records of both heads and the two recomputed logit rows per batch row
+    assert n > 2 * 256 * 128256 * 4
+    assert L.spec_lmhead_sample_workspace_size(0, 3, 100, 128) == 0
+    assert L.spec_lmhead_sample_workspace_size(1, 65, 100, 128) == 0
+    assert L.spec_lmhead_sample_workspace_size(1, 3, 100, 100) == 0
+    assert L.spec_lmhead_sample_workspace_size(1, 3, (1 << 23) + 1, 128) == 0
+    assert L.spec_lmhead_sample_workspace_size(1, 0, 100, 128) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"B": 0}, -2),
+    ({"k": 65}, -2),
+    ({"d": 192}, -2),
+    ({"V": (1 << 23) + 1}, -2),
+    ({"T": 0.0}, -5),
+    ({"T": float("inf")}, -5),
+    ({"hidden": None}, -1),
+    ({"uniforms": None}, -1),
+    ({"dhidden": None}, -1),
+    ({"tokens": None}, -1),
+    ({"dweight": FAKE}, -1),                  # a draft head without its scales
+    ({"gap": None}, -1),
+    ({"hidden": FAKE + 4}, -7),
+    ({"dhidden": FAKE + 8}, -7),
+    ({"tprob": FAKE + 2}, -7),
+    ({"ws": None}, -6),
+    ({"ws_bytes": 256}, -6),
+    ({"ws": 0x100010}, -7),
+])
+def test_lmhead_sample_rejects_synchronously(kw, code):
+    a = dict(hidden=FAKE, h_scale=FAKE, weight=FAKE, w_scale=FAKE, dhidden=FAKE, dh_scale=FAKE, dweight=None,
+             dw_scale=None, tokens=FAKE, uniforms=FAKE, T=1.0, B=4, k=3, V=1000, d=256, acc=FAKE, out=FAKE,
+             gap=FAKE, tprob=None, dprob=None, ws=0x100000, ws_bytes=1 << 26)
+    a.update(kw)
+    args = (a["hidden"], a["h_scale"], a["weight"], a["w_scale"], a["dhidden"], a["dh_scale"], a["dweight"],
+            a["dw_scale"], a["tokens"], a["uniforms"], a["T"], a["B"], a["k"], a["V"], a["d"], a["acc"],
+            a["out"], a["gap"], a["tprob"], a["dprob"], a["ws"], a["ws_bytes"], None)
+    rc = tv.lib().spec_verify_lmhead_sample(*args)
+    assert rc == code, binding.last_error()
+    assert binding.last_error()
+    ev = (ctypes.c_void_p * 4)(None, None, None, None)
+    rc = tv.lib().spec_verify_lmhead_sample_timed(*args, ctypes.cast(ev, ctypes.c_void_p))
     assert rc in (code, -1)
 
 

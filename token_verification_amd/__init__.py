@@ -18,5 +18,6 @@ from .binding import (  # noqa: F401
     spec_gate,
     spec_verify,
     spec_verify_lmhead,
+    spec_verify_lmhead_sample,
     workspace_size,
 )

@@ -83,6 +83,14 @@ def lib():
                 L.spec_verify_lmhead_timed.restype = ctypes.c_int
                 L.spec_lmhead_workspace_size.argtypes = [I, I, I, I]
                 L.spec_lmhead_workspace_size.restype = S
+                L.spec_verify_lmhead_sample.argtypes = [P, P, P, P, P, P, P, P, P, P, F, I, I, I, I,
+                                                        P, P, P, P, P, P, S, P]
+                L.spec_verify_lmhead_sample.restype = ctypes.c_int
+                L.spec_verify_lmhead_sample_timed.argtypes = [P, P, P, P, P, P, P, P, P, P, F, I, I, I, I,
+                                                              P, P, P, P, P, P, S, P, P]
+                L.spec_verify_lmhead_sample_timed.restype = ctypes.c_int
+                L.spec_lmhead_sample_workspace_size.argtypes = [I, I, I, I]
+                L.spec_lmhead_sample_workspace_size.restype = S
                 L.spec_verify_last_error.restype = ctypes.c_char_p
                 L.spec_verify_version.restype = ctypes.c_char_p
                 _lib = L
@@ -445,6 +453,104 @@ def spec_verify_lmhead(hidden: torch.Tensor, hidden_scale: torch.Tensor, weight:
         rc = lib().spec_verify_lmhead_timed(*args, ctypes.cast(arr, ctypes.c_void_p))
     else:
         rc = lib().spec_verify_lmhead(*args)
+    if rc != 0:
+        raise SpecVerifyError(rc, last_error())
+    return out
+
+
+def spec_verify_lmhead_sample(hidden: torch.Tensor, hidden_scale: torch.Tensor, weight: torch.Tensor,
+                              weight_scale: torch.Tensor, draft_hidden: Optional[torch.Tensor],
+                              draft_hidden_scale: Optional[torch.Tensor], tokens: torch.Tensor,
+                              uniforms: torch.Tensor, temperature: float, *,
+                              draft_weight: Optional[torch.Tensor] = None,
+                              draft_weight_scale: Optional[torch.Tensor] = None, return_probs: bool = True,
+                              workspace: Optional[torch.Tensor] = None, out: Optional[VerifyResult] = None,
+                              phase_events=None) -> VerifyResult:
+    """Sampling-mode verification fused with int8 LM heads (see include/spec_verify.h).
+
+    hidden int8 [B*(k+1), d] and hidden_scale float32 [B*(k+1)]: the target's
+    rows (row b*(k+1)+i: position i of batch row b); draft_hidden int8 [B*k, d]
+    and draft_hidden_scale [B*k] (None when k = 0); weight int8 [V, d] and
+    weight_scale float32 [V]: the target's head, which the draft shares unless
+    draft_weight / draft_weight_scale are given; tokens int32 [B, k]; uniforms
+    float32 [B, k+1, 2]. With phase_events (four torch.cuda.Event created with
+    enable_timing=True) the call records them before the head passes, after
+    them, after the merges of their records, and after the decisions and the
+    draw.
+    """
+    if tokens.dim() != 2 or tokens.dtype != torch.int32:
+        raise ValueError("tokens must be int32 [B, k]")
+    B, k = tokens.shape
+    for t, nm in ((hidden, "hidden"), (weight, "weight")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != torch.int8 or not t.is_cuda:
+            raise ValueError(f"{nm} must be an int8 2-D device tensor")
+    M, d = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    if weight.shape[1] != d:
+        raise ValueError("hidden and weight must share d")
+    if M != B * (k + 1):
+        raise ValueError("hidden must hold B*(k+1) rows")
+    if hidden_scale.shape != (M,) or weight_scale.shape != (V,) or hidden_scale.dtype != torch.float32 \
+            or weight_scale.dtype != torch.float32:
+        raise ValueError("hidden_scale [B*(k+1)] and weight_scale [V] must be float32")
+    if k > 0:
+        if draft_hidden is None or draft_hidden_scale is None:
+            raise ValueError("draft_hidden and draft_hidden_scale are required when k > 0")
+        if draft_hidden.dtype != torch.int8 or tuple(draft_hidden.shape) != (B * k, d):
+            raise ValueError("draft_hidden must be int8 [B*k, d]")
+        if draft_hidden_scale.dtype != torch.float32 or tuple(draft_hidden_scale.shape) != (B * k,):
+            raise ValueError("draft_hidden_scale must be float32 [B*k]")
+    else:
+        draft_hidden = draft_hidden_scale = None
+    if (draft_weight is None) != (draft_weight_scale is None):
+        raise ValueError("give draft_weight and draft_weight_scale together, or neither")
+    if draft_weight is not None:
+        if draft_weight.dtype != torch.int8 or tuple(draft_weight.shape) != (V, d):
+            raise ValueError("draft_weight must be int8 [V, d]")
+        if draft_weight_scale.dtype != torch.float32 or tuple(draft_weight_scale.shape) != (V,):
+            raise ValueError("draft_weight_scale must be float32 [V]")
+    if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, k + 1, 2):
+        raise ValueError("uniforms must be float32 [B, k+1, 2]")
+    for t in (hidden, hidden_scale, weight, weight_scale, tokens, uniforms, draft_hidden, draft_hidden_scale,
+              draft_weight, draft_weight_scale):
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    probs = return_probs and k > 0
+    if out is None:
+        out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                           torch.empty((B, k + 1), dtype=torch.float32, device=dev),
+                           torch.empty((B, k), dtype=torch.float32, device=dev) if probs else None,
+                           torch.empty((B, k), dtype=torch.float32, device=dev) if probs else None)
+    else:
+        _check_out(out, B, k, dev, probs)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = int(lib().spec_lmhead_sample_workspace_size(B, k, V, d))
+    if need == 0:
+        raise SpecVerifyError(-2, f"unsupported sizes B={B} k={k} V={V} d={d}")
+    ws = _workspace(dev, stream, need) if workspace is None else _user_workspace(workspace, dev, need)
+    args = (_ptr(hidden), _ptr(hidden_scale), _ptr(weight), _ptr(weight_scale), _ptr(draft_hidden),
+            _ptr(draft_hidden_scale), _ptr(draft_weight), _ptr(draft_weight_scale), _ptr(tokens), _ptr(uniforms),
+            float(temperature), B, k, V, d, _ptr(out.accepted_len), _ptr(out.out_tokens), _ptr(out.gap),
+            _ptr(out.target_prob), _ptr(out.draft_prob),
+            ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), ctypes.c_void_p(stream))
+    if phase_events is not None:
+        if len(phase_events) != 4:
+            raise ValueError("phase_events must hold four events")
+        handles = []
+        for ev in phase_events:
+            if not ev.cuda_event:                         # torch creates events lazily
+                ev.record(torch.cuda.current_stream(dev))
+            handles.append(ev.cuda_event)
+        arr = (ctypes.c_void_p * 4)(*handles)
+        rc = lib().spec_verify_lmhead_sample_timed(*args, ctypes.cast(arr, ctypes.c_void_p))
+    else:
+        rc = lib().spec_verify_lmhead_sample(*args)
     if rc != 0:
         raise SpecVerifyError(rc, last_error())
     return out

@@ -1305,9 +1305,10 @@ __device__ inline Pass2 pass2_rows(const Params& P, int b, const BatchRec& br) {
     const int k = P.k, V = P.V, a = br.a < 0 ? 0 : br.a;
     Pass2 Q;
     Q.resid = a < br.kb;
-    Q.rowT = static_cast<const char*>(P.tgt) + (static_cast<size_t>(b) * (k + 1) + a) * V * E::ES;
-    Q.rowD = Q.resid ? static_cast<const char*>(P.dft) + (static_cast<size_t>(b) * k + a) * V * E::ES
-                     : Q.rowT;
+    const size_t rt = static_cast<size_t>(b) * (k + 1) + a;
+    const size_t rd = static_cast<size_t>(b) * k + a;
+    Q.rowT = static_cast<const char*>(P.tgt) + rt * V * E::ES;
+    Q.rowD = Q.resid ? static_cast<const char*>(P.dft) + rd * V * E::ES : Q.rowT;
     Q.bytes = static_cast<unsigned>(V) * E::ES;
     Q.invT = P.invT;
     const double mp = br.mp, mq = Q.resid ? static_cast<double>(br.mq) : mp;
@@ -2079,16 +2080,45 @@ struct HeadRec {                        // one hidden row over one vocabulary ti
     int flags;                          // bit 0: a NaN logit
 };
 
+// Sampling mode: one hidden row over one vocabulary tile, in pass 1's terms
+// (top-2, the sum 2^(x*c - ref) for an integer ref, a NaN flag).
+struct alignas(8) HeadRecS {
+    float t1, t2, ref;
+    int flags;                          // bit 0: a NaN logit
+    double s;
+};
+
+// The epilogue a head workgroup runs on its accumulators.
+enum : int { EPI_GREEDY = 0, EPI_SAMPLE = 1 };
+
 struct HeadParams {
     const signed char* h;               // [M, d]
     const float* hs;                    // [M]
     const signed char* w;               // [V, d]
     const float* ws;                    // [V]
-    HeadRec* rec;                       // [M, nvt]
+    HeadRec* rec;                       // [M, nvt] (greedy)
     TileRec* tiles;                     // [2M], row m's merged record at 2m
     int M, V, d;
     int nvt, nmt;                       // vocabulary and hidden-row tiles
+    // sampling: records, the exponent scale, and which draft token each row holds
+    HeadRecS* recs;                     // [M, nvt]
+    float ch, cl;                       // log2(e)/T = ch + cl, as pass 1's
+    const int* tok;                     // draft tokens [B, k]
+    int k;
+    int role;                           // 0: target rows b*(k+1)+i, 1: draft rows b*k+i
+    int rpb;                            // rows per batch row of the merged records (2k+1)
+    float* logits;                      // [M, V] float32, every logit (sampling)
+    double* exptab;                     // pass 2's exp table, written by one merge (or NULL)
 };
+
+// The draft token whose logit hidden row m carries (-1: none; the bonus row).
+__device__ inline int head_row_token(const HeadParams& H, int m) {
+    if (H.role == 0) {
+        const int i = m % (H.k + 1);
+        return i < H.k ? H.tok[static_cast<size_t>(m / (H.k + 1)) * H.k + i] : -1;
+    }
+    return H.tok[m];
+}
 
 // Fold logit x of vocabulary index v (ascending within a lane) into a top-2
 // and first argmax; NaN never enters.
@@ -2138,6 +2168,77 @@ __device__ inline void head_epilogue(const HeadParams& H, const i32x16 (&acc)[4]
                 head_take(x, v, T1[mb], T2[mb], I1[mb]);
             }
     }
+}
+
+// Sampling mode: scale one lane's accumulators to logits and fold them, for
+// each of its MB hidden rows, into pass 1's terms over the lane's 64 logits,
+// eight at a time and in one pass, as pass 1's lanes do: the top-2, a NaN
+// flag, and the sum 2^(x*c - ref) whose integer reference follows the running
+// maximum (ref = ceil(max * ch), the sum rescaled by an exact power of two
+// when it moves; eight terms summed in float32, then in double; a +inf logit
+// poisons the sum). WB adds -inf past V (the tile edge) and 0 elsewhere, so
+// the edge costs no per-entry compare: fmaf(a, w, 0) rounds as a * w does.
+// The code has no branch, so the accumulators stay in place.
+template <int MB>
+__device__ inline void head_epilogue_sample(const HeadParams& H, const i32x16 (&acc)[4][MB], const float* WS,
+                                            const float* WB, int mrow, int vw, int hi, HeadRecS (&o)[MB]) {
+    float hsv[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = mrow + 32 * mb;
+        hsv[mb] = m < H.M ? H.hs[m] : 0.0f;
+        o[mb] = HeadRecS{-INFINITY, -INFINITY, 0.0f, 0, 0.0};
+    }
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+        const int vloc = 128 * vw + 32 * vb + 4 * hi;     // the lane's entries: vloc + 8*(q/4) + q%4
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            float wsv[8], wbv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int q = 8 * g + j;
+                wsv[j] = WS[vloc + 8 * (q >> 2) + (q & 3)];
+                wbv[j] = WB[vloc + 8 * (q >> 2) + (q & 3)];
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                HeadRecS& r = o[mb];
+                const float before = r.t1;
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float y = fmaf(static_cast<float>(acc[vb][mb][8 * g + j]) * hsv[mb], wsv[j], wbv[j]);
+                    r.flags |= y != y ? 1 : 0;
+                    r.t2 = fmaxf(r.t2, fminf(r.t1, y));
+                    r.t1 = fmaxf(r.t1, y);
+                    x[j] = y;
+                }
+                // the shift is 0 unless the maximum rose
+                const float nr = r.t1 > before ? ceilf(r.t1 * H.ch) : r.ref;
+                const bool bad = !(nr <= 3.0e38f);                 // +inf logit or overflow: poison
+                const int sh = static_cast<int>(fmaxf(r.ref - nr, -2000.0f));
+                r.s = bad ? __builtin_nan("") : ldexp(r.s, sh);
+                r.ref = bad ? 0.0f : nr;
+                float e[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) e[j] = exp_term(x[j], H.ch, H.cl, r.ref);
+#pragma unroll
+                for (int w = 1; w < 8; w <<= 1) {
+#pragma unroll
+                    for (int j = 0; j + w < 8; j += 2 * w) e[j] += e[j + w];
+                }
+                r.s += static_cast<double>(e[0]);
+            }
+        }
+    }
+}
+
+// Merge two sampling records of one hidden row (disjoint vocabulary ranges).
+__device__ inline void head_recs_merge(HeadRecS& a, const HeadRecS& b) {
+    top2_merge(a.t1, a.t2, b.t1, b.t2);
+    sref_merge(a.ref, a.s, b.ref, b.s);
+    a.flags |= b.flags;
 }
 
 // What a head workgroup needs besides its main loop: its tile (workgroup b
@@ -2193,6 +2294,85 @@ struct HeadTile {
             H.rec[static_cast<size_t>(m0 + t) * H.nvt + vt] = o;
         }
     }
+
+    // Sampling: the same exchange with pass 1's terms; one HeadRecS per row.
+    __device__ void finish_sample(const HeadParams& H, const i32x16 (&acc)[4][MB], unsigned char* S) const {
+        HeadRecS o[MB];
+        const int mrow = m0 + 32 * MB * mw + r;
+        float* WS = reinterpret_cast<float*>(S + 2 * BM * sizeof(HeadRecS));
+        float* WB = WS + HV;
+        static_assert(NTH == HV, "one weight scale per thread");
+        WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+        WB[t] = v0 + t < H.V ? 0.0f : -INFINITY;
+        __syncthreads();
+        head_epilogue_sample<MB>(H, acc, WS, WB, mrow, vw, hi, o);
+        HeadRecS* L = reinterpret_cast<HeadRecS*>(S);      // [2][BM]: per vocabulary wave
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            HeadRecS p;
+            p.t1 = __shfl_xor(o[mb].t1, 32, 64); p.t2 = __shfl_xor(o[mb].t2, 32, 64);
+            p.ref = __shfl_xor(o[mb].ref, 32, 64); p.flags = __shfl_xor(o[mb].flags, 32, 64);
+            p.s = __shfl_xor(o[mb].s, 32, 64);
+            head_recs_merge(o[mb], p);
+            if (hi == 0) L[vw * BM + 32 * MB * mw + 32 * mb + r] = o[mb];
+        }
+        __syncthreads();
+        if (t < nm) {
+            HeadRecS a = L[t];
+            head_recs_merge(a, L[BM + t]);
+            H.recs[static_cast<size_t>(m0 + t) * H.nvt + vt] = a;
+        }
+    }
+
+    // Logit store: logits[m, v] in float32 for every row m < M and v < V. One
+    // hidden-row block mb at a time, the 64 rows x 256 logits of the tile go
+    // through LDS (row pitch 260 floats, so the 16-byte writes of 16
+    // consecutive rows hit distinct banks), and each wave then stores whole
+    // rows: 64 lanes x 16 bytes = one contiguous 1 KB segment per instruction,
+    // where the accumulator layout would give each store 32 rows.
+    __device__ void finish_logits(const HeadParams& H, const i32x16 (&acc)[4][MB], unsigned char* S) const {
+        constexpr int PITCH = HV + 4;
+        float* R = reinterpret_cast<float*>(S);                         // [64][PITCH]
+        float* WS = R + 64 * PITCH;
+        WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+        const bool vec = (H.V & 3) == 0;                   // rows start 16-byte aligned
+        const int lr = 32 * mw + r;                        // the lane's row in the slab
+        __syncthreads();
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = m0 + 32 * MB * mw + 32 * mb + r;
+            const float hsv = m < H.M ? H.hs[m] : 0.0f;
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int col = 128 * vw + 32 * vb + 8 * c + 4 * hi;
+                    f32x4 y;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        y[j] = (static_cast<float>(acc[vb][mb][4 * c + j]) * hsv) * WS[col + j];
+                    *reinterpret_cast<f32x4*>(R + lr * PITCH + col) = y;
+                }
+            __syncthreads();
+            const int ch = t & 63, v = v0 + 4 * ch;
+#pragma unroll 4
+            for (int it = 0; it < 16; ++it) {
+                const int row = 4 * it + (t >> 6);
+                const int mm = m0 + 32 * MB * (row >> 5) + 32 * mb + (row & 31);
+                if (mm >= H.M) continue;
+                const f32x4 y = *reinterpret_cast<const f32x4*>(R + row * PITCH + 4 * ch);
+                float* dst = H.logits + static_cast<size_t>(mm) * H.V + v;
+                if (vec && v + 3 < H.V) {
+                    __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(dst));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (v + j < H.V) __builtin_nontemporal_store(y[j], dst + j);
+                }
+            }
+            __syncthreads();
+        }
+    }
 };
 
 template <int MB>
@@ -2233,7 +2413,7 @@ __device__ inline void wait_stages(int stages) {
     else __builtin_amdgcn_s_waitcnt(vm_wait(0));
 }
 
-template <int MB, int NBUF>
+template <int MB, int NBUF, int EPI = EPI_GREEDY>
 __device__ __attribute__((always_inline)) inline void head_main(const HeadParams& H) {
     constexpr int BM = 64 * MB;
     constexpr int ST = (HV + BM) * HKW;                    // bytes per stage
@@ -2303,7 +2483,16 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
         mma(1);
     }
     __syncthreads();                                       // every wave is done with the stages
-    w.finish(H, acc, S);
+    // the epilogues reuse the stage buffers
+    static_assert(NBUF * ST >= 2 * BM * static_cast<int>(sizeof(HeadRec)) + HV * 4, "greedy exchange");
+    static_assert(NBUF * ST >= 2 * BM * static_cast<int>(sizeof(HeadRecS)) + 2 * HV * 4, "sampling exchange");
+    static_assert(NBUF * ST >= (64 * (HV + 4) + HV) * 4, "logit slab");
+    if constexpr (EPI == EPI_SAMPLE) {
+        w.finish_sample(H, acc, S);
+        w.finish_logits(H, acc, S);                        // after the exchange: the LDS is free again
+    } else {
+        w.finish(H, acc, S);
+    }
 }
 
 // 256-row tiles: 128 x 128 per wave, one wave per SIMD (256 accumulator
@@ -2317,6 +2506,66 @@ __global__ __launch_bounds__(NTH) void head_kernel_mid(HeadParams H) { head_main
 // CU interleave), three 24 KB stage buffers.
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_narrow(HeadParams H) {
     head_main<2, 3>(H);
+}
+
+// Sampling mode, with the same tiles: pass 1's terms per row and vocabulary
+// tile, and every logit stored for the draw.
+__global__ __launch_bounds__(NTH) void head_kernel_wide_s(HeadParams H) { head_main<4, 4, EPI_SAMPLE>(H); }
+__global__ __launch_bounds__(NTH) void head_kernel_mid_s(HeadParams H) { head_main<3, 4, EPI_SAMPLE>(H); }
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_narrow_s(HeadParams H) {
+    head_main<2, 3, EPI_SAMPLE>(H);
+}
+
+// Sampling mode, one wave per hidden row: merge its vocabulary-tile records
+// (in tile order per lane, then a fixed butterfly) into pass 1's record of
+// its row: target row b*(k+1)+i is row b*rpb+i, draft row b*k+i is row
+// b*rpb+k+1+i, at slot 2*row (pass 1's slot rule with one slice per row).
+__global__ __launch_bounds__(NT) void head_merge_sample_kernel(HeadParams H) {
+    if (H.exptab && blockIdx.x == 0)
+        for (int j = static_cast<int>(threadIdx.x); j < EXP_N; j += NT) H.exptab[j] = exp2(static_cast<double>(j) / EXP_N);
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int m = static_cast<int>(blockIdx.x) * NWAVE + (static_cast<int>(threadIdx.x) >> 6);
+    if (m >= H.M) return;                                  // uniform per wave
+    HeadRecS a{-INFINITY, -INFINITY, 0.0f, 0, 0.0};
+    const HeadRecS* R = H.recs + static_cast<size_t>(m) * H.nvt;
+    for (int j = lane; j < H.nvt; j += 64) head_recs_merge(a, R[j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        HeadRecS p;
+        p.t1 = __shfl_xor(a.t1, off, 64); p.t2 = __shfl_xor(a.t2, off, 64);
+        p.ref = __shfl_xor(a.ref, off, 64); p.flags = __shfl_xor(a.flags, off, 64);
+        p.s = __shfl_xor(a.s, off, 64);
+        head_recs_merge(a, p);
+    }
+    // the draft token's logit, from the same int8 rows: the int32 dot product
+    // is exact in any order, so it equals the tile's accumulator entry, and
+    // it is scaled as the epilogue scales it
+    const int tok = head_row_token(H, m);
+    const bool has = tok >= 0 && tok < H.V;                // uniform per wave
+    float lx = 0.0f;
+    if (has) {
+        const int* hr = reinterpret_cast<const int*>(H.h + static_cast<size_t>(m) * H.d);
+        const int* wr = reinterpret_cast<const int*>(H.w + static_cast<size_t>(tok) * H.d);
+        int dot = 0;
+        for (int j = lane; j < H.d / 4; j += 64) {
+            const int x = hr[j], y = wr[j];
+#pragma unroll
+            for (int b = 0; b < 32; b += 8)
+                dot += static_cast<int>(static_cast<signed char>(x >> b)) * static_cast<int>(static_cast<signed char>(y >> b));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        lx = fmaf(static_cast<float>(dot) * H.hs[m], H.ws[tok], 0.0f);
+    }
+    if (lane == 0) {
+        const int k = H.k;
+        const long long row = H.role == 0 ? static_cast<long long>(m / (k + 1)) * H.rpb + m % (k + 1)
+                                          : static_cast<long long>(m / k) * H.rpb + k + 1 + m % k;
+        TileRec tr;
+        tr.t1 = a.t1; tr.t2 = a.t2; tr.ref = a.ref; tr.idx = 0x7fffffff; tr.s = a.s; tr.lx = lx;
+        tr.flags = (a.flags & 1) | (has ? 2 : 0);
+        H.tiles[2 * row] = tr;
+    }
 }
 
 // One wave per hidden row: merge its vocabulary-tile records into the row's
@@ -2465,6 +2714,34 @@ int seg_blocks_per_cu(int dev) {
     return n;
 }
 
+// Pass 2 and the draw of a sampling call whose pass-1 records (and pass 2's
+// tables) are in place: one resident round of workgroups split evenly over
+// the batch rows, then one draw workgroup per batch row. ev (or null): ev[0]
+// after pass 2, ev[1] after the draw.
+template <class E>
+hipError_t launch_pass2(Params& P, int dev, int ncu, hipStream_t s, hipEvent_t const* ev) {
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+    long long slots = static_cast<long long>(ncu) *
+        (P.vec_ok ? seg_blocks_per_cu<E, true>(dev) : seg_blocks_per_cu<E, false>(dev));
+    if (slots > SLOTS_CAP) slots = SLOTS_CAP;
+    long long W = (slots + P.B - 1) / P.B;
+    if (W > P.wpb) W = P.wpb;                              // the plan's bound (workspace size)
+    if (W < 1) W = 1;
+    P.wpb = static_cast<int>(W);
+    P.nseg = P.wpb * (NTS / 64);
+    P.vps = (P.nvec + P.nseg - 1) / P.nseg;
+    const unsigned G2 = static_cast<unsigned>(static_cast<long long>(P.B) * W);
+    if (P.vec_ok) hipLaunchKernelGGL((seg_kernel<E, true>), dim3(G2), dim3(NTS), 0, s, P);
+    else hipLaunchKernelGGL((seg_kernel<E, false>), dim3(G2), dim3(NTS), 0, s, P);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark(0);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((draw_kernel<E>), dim3(P.B), dim3(NT2), 0, s, P);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(1);
+    return e;
+}
+
 // Phase events of spec_verify_timed (null otherwise): ev[0] before the first
 // kernel, ev[1] after pass 1, ev[2] after the decisions and pass 2, ev[3] after
 // the draw (greedy mode records ev[2] and ev[3] together).
@@ -2512,26 +2789,7 @@ hipError_t launch_all(Params& P, int dev, int ncu, hipStream_t s, hipEvent_t con
         if (e == hipSuccess) e = mark(3);
         return e;
     }
-    // pass 2: one resident round of workgroups, split evenly over the batch rows
-    long long slots = static_cast<long long>(ncu) *
-        (P.vec_ok ? seg_blocks_per_cu<E, true>(dev) : seg_blocks_per_cu<E, false>(dev));
-    if (slots > SLOTS_CAP) slots = SLOTS_CAP;
-    long long W = (slots + P.B - 1) / P.B;
-    if (W > P.wpb) W = P.wpb;                              // the plan's bound (workspace size)
-    if (W < 1) W = 1;
-    P.wpb = static_cast<int>(W);
-    P.nseg = P.wpb * (NTS / 64);
-    P.vps = (P.nvec + P.nseg - 1) / P.nseg;
-    const unsigned G2 = static_cast<unsigned>(static_cast<long long>(P.B) * W);
-    if (P.vec_ok) hipLaunchKernelGGL((seg_kernel<E, true>), dim3(G2), dim3(NTS), 0, s, P);
-    else hipLaunchKernelGGL((seg_kernel<E, false>), dim3(G2), dim3(NTS), 0, s, P);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = mark(2);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((draw_kernel<E>), dim3(P.B), dim3(NT2), 0, s, P);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = mark(3);
-    return e;
+    return launch_pass2<E>(P, dev, ncu, s, ev ? ev + 2 : nullptr);
 }
 
 struct GateOut {
@@ -2542,13 +2800,32 @@ struct GateOut {
 };
 
 // Fill the launch parameters of checked arguments and enqueue the kernels.
+// c = ch + cl. ch: c rounded toward zero to (bf16) 16 or (fp32) 24
+// significant bits, so x*ch is exact for bf16 x. cl: the rest, kept strictly
+// positive so that x = -inf gives -inf (not -inf + inf) in x*ch - ref + x*cl.
+void split_c(double c, int dtype, float& ch, float& cl) {
+    ch = static_cast<float>(c);
+    uint32_t u;
+    memcpy(&u, &ch, 4);
+    if (static_cast<double>(ch) > c) --u;                  // toward zero
+    const uint32_t unit = dtype == SPEC_DTYPE_BF16 ? 0x100u : 0x1u;
+    u &= ~(unit - 1u);
+    memcpy(&ch, &u, 4);
+    if (static_cast<double>(ch) == c && u >= unit) {
+        u -= unit;
+        memcpy(&ch, &u, 4);
+    }
+    cl = static_cast<float>(c - static_cast<double>(ch));
+    if (!(cl > 0.0f)) cl = 1.17549435e-38f;                // smallest normal float
+}
+
 int enqueue(const Plan& plan, const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
             const int32_t* draft_len, const float* uniforms, float temperature, int mode, int32_t B, int32_t k,
             int32_t V, int dtype, int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
             float* draft_prob, const GateOut* gate, void* workspace, void* stream,
             void* const* events = nullptr) {
     char* ws = static_cast<char*>(workspace);
-    Params P;
+    Params P{};
     P.tgt = target_logits;
     P.dft = draft_logits;
     P.tok = draft_tokens;
@@ -2576,23 +2853,8 @@ int enqueue(const Plan& plan, const void* target_logits, const void* draft_logit
     P.force_exact = (fe && fe[0] == '1') ? 1 : 0;
     const double Td = mode == SPEC_MODE_SAMPLE ? static_cast<double>(temperature) : 1.0;
     const double c = 1.4426950408889634 / Td;
-    // c = ch + cl. ch: c rounded toward zero to (bf16) 16 or (fp32) 24
-    // significant bits, so x*ch is exact for bf16 x. cl: the rest, kept
-    // strictly positive so that x = -inf gives -inf (not -inf + inf) in
-    // x*ch - ref + x*cl.
-    float ch = static_cast<float>(c);
-    uint32_t u;
-    memcpy(&u, &ch, 4);
-    if (static_cast<double>(ch) > c) --u;                  // toward zero
-    const uint32_t unit = dtype == SPEC_DTYPE_BF16 ? 0x100u : 0x1u;
-    u &= ~(unit - 1u);
-    memcpy(&ch, &u, 4);
-    if (static_cast<double>(ch) == c && u >= unit) {
-        u -= unit;
-        memcpy(&ch, &u, 4);
-    }
-    float cl = static_cast<float>(c - static_cast<double>(ch));
-    if (!(cl > 0.0f)) cl = 1.17549435e-38f;                // smallest normal float
+    float ch, cl;
+    split_c(c, dtype, ch, cl);
     P.ch = ch;
     P.cl = cl;
     P.c = static_cast<double>(P.ch) + static_cast<double>(P.cl);
@@ -2689,18 +2951,23 @@ struct HeadPlan {
     size_t o_rec, o_tiles, total;
 };
 
+// Hidden-row blocks per wave for M rows: wider tiles reuse each staged
+// operand more; a narrower one when it pads the hidden rows clearly less
+// (e.g. 384 rows: 2 x 192, not 2 x 256).
+int head_mb(long long M) {
+    const long long pad4 = (M + 255) / 256 * 256, pad3 = (M + 191) / 192 * 192, pad2 = (M + 127) / 128 * 128;
+    if (pad4 * 10 <= (pad3 < pad2 ? pad3 : pad2) * 11) return 4;
+    if (pad3 * 10 <= pad2 * 11) return 3;
+    return 2;
+}
+
 bool make_head_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadPlan& p) {
     if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K || V < 1 || V > (1 << 29)) return false;
     if (d < HK || d > HEAD_MAX_D || d % HK != 0) return false;
     const long long M = static_cast<long long>(B) * (k + 1);
     if (M > (1 << 26)) return false;
     const long long nvt = (V + HV - 1) / HV;
-    // wider tiles reuse each staged operand more; a narrower one when it pads
-    // the hidden rows clearly less (e.g. 384 rows: 2 x 192, not 2 x 256)
-    const long long pad4 = (M + 255) / 256 * 256, pad3 = (M + 191) / 192 * 192, pad2 = (M + 127) / 128 * 128;
-    if (pad4 * 10 <= (pad3 < pad2 ? pad3 : pad2) * 11) p.mb = 4;
-    else if (pad3 * 10 <= pad2 * 11) p.mb = 3;
-    else p.mb = 2;
+    p.mb = head_mb(M);
     const long long nmt = (M + 64 * p.mb - 1) / (64 * p.mb);
     if (nvt * nmt >= (1ll << 31)) return false;
     p.M = static_cast<int>(M);
@@ -2825,6 +3092,169 @@ int scratch_ptr(int dev, void** out) {
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------ LM head, sampling mode
+
+struct HeadSamplePlan {
+    Plan pv;                            // pass 2's part of the verify plan (batch records, segments)
+    int nvt, mbT, mbD;
+    size_t o_recT, o_recD, o_tiles, o_bat, o_segs, o_exp, o_lt, o_ld, total;
+};
+
+bool make_head_sample_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadSamplePlan& p) {
+    if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K || V < 1 || V > (1 << 29)) return false;
+    if (d < HK || d > HEAD_MAX_D || d % HK != 0) return false;
+    const long long MT = static_cast<long long>(B) * (k + 1), MD = static_cast<long long>(B) * k;
+    if (MT > (1 << 26)) return false;
+    if (!make_plan(B, k, V, SPEC_MODE_SAMPLE, SPEC_DTYPE_F32, p.pv)) return false;
+    const long long nvt = (V + HV - 1) / HV;
+    p.mbT = head_mb(MT);
+    p.mbD = head_mb(MD > 0 ? MD : 1);
+    if (nvt * ((MT + 127) / 128) >= (1ll << 31)) return false;
+    p.nvt = static_cast<int>(nvt);
+    const size_t rows = static_cast<size_t>(B) * (2 * k + 1);
+    size_t o = 0;
+    p.o_recT = o; o = align256(o + static_cast<size_t>(MT) * nvt * sizeof(HeadRecS));
+    p.o_recD = o; o = align256(o + static_cast<size_t>(MD) * nvt * sizeof(HeadRecS));
+    p.o_tiles = o; o = align256(o + 2 * rows * sizeof(TileRec));
+    p.o_bat = o; o = align256(o + static_cast<size_t>(B) * sizeof(BatchRec));
+    p.o_segs = o; o = align256(o + static_cast<size_t>(B) * p.pv.wmax * (NTS / 64) * sizeof(SegRec));
+    p.o_exp = o; o = align256(o + EXP_N * sizeof(double));
+    p.o_lt = o; o = align256(o + static_cast<size_t>(MT) * V * sizeof(float));
+    p.o_ld = o; o = align256(o + static_cast<size_t>(MD) * V * sizeof(float));
+    p.total = o;
+    return true;
+}
+
+hipError_t launch_head_sample(HeadParams& H, int mb, hipStream_t s) {
+    H.nmt = (H.M + 64 * mb - 1) / (64 * mb);
+    const dim3 grid(static_cast<unsigned>(H.nvt) * static_cast<unsigned>(H.nmt));
+    if (mb == 4) hipLaunchKernelGGL(head_kernel_wide_s, grid, dim3(NTH), 0, s, H);
+    else if (mb == 3) hipLaunchKernelGGL(head_kernel_mid_s, grid, dim3(NTH), 0, s, H);
+    else hipLaunchKernelGGL(head_kernel_narrow_s, grid, dim3(NTH), 0, s, H);
+    return hipGetLastError();
+}
+
+int run_head_sample(const int8_t* th, const float* ths, const int8_t* tw, const float* tws, const int8_t* dh,
+                    const float* dhs, const int8_t* dw, const float* dws, const int32_t* draft_tokens,
+                    const float* uniforms, float temperature, int32_t B, int32_t k, int32_t V, int32_t d,
+                    int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
+                    float* draft_prob, void* workspace, size_t workspace_bytes, void* stream,
+                    void* const* events) {
+    if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K || V < 1 || V > (1 << 29))
+        return fail(SPEC_ERR_SHAPE, "need 1 <= B <= 2^21, 0 <= k <= %d, 1 <= V <= 2^29 (got B=%d k=%d V=%d)",
+                    SPEC_MAX_K, B, k, V);
+    if (d < HK || d > HEAD_MAX_D || d % HK != 0)
+        return fail(SPEC_ERR_SHAPE, "d must be a multiple of %d in [%d, %d] (got %d)", HK, HK, HEAD_MAX_D, d);
+    if (V > SPEC_MAX_V_SAMPLE)
+        return fail(SPEC_ERR_SHAPE, "sampling mode supports V <= %d (got %d)", SPEC_MAX_V_SAMPLE, V);
+    HeadSamplePlan plan;
+    if (!make_head_sample_plan(B, k, V, d, plan))
+        return fail(SPEC_ERR_SHAPE, "sizes B=%d k=%d V=%d d=%d exceed the supported range", B, k, V, d);
+    if (!(temperature > 0.0f) || !(temperature < INFINITY))
+        return fail(SPEC_ERR_TEMP, "temperature must be finite and > 0 (got %g)", static_cast<double>(temperature));
+    if (!th || !ths || !tw || !tws || !uniforms)
+        return fail(SPEC_ERR_NULL, "the target head, its hidden rows, their scales and the uniforms are required");
+    if (k > 0 && (!draft_tokens || !dh || !dhs))
+        return fail(SPEC_ERR_NULL, "draft_tokens and the draft hidden rows and scales are required when k > 0");
+    if ((dw == nullptr) != (dws == nullptr))
+        return fail(SPEC_ERR_NULL, "draft_weight and draft_weight_scale must both be given or both be NULL");
+    if (!accepted_len || !out_tokens || !gap) return fail(SPEC_ERR_NULL, "an output pointer is NULL");
+    if (!aligned(th, 16) || !aligned(tw, 16) || (dh && !aligned(dh, 16)) || (dw && !aligned(dw, 16)))
+        return fail(SPEC_ERR_ALIGN, "hidden rows and weights must be 16-byte aligned");
+    if (!aligned(ths, 4) || !aligned(tws, 4) || (dhs && !aligned(dhs, 4)) || (dws && !aligned(dws, 4)) ||
+        (draft_tokens && !aligned(draft_tokens, 4)) || !aligned(uniforms, 4) || !aligned(accepted_len, 4) ||
+        !aligned(out_tokens, 4) || !aligned(gap, 4) || (target_prob && !aligned(target_prob, 4)) ||
+        (draft_prob && !aligned(draft_prob, 4)))
+        return fail(SPEC_ERR_ALIGN, "a pointer is not aligned to its element size");
+    if (!workspace || workspace_bytes < plan.total)
+        return fail(SPEC_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", plan.total, workspace_bytes,
+                    workspace ? "" : ", NULL");
+    if (!aligned(workspace, 256)) return fail(SPEC_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (events && (!events[0] || !events[1] || !events[2] || !events[3]))
+        return fail(SPEC_ERR_NULL, "spec_verify_lmhead_sample_timed needs four events");
+    if (!dw) { dw = tw; dws = tws; }                       // the draft shares the target's head
+
+    char* ws = static_cast<char*>(workspace);
+    const double c = 1.4426950408889634 / static_cast<double>(temperature);
+    float ch, cl;
+    split_c(c, SPEC_DTYPE_F32, ch, cl);
+    TileRec* tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
+    const int rpb = 2 * k + 1;
+
+    HeadParams HT{};
+    HT.h = reinterpret_cast<const signed char*>(th); HT.hs = ths;
+    HT.w = reinterpret_cast<const signed char*>(tw); HT.ws = tws;
+    HT.recs = reinterpret_cast<HeadRecS*>(ws + plan.o_recT);
+    HT.tiles = tiles;
+    HT.M = B * (k + 1); HT.V = V; HT.d = d; HT.nvt = plan.nvt;
+    HT.ch = ch; HT.cl = cl; HT.tok = draft_tokens; HT.k = k; HT.role = 0; HT.rpb = rpb;
+    HT.logits = reinterpret_cast<float*>(ws + plan.o_lt);
+    HT.exptab = reinterpret_cast<double*>(ws + plan.o_exp);
+    HeadParams HD = HT;
+    HD.h = reinterpret_cast<const signed char*>(dh); HD.hs = dhs;
+    HD.w = reinterpret_cast<const signed char*>(dw); HD.ws = dws;
+    HD.recs = reinterpret_cast<HeadRecS*>(ws + plan.o_recD);
+    HD.M = B * k; HD.role = 1;
+    HD.logits = reinterpret_cast<float*>(ws + plan.o_ld);
+    HD.exptab = nullptr;
+
+    // decisions and pass 2: the verify parameters over the stored logits
+    // ([B, k+1, V] and [B, k, V], as spec_verify takes them)
+    Params P{};
+    P.tgt = ws + plan.o_lt;
+    P.dft = ws + plan.o_ld;
+    P.tok = draft_tokens;
+    P.uni = uniforms;
+    P.acc_len = accepted_len; P.out_tok = out_tokens; P.gap = gap;
+    P.tprob = k > 0 ? target_prob : nullptr;
+    P.dprob = k > 0 ? draft_prob : nullptr;
+    P.B = B; P.k = k; P.V = V;
+    P.rpb = rpb;
+    P.nvec = plan.pv.nvec;
+    P.wpb = plan.pv.wmax;
+    P.N = static_cast<long long>(B) * rpb * V;
+    P.L = V;                                               // one slice per row: row r's record at 2r
+    P.G = B * rpb;
+    P.mode = SPEC_MODE_SAMPLE;
+    const char* fe = getenv("SPEC_VERIFY_FORCE_EXACT_PATH");
+    P.force_exact = (fe && fe[0] == '1') ? 1 : 0;
+    P.ch = ch; P.cl = cl;
+    P.c = static_cast<double>(ch) + static_cast<double>(cl);
+    P.invT = 1.0 / static_cast<double>(temperature);
+    P.vec_ok = (static_cast<size_t>(V) * 4) % 16 == 0;
+    P.tiles = tiles;
+    P.bat = reinterpret_cast<BatchRec*>(ws + plan.o_bat);
+    P.segs = reinterpret_cast<SegRec*>(ws + plan.o_segs);
+    P.exptab = reinterpret_cast<double*>(ws + plan.o_exp);
+    P.tab_on = 0;
+
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+        return fail(SPEC_ERR_HIP, "cannot query the current HIP device");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
+    hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = launch_head_sample(HT, plan.mbT, s);
+    if (e == hipSuccess && k > 0) e = launch_head_sample(HD, plan.mbD, s);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(head_merge_sample_kernel, dim3(static_cast<unsigned>((HT.M + NWAVE - 1) / NWAVE)),
+                           dim3(NT), 0, s, HT);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess && k > 0) {
+        hipLaunchKernelGGL(head_merge_sample_kernel, dim3(static_cast<unsigned>((HD.M + NWAVE - 1) / NWAVE)),
+                           dim3(NT), 0, s, HD);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
+    if (e == hipSuccess) e = launch_pass2<F32>(P, dev, ncu, s, nullptr);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[3], s);
+    if (e != hipSuccess) return fail(SPEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return SPEC_OK;
+}
 
 extern "C" {
 
@@ -2964,6 +3394,41 @@ int spec_verify_lmhead_timed(const int8_t* hidden, const float* hidden_scale, co
     if (!events) return fail(SPEC_ERR_NULL, "spec_verify_lmhead_timed needs three events");
     return run_head(hidden, hidden_scale, weight, weight_scale, draft_tokens, B, k, V, d, accepted_len,
                     out_tokens, gap, workspace, workspace_bytes, stream, events);
+}
+
+size_t spec_lmhead_sample_workspace_size(int32_t B, int32_t k, int32_t V, int32_t d) {
+    HeadSamplePlan p;
+    if (V > SPEC_MAX_V_SAMPLE || !make_head_sample_plan(B, k, V, d, p)) return 0;
+    return p.total;
+}
+
+int spec_verify_lmhead_sample(const int8_t* target_hidden, const float* target_hidden_scale,
+                              const int8_t* target_weight, const float* target_weight_scale,
+                              const int8_t* draft_hidden, const float* draft_hidden_scale,
+                              const int8_t* draft_weight, const float* draft_weight_scale,
+                              const int32_t* draft_tokens, const float* uniforms, float temperature, int32_t B,
+                              int32_t k, int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens,
+                              float* gap, float* target_prob, float* draft_prob, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return run_head_sample(target_hidden, target_hidden_scale, target_weight, target_weight_scale, draft_hidden,
+                           draft_hidden_scale, draft_weight, draft_weight_scale, draft_tokens, uniforms,
+                           temperature, B, k, V, d, accepted_len, out_tokens, gap, target_prob, draft_prob,
+                           workspace, workspace_bytes, stream, nullptr);
+}
+
+int spec_verify_lmhead_sample_timed(const int8_t* target_hidden, const float* target_hidden_scale,
+                                    const int8_t* target_weight, const float* target_weight_scale,
+                                    const int8_t* draft_hidden, const float* draft_hidden_scale,
+                                    const int8_t* draft_weight, const float* draft_weight_scale,
+                                    const int32_t* draft_tokens, const float* uniforms, float temperature,
+                                    int32_t B, int32_t k, int32_t V, int32_t d, int32_t* accepted_len,
+                                    int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
+                                    void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    if (!events) return fail(SPEC_ERR_NULL, "spec_verify_lmhead_sample_timed needs four events");
+    return run_head_sample(target_hidden, target_hidden_scale, target_weight, target_weight_scale, draft_hidden,
+                           draft_hidden_scale, draft_weight, draft_weight_scale, draft_tokens, uniforms,
+                           temperature, B, k, V, d, accepted_len, out_tokens, gap, target_prob, draft_prob,
+                           workspace, workspace_bytes, stream, events);
 }
 
 const char* spec_verify_last_error(void) { return g_err; }

@@ -312,3 +312,31 @@ def make_lmhead(B: int, k: int, V: int, d: int = LMHEAD_D, seed: int = 0, device
     tok = torch.where(swap, rnd, tok).to(torch.int32)
     return {"hidden": h.to(torch.int8), "hidden_scale": hs.float(), "weight": w.to(torch.int8),
             "weight_scale": ws.float(), "tokens": tok, "B": B, "k": k, "V": V, "d": d}
+
+
+def make_lmhead_sample(B: int, k: int, V: int, d: int = LMHEAD_D, seed: int = 0, device="cpu",
+                       draft_head: bool = False):
+    """make_lmhead's target head and rows, plus a draft's hidden rows and uniforms.
+
+    Draft hidden row b*k + i is the target's row b*(k+1) + i mixed with fresh
+    noise: round(0.8 * h_t + N(0, 18^2)) clipped, so the draft leans to the
+    same planted row, less sharply. With draft_head, the draft has a head of
+    its own: the target's weights plus round(N(0, 12^2)), clipped, with its own
+    scales. Draft tokens are the planted rows with 30% replaced by uniform
+    random ids (as make_lmhead); uniforms [B, k+1, 2] ~ U[0, 1) float32.
+    """
+    x = make_lmhead(B, k, V, d, seed=seed, device=device)
+    g = _gen(device, "lmhead_sample", B, k, V, d, seed)
+    ht = x["hidden"].view(B, k + 1, d)[:, :k].reshape(B * k, d).float()
+    hd = (ht * 0.8 + torch.randn((B * k, d), generator=g, device=device) * 18.0).round_().clamp_(-127, 127)
+    x["draft_hidden"] = hd.to(torch.int8)
+    x["draft_hidden_scale"] = x["hidden_scale"].view(B, k + 1)[:, :k].reshape(B * k).clone() * 1.25
+    if draft_head:
+        wd = x["weight"].float() + torch.randn((V, d), generator=g, device=device) * 12.0
+        x["draft_weight"] = wd.round_().clamp_(-127, 127).to(torch.int8)
+        x["draft_weight_scale"] = (torch.rand(V, generator=g, device=device) * 0.2 + 0.9) / 128.0
+    else:
+        x["draft_weight"] = None
+        x["draft_weight_scale"] = None
+    x["uniforms"] = torch.rand((B, k + 1, 2), generator=g, device=device, dtype=torch.float32)
+    return x
