@@ -138,6 +138,9 @@ def main() -> int:
                          "hidden rows; the draft shares the head unless --draft-head)")
     ap.add_argument("--draft-head", action="store_true",
                     help="with --lmhead-sample: the draft has an int8 head of its own")
+    ap.add_argument("--no-context", action="store_true",
+                    help="with --lmhead / --lmhead-sample: skip the library and unfused comparisons "
+                         "(run after the timed region), so a profile holds only the fused call")
     ap.add_argument("--probe", choices=["copy", "sum"], default=None,
                     help="instead of the verify step, time a plain 1 GiB device copy (or a "
                          "read-only sum): achievable-bandwidth context and the known-size "
@@ -543,6 +546,8 @@ def lmhead_bench(args, torch, np) -> int:
     # context: the library int8 GEMM alone (hipBLASLt through torch._int_mm, int32
     # logits written out), which an unfused path would follow with scaling and a verify
     try:
+        if args.no_context:
+            raise RuntimeError("skipped (--no-context)")
         wt = x["weight"].t()
         for _ in range(3):
             torch._int_mm(x["hidden"], wt)
@@ -648,6 +653,8 @@ def lmhead_sample_bench(args, torch, np) -> int:
     # through torch._int_mm) writing int32 logits, float32 scaling by torch, and
     # spec_verify over the stored [B, k+1, V] and [B, k, V] logits
     try:
+        if args.no_context:
+            raise RuntimeError("skipped (--no-context)")
         wt = x["weight"].t()
         wd = wt if not own else x["draft_weight"].t()
         wsd = x["weight_scale"] if not own else x["draft_weight_scale"]
