@@ -2471,17 +2471,21 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     wait_stages<LPW>(min(P, nks) - 1);                     // stage 0 is in
     __syncthreads();
     frag(0, 0, 0);
-    for (int ks = 0; ks < nks; ++ks) {
+    // the last stage is peeled off, so the second MFMA group of every loop
+    // stage is reached only past the barrier (whose wait retired the reads of
+    // its operands): no LDS wait holds it up behind the next stage's reads
+    for (int ks = 0; ks < nks - 1; ++ks) {
         frag(ks, 1, 1);
         mma(0);
-        if (ks + 1 < nks) {
-            wait_stages<LPW>(min(P - 2, nks - 2 - ks));    // stage ks + 1 is in
-            __syncthreads();
-            if (ks + P < nks) issue(ks + P);
-            frag(ks + 1, 0, 0);
-        }
+        wait_stages<LPW>(min(P - 2, nks - 2 - ks));        // stage ks + 1 is in
+        __syncthreads();
+        if (ks + P < nks) issue(ks + P);
+        frag(ks + 1, 0, 0);
         mma(1);
     }
+    frag(nks - 1, 1, 1);
+    mma(0);
+    mma(1);
     __syncthreads();                                       // every wave is done with the stages
     // the epilogues reuse the stage buffers
     static_assert(NBUF * ST >= 2 * BM * static_cast<int>(sizeof(HeadRec)) + HV * 4, "greedy exchange");
