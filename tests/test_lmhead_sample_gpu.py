@@ -188,3 +188,37 @@ def test_lmhead_sample_equals_verify_on_stored_logits():
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     for a, b in zip(fused[3:], plain[3:]):
         assert torch.allclose(a, b, rtol=1e-6, atol=0.0, equal_nan=True)
+
+
+def draw_shape(rng):
+    while True:
+        B = int(rng.integers(1, 41))
+        k = int(rng.choice([0, 1, 2, 3, 5, 8, 13]))
+        V = max(1, int(np.exp(rng.uniform(0.0, np.log(40_000)))) + int(rng.integers(-3, 4)))
+        d = int(rng.choice([128, 256, 384, 640, 1024]))
+        if B * (2 * k + 1) * V * d <= 2e10:
+            return B, k, V, d
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_lmhead_sample_random_shapes(seed):
+    # seeded random shapes (every tile width, vocabulary tails of any length,
+    # k up to 13), temperatures, shared or separate draft heads, and injected
+    # invalid rows and extreme uniforms, each against the oracle
+    rng = np.random.default_rng(20_000 + seed)
+    B, k, V, d = draw_shape(rng)
+    T = float(rng.choice([0.3, 0.7, 1.0, 1.6]))
+    own = bool(rng.random() < 0.5)
+    say("lmhead sample random", seed, B, k, V, d, T, own)
+    x = workloads.make_lmhead_sample(B, k, V, d, seed=seed, draft_head=own)
+    if B > 3 and rng.random() < 0.3:
+        x["hidden_scale"][int(rng.integers(0, B * (k + 1)))] = float("nan")
+    if B > 3 and k > 0 and rng.random() < 0.3:
+        x["tokens"][int(rng.integers(0, B)), int(rng.integers(0, k))] = V
+    if B > 1:
+        x["uniforms"][0, :, :] = 0.0
+        x["uniforms"][-1, :, :] = float(np.nextafter(np.float32(1.0), np.float32(0.0)))
+    r = run(to_dev(x), T)
+    torch.cuda.synchronize()
+    st = compare(r, oracle_of(x, T), "f32", False)
+    say("  ", st)
