@@ -291,7 +291,7 @@ int spec_verify_lmhead_timed(const int8_t* hidden, const float* hidden_scale, co
  * 1 <= V <= SPEC_MAX_V_SAMPLE, B*(k+1) <= 2^26; temperature finite and > 0.
  * Workspace: at least spec_lmhead_sample_workspace_size() bytes (about
  * B*(2k+1)*V*4 for the logits, plus per-tile records), 256-byte aligned, no
- * initialisation needed, one call at a time. Enqueues six kernels (four when k = 0) on
+ * initialisation needed, one call at a time. Enqueues five kernels (four when k = 0) on
  * `stream`; no allocation, no host synchronisation. Errors: SPEC_ERR_SHAPE,
  * SPEC_ERR_TEMP, SPEC_ERR_NULL, SPEC_ERR_ALIGN, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP
  * (nothing enqueued).

@@ -25,6 +25,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <tuple>
 #include <thread>
 #include <vector>
 
@@ -351,25 +352,25 @@ inline void emu_run_wg(EmuWG& w, unsigned wg, unsigned nthreads) {
 
 inline int& emu_pool() { static int n = 1; return n; }
 
-template <class P>
+template <class... P>
 struct EmuLaunch {
-    void (*kernel)(P);
-    P params;
+    void (*kernel)(P...);
+    std::tuple<P...> params;
     static void call(void* self) {
         auto* s = static_cast<EmuLaunch*>(self);
-        s->kernel(s->params);
+        std::apply(s->kernel, s->params);
     }
 };
 
-template <class P>
-inline void emu_launch(void (*kernel)(P), dim3 grid, dim3 block, P params) {
+template <class... P, class... A>
+inline void emu_launch(void (*kernel)(P...), dim3 grid, dim3 block, A... args) {
     gridDim = EmuIdx{grid.x, 1, 1};
     blockDim = EmuIdx{block.x, 1, 1};
-    EmuLaunch<P> L{kernel, params};
+    EmuLaunch<P...> L{kernel, std::tuple<P...>(args...)};
     std::atomic<unsigned> next{0};
     auto worker = [&] {
         EmuWG w;
-        w.body = &EmuLaunch<P>::call;
+        w.body = &EmuLaunch<P...>::call;
         w.arg = &L;
         for (;;) {
             const unsigned wg = next.fetch_add(1);

@@ -2108,7 +2108,7 @@ struct HeadParams {
     int role;                           // 0: target rows b*(k+1)+i, 1: draft rows b*k+i
     int rpb;                            // rows per batch row of the merged records (2k+1)
     float* logits;                      // [M, V] float32, every logit (sampling)
-    double* exptab;                     // pass 2's exp table, written by one merge (or NULL)
+    double* exptab;                     // pass 2's exp table (sampling, target head), written by the merge
 };
 
 // The draft token whose logit hidden row m carries (-1: none; the bonus row).
@@ -2520,19 +2520,17 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void h
     head_main<2, 3, EPI_SAMPLE>(H);
 }
 
-// Sampling mode, one wave per hidden row: merge its vocabulary-tile records
-// (in tile order per lane, then a fixed butterfly) into pass 1's record of
-// its row: target row b*(k+1)+i is row b*rpb+i, draft row b*k+i is row
-// b*rpb+k+1+i, at slot 2*row (pass 1's slot rule with one slice per row).
-__global__ __launch_bounds__(NT) void head_merge_sample_kernel(HeadParams H) {
-    if (H.exptab && blockIdx.x == 0)
-        for (int j = static_cast<int>(threadIdx.x); j < EXP_N; j += NT) H.exptab[j] = exp2(static_cast<double>(j) / EXP_N);
-    const int lane = static_cast<int>(threadIdx.x) & 63;
-    const int m = static_cast<int>(blockIdx.x) * NWAVE + (static_cast<int>(threadIdx.x) >> 6);
-    if (m >= H.M) return;                                  // uniform per wave
+// Sampling mode, one workgroup per hidden row: merge its vocabulary-tile
+// records (a fixed order: per thread in tile order, a butterfly per wave, then
+// the waves in order) into pass 1's record of its row: target row b*(k+1)+i is
+// row b*rpb+i, draft row b*k+i is row b*rpb+k+1+i, at slot 2*row (pass 1's
+// slot rule with one slice per row).
+__device__ __attribute__((always_inline)) inline void head_merge_sample_row(const HeadParams& H, int m,
+                                                                       HeadRecS (&Lr)[NWAVE], int (&Ld)[NWAVE]) {
+    const int t = static_cast<int>(threadIdx.x), lane = t & 63, wv = t >> 6;
     HeadRecS a{-INFINITY, -INFINITY, 0.0f, 0, 0.0};
     const HeadRecS* R = H.recs + static_cast<size_t>(m) * H.nvt;
-    for (int j = lane; j < H.nvt; j += 64) head_recs_merge(a, R[j]);
+    for (int j = t; j < H.nvt; j += NT) head_recs_merge(a, R[j]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         HeadRecS p;
@@ -2545,31 +2543,50 @@ __global__ __launch_bounds__(NT) void head_merge_sample_kernel(HeadParams H) {
     // is exact in any order, so it equals the tile's accumulator entry, and
     // it is scaled as the epilogue scales it
     const int tok = head_row_token(H, m);
-    const bool has = tok >= 0 && tok < H.V;                // uniform per wave
-    float lx = 0.0f;
+    const bool has = tok >= 0 && tok < H.V;                // uniform per workgroup
+    int dot = 0;
     if (has) {
-        const int* hr = reinterpret_cast<const int*>(H.h + static_cast<size_t>(m) * H.d);
-        const int* wr = reinterpret_cast<const int*>(H.w + static_cast<size_t>(tok) * H.d);
-        int dot = 0;
-        for (int j = lane; j < H.d / 4; j += 64) {
-            const int x = hr[j], y = wr[j];
+        const u32x4* hr = reinterpret_cast<const u32x4*>(H.h + static_cast<size_t>(m) * H.d);
+        const u32x4* wr = reinterpret_cast<const u32x4*>(H.w + static_cast<size_t>(tok) * H.d);
+        for (int j = t; j < H.d / 16; j += NT) {
+            const u32x4 x = hr[j], y = wr[j];
 #pragma unroll
-            for (int b = 0; b < 32; b += 8)
-                dot += static_cast<int>(static_cast<signed char>(x >> b)) * static_cast<int>(static_cast<signed char>(y >> b));
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int b = 0; b < 32; b += 8)
+                    dot += static_cast<int>(static_cast<signed char>(x[q] >> b)) *
+                           static_cast<int>(static_cast<signed char>(y[q] >> b));
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-        lx = fmaf(static_cast<float>(dot) * H.hs[m], H.ws[tok], 0.0f);
     }
-    if (lane == 0) {
+    if (lane == 0) { Lr[wv] = a; Ld[wv] = dot; }
+    __syncthreads();
+    if (t == 0) {
+        HeadRecS r = Lr[0];
+        int acc = Ld[0];
+        for (int w = 1; w < NWAVE; ++w) { head_recs_merge(r, Lr[w]); acc += Ld[w]; }
+        const float lx = has ? fmaf(static_cast<float>(acc) * H.hs[m], H.ws[tok], 0.0f) : 0.0f;
         const int k = H.k;
         const long long row = H.role == 0 ? static_cast<long long>(m / (k + 1)) * H.rpb + m % (k + 1)
                                           : static_cast<long long>(m / k) * H.rpb + k + 1 + m % k;
         TileRec tr;
-        tr.t1 = a.t1; tr.t2 = a.t2; tr.ref = a.ref; tr.idx = 0x7fffffff; tr.s = a.s; tr.lx = lx;
-        tr.flags = (a.flags & 1) | (has ? 2 : 0);
+        tr.t1 = r.t1; tr.t2 = r.t2; tr.ref = r.ref; tr.idx = 0x7fffffff; tr.s = r.s; tr.lx = lx;
+        tr.flags = (r.flags & 1) | (has ? 2 : 0);
         H.tiles[2 * row] = tr;
     }
+}
+
+// Both heads' rows in one launch: workgroups 0 .. T.M-1 take the target's
+// rows, the rest the draft's; the first also writes pass 2's exp table.
+__global__ __launch_bounds__(NT) void head_merge_sample_kernel(HeadParams T, HeadParams D) {
+    __shared__ HeadRecS Lr[NWAVE];
+    __shared__ int Ld[NWAVE];
+    const int b = static_cast<int>(blockIdx.x);
+    if (b == 0)
+        for (int j = static_cast<int>(threadIdx.x); j < EXP_N; j += NT) T.exptab[j] = exp2(static_cast<double>(j) / EXP_N);
+    if (b < T.M) head_merge_sample_row(T, b, Lr, Ld);       // uniform per workgroup
+    else head_merge_sample_row(D, b - T.M, Lr, Ld);
 }
 
 // One wave per hidden row: merge its vocabulary-tile records into the row's
@@ -3244,13 +3261,7 @@ int run_head_sample(const int8_t* th, const float* ths, const int8_t* tw, const 
     if (e == hipSuccess && k > 0) e = launch_head_sample(HD, plan.mbD, s);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(head_merge_sample_kernel, dim3(static_cast<unsigned>((HT.M + NWAVE - 1) / NWAVE)),
-                           dim3(NT), 0, s, HT);
-        e = hipGetLastError();
-    }
-    if (e == hipSuccess && k > 0) {
-        hipLaunchKernelGGL(head_merge_sample_kernel, dim3(static_cast<unsigned>((HD.M + NWAVE - 1) / NWAVE)),
-                           dim3(NT), 0, s, HD);
+        hipLaunchKernelGGL(head_merge_sample_kernel, dim3(static_cast<unsigned>(HT.M + HD.M)), dim3(NT), 0, s, HT, HD);
         e = hipGetLastError();
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], s);
