@@ -95,6 +95,7 @@ inline double __hiloint2double(int hi, int lo) {
     double d; memcpy(&d, &u, 8); return d;
 }
 #define __builtin_amdgcn_sched_barrier(n) ((void)0)
+#define __builtin_amdgcn_sched_group_barrier(mask, size, id) ((void)0)
 #define __builtin_amdgcn_s_waitcnt(n) __atomic_thread_fence(__ATOMIC_SEQ_CST)
 #define __builtin_amdgcn_fence(...) __atomic_thread_fence(__ATOMIC_SEQ_CST)
 #define __builtin_amdgcn_s_barrier() __syncthreads()

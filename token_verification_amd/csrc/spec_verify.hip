@@ -3029,7 +3029,7 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
         return fail(SPEC_ERR_NULL, "spec_verify_lmhead_timed needs three events");
 
     char* ws = static_cast<char*>(workspace);
-    HeadParams H;
+    HeadParams H{};
     H.h = reinterpret_cast<const signed char*>(hidden);
     H.hs = hidden_scale;
     H.w = reinterpret_cast<const signed char*>(weight);
@@ -3367,7 +3367,7 @@ int spec_commit(const int32_t* accepted_len, int32_t B, int32_t k, int32_t* kv_l
         return fail(SPEC_ERR_ALIGN, "pointers must be 4-byte aligned and state_bytes a multiple of 4");
     if (has_state && state_bytes > (static_cast<size_t>(1) << 40))
         return fail(SPEC_ERR_SHAPE, "state_bytes %zu is too large", state_bytes);
-    CommitParams C;
+    CommitParams C{};
     C.acc = accepted_len;
     C.kv_len = kv_len;
     C.slots = static_cast<const char*>(has_state ? slots : nullptr);
