@@ -2245,9 +2245,10 @@ __device__ inline void head_recs_merge(HeadRecS& a, const HeadRecS& b) {
 // runs on XCD b % 8, so tiles are dealt out in 8 contiguous runs, one per
 // XCD: the hidden-row tiles of a vocabulary tile run together and share its
 // weights through that XCD's L2) and the epilogue.
-template <int MB>
+template <int MB, int NMW = 2>
 struct HeadTile {
-    static constexpr int BM = 64 * MB;                     // hidden rows per tile
+    static constexpr int BM = 32 * MB * NMW;               // hidden rows per tile
+    static constexpr int NTHR = 128 * NMW;                 // threads: 2 x NMW waves
     int t, vw, mw, r, hi, vt, v0, m0, nv, nm;
 
     __device__ explicit HeadTile(const HeadParams& H) {
@@ -2273,8 +2274,8 @@ struct HeadTile {
         // epilogue reads them with short LDS loads instead of holding many
         // global loads in flight beside the accumulators
         float* WS = reinterpret_cast<float*>(S + 2 * BM * sizeof(HeadRec));
-        static_assert(NTH == HV, "one weight scale per thread");
-        WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+        static_assert(NTHR >= HV, "one weight scale per thread");
+        if (t < HV) WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
         __syncthreads();
         if (v0 + HV <= H.V) head_epilogue<MB, false>(H, acc, WS, v0, mrow, vw, hi, T1, T2, I1, FL);
         else head_epilogue<MB, true>(H, acc, WS, v0, mrow, vw, hi, T1, T2, I1, FL);
@@ -2301,9 +2302,11 @@ struct HeadTile {
         const int mrow = m0 + 32 * MB * mw + r;
         float* WS = reinterpret_cast<float*>(S + 2 * BM * sizeof(HeadRecS));
         float* WB = WS + HV;
-        static_assert(NTH == HV, "one weight scale per thread");
-        WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
-        WB[t] = v0 + t < H.V ? 0.0f : -INFINITY;
+        static_assert(NTHR >= HV, "one weight scale per thread");
+        if (t < HV) {
+            WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+            WB[t] = v0 + t < H.V ? 0.0f : -INFINITY;
+        }
         __syncthreads();
         head_epilogue_sample<MB>(H, acc, WS, WB, mrow, vw, hi, o);
         HeadRecS* L = reinterpret_cast<HeadRecS*>(S);      // [2][BM]: per vocabulary wave
@@ -2334,43 +2337,48 @@ struct HeadTile {
         constexpr int PITCH = HV + 4;
         float* R = reinterpret_cast<float*>(S);                         // [64][PITCH]
         float* WS = R + 64 * PITCH;
-        WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+        if (t < HV) WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
         const bool vec = (H.V & 3) == 0;                   // rows start 16-byte aligned
-        const int lr = 32 * mw + r;                        // the lane's row in the slab
+        const int lr = 32 * (mw & 1) + r;                  // the lane's row in the slab
         __syncthreads();
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int m = m0 + 32 * MB * mw + 32 * mb + r;
             const float hsv = m < H.M ? H.hs[m] : 0.0f;
 #pragma unroll
-            for (int vb = 0; vb < 4; ++vb)
+            for (int h = 0; h < NMW / 2; ++h) {            // the slab holds the rows of waves 2h, 2h+1
+                if ((mw >> 1) == h) {                      // uniform per wave
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int col = 128 * vw + 32 * vb + 8 * c + 4 * hi;
-                    f32x4 y;
+                    for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        y[j] = (static_cast<float>(acc[vb][mb][4 * c + j]) * hsv) * WS[col + j];
-                    *reinterpret_cast<f32x4*>(R + lr * PITCH + col) = y;
+                        for (int c = 0; c < 4; ++c) {
+                            const int col = 128 * vw + 32 * vb + 8 * c + 4 * hi;
+                            f32x4 y;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                y[j] = (static_cast<float>(acc[vb][mb][4 * c + j]) * hsv) * WS[col + j];
+                            *reinterpret_cast<f32x4*>(R + lr * PITCH + col) = y;
+                        }
                 }
-            __syncthreads();
-            const int ch = t & 63, v = v0 + 4 * ch;
+                __syncthreads();
+                const int ch = t & 63, v = v0 + 4 * ch;
 #pragma unroll 4
-            for (int it = 0; it < 16; ++it) {
-                const int row = 4 * it + (t >> 6);
-                const int mm = m0 + 32 * MB * (row >> 5) + 32 * mb + (row & 31);
-                if (mm >= H.M) continue;
-                const f32x4 y = *reinterpret_cast<const f32x4*>(R + row * PITCH + 4 * ch);
-                float* dst = H.logits + static_cast<size_t>(mm) * H.V + v;
-                if (vec && v + 3 < H.V) {
-                    __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(dst));
-                } else {
+                for (int it = 0; it < 64 * 64 / NTHR; ++it) {
+                    const int row = (NTHR / 64) * it + (t >> 6);
+                    const int mm = m0 + 32 * MB * (2 * h + (row >> 5)) + 32 * mb + (row & 31);
+                    if (mm >= H.M) continue;
+                    const f32x4 y = *reinterpret_cast<const f32x4*>(R + row * PITCH + 4 * ch);
+                    float* dst = H.logits + static_cast<size_t>(mm) * H.V + v;
+                    if (vec && v + 3 < H.V) {
+                        __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(dst));
+                    } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (v + j < H.V) __builtin_nontemporal_store(y[j], dst + j);
+                        for (int j = 0; j < 4; ++j)
+                            if (v + j < H.V) __builtin_nontemporal_store(y[j], dst + j);
+                    }
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 };
@@ -2385,7 +2393,7 @@ __device__ inline void acc_zero(i32x16 (&acc)[4][MB]) {
             for (int q = 0; q < 16; ++q) acc[vb][mb][q] = 0;
 }
 
-// The main loop: 2 x 2 waves of 128 x 32*MB. The d-slices go from memory
+// The main loop: 2 x NMW waves of 128 x 32*MB. The d-slices go from memory
 // straight into LDS (16-byte buffer loads with the LDS as destination, no
 // staging registers): 64 bytes of d per stage, NBUF stage buffers, the loads
 // of NBUF - 1 stages in flight. Stage layout: row q (256 weight rows, then
@@ -2413,36 +2421,39 @@ __device__ inline void wait_stages(int stages) {
     else __builtin_amdgcn_s_waitcnt(vm_wait(0));
 }
 
-template <int MB, int NBUF, int EPI = EPI_GREEDY>
+template <int MB, int NBUF, int EPI = EPI_GREEDY, int NMW = 2>
 __device__ __attribute__((always_inline)) inline void head_main(const HeadParams& H) {
-    constexpr int BM = 64 * MB;
+    constexpr int NW = 2 * NMW;                            // waves
+    constexpr int BM = 32 * MB * NMW;
     constexpr int ST = (HV + BM) * HKW;                    // bytes per stage
-    constexpr int LPW = 4 + MB;                            // load instructions per wave and stage
+    constexpr int WRW = HV / NW, HRW = BM / NW;            // weight and hidden rows each wave loads
+    constexpr int LPW = (WRW + HRW) / 16;                  // load instructions per wave and stage
+    static_assert(WRW % 16 == 0 && HRW % 16 == 0, "whole load instructions");
     constexpr int P = NBUF - 1;                            // stages in flight
     static_assert(2 * LPW <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(16))) unsigned char S[NBUF * ST];
-    const HeadTile<MB> w(H);
+    const HeadTile<MB, NMW> w(H);
     const int lane = w.t & 63, wv = w.t >> 6;
     const unsigned d = static_cast<unsigned>(H.d);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(w.v0) * d, static_cast<unsigned>(w.nv) * d);
     const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(w.m0) * d, static_cast<unsigned>(w.nm) * d);
-    // loads: weight instruction j of wave wv fills rows wv*64 + 16j .. +15,
-    // hidden instruction j rows wv*16*MB + 16j .. +15; lane l lands on row
+    // loads: weight instruction j of wave wv fills rows wv*WRW + 16j .. +15,
+    // hidden instruction j rows wv*HRW + 16j .. +15; lane l lands on row
     // + l/4, physical chunk l % 4, which holds logical chunk
     // (l % 4) ^ ((l >> 4) & 3); rows past the tile load zeros
     const unsigned cl = static_cast<unsigned>(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-    const unsigned low = static_cast<unsigned>(wv * 64 + (lane >> 2)) * d + cl;
-    const unsigned loh = static_cast<unsigned>(wv * 16 * MB + (lane >> 2)) * d + cl;
+    const unsigned low = static_cast<unsigned>(wv * WRW + (lane >> 2)) * d + cl;
+    const unsigned loh = static_cast<unsigned>(wv * HRW + (lane >> 2)) * d + cl;
     auto issue = [&](int ks) {
         unsigned char* B = S + (ks % NBUF) * ST;
         const unsigned k0 = static_cast<unsigned>(ks * HKW);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(B + (wv * 64 + 16 * j) * HKW), 16,
+        for (int j = 0; j < WRW / 16; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(B + (wv * WRW + 16 * j) * HKW), 16,
                                                      static_cast<int>(low + k0 + 16u * j * d), 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < MB; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(B + (HV + wv * 16 * MB + 16 * j) * HKW), 16,
+        for (int j = 0; j < HRW / 16; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(B + (HV + wv * HRW + 16 * j) * HKW), 16,
                                                      static_cast<int>(loh + k0 + 16u * j * d), 0, 0, 0);
     };
     // operands: A row 128*vw + 32*vb + r, B row 256 + 32*MB*mw + 32*mb + r;
@@ -2499,9 +2510,14 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     }
 }
 
-// 256-row tiles: 128 x 128 per wave, one wave per SIMD (256 accumulator
-// registers in AGPRs), four 32 KB stage buffers.
-__global__ __launch_bounds__(NTH) void head_kernel_wide(HeadParams H) { head_main<4, 4>(H); }
+// 256-row tiles: 2 x 4 waves of 128 x 64, two waves per SIMD (128
+// accumulator registers each), four 32 KB stage buffers. Against 2 x 2 waves
+// of 128 x 128 at one wave per SIMD (the sampling kernel's shape) the bytes per
+// MFMA are the same and one wave's waits overlap the other's MFMAs: 5-6%
+// faster at M = 1024 and 4608.
+__global__ __launch_bounds__(2 * NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_wide(HeadParams H) {
+    head_main<2, 4, EPI_GREEDY, 4>(H);
+}
 
 // 192-row tiles: 128 x 96 per wave, one wave per SIMD, four 28 KB stage buffers.
 __global__ __launch_bounds__(NTH) void head_kernel_mid(HeadParams H) { head_main<3, 4>(H); }
@@ -2512,13 +2528,16 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void h
     head_main<2, 3>(H);
 }
 
-// Sampling mode, with the same tiles: pass 1's terms per row and vocabulary
-// tile, and every logit stored for the draw.
+// Sampling mode, with the same tile sizes: pass 1's terms per row and
+// vocabulary tile, and every logit stored for the draw. Its 256-row tiles keep
+// 2 x 2 waves of 128 x 128 at one wave per SIMD: the 8-wave shape spilled in
+// this epilogue and measured 2-4% slower.
 __global__ __launch_bounds__(NTH) void head_kernel_wide_s(HeadParams H) { head_main<4, 4, EPI_SAMPLE>(H); }
 __global__ __launch_bounds__(NTH) void head_kernel_mid_s(HeadParams H) { head_main<3, 4, EPI_SAMPLE>(H); }
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_narrow_s(HeadParams H) {
     head_main<2, 3, EPI_SAMPLE>(H);
 }
+
 
 // Sampling mode, one workgroup per hidden row: merge its vocabulary-tile
 // records (a fixed order: per thread in tile order, a butterfly per wave, then
@@ -3060,7 +3079,7 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
     if (e == hipSuccess) {
         const dim3 grid(static_cast<unsigned>(plan.nvt) * static_cast<unsigned>(H.nmt));
-        if (plan.mb == 4) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(NTH), 0, s, H);
+        if (plan.mb == 4) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(2 * NTH), 0, s, H);
         else if (plan.mb == 3) hipLaunchKernelGGL(head_kernel_mid, grid, dim3(NTH), 0, s, H);
         else hipLaunchKernelGGL(head_kernel_narrow, grid, dim3(NTH), 0, s, H);
         e = hipGetLastError();
