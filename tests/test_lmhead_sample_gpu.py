@@ -73,6 +73,8 @@ def subset(r, rows):
     (40, 5, 32000, 1024, 0.4, True),   # sharp rows, separate head, 125 vocabulary tiles
     (96, 3, 3000, 640, 1.0, False),    # 384 / 288 rows: 192-row tiles
     (160, 3, 3000, 640, 1.6, True),    # 640 / 480 rows: 128-row tiles (the narrow kernel)
+    (1, 4, 128256, 4096, 1.0, False),  # one batch row over a full-size shared head (one pass, 9 rows)
+    (3, 7, 50000, 512, 0.8, False),    # 24 + 21 rows in one pass: the draft's rows start mid-tile
 ])
 def test_lmhead_sample_matches_oracle(B, k, V, d, T, own):
     say("lmhead sample", B, k, V, d, T, own)

@@ -3135,10 +3135,34 @@ int scratch_ptr(int dev, void** out) {
 
 // ------------------------------------------------------------------ LM head, sampling mode
 
+// A shared head: the target's hidden rows, then the draft's, copied into one
+// matrix (with their scales) for a single pass over the head, which then
+// streams its weights once instead of once per set of rows. One workgroup per
+// row; d is a multiple of 128, so rows are whole 16-byte vectors.
+struct ConcatParams {
+    const signed char* a;
+    const signed char* b;
+    const float* as;
+    const float* bs;
+    signed char* out;
+    float* outs;
+    int na, d;
+};
+
+__global__ __launch_bounds__(NT) void head_concat_kernel(ConcatParams C) {
+    const int m = static_cast<int>(blockIdx.x), t = static_cast<int>(threadIdx.x);
+    const bool first = m < C.na;
+    const int row = first ? m : m - C.na;
+    const u32x4* src = reinterpret_cast<const u32x4*>((first ? C.a : C.b) + static_cast<size_t>(row) * C.d);
+    u32x4* dst = reinterpret_cast<u32x4*>(C.out + static_cast<size_t>(m) * C.d);
+    for (int i = t; i < C.d / 16; i += NT) dst[i] = src[i];
+    if (t == 0) C.outs[m] = first ? C.as[row] : C.bs[row];
+}
+
 struct HeadSamplePlan {
     Plan pv;                            // pass 2's part of the verify plan (batch records, segments)
-    int nvt, mbT, mbD;
-    size_t o_recT, o_recD, o_tiles, o_bat, o_segs, o_exp, o_lt, o_ld, total;
+    int nvt, mbT, mbD, mbC;
+    size_t o_recT, o_recD, o_tiles, o_bat, o_segs, o_exp, o_lt, o_ld, o_hc, o_hsc, total;
 };
 
 bool make_head_sample_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadSamplePlan& p) {
@@ -3150,18 +3174,23 @@ bool make_head_sample_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadSampl
     const long long nvt = (V + HV - 1) / HV;
     p.mbT = head_mb(MT);
     p.mbD = head_mb(MD > 0 ? MD : 1);
+    p.mbC = head_mb(MT + MD);
     if (nvt * ((MT + 127) / 128) >= (1ll << 31)) return false;
     p.nvt = static_cast<int>(nvt);
     const size_t rows = static_cast<size_t>(B) * (2 * k + 1);
     size_t o = 0;
-    p.o_recT = o; o = align256(o + static_cast<size_t>(MT) * nvt * sizeof(HeadRecS));
-    p.o_recD = o; o = align256(o + static_cast<size_t>(MD) * nvt * sizeof(HeadRecS));
+    // the draft's records and logits follow the target's without a gap, so
+    // one launch over both sets of rows (a shared head) fills them in order
+    p.o_recT = o; p.o_recD = o + static_cast<size_t>(MT) * nvt * sizeof(HeadRecS);
+    o = align256(p.o_recD + static_cast<size_t>(MD) * nvt * sizeof(HeadRecS));
     p.o_tiles = o; o = align256(o + 2 * rows * sizeof(TileRec));
     p.o_bat = o; o = align256(o + static_cast<size_t>(B) * sizeof(BatchRec));
     p.o_segs = o; o = align256(o + static_cast<size_t>(B) * p.pv.wmax * (NTS / 64) * sizeof(SegRec));
     p.o_exp = o; o = align256(o + EXP_N * sizeof(double));
-    p.o_lt = o; o = align256(o + static_cast<size_t>(MT) * V * sizeof(float));
-    p.o_ld = o; o = align256(o + static_cast<size_t>(MD) * V * sizeof(float));
+    p.o_lt = o; p.o_ld = o + static_cast<size_t>(MT) * V * sizeof(float);
+    o = align256(p.o_ld + static_cast<size_t>(MD) * V * sizeof(float));
+    p.o_hc = o; o = align256(o + static_cast<size_t>(MT + MD) * d);
+    p.o_hsc = o; o = align256(o + static_cast<size_t>(MT + MD) * sizeof(float));
     p.total = o;
     return true;
 }
@@ -3213,6 +3242,7 @@ int run_head_sample(const int8_t* th, const float* ths, const int8_t* tw, const 
     if (!aligned(workspace, 256)) return fail(SPEC_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (events && (!events[0] || !events[1] || !events[2] || !events[3]))
         return fail(SPEC_ERR_NULL, "spec_verify_lmhead_sample_timed needs four events");
+    const bool shared = dw == nullptr || (dw == tw && dws == tws);
     if (!dw) { dw = tw; dws = tws; }                       // the draft shares the target's head
 
     char* ws = static_cast<char*>(workspace);
@@ -3276,8 +3306,25 @@ int run_head_sample(const int8_t* th, const float* ths, const int8_t* tw, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
-    if (e == hipSuccess) e = launch_head_sample(HT, plan.mbT, s);
-    if (e == hipSuccess && k > 0) e = launch_head_sample(HD, plan.mbD, s);
+    if (shared && k > 0) {
+        // one pass over the shared head for both sets of rows: records and
+        // logits land in the target's then the draft's (contiguous) slots
+        ConcatParams C;
+        C.a = HT.h; C.b = HD.h; C.as = ths; C.bs = dhs;
+        C.out = reinterpret_cast<signed char*>(ws + plan.o_hc);
+        C.outs = reinterpret_cast<float*>(ws + plan.o_hsc);
+        C.na = HT.M; C.d = d;
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(head_concat_kernel, dim3(static_cast<unsigned>(HT.M + HD.M)), dim3(NT), 0, s, C);
+            e = hipGetLastError();
+        }
+        HeadParams HC = HT;
+        HC.h = C.out; HC.hs = C.outs; HC.M = HT.M + HD.M;
+        if (e == hipSuccess) e = launch_head_sample(HC, plan.mbC, s);
+    } else {
+        if (e == hipSuccess) e = launch_head_sample(HT, plan.mbT, s);
+        if (e == hipSuccess && k > 0) e = launch_head_sample(HD, plan.mbD, s);
+    }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
     if (e == hipSuccess) {
         hipLaunchKernelGGL(head_merge_sample_kernel, dim3(static_cast<unsigned>(HT.M + HD.M)), dim3(NT), 0, s, HT, HD);
