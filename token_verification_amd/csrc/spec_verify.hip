@@ -2274,8 +2274,7 @@ struct HeadTile {
         // epilogue reads them with short LDS loads instead of holding many
         // global loads in flight beside the accumulators
         float* WS = reinterpret_cast<float*>(S + 2 * BM * sizeof(HeadRec));
-        static_assert(NTHR >= HV, "one weight scale per thread");
-        if (t < HV) WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+        for (int i = t; i < HV; i += NTHR) WS[i] = v0 + i < H.V ? H.ws[v0 + i] : 0.0f;
         __syncthreads();
         if (v0 + HV <= H.V) head_epilogue<MB, false>(H, acc, WS, v0, mrow, vw, hi, T1, T2, I1, FL);
         else head_epilogue<MB, true>(H, acc, WS, v0, mrow, vw, hi, T1, T2, I1, FL);
@@ -2302,10 +2301,9 @@ struct HeadTile {
         const int mrow = m0 + 32 * MB * mw + r;
         float* WS = reinterpret_cast<float*>(S + 2 * BM * sizeof(HeadRecS));
         float* WB = WS + HV;
-        static_assert(NTHR >= HV, "one weight scale per thread");
-        if (t < HV) {
-            WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
-            WB[t] = v0 + t < H.V ? 0.0f : -INFINITY;
+        for (int i = t; i < HV; i += NTHR) {
+            WS[i] = v0 + i < H.V ? H.ws[v0 + i] : 0.0f;
+            WB[i] = v0 + i < H.V ? 0.0f : -INFINITY;
         }
         __syncthreads();
         head_epilogue_sample<MB>(H, acc, WS, WB, mrow, vw, hi, o);
@@ -2333,11 +2331,14 @@ struct HeadTile {
     // consecutive rows hit distinct banks), and each wave then stores whole
     // rows: 64 lanes x 16 bytes = one contiguous 1 KB segment per instruction,
     // where the accumulator layout would give each store 32 rows.
+    static constexpr int SR = NMW < 2 ? 32 * NMW : 64;    // rows of the logit slab
+    static constexpr int NH = NMW < 2 ? 1 : NMW / 2;       // slab rounds per hidden-row block
+
     __device__ void finish_logits(const HeadParams& H, const i32x16 (&acc)[4][MB], unsigned char* S) const {
         constexpr int PITCH = HV + 4;
-        float* R = reinterpret_cast<float*>(S);                         // [64][PITCH]
-        float* WS = R + 64 * PITCH;
-        if (t < HV) WS[t] = v0 + t < H.V ? H.ws[v0 + t] : 0.0f;
+        float* R = reinterpret_cast<float*>(S);                         // [SR][PITCH]
+        float* WS = R + SR * PITCH;
+        for (int i = t; i < HV; i += NTHR) WS[i] = v0 + i < H.V ? H.ws[v0 + i] : 0.0f;
         const bool vec = (H.V & 3) == 0;                   // rows start 16-byte aligned
         const int lr = 32 * (mw & 1) + r;                  // the lane's row in the slab
         __syncthreads();
@@ -2346,7 +2347,7 @@ struct HeadTile {
             const int m = m0 + 32 * MB * mw + 32 * mb + r;
             const float hsv = m < H.M ? H.hs[m] : 0.0f;
 #pragma unroll
-            for (int h = 0; h < NMW / 2; ++h) {            // the slab holds the rows of waves 2h, 2h+1
+            for (int h = 0; h < NH; ++h) {                 // the slab holds the rows of waves 2h, 2h+1
                 if ((mw >> 1) == h) {                      // uniform per wave
 #pragma unroll
                     for (int vb = 0; vb < 4; ++vb)
@@ -2363,7 +2364,7 @@ struct HeadTile {
                 __syncthreads();
                 const int ch = t & 63, v = v0 + 4 * ch;
 #pragma unroll 4
-                for (int it = 0; it < 64 * 64 / NTHR; ++it) {
+                for (int it = 0; it < SR * 64 / NTHR; ++it) {
                     const int row = (NTHR / 64) * it + (t >> 6);
                     const int mm = m0 + 32 * MB * (2 * h + (row >> 5)) + 32 * mb + (row & 31);
                     if (mm >= H.M) continue;
@@ -2414,10 +2415,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // wait until at most `stages` later stages (LPW loads each) of this wave are in flight
-template <int LPW>
+template <int LPW, int MAXS>
 __device__ inline void wait_stages(int stages) {
-    if (stages >= 2) __builtin_amdgcn_s_waitcnt(vm_wait(2 * LPW));
-    else if (stages == 1) __builtin_amdgcn_s_waitcnt(vm_wait(LPW));
+    static_assert(MAXS * LPW <= 63 && MAXS <= 4, "vmcnt range");
+    if (MAXS >= 4 && stages >= 4) __builtin_amdgcn_s_waitcnt(vm_wait(4 * LPW));
+    else if (MAXS >= 3 && stages >= 3) __builtin_amdgcn_s_waitcnt(vm_wait(3 * LPW));
+    else if (MAXS >= 2 && stages >= 2) __builtin_amdgcn_s_waitcnt(vm_wait(2 * LPW));
+    else if (stages >= 1) __builtin_amdgcn_s_waitcnt(vm_wait(LPW));
     else __builtin_amdgcn_s_waitcnt(vm_wait(0));
 }
 
@@ -2430,7 +2434,6 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     constexpr int LPW = (WRW + HRW) / 16;                  // load instructions per wave and stage
     static_assert(WRW % 16 == 0 && HRW % 16 == 0, "whole load instructions");
     constexpr int P = NBUF - 1;                            // stages in flight
-    static_assert(2 * LPW <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(16))) unsigned char S[NBUF * ST];
     const HeadTile<MB, NMW> w(H);
     const int lane = w.t & 63, wv = w.t >> 6;
@@ -2479,7 +2482,7 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     };
     const int nks = H.d / HKW;                             // >= 2
     for (int q = 0; q < P && q < nks; ++q) issue(q);
-    wait_stages<LPW>(min(P, nks) - 1);                     // stage 0 is in
+    wait_stages<LPW, P - 1>(min(P, nks) - 1);              // stage 0 is in
     __syncthreads();
     frag(0, 0, 0);
     // the last stage is peeled off, so the second MFMA group of every loop
@@ -2488,7 +2491,7 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     for (int ks = 0; ks < nks - 1; ++ks) {
         frag(ks, 1, 1);
         mma(0);
-        wait_stages<LPW>(min(P - 2, nks - 2 - ks));        // stage ks + 1 is in
+        wait_stages<LPW, P - 1>(min(P - 2, nks - 2 - ks)); // stage ks + 1 is in
         __syncthreads();
         if (ks + P < nks) issue(ks + P);
         frag(ks + 1, 0, 0);
@@ -2501,7 +2504,7 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     // the epilogues reuse the stage buffers
     static_assert(NBUF * ST >= 2 * BM * static_cast<int>(sizeof(HeadRec)) + HV * 4, "greedy exchange");
     static_assert(NBUF * ST >= 2 * BM * static_cast<int>(sizeof(HeadRecS)) + 2 * HV * 4, "sampling exchange");
-    static_assert(NBUF * ST >= (64 * (HV + 4) + HV) * 4, "logit slab");
+    static_assert(NBUF * ST >= (HeadTile<MB, NMW>::SR * (HV + 4) + HV) * 4, "logit slab");
     if constexpr (EPI == EPI_SAMPLE) {
         w.finish_sample(H, acc, S);
         w.finish_logits(H, acc, S);                        // after the exchange: the LDS is free again
@@ -2528,6 +2531,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void h
     head_main<2, 3>(H);
 }
 
+// 32-row tiles for a handful of hidden rows, where the call streams the head
+// and the MFMAs are a small part of it: 2 waves of 128 x 32, 18 KB stages,
+// four buffers (three stages of loads in flight), two workgroups per CU; a
+// 128-row tile would stage and multiply 96 rows of padding.
+__global__ __launch_bounds__(NTH / 2) void head_kernel_tiny(HeadParams H) { head_main<1, 4, EPI_GREEDY, 1>(H); }
+
 // Sampling mode, with the same tile sizes: pass 1's terms per row and
 // vocabulary tile, and every logit stored for the draw. Its 256-row tiles keep
 // 2 x 2 waves of 128 x 128 at one wave per SIMD: the 8-wave shape spilled in
@@ -2537,6 +2546,7 @@ __global__ __launch_bounds__(NTH) void head_kernel_mid_s(HeadParams H) { head_ma
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel_narrow_s(HeadParams H) {
     head_main<2, 3, EPI_SAMPLE>(H);
 }
+__global__ __launch_bounds__(NTH / 2) void head_kernel_tiny_s(HeadParams H) { head_main<1, 4, EPI_SAMPLE, 1>(H); }
 
 
 // Sampling mode, one workgroup per hidden row: merge its vocabulary-tile
@@ -2987,18 +2997,19 @@ constexpr int HEAD_MAX_D = 65536;       // |acc| <= 2^14 * d stays inside int32
 
 struct HeadPlan {
     int M, nvt;
-    int mb;                             // hidden-row blocks per wave: tiles of 64*mb rows
+    int bm;                             // hidden rows per tile: 256, 192, 128 or 32
     size_t o_rec, o_tiles, total;
 };
 
-// Hidden-row blocks per wave for M rows: wider tiles reuse each staged
-// operand more; a narrower one when it pads the hidden rows clearly less
-// (e.g. 384 rows: 2 x 192, not 2 x 256).
-int head_mb(long long M) {
+// Hidden rows per tile for M rows: wider tiles reuse each staged operand
+// more; a narrower one when it pads the hidden rows clearly less (e.g. 384
+// rows: 2 x 192, not 2 x 256); 32-row tiles for at most 32 rows.
+int head_bm(long long M) {
+    if (M <= 32) return 32;
     const long long pad4 = (M + 255) / 256 * 256, pad3 = (M + 191) / 192 * 192, pad2 = (M + 127) / 128 * 128;
-    if (pad4 * 10 <= (pad3 < pad2 ? pad3 : pad2) * 11) return 4;
-    if (pad3 * 10 <= pad2 * 11) return 3;
-    return 2;
+    if (pad4 * 10 <= (pad3 < pad2 ? pad3 : pad2) * 11) return 256;
+    if (pad3 * 10 <= pad2 * 11) return 192;
+    return 128;
 }
 
 bool make_head_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadPlan& p) {
@@ -3007,8 +3018,8 @@ bool make_head_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadPlan& p) {
     const long long M = static_cast<long long>(B) * (k + 1);
     if (M > (1 << 26)) return false;
     const long long nvt = (V + HV - 1) / HV;
-    p.mb = head_mb(M);
-    const long long nmt = (M + 64 * p.mb - 1) / (64 * p.mb);
+    p.bm = head_bm(M);
+    const long long nmt = (M + p.bm - 1) / p.bm;
     if (nvt * nmt >= (1ll << 31)) return false;
     p.M = static_cast<int>(M);
     p.nvt = static_cast<int>(nvt);
@@ -3057,7 +3068,7 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     H.tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
     H.M = plan.M; H.V = V; H.d = d;
     H.nvt = plan.nvt;
-    H.nmt = (plan.M + 64 * plan.mb - 1) / (64 * plan.mb);
+    H.nmt = (plan.M + plan.bm - 1) / plan.bm;
     // the greedy decisions read the merged records as pass 1's, one slice per row
     Params P;
     memset(&P, 0, sizeof P);
@@ -3079,9 +3090,10 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     hipError_t e = ev ? hipEventRecord(ev[0], s) : hipSuccess;
     if (e == hipSuccess) {
         const dim3 grid(static_cast<unsigned>(plan.nvt) * static_cast<unsigned>(H.nmt));
-        if (plan.mb == 4) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(2 * NTH), 0, s, H);
-        else if (plan.mb == 3) hipLaunchKernelGGL(head_kernel_mid, grid, dim3(NTH), 0, s, H);
-        else hipLaunchKernelGGL(head_kernel_narrow, grid, dim3(NTH), 0, s, H);
+        if (plan.bm == 256) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(2 * NTH), 0, s, H);
+        else if (plan.bm == 192) hipLaunchKernelGGL(head_kernel_mid, grid, dim3(NTH), 0, s, H);
+        else if (plan.bm == 128) hipLaunchKernelGGL(head_kernel_narrow, grid, dim3(NTH), 0, s, H);
+        else hipLaunchKernelGGL(head_kernel_tiny, grid, dim3(NTH / 2), 0, s, H);
         e = hipGetLastError();
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
@@ -3161,7 +3173,7 @@ __global__ __launch_bounds__(NT) void head_concat_kernel(ConcatParams C) {
 
 struct HeadSamplePlan {
     Plan pv;                            // pass 2's part of the verify plan (batch records, segments)
-    int nvt, mbT, mbD, mbC;
+    int nvt, bmT, bmD, bmC;
     size_t o_recT, o_recD, o_tiles, o_bat, o_segs, o_exp, o_lt, o_ld, o_hc, o_hsc, total;
 };
 
@@ -3172,10 +3184,10 @@ bool make_head_sample_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadSampl
     if (MT > (1 << 26)) return false;
     if (!make_plan(B, k, V, SPEC_MODE_SAMPLE, SPEC_DTYPE_F32, p.pv)) return false;
     const long long nvt = (V + HV - 1) / HV;
-    p.mbT = head_mb(MT);
-    p.mbD = head_mb(MD > 0 ? MD : 1);
-    p.mbC = head_mb(MT + MD);
-    if (nvt * ((MT + 127) / 128) >= (1ll << 31)) return false;
+    p.bmT = head_bm(MT);
+    p.bmD = head_bm(MD > 0 ? MD : 1);
+    p.bmC = head_bm(MT + MD);
+    if (nvt * ((MT + MD + 31) / 32) >= (1ll << 31)) return false;
     p.nvt = static_cast<int>(nvt);
     const size_t rows = static_cast<size_t>(B) * (2 * k + 1);
     size_t o = 0;
@@ -3195,12 +3207,13 @@ bool make_head_sample_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadSampl
     return true;
 }
 
-hipError_t launch_head_sample(HeadParams& H, int mb, hipStream_t s) {
-    H.nmt = (H.M + 64 * mb - 1) / (64 * mb);
+hipError_t launch_head_sample(HeadParams& H, int bm, hipStream_t s) {
+    H.nmt = (H.M + bm - 1) / bm;
     const dim3 grid(static_cast<unsigned>(H.nvt) * static_cast<unsigned>(H.nmt));
-    if (mb == 4) hipLaunchKernelGGL(head_kernel_wide_s, grid, dim3(NTH), 0, s, H);
-    else if (mb == 3) hipLaunchKernelGGL(head_kernel_mid_s, grid, dim3(NTH), 0, s, H);
-    else hipLaunchKernelGGL(head_kernel_narrow_s, grid, dim3(NTH), 0, s, H);
+    if (bm == 256) hipLaunchKernelGGL(head_kernel_wide_s, grid, dim3(NTH), 0, s, H);
+    else if (bm == 192) hipLaunchKernelGGL(head_kernel_mid_s, grid, dim3(NTH), 0, s, H);
+    else if (bm == 128) hipLaunchKernelGGL(head_kernel_narrow_s, grid, dim3(NTH), 0, s, H);
+    else hipLaunchKernelGGL(head_kernel_tiny_s, grid, dim3(NTH / 2), 0, s, H);
     return hipGetLastError();
 }
 
@@ -3320,10 +3333,10 @@ int run_head_sample(const int8_t* th, const float* ths, const int8_t* tw, const 
         }
         HeadParams HC = HT;
         HC.h = C.out; HC.hs = C.outs; HC.M = HT.M + HD.M;
-        if (e == hipSuccess) e = launch_head_sample(HC, plan.mbC, s);
+        if (e == hipSuccess) e = launch_head_sample(HC, plan.bmC, s);
     } else {
-        if (e == hipSuccess) e = launch_head_sample(HT, plan.mbT, s);
-        if (e == hipSuccess && k > 0) e = launch_head_sample(HD, plan.mbD, s);
+        if (e == hipSuccess) e = launch_head_sample(HT, plan.bmT, s);
+        if (e == hipSuccess && k > 0) e = launch_head_sample(HD, plan.bmD, s);
     }
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], s);
     if (e == hipSuccess) {
