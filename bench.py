@@ -489,6 +489,22 @@ def commit_bench(args, torch, np) -> int:
 PEAK_INT8_TOPS = 5000.0    # MI355X dense int8 matrix peak, TOP/s
 
 
+def head_roofline(ops: float, nbytes: int, seconds: float, traffic):
+    """Roofline of LM-head kernels taking `seconds`: against the int8 MFMA peak
+    when the 2-op multiply-adds take longer there than the algorithmic bytes
+    (weights and hidden rows, read once) take at the HBM peak, else against
+    the HBM peak (a handful of hidden rows: the call streams the head)."""
+    if ops / (PEAK_INT8_TOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9):
+        a = ops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": round(a / PEAK_INT8_TOPS, 4), "traffic": traffic, "algorithmic_ops_per_launch": ops,
+                "algorithmic_bytes_per_launch": nbytes}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4), "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+            "algorithmic_ops_per_launch": ops}
+
+
 def lmhead_bench(args, torch, np) -> int:
     import token_verification_amd as tv
     import workloads
@@ -516,7 +532,6 @@ def lmhead_bench(args, torch, np) -> int:
     tail = np.array([e[1].elapsed_time(e[2]) for e in evs])
     call = np.array([e[0].elapsed_time(e[2]) for e in evs])
     ops = 2.0 * M * V * d                                  # int8 multiply-adds, counted as two ops
-    achieved = ops / (float(head.mean()) * 1e-3) / 1e12
     wbytes = V * d + M * d + 4 * (V + M)
     positions = B * k
     acc = out.accepted_len.cpu().numpy()
@@ -534,11 +549,9 @@ def lmhead_bench(args, torch, np) -> int:
         "phase_us": {"lmhead_kernel": round(float(head.mean()) * 1e3, 2),
                      "merge_and_decide": round(float(tail.mean()) * 1e3, 2),
                      "call": round(float(call.mean()) * 1e3, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": counter_traffic(f"spec_verify_lmhead_b{B}_k{k}_v{V}_d{d}_int8",
-                                                "traffic_bytes_lmhead_kernel"),
-                     "algorithmic_ops_per_launch": ops},
+        "roofline": head_roofline(ops, wbytes, float(head.mean()) * 1e-3,
+                                  counter_traffic(f"spec_verify_lmhead_b{B}_k{k}_v{V}_d{d}_int8",
+                                                  "traffic_bytes_lmhead_kernel")),
         "hbm_context": {"weight_and_hidden_bytes": wbytes,
                         "GB_per_s": round(wbytes / (float(head.mean()) * 1e-3) / 1e9, 1)},
         "accepted_mean": round(float(acc[acc >= 0].mean()), 3) if (acc >= 0).any() else None,
@@ -621,7 +634,6 @@ def lmhead_sample_bench(args, torch, np) -> int:
     callt = np.array([e[0].elapsed_time(e[3]) for e in evs])
     heads = ph[:, 0]
     ops = 2.0 * (MT + MD) * V * d                          # int8 multiply-adds of both heads, two ops each
-    achieved = ops / (float(heads.mean()) * 1e-3) / 1e12
     wbytes = (2 if own else 1) * (V * d + 4 * V) + (MT + MD) * (d + 4)
     positions = B * k
     acc = out.accepted_len.cpu().numpy()
@@ -641,10 +653,8 @@ def lmhead_sample_bench(args, torch, np) -> int:
                      "merges": round(float(ph[:, 1].mean()) * 1e3, 2),
                      "decide_and_draw": round(float(ph[:, 2].mean()) * 1e3, 2),
                      "call": round(float(callt.mean()) * 1e3, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": counter_traffic(f"spec_verify_{tag}", "traffic_bytes_head_passes"),
-                     "algorithmic_ops_per_launch": ops},
+        "roofline": head_roofline(ops, wbytes, float(heads.mean()) * 1e-3,
+                                  counter_traffic(f"spec_verify_{tag}", "traffic_bytes_head_passes")),
         "hbm_context": {"weight_and_hidden_bytes": wbytes,
                         "GB_per_s": round(wbytes / (float(heads.mean()) * 1e-3) / 1e9, 1)},
         "accepted_mean": round(float(acc[acc >= 0].mean()), 3) if (acc >= 0).any() else None,
