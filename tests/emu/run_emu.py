@@ -416,7 +416,7 @@ def lmhead_sample():
     for B, k, V, d, T, own, pool in ((3, 2, 700, 256, 1.0, False, 1), (50, 3, 300, 128, 0.7, True, 2),
                                      (4, 0, 257, 128, 1.3, False, 1), (48, 3, 500, 128, 1.0, False, 2),
                                      (16, 5, 1500, 384, 0.3, True, 2), (5, 2, 1, 128, 0.7, True, 1),
-                                     (3, 13, 6, 128, 1.0, False, 2)):
+                                     (3, 13, 6, 128, 1.0, False, 2), (64, 3, 600, 256, 0.9, False, 2)):
         x = workloads.make_lmhead_sample(B, k, V, d, seed=1, draft_head=own)
         if B >= 48:
             x["hidden_scale"][0] = float("nan")            # batch row 0: NaN target logits
