@@ -347,7 +347,9 @@ def lmhead():
     # int8 LM head fused with greedy verification: partial vocabulary and
     # hidden-row tiles, several LDS stages, k = 0, NaN / inf scales, a token
     # outside [0, V), ties at the top
-    for B, k, V, d, pool in ((3, 2, 700, 256, 1), (50, 3, 300, 128, 2), (4, 0, 257, 128, 1), (64, 3, 600, 256, 2), (48, 3, 500, 128, 2)):
+    # the last two: 16 and 18 tiles of 256 rows, one hidden tile ragged
+    for B, k, V, d, pool in ((3, 2, 700, 256, 1), (50, 3, 300, 128, 2), (4, 0, 257, 128, 1), (64, 3, 600, 256, 2),
+                             (48, 3, 500, 128, 2), (64, 3, 4000, 128, 2), (125, 3, 2100, 256, 2)):
         x = workloads.make_lmhead(B, k, V, d, seed=1)
         if B >= 50:
             x["hidden_scale"][0] = float("nan")            # batch row 0: NaN logits
