@@ -75,6 +75,8 @@ def oracle_of(x, rows=None):
     (64, 3, 2000, 256),         # 256-row tiles, four stages (the prologue fills three)
     (96, 3, 3000, 640),         # 384 rows: two 192-row tiles, ten stages
     (160, 3, 3000, 640),        # 640 rows: five 128-row tiles (the narrow kernel), ten stages
+    (2, 4, 70001, 1536),        # 10 rows: a 32-row tile with 512-byte stages (12), vocabulary tail
+    (4, 7, 3000, 512),          # 32 rows: the 512-byte stages at their fewest (four)
 ])
 def test_lmhead_matches_oracle(B, k, V, d):
     say("lmhead", B, k, V, d)

@@ -75,6 +75,8 @@ def subset(r, rows):
     (160, 3, 3000, 640, 1.6, True),    # 640 / 480 rows: 128-row tiles (the narrow kernel)
     (1, 4, 128256, 4096, 1.0, False),  # one batch row over a full-size shared head (one pass, 9 rows)
     (3, 7, 50000, 512, 0.8, False),    # 24 + 21 rows in one pass: the draft's rows start mid-tile
+    (2, 3, 40000, 1536, 0.7, True),    # 8 / 6 rows, separate heads: 32-row tiles with 512-byte stages
+    (1, 2, 5000, 512, 1.0, False),     # 3 + 2 rows in one pass, the 512-byte stages at their fewest
 ])
 def test_lmhead_sample_matches_oracle(B, k, V, d, T, own):
     say("lmhead sample", B, k, V, d, T, own)

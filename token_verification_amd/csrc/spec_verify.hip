@@ -2513,6 +2513,104 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     }
 }
 
+// 32-row tiles when d is a multiple of 512. Such a call streams the head from
+// HBM, and the rate of that stream depends on how much of each weight row one
+// stage takes: in a probe of these loads alone, 64 bytes of 256 rows per
+// stage (head_main's shape) streamed at ~4.2 TB/s and 512 bytes of 64 rows at
+// ~5.0. So a stage here holds 512 bytes of d for one 32-row block of each
+// wave (block ks % 4 of its four, bytes 512 * (ks / 4) on) and of the 32
+// hidden rows: 48 KB, three buffers, one workgroup per CU, 16 MFMAs per wave
+// and stage. Against head_main's 32-row tile the kernel measured 1-5% faster
+// at V = 128256, d = 4096, and 18% at V = 151936 (594 tiles, which also fit
+// one workgroup per CU better than two).
+// Rows are 512 bytes in LDS; logical chunk c of stage row R sits at physical
+// chunk c ^ (R % 16), so the operand reads of 16 consecutive lanes (rows
+// r..r+15, one chunk) cover all banks, and each loading lane fetches the
+// chunk that lands at its position. At the barrier of stage ks every wave has
+// read all of stage ks, so stage ks + 3 goes into its buffer. The epilogues
+// are head_main's (same accumulator layout).
+template <int EPI>
+__device__ __attribute__((always_inline)) inline void head_main_w512(const HeadParams& H) {
+    using Tile = HeadTile<1, 1>;
+    constexpr int RB = 512;                                // bytes of d per stage and row
+    constexpr int ST = (64 + 32) * RB;                     // 2 x 32 weight rows, 32 hidden rows
+    constexpr int NBUF = 3, P = 3;                         // stages in flight
+    constexpr int LPW = (32 + 16) * RB / 1024;             // load instructions per wave and stage
+    __shared__ __attribute__((aligned(16))) unsigned char S[NBUF * ST];
+    const Tile w(H);
+    const int lane = w.t & 63, wv = w.t >> 6;
+    const unsigned d = static_cast<unsigned>(H.d);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(w.v0) * d, static_cast<unsigned>(w.nv) * d);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(w.m0) * d, static_cast<unsigned>(w.nm) * d);
+    // load j of wave wv fills stage rows 2j and 2j + 1 of its weight block
+    // (rows 32*wv + ..) and of its half of the hidden rows (rows 64 + 16*wv
+    // + ..); lane l lands on the first + l/32, physical chunk l % 32
+    const int lr = lane >> 5, pc = lane & 31;
+    auto issue = [&](int ks) {
+        unsigned char* B = S + (ks % NBUF) * ST;
+        const int vb = ks & 3;
+        const unsigned k0 = static_cast<unsigned>(ks >> 2) * RB;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const unsigned c = static_cast<unsigned>(pc ^ ((2 * j + lr) & 15));
+            const unsigned row = static_cast<unsigned>(128 * wv + 32 * vb + 2 * j + lr);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(B + (32 * wv + 2 * j) * RB), 16,
+                                                     static_cast<int>(row * d + k0 + 16u * c), 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const unsigned c = static_cast<unsigned>(pc ^ ((2 * j + lr) & 15));
+            const unsigned row = static_cast<unsigned>(16 * wv + 2 * j + lr);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(B + (64 + 16 * wv + 2 * j) * RB), 16,
+                                                     static_cast<int>(row * d + k0 + 16u * c), 0, 0, 0);
+        }
+    };
+    // operands of K step s (16 per stage): A row 32*vw + r, B row 64 + r,
+    // logical chunk 2s + hi; both rows are r modulo 16
+    const int ra = (32 * w.vw + w.r) * RB, rb = (64 + w.r) * RB, sw = w.r & 15;
+    i32x4 fa[2], fb[2];
+    auto frag = [&](int ks, int s, int slot) {
+        const unsigned char* B = S + (ks % NBUF) * ST;
+        const int co = ((2 * s + w.hi) ^ sw) << 4;
+        fa[slot] = *reinterpret_cast<const i32x4*>(B + ra + co);
+        fb[slot] = *reinterpret_cast<const i32x4*>(B + rb + co);
+    };
+    i32x16 acc[4][1];
+    acc_zero<1>(acc);
+    const int nks = 4 * (H.d / RB);                        // >= 4
+    for (int q = 0; q < P; ++q) issue(q);
+    wait_stages<LPW, P - 1>(P - 1);                        // stage 0 is in
+    __syncthreads();
+    frag(0, 0, 0);
+    for (int kq = 0; kq < nks; kq += 4) {
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) {
+            const int ks = kq + vb;
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                frag(ks, s + 1, (s + 1) & 1);
+                acc[vb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s & 1], fb[s & 1], acc[vb][0], 0, 0, 0);
+            }
+            if (ks + 1 < nks) {                            // uniform
+                wait_stages<LPW, P - 1>(min(P - 2, nks - 2 - ks)); // stage ks + 1 is in
+                __syncthreads();
+                if (ks + P < nks) issue(ks + P);
+                frag(ks + 1, 0, 0);
+            }
+            acc[vb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[1], fb[1], acc[vb][0], 0, 0, 0);
+        }
+    }
+    __syncthreads();                                       // every wave is done with the stages
+    static_assert(NBUF * ST >= 2 * Tile::BM * static_cast<int>(sizeof(HeadRecS)) + 2 * HV * 4, "exchange");
+    static_assert(NBUF * ST >= (Tile::SR * (HV + 4) + HV) * 4, "logit slab");
+    if constexpr (EPI == EPI_SAMPLE) {
+        w.finish_sample(H, acc, S);
+        w.finish_logits(H, acc, S);
+    } else {
+        w.finish(H, acc, S);
+    }
+}
+
 // 256-row tiles: 2 x 4 waves of 128 x 64, two waves per SIMD (128
 // accumulator registers each), four 32 KB stage buffers. Against 2 x 2 waves
 // of 128 x 128 at one wave per SIMD (the sampling kernel's shape) the bytes per
@@ -2536,6 +2634,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void h
 // four buffers (three stages of loads in flight), two workgroups per CU; a
 // 128-row tile would stage and multiply 96 rows of padding.
 __global__ __launch_bounds__(NTH / 2) void head_kernel_tiny(HeadParams H) { head_main<1, 4, EPI_GREEDY, 1>(H); }
+__global__ __launch_bounds__(NTH / 2) void head_kernel_tiny_w(HeadParams H) { head_main_w512<EPI_GREEDY>(H); }
 
 // Sampling mode, with the same tile sizes: pass 1's terms per row and
 // vocabulary tile, and every logit stored for the draw. Its 256-row tiles keep
@@ -2547,6 +2646,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void h
     head_main<2, 3, EPI_SAMPLE>(H);
 }
 __global__ __launch_bounds__(NTH / 2) void head_kernel_tiny_s(HeadParams H) { head_main<1, 4, EPI_SAMPLE, 1>(H); }
+__global__ __launch_bounds__(NTH / 2) void head_kernel_tiny_ws(HeadParams H) { head_main_w512<EPI_SAMPLE>(H); }
 
 
 // Sampling mode, one workgroup per hidden row: merge its vocabulary-tile
@@ -3093,6 +3193,7 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
         if (plan.bm == 256) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(2 * NTH), 0, s, H);
         else if (plan.bm == 192) hipLaunchKernelGGL(head_kernel_mid, grid, dim3(NTH), 0, s, H);
         else if (plan.bm == 128) hipLaunchKernelGGL(head_kernel_narrow, grid, dim3(NTH), 0, s, H);
+        else if (d % 512 == 0) hipLaunchKernelGGL(head_kernel_tiny_w, grid, dim3(NTH / 2), 0, s, H);
         else hipLaunchKernelGGL(head_kernel_tiny, grid, dim3(NTH / 2), 0, s, H);
         e = hipGetLastError();
     }
@@ -3213,6 +3314,7 @@ hipError_t launch_head_sample(HeadParams& H, int bm, hipStream_t s) {
     if (bm == 256) hipLaunchKernelGGL(head_kernel_wide_s, grid, dim3(NTH), 0, s, H);
     else if (bm == 192) hipLaunchKernelGGL(head_kernel_mid_s, grid, dim3(NTH), 0, s, H);
     else if (bm == 128) hipLaunchKernelGGL(head_kernel_narrow_s, grid, dim3(NTH), 0, s, H);
+    else if (H.d % 512 == 0) hipLaunchKernelGGL(head_kernel_tiny_ws, grid, dim3(NTH / 2), 0, s, H);
     else hipLaunchKernelGGL(head_kernel_tiny_s, grid, dim3(NTH / 2), 0, s, H);
     return hipGetLastError();
 }
