@@ -505,6 +505,33 @@ def head_roofline(ops: float, nbytes: int, seconds: float, traffic):
             "algorithmic_ops_per_launch": ops}
 
 
+def timed_calls(torch, fn, steps):
+    """Wall seconds for `steps` calls of fn back to back, and the GPU ms per
+    call between one event pair on the current stream around all of them."""
+    stream = torch.cuda.current_stream()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for _ in range(steps):
+        fn()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, g0.elapsed_time(g1) / steps
+
+
+def materialized_events(torch, steps, n):
+    """steps x n timing events, each recorded once beforehand: torch creates an
+    event's handle at its first record, which would otherwise add a record of
+    its own inside the timed loop."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
+    for e in evs:
+        for ev in e:
+            ev.record()
+    torch.cuda.synchronize()
+    return evs
+
+
 def lmhead_bench(args, torch, np) -> int:
     import token_verification_amd as tv
     import workloads
@@ -522,12 +549,14 @@ def lmhead_bench(args, torch, np) -> int:
     for _ in range(args.warmup):
         tv.spec_verify_lmhead(*a, out=out)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
+    # the timed region: plain calls back to back (events between the calls
+    # would add their own gaps to the stream); then, in a loop of its own, the
+    # phases from events the library records between its kernels
+    wall, k_ms = timed_calls(torch, lambda: tv.spec_verify_lmhead(*a, out=out), args.steps)
+    evs = materialized_events(torch, args.steps, 3)
     for i in range(args.steps):
         tv.spec_verify_lmhead(*a, out=out, phase_events=evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     head = np.array([e[0].elapsed_time(e[1]) for e in evs])
     tail = np.array([e[1].elapsed_time(e[2]) for e in evs])
     call = np.array([e[0].elapsed_time(e[2]) for e in evs])
@@ -546,6 +575,7 @@ def lmhead_bench(args, torch, np) -> int:
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": f"lmhead_b{B}_k{k}_v{V}_d{d}_int8", "B": B, "k": k, "V": V, "d": d,
                    "hidden_rows": M},
+        "gpu_us_per_step": round(k_ms * 1e3, 2),
         "phase_us": {"lmhead_kernel": round(float(head.mean()) * 1e3, 2),
                      "merge_and_decide": round(float(tail.mean()) * 1e3, 2),
                      "call": round(float(call.mean()) * 1e3, 2)},
@@ -624,12 +654,11 @@ def lmhead_sample_bench(args, torch, np) -> int:
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
+    wall, k_ms = timed_calls(torch, call, args.steps)     # as in lmhead_bench
+    evs = materialized_events(torch, args.steps, 4)
     for i in range(args.steps):
         call(phase_events=evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
     callt = np.array([e[0].elapsed_time(e[3]) for e in evs])
     heads = ph[:, 0]
@@ -649,6 +678,7 @@ def lmhead_sample_bench(args, torch, np) -> int:
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": tag, "B": B, "k": k, "V": V, "d": d, "T": T,
                    "target_rows": MT, "draft_rows": MD, "draft_head": "own" if own else "shared"},
+        "gpu_us_per_step": round(k_ms * 1e3, 2),
         "phase_us": {"head_passes": round(float(heads.mean()) * 1e3, 2),
                      "merges": round(float(ph[:, 1].mean()) * 1e3, 2),
                      "decide_and_draw": round(float(ph[:, 2].mean()) * 1e3, 2),
