@@ -348,10 +348,12 @@ def lmhead():
     # hidden-row tiles, several LDS stages, k = 0, NaN / inf scales, a token
     # outside [0, V), ties at the top
     # then 16 and 18 tiles of 256 rows (one hidden tile ragged), 32-row tiles
-    # with 512-byte stages (d = 512, 1536), and 50 rows in a 128-row tile
+    # with 512-byte stages (d = 512, 1536), and 50 and 48 rows in a 128-row
+    # tile (d = 512, 768)
     for B, k, V, d, pool in ((3, 2, 700, 256, 1), (50, 3, 300, 128, 2), (4, 0, 257, 128, 1), (64, 3, 600, 256, 2),
                              (48, 3, 500, 128, 2), (64, 3, 4000, 128, 2), (125, 3, 2100, 256, 2),
-                             (3, 2, 700, 512, 1), (2, 5, 1300, 1536, 2), (10, 4, 1300, 512, 2)):
+                             (3, 2, 700, 512, 1), (2, 5, 1300, 1536, 2), (10, 4, 1300, 512, 2),
+                             (12, 3, 900, 768, 1)):
         x = workloads.make_lmhead(B, k, V, d, seed=1)
         if B >= 50:
             x["hidden_scale"][0] = float("nan")            # batch row 0: NaN logits
@@ -417,14 +419,14 @@ def run_lmhead_sample(x, T, pool=1):
 def lmhead_sample():
     # sampling-mode verify fused with int8 heads: shared and separate draft
     # heads, partial tiles, k = 0, NaN / inf scales, a token outside [0, V);
-    # two take 32-row tiles with 512-byte stages; the last, 36 rows in one
-    # pass, a 128-row tile
+    # two take 32-row tiles with 512-byte stages, the last two (36 and 42
+    # rows in one pass) a 128-row tile
     for B, k, V, d, T, own, pool in ((3, 2, 700, 256, 1.0, False, 1), (50, 3, 300, 128, 0.7, True, 2),
                                      (4, 0, 257, 128, 1.3, False, 1), (48, 3, 500, 128, 1.0, False, 2),
                                      (16, 5, 1500, 384, 0.3, True, 2), (5, 2, 1, 128, 0.7, True, 1),
                                      (3, 13, 6, 128, 1.0, False, 2), (64, 3, 600, 256, 0.9, False, 2),
                                      (3, 2, 700, 512, 1.0, False, 1), (2, 4, 1300, 1536, 0.8, True, 2),
-                                     (4, 4, 900, 1024, 1.0, False, 2)):
+                                     (4, 4, 900, 1024, 1.0, False, 2), (6, 3, 700, 256, 0.7, False, 1)):
         x = workloads.make_lmhead_sample(B, k, V, d, seed=1, draft_head=own)
         if B >= 48:
             x["hidden_scale"][0] = float("nan")            # batch row 0: NaN target logits

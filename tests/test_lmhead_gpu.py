@@ -77,6 +77,7 @@ def oracle_of(x, rows=None):
     (160, 3, 3000, 640),        # 640 rows: five 128-row tiles (the narrow kernel), ten stages
     (2, 4, 70001, 1536),        # 10 rows: a 32-row tile with 512-byte stages (12), vocabulary tail
     (4, 7, 3000, 512),          # 32 rows: the 512-byte stages at their fewest (four)
+    (10, 4, 5000, 768),         # 50 rows: one 128-row tile, d not a multiple of 512, vocabulary tail
 ])
 def test_lmhead_matches_oracle(B, k, V, d):
     say("lmhead", B, k, V, d)

@@ -77,6 +77,8 @@ def subset(r, rows):
     (3, 7, 50000, 512, 0.8, False),    # 24 + 21 rows in one pass: the draft's rows start mid-tile
     (2, 3, 40000, 1536, 0.7, True),    # 8 / 6 rows, separate heads: 32-row tiles with 512-byte stages
     (1, 2, 5000, 512, 1.0, False),     # 3 + 2 rows in one pass, the 512-byte stages at their fewest
+    (6, 3, 9000, 512, 0.9, False),     # 24 + 18 rows in one pass: one 128-row tile (the uncapped kernel)
+    (10, 4, 3000, 1024, 1.0, True),    # 50 / 40 rows, separate heads: 128-row tiles
 ])
 def test_lmhead_sample_matches_oracle(B, k, V, d, T, own):
     say("lmhead sample", B, k, V, d, T, own)
