@@ -26,7 +26,10 @@ residual mass rounded to zero (flag bit 0) must match the oracle exactly.
 
 Floating outputs: gap and p(x)/q(x) within 1e-5 absolute for float32 inputs
 and 2e-3 for bfloat16 inputs (the gap of bf16 inputs is a difference of two
-bf16 values and is compared exactly in practice).
+bf16 values and is compared exactly in practice). The kernel forms the gap as
+one float32 subtraction of two exact float32 logits, so a gap may also differ
+by half a float32 ulp of itself (2^-24 of its size), which is the larger bound
+once gaps pass ~170.
 """
 from __future__ import annotations
 
@@ -106,9 +109,10 @@ def compare(gpu, ref, dtype: str, greedy: bool):
     assert (np.isfinite(g_gpu) == fin).all(), "gap finiteness differs"
     assert (np.isnan(g_gpu) == np.isnan(g_ref)).all(), "gap NaN positions differ"
     if fin.any():
-        err = np.abs(g_gpu[fin] - g_ref[fin]).max()
-        stats["gap_err"] = float(err)
-        assert err <= tol, f"gap error {err} > {tol}"
+        dev = np.abs(g_gpu[fin] - g_ref[fin])
+        bound = np.maximum(tol, 2.0 ** -24 * np.abs(g_ref[fin]))
+        stats["gap_err"] = float(dev.max())
+        assert (dev <= bound).all(), f"gap error {float(dev.max())} beyond max({tol}, 2^-24 |gap|)"
     if not greedy and gpu.target_prob is not None and ref.p_tok.size:
         for name, g, r in (("p", gpu.target_prob, ref.p_tok), ("q", gpu.draft_prob, ref.q_tok)):
             gg = g.cpu().numpy().astype(np.float64)[valid]

@@ -90,6 +90,17 @@ def test_lmhead_sample_matches_oracle(B, k, V, d, T, own):
     say("  ", st, "accepted", np.bincount(acc[acc >= 0], minlength=k + 1).tolist())
 
 
+@pytest.mark.parametrize("B,k,V,d,own", [(1, 2, 1000, 65536, False), (2, 1, 700, 65408, True)])
+def test_lmhead_sample_largest_d(B, k, V, d, own):
+    # the largest d through both 32-row tiles (512- and 64-byte stages)
+    say("lmhead sample largest d", B, k, V, d, own)
+    x = workloads.make_lmhead_sample(B, k, V, d, seed=5, draft_head=own)
+    r = run(to_dev(x), 1.0)
+    torch.cuda.synchronize()
+    st = compare(r, oracle_of(x, 1.0), "f32", False)
+    say("  ", st)
+
+
 def test_lmhead_sample_invalid_rows_and_extreme_uniforms():
     B, k, V, d, T = 50, 3, 3000, 256, 1.0
     x = workloads.make_lmhead_sample(B, k, V, d, seed=4)
