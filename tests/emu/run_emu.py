@@ -353,7 +353,7 @@ def lmhead():
     for B, k, V, d, pool in ((3, 2, 700, 256, 1), (50, 3, 300, 128, 2), (4, 0, 257, 128, 1), (64, 3, 600, 256, 2),
                              (48, 3, 500, 128, 2), (64, 3, 4000, 128, 2), (125, 3, 2100, 256, 2),
                              (3, 2, 700, 512, 1), (2, 5, 1300, 1536, 2), (10, 4, 1300, 512, 2),
-                             (12, 3, 900, 768, 1)):
+                             (12, 3, 900, 768, 1), (2, 3, 1, 512, 1), (3, 1, 255, 1024, 2)):
         x = workloads.make_lmhead(B, k, V, d, seed=1)
         if B >= 50:
             x["hidden_scale"][0] = float("nan")            # batch row 0: NaN logits

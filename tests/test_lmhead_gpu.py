@@ -81,6 +81,8 @@ def oracle_of(x, rows=None):
     (2, 4, 70001, 1536),        # 10 rows: a 32-row tile with 512-byte stages (12), vocabulary tail
     (4, 7, 3000, 512),          # 32 rows: the 512-byte stages at their fewest (four)
     (10, 4, 5000, 768),         # 50 rows: one 128-row tile, d not a multiple of 512, vocabulary tail
+    (2, 3, 1, 512),             # V = 1: one vocabulary row in a 256-row tile, 512-byte stages
+    (3, 1, 255, 1024),          # V = 255: one partial vocabulary tile, 512-byte stages
 ])
 def test_lmhead_matches_oracle(B, k, V, d):
     say("lmhead", B, k, V, d)
