@@ -324,6 +324,60 @@ int spec_verify_lmhead_sample_timed(const int8_t* target_hidden, const float* ta
                                     void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
 /*
+ * The LM heads above in a tile-major layout, written once per head (a head is
+ * static) so that the head kernels stream it in long contiguous runs: the
+ * multiply-adds and results are those of the row-major calls, bit for bit.
+ * ("Speculative Decoding: The Physics of Stolen Time", section 1, stage 2, and
+ * the gnosis design note, "Cost / correctness constraints": the verify pass
+ * applies the head to every speculated position; this only changes where its
+ * bytes sit.)
+ *
+ * Layout: for each vocabulary tile of 256 rows (zeros past V) and each 64 bytes
+ * of d, one contiguous 16 KB block holding those 64 bytes of the tile's 256
+ * rows in the order the head kernels stage them (row r at 64 r, its 16-byte
+ * chunk p holding chunk p ^ ((r >> 2) & 3) of the row's 64 bytes).
+ */
+
+/* Bytes of the tile-major copy of an int8 head [V, d]: ceil(V/256)*256*d
+ * (0 if V or d is outside the ranges spec_verify_lmhead accepts). Host-only. */
+size_t spec_lmhead_packed_size(int32_t V, int32_t d);
+
+/*
+ * Enqueue on `stream` the kernel that writes weight (int8 [V, d], row-major,
+ * device) into packed (device, at least spec_lmhead_packed_size(V, d) bytes,
+ * both 16-byte aligned). The caller owns both buffers. Errors as above
+ * (SPEC_ERR_SHAPE, SPEC_ERR_NULL, SPEC_ERR_ALIGN, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP);
+ * nothing is enqueued on an argument error.
+ */
+int spec_lmhead_pack(const int8_t* weight, int32_t V, int32_t d, int8_t* packed, size_t packed_bytes, void* stream);
+
+/*
+ * spec_verify_lmhead / spec_verify_lmhead_timed with the head in the tile-major
+ * layout (packed_weight as written by spec_lmhead_pack for this V and d).
+ * events: NULL, or the three events of spec_verify_lmhead_timed. Same
+ * arguments, workspace, results and errors otherwise.
+ */
+int spec_verify_lmhead_packed(const int8_t* hidden, const float* hidden_scale, const int8_t* packed_weight,
+                              const float* weight_scale, const int32_t* draft_tokens, int32_t B, int32_t k,
+                              int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                              void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * spec_verify_lmhead_sample / _timed with both heads in the tile-major layout
+ * (draft_packed_weight NULL for a shared head, as draft_weight there). events:
+ * NULL, or the four events of spec_verify_lmhead_sample_timed. Same arguments,
+ * workspace, results and errors otherwise.
+ */
+int spec_verify_lmhead_sample_packed(const int8_t* target_hidden, const float* target_hidden_scale,
+                                     const int8_t* target_packed_weight, const float* target_weight_scale,
+                                     const int8_t* draft_hidden, const float* draft_hidden_scale,
+                                     const int8_t* draft_packed_weight, const float* draft_weight_scale,
+                                     const int32_t* draft_tokens, const float* uniforms, float temperature,
+                                     int32_t B, int32_t k, int32_t V, int32_t d, int32_t* accepted_len,
+                                     int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
+                                     void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation): spec_verify with the
  * library's own device scratch buffer in place of a caller workspace. Every other

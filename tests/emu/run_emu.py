@@ -314,7 +314,22 @@ def exact_path():
     del os.environ["SPEC_VERIFY_FORCE_EXACT_PATH"]
 
 
-def run_lmhead(x, pool=1):
+def pack_head(w, V, d):
+    """The tile-major copy of a head, written by the library's pack kernel
+    (kept referenced by the caller while the library reads it)."""
+    L.spec_lmhead_packed_size.argtypes = [I, I]
+    L.spec_lmhead_packed_size.restype = S
+    L.spec_lmhead_pack.argtypes = [P, I, I, P, S, P]
+    L.spec_lmhead_pack.restype = ctypes.c_int
+    n = L.spec_lmhead_packed_size(V, d)
+    buf = np.frombuffer(os.urandom(n + 16), np.uint8).copy()
+    o = (-buf.ctypes.data) % 16
+    view = buf[o:o + n]
+    assert L.spec_lmhead_pack(ptr(w), V, d, ptr(view), n, None) == 0, L.spec_verify_last_error()
+    return view
+
+
+def run_lmhead(x, pool=1, packed=False):
     from oracle.lmhead import lmhead_greedy_ref
     B, k, V, d = x["B"], x["k"], x["V"], x["d"]
     h, hs, w, ws = (np.ascontiguousarray(x[n].numpy()) for n in ("hidden", "hidden_scale", "weight", "weight_scale"))
@@ -328,8 +343,15 @@ def run_lmhead(x, pool=1):
     base = wsp.ctypes.data
     off = (-base) % 256
     L.spec_verify_emu_set_pool(pool)
-    rc = L.spec_verify_lmhead(ptr(h), ptr(hs), ptr(w), ptr(ws), ptr(tok), B, k, V, d, ptr(acc), ptr(out),
-                              ptr(gap), ctypes.c_void_p(base + off), nb, None)
+    if packed:
+        L.spec_verify_lmhead_packed.argtypes = [P, P, P, P, P, I, I, I, I, P, P, P, P, S, P, P]
+        L.spec_verify_lmhead_packed.restype = ctypes.c_int
+        pw = pack_head(w, V, d)
+        rc = L.spec_verify_lmhead_packed(ptr(h), ptr(hs), ptr(pw), ptr(ws), ptr(tok), B, k, V, d, ptr(acc),
+                                         ptr(out), ptr(gap), ctypes.c_void_p(base + off), nb, None, None)
+    else:
+        rc = L.spec_verify_lmhead(ptr(h), ptr(hs), ptr(w), ptr(ws), ptr(tok), B, k, V, d, ptr(acc), ptr(out),
+                                  ptr(gap), ctypes.c_void_p(base + off), nb, None)
     assert rc == 0, (rc, L.spec_verify_last_error())
     ref = lmhead_greedy_ref(h, hs, w, ws, tok, B, k)
     assert (acc == ref.accepted_len).all(), (acc, ref.accepted_len)
@@ -362,11 +384,13 @@ def lmhead():
             x["hidden"][12:16] = 0                         # batch row 3: all logits 0, a tie at 0
             x["tokens"][3, :] = 0
         acc = run_lmhead(x, pool=pool)
+        if d in (256, 512) and V > 1:                       # the same through the tile-major layout
+            assert (run_lmhead(x, pool=pool, packed=True) == acc).all()
         if B >= 50:
             assert acc[0] == -1 and acc[1] == -1 and acc[2] == -1 and acc[3] == 3
 
 
-def run_lmhead_sample(x, T, pool=1):
+def run_lmhead_sample(x, T, pool=1, packed=False):
     # set here, not at import: libraries built from older sources lack the symbol
     from oracle.lmhead import lmhead_sample_ref
     L.spec_verify_lmhead_sample.argtypes = [P, P, P, P, P, P, P, P, P, P, F, I, I, I, I, P, P, P, P, P, P, S, P]
@@ -389,11 +413,21 @@ def run_lmhead_sample(x, T, pool=1):
     base = wsp.ctypes.data
     off = (-base) % 256
     L.spec_verify_emu_set_pool(pool)
-    rc = L.spec_verify_lmhead_sample(
-        ptr(arr["hidden"]), ptr(arr["hidden_scale"]), ptr(arr["weight"]), ptr(arr["weight_scale"]),
-        ptr(arr["draft_hidden"]), ptr(arr["draft_hidden_scale"]), ptr(arr["draft_weight"]),
+    wt, wd = arr["weight"], arr["draft_weight"]
+    fn = L.spec_verify_lmhead_sample
+    tail = ()
+    if packed:
+        L.spec_verify_lmhead_sample_packed.argtypes = [P, P, P, P, P, P, P, P, P, P, F, I, I, I, I, P, P, P, P, P,
+                                                       P, S, P, P]
+        L.spec_verify_lmhead_sample_packed.restype = ctypes.c_int
+        wt = pack_head(wt, V, d)
+        wd = None if wd is None else pack_head(wd, V, d)
+        fn, tail = L.spec_verify_lmhead_sample_packed, (None,)
+    rc = fn(
+        ptr(arr["hidden"]), ptr(arr["hidden_scale"]), ptr(wt), ptr(arr["weight_scale"]),
+        ptr(arr["draft_hidden"]), ptr(arr["draft_hidden_scale"]), ptr(wd),
         ptr(arr["draft_weight_scale"]), ptr(tok), ptr(arr["uniforms"]), ctypes.c_float(T), B, k, V, d,
-        ptr(acc), ptr(out), ptr(gap), ptr(tp), ptr(dp), ctypes.c_void_p(base + off), nb, None)
+        ptr(acc), ptr(out), ptr(gap), ptr(tp), ptr(dp), ctypes.c_void_p(base + off), nb, None, *tail)
     assert rc == 0, (rc, L.spec_verify_last_error())
     ref = lmhead_sample_ref(arr["hidden"], arr["hidden_scale"], arr["weight"], arr["weight_scale"],
                             arr["draft_hidden"], arr["draft_hidden_scale"], arr["draft_weight"],
@@ -433,6 +467,8 @@ def lmhead_sample():
             x["draft_hidden_scale"][3] = float("inf")      # batch row 1: +-inf / NaN draft logits
             x["tokens"][2, 1] = V                          # batch row 2: token out of range
         acc = run_lmhead_sample(x, T, pool=pool)
+        if d in (256, 512, 1024) and B <= 16:               # the same through the tile-major layout
+            assert (run_lmhead_sample(x, T, pool=pool, packed=True) == acc).all()
         if B >= 48:
             assert acc[0] == -1 and acc[1] == -1 and acc[2] == -1
         print("  accepted", np.bincount(acc[acc >= 0], minlength=k + 1).tolist(), flush=True)

@@ -27,7 +27,7 @@ def test_exports_match_header():
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     exported = {s for s in exported if s.startswith("spec_")}
     assert declared() == exported
-    assert len(exported) == 17
+    assert len(exported) == 21
 
 
 def test_version():
@@ -218,6 +218,27 @@ def test_lmhead_rejects_synchronously(kw, code):
                                            a["B"], a["k"], a["V"], a["d"], a["acc"], a["out"], a["gap"],
                                            a["ws"], a["ws_bytes"], None, ctypes.cast(ev, ctypes.c_void_p))
     assert rc in (code, -1)
+    # the tile-major entry point validates the same arguments the same way
+    rc = tv.lib().spec_verify_lmhead_packed(a["hidden"], a["h_scale"], a["weight"], a["w_scale"], a["tokens"],
+                                            a["B"], a["k"], a["V"], a["d"], a["acc"], a["out"], a["gap"],
+                                            a["ws"], a["ws_bytes"], None, None)
+    assert rc == code
+
+
+def test_lmhead_packed_size_and_pack_rejects():
+    L = tv.lib()
+    assert L.spec_lmhead_packed_size(1000, 4096) == 4 * 256 * 4096     # whole 256-row tiles
+    assert L.spec_lmhead_packed_size(256, 128) == 256 * 128
+    assert L.spec_lmhead_packed_size(257, 128) == 512 * 128
+    assert L.spec_lmhead_packed_size(0, 128) == 0
+    assert L.spec_lmhead_packed_size(100, 100) == 0                    # d not a multiple of 128
+    assert L.spec_lmhead_packed_size(100, 65536 + 128) == 0
+    need = L.spec_lmhead_packed_size(1000, 256)
+    for args, code in (((FAKE, 0, 256, FAKE, need, None), -2), ((None, 1000, 256, FAKE, need, None), -1),
+                       ((FAKE, 1000, 256, None, need, None), -1), ((FAKE + 8, 1000, 256, FAKE, need, None), -7),
+                       ((FAKE, 1000, 256, FAKE, need - 16, None), -6)):
+        assert L.spec_lmhead_pack(*args) == code
+        assert binding.last_error()
 
 
 def test_lmhead_sample_workspace_size():
@@ -267,6 +288,7 @@ def test_lmhead_sample_rejects_synchronously(kw, code):
     ev = (ctypes.c_void_p * 4)(None, None, None, None)
     rc = tv.lib().spec_verify_lmhead_sample_timed(*args, ctypes.cast(ev, ctypes.c_void_p))
     assert rc in (code, -1)
+    assert tv.lib().spec_verify_lmhead_sample_packed(*args, None) == code
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch_on_the_host():

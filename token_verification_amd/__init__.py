@@ -11,9 +11,11 @@ from .binding import (  # noqa: F401
     GREEDY,
     MARGIN,
     SAMPLE,
+    PackedHead,
     SpecVerifyError,
     check_args,
     lib,
+    pack_lmhead,
     spec_commit,
     spec_gate,
     spec_verify,

@@ -91,6 +91,14 @@ def lib():
                 L.spec_verify_lmhead_sample_timed.restype = ctypes.c_int
                 L.spec_lmhead_sample_workspace_size.argtypes = [I, I, I, I]
                 L.spec_lmhead_sample_workspace_size.restype = S
+                L.spec_lmhead_packed_size.argtypes = [I, I]
+                L.spec_lmhead_packed_size.restype = S
+                L.spec_lmhead_pack.argtypes = [P, I, I, P, S, P]
+                L.spec_lmhead_pack.restype = ctypes.c_int
+                L.spec_verify_lmhead_packed.argtypes = [P, P, P, P, P, I, I, I, I, P, P, P, P, S, P, P]
+                L.spec_verify_lmhead_packed.restype = ctypes.c_int
+                L.spec_verify_lmhead_sample_packed.argtypes = list(L.spec_verify_lmhead_sample_timed.argtypes)
+                L.spec_verify_lmhead_sample_packed.restype = ctypes.c_int
                 L.spec_verify_last_error.restype = ctypes.c_char_p
                 L.spec_verify_version.restype = ctypes.c_char_p
                 _lib = L
@@ -394,6 +402,50 @@ def spec_commit(accepted_len: torch.Tensor, k: int, kv_len: Optional[torch.Tenso
         raise SpecVerifyError(rc, last_error())
 
 
+class PackedHead(NamedTuple):
+    """An int8 LM head [V, d] in the tile-major layout (spec_lmhead_pack)."""
+    data: torch.Tensor                                    # int8, spec_lmhead_packed_size(V, d) bytes
+    V: int
+    d: int
+
+
+def pack_lmhead(weight: torch.Tensor) -> PackedHead:
+    """The tile-major copy of an int8 head weight [V, d] (see include/spec_verify.h),
+    written on the current stream; pass it as `weight` / `draft_weight` to
+    spec_verify_lmhead and spec_verify_lmhead_sample."""
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2 or weight.dtype != torch.int8 \
+            or not weight.is_cuda or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous int8 2-D device tensor")
+    V, d = weight.shape
+    need = int(lib().spec_lmhead_packed_size(V, d))
+    if need == 0:
+        raise SpecVerifyError(-2, f"unsupported sizes V={V} d={d}")
+    data = torch.empty(need, dtype=torch.int8, device=weight.device)
+    stream = torch.cuda.current_stream(weight.device).cuda_stream
+    rc = lib().spec_lmhead_pack(_ptr(weight), V, d, _ptr(data), need, ctypes.c_void_p(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, last_error())
+    return PackedHead(data, int(V), int(d))
+
+
+def _head_arg(w, d: int, name: str):
+    """(tensor to pass, V, packed) for a head given row-major or packed."""
+    if isinstance(w, PackedHead):
+        t = w.data
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int8 or not t.is_cuda or t.dim() != 1:
+            raise ValueError(f"{name}.data must be an int8 1-D device tensor")
+        if w.d != d:
+            raise ValueError(f"hidden and {name} must share d")
+        if t.numel() < int(lib().spec_lmhead_packed_size(w.V, w.d)):
+            raise ValueError(f"{name}.data is smaller than the packed head")
+        return t, int(w.V), True
+    if not isinstance(w, torch.Tensor) or w.dim() != 2 or w.dtype != torch.int8 or not w.is_cuda:
+        raise ValueError(f"{name} must be an int8 2-D device tensor or a PackedHead")
+    if w.shape[1] != d:
+        raise ValueError(f"hidden and {name} must share d")
+    return w, int(w.shape[0]), False
+
+
 def spec_verify_lmhead(hidden: torch.Tensor, hidden_scale: torch.Tensor, weight: torch.Tensor,
                        weight_scale: torch.Tensor, tokens: torch.Tensor, *,
                        workspace: Optional[torch.Tensor] = None, out: Optional[VerifyResult] = None,
@@ -402,17 +454,15 @@ def spec_verify_lmhead(hidden: torch.Tensor, hidden_scale: torch.Tensor, weight:
 
     hidden int8 [B*(k+1), d] (row b*(k+1)+i: position i of batch row b),
     hidden_scale float32 [B*(k+1)], weight int8 [V, d], weight_scale float32
-    [V], tokens int32 [B, k], all on one device. With phase_events (three
-    torch.cuda.Event created with enable_timing=True) the call records them
-    before the LM-head kernel, after it and after the decisions.
+    [V], tokens int32 [B, k], all on one device; weight may instead be a
+    PackedHead (pack_lmhead). With phase_events (three torch.cuda.Event
+    created with enable_timing=True) the call records them before the LM-head
+    kernel, after it and after the decisions.
     """
-    for t, nm in ((hidden, "hidden"), (weight, "weight")):
-        if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != torch.int8 or not t.is_cuda:
-            raise ValueError(f"{nm} must be an int8 2-D device tensor")
+    if not isinstance(hidden, torch.Tensor) or hidden.dim() != 2 or hidden.dtype != torch.int8 or not hidden.is_cuda:
+        raise ValueError("hidden must be an int8 2-D device tensor")
     M, d = hidden.shape
-    V = weight.shape[0]
-    if weight.shape[1] != d:
-        raise ValueError("hidden and weight must share d")
+    weight, V, packed = _head_arg(weight, d, "weight")
     if tokens.dim() != 2 or tokens.dtype != torch.int32:
         raise ValueError("tokens must be int32 [B, k]")
     B, k = tokens.shape
@@ -450,7 +500,10 @@ def spec_verify_lmhead(hidden: torch.Tensor, hidden_scale: torch.Tensor, weight:
                 ev.record(torch.cuda.current_stream(dev))
             handles.append(ev.cuda_event)
         arr = (ctypes.c_void_p * 3)(*handles)
-        rc = lib().spec_verify_lmhead_timed(*args, ctypes.cast(arr, ctypes.c_void_p))
+        evp = ctypes.cast(arr, ctypes.c_void_p)
+        rc = lib().spec_verify_lmhead_packed(*args, evp) if packed else lib().spec_verify_lmhead_timed(*args, evp)
+    elif packed:
+        rc = lib().spec_verify_lmhead_packed(*args, None)
     else:
         rc = lib().spec_verify_lmhead(*args)
     if rc != 0:
@@ -473,7 +526,8 @@ def spec_verify_lmhead_sample(hidden: torch.Tensor, hidden_scale: torch.Tensor, 
     and draft_hidden_scale [B*k] (None when k = 0); weight int8 [V, d] and
     weight_scale float32 [V]: the target's head, which the draft shares unless
     draft_weight / draft_weight_scale are given; tokens int32 [B, k]; uniforms
-    float32 [B, k+1, 2]. With phase_events (four torch.cuda.Event created with
+    float32 [B, k+1, 2]. weight and draft_weight may instead be PackedHead
+    (pack_lmhead), both or neither. With phase_events (four torch.cuda.Event created with
     enable_timing=True) the call records them before the head passes, after
     them, after the merges of their records, and after the decisions and the
     draw.
@@ -481,14 +535,11 @@ def spec_verify_lmhead_sample(hidden: torch.Tensor, hidden_scale: torch.Tensor, 
     if tokens.dim() != 2 or tokens.dtype != torch.int32:
         raise ValueError("tokens must be int32 [B, k]")
     B, k = tokens.shape
-    for t, nm in ((hidden, "hidden"), (weight, "weight")):
-        if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != torch.int8 or not t.is_cuda:
-            raise ValueError(f"{nm} must be an int8 2-D device tensor")
+    if not isinstance(hidden, torch.Tensor) or hidden.dim() != 2 or hidden.dtype != torch.int8 or not hidden.is_cuda:
+        raise ValueError("hidden must be an int8 2-D device tensor")
     M, d = hidden.shape
-    V = weight.shape[0]
+    weight, V, packed = _head_arg(weight, d, "weight")
     dev = hidden.device
-    if weight.shape[1] != d:
-        raise ValueError("hidden and weight must share d")
     if M != B * (k + 1):
         raise ValueError("hidden must hold B*(k+1) rows")
     if hidden_scale.shape != (M,) or weight_scale.shape != (V,) or hidden_scale.dtype != torch.float32 \
@@ -506,8 +557,9 @@ def spec_verify_lmhead_sample(hidden: torch.Tensor, hidden_scale: torch.Tensor, 
     if (draft_weight is None) != (draft_weight_scale is None):
         raise ValueError("give draft_weight and draft_weight_scale together, or neither")
     if draft_weight is not None:
-        if draft_weight.dtype != torch.int8 or tuple(draft_weight.shape) != (V, d):
-            raise ValueError("draft_weight must be int8 [V, d]")
+        draft_weight, dV, dpacked = _head_arg(draft_weight, d, "draft_weight")
+        if dV != V or dpacked != packed:
+            raise ValueError("draft_weight must be int8 [V, d], packed if and only if weight is")
         if draft_weight_scale.dtype != torch.float32 or tuple(draft_weight_scale.shape) != (V,):
             raise ValueError("draft_weight_scale must be float32 [V]")
     if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, k + 1, 2):
@@ -548,7 +600,11 @@ def spec_verify_lmhead_sample(hidden: torch.Tensor, hidden_scale: torch.Tensor, 
                 ev.record(torch.cuda.current_stream(dev))
             handles.append(ev.cuda_event)
         arr = (ctypes.c_void_p * 4)(*handles)
-        rc = lib().spec_verify_lmhead_sample_timed(*args, ctypes.cast(arr, ctypes.c_void_p))
+        evp = ctypes.cast(arr, ctypes.c_void_p)
+        rc = (lib().spec_verify_lmhead_sample_packed(*args, evp) if packed
+              else lib().spec_verify_lmhead_sample_timed(*args, evp))
+    elif packed:
+        rc = lib().spec_verify_lmhead_sample_packed(*args, None)
     else:
         rc = lib().spec_verify_lmhead_sample(*args)
     if rc != 0:

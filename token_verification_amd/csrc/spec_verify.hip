@@ -2109,6 +2109,7 @@ struct HeadParams {
     int rpb;                            // rows per batch row of the merged records (2k+1)
     float* logits;                      // [M, V] float32, every logit (sampling)
     double* exptab;                     // pass 2's exp table (sampling, target head), written by the merge
+    int packed;                         // w in the tile-major layout of head_pack_kernel
 };
 
 // The draft token whose logit hidden row m carries (-1: none; the bonus row).
@@ -2438,14 +2439,23 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
     const HeadTile<MB, NMW> w(H);
     const int lane = w.t & 63, wv = w.t >> 6;
     const unsigned d = static_cast<unsigned>(H.d);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(H.w + static_cast<size_t>(w.v0) * d, static_cast<unsigned>(w.nv) * d);
+    // weights row-major: the tile's nv rows; tile-major (head_pack_kernel):
+    // the tile's HV rows, stage ks a contiguous 16 KB image of the stage
+    // buffer's weight part, zeros past V
+    const __amdgpu_buffer_rsrc_t rw =
+        H.packed ? make_rsrc(H.w + static_cast<size_t>(w.vt) * HV * d, static_cast<unsigned>(HV) * d)
+                 : make_rsrc(H.w + static_cast<size_t>(w.v0) * d, static_cast<unsigned>(w.nv) * d);
     const __amdgpu_buffer_rsrc_t rh = make_rsrc(H.h + static_cast<size_t>(w.m0) * d, static_cast<unsigned>(w.nm) * d);
     // loads: weight instruction j of wave wv fills rows wv*WRW + 16j .. +15,
     // hidden instruction j rows wv*HRW + 16j .. +15; lane l lands on row
     // + l/4, physical chunk l % 4, which holds logical chunk
-    // (l % 4) ^ ((l >> 4) & 3); rows past the tile load zeros
+    // (l % 4) ^ ((l >> 4) & 3); rows past the tile load zeros. In the
+    // tile-major layout the image is stored as it lands: lane l at 16 l.
     const unsigned cl = static_cast<unsigned>(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-    const unsigned low = static_cast<unsigned>(wv * WRW + (lane >> 2)) * d + cl;
+    const unsigned low = H.packed ? static_cast<unsigned>(wv * WRW * HKW + 16 * lane)
+                                  : static_cast<unsigned>(wv * WRW + (lane >> 2)) * d + cl;
+    const unsigned wjs = H.packed ? 16u * HKW : 16u * d;  // per load instruction
+    const unsigned wks = H.packed ? static_cast<unsigned>(HV * HKW) : static_cast<unsigned>(HKW); // per stage
     const unsigned loh = static_cast<unsigned>(wv * HRW + (lane >> 2)) * d + cl;
     auto issue = [&](int ks) {
         unsigned char* B = S + (ks % NBUF) * ST;
@@ -2453,7 +2463,8 @@ __device__ __attribute__((always_inline)) inline void head_main(const HeadParams
 #pragma unroll
         for (int j = 0; j < WRW / 16; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(B + (wv * WRW + 16 * j) * HKW), 16,
-                                                     static_cast<int>(low + k0 + 16u * j * d), 0, 0, 0);
+                                                     static_cast<int>(low + static_cast<unsigned>(ks) * wks + wjs * j),
+                                                     0, 0, 0);
 #pragma unroll
         for (int j = 0; j < HRW / 16; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(B + (HV + wv * HRW + 16 * j) * HKW), 16,
@@ -2655,6 +2666,29 @@ __global__ __launch_bounds__(NTH / 2) void head_kernel_tiny_s(HeadParams H) { he
 __global__ __launch_bounds__(NTH / 2) void head_kernel_tiny_ws(HeadParams H) { head_main_w512<EPI_SAMPLE>(H); }
 
 
+// The tile-major layout of an int8 head [V, d]: for vocabulary tile vt (HV
+// rows, zeros past V) and stage ks (HKW bytes of d), a contiguous HV x HKW
+// block that is the stage buffer's weight part as head_main loads it: row R
+// at R * HKW, its physical 16-byte chunk p holding logical chunk
+// p ^ ((R >> 2) & 3). A stage's weight loads then read 16 KB in one run.
+// One thread per 16-byte output chunk.
+__global__ __launch_bounds__(NT) void head_pack_kernel(const signed char* w, int V, int d, signed char* out,
+                                                       long long nchunks) {
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    const long long per_tile = static_cast<long long>(HV) * d / 16;
+    for (long long i = static_cast<long long>(blockIdx.x) * NT + threadIdx.x; i < nchunks;
+         i += static_cast<long long>(gridDim.x) * NT) {
+        const long long vt = i / per_tile, rem = i % per_tile;
+        const int ks = static_cast<int>(rem / (HV * HKW / 16));
+        const int rr = static_cast<int>(rem % (HV * HKW / 16));
+        const int R = rr / (HKW / 16), c = (rr % (HKW / 16)) ^ ((R >> 2) & 3);
+        const long long v = vt * HV + R;
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (v < V) x = *reinterpret_cast<const u32x4_t*>(w + v * d + ks * HKW + 16 * c);
+        *reinterpret_cast<u32x4_t*>(out + 16 * i) = x;
+    }
+}
+
 // Sampling mode, one workgroup per hidden row: merge its vocabulary-tile
 // records (a fixed order: per thread in tile order, a butterfly per wave, then
 // the waves in order) into pass 1's record of its row: target row b*(k+1)+i is
@@ -2682,9 +2716,14 @@ __device__ __attribute__((always_inline)) inline void head_merge_sample_row(cons
     int dot = 0;
     if (has) {
         const u32x4* hr = reinterpret_cast<const u32x4*>(H.h + static_cast<size_t>(m) * H.d);
-        const u32x4* wr = reinterpret_cast<const u32x4*>(H.w + static_cast<size_t>(tok) * H.d);
+        // row-major: 16-byte chunk j of the row at j; tile-major: chunk c of
+        // stage ks = j / 4 at physical chunk c ^ ((R >> 2) & 3) of row R
+        const int R = tok % HV;
+        const u32x4* wr = reinterpret_cast<const u32x4*>(
+            H.packed ? H.w + static_cast<size_t>(tok / HV) * HV * H.d + R * HKW : H.w + static_cast<size_t>(tok) * H.d);
         for (int j = t; j < H.d / 16; j += NT) {
-            const u32x4 x = hr[j], y = wr[j];
+            const int wj = H.packed ? (j >> 2) * (HV * HKW / 16) + ((j & 3) ^ ((R >> 2) & 3)) : j;
+            const u32x4 x = hr[j], y = wr[wj];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -3139,7 +3178,7 @@ bool make_head_plan(int32_t B, int32_t k, int32_t V, int32_t d, HeadPlan& p) {
 int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weight, const float* weight_scale,
              const int32_t* draft_tokens, int32_t B, int32_t k, int32_t V, int32_t d, int32_t* accepted_len,
              int32_t* out_tokens, float* gap, void* workspace, size_t workspace_bytes, void* stream,
-             void* const* events) {
+             void* const* events, int packed = 0) {
     if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K || V < 1 || V > (1 << 29))
         return fail(SPEC_ERR_SHAPE, "need 1 <= B <= 2^21, 0 <= k <= %d, 1 <= V <= 2^29 (got B=%d k=%d V=%d)",
                     SPEC_MAX_K, B, k, V);
@@ -3169,6 +3208,7 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
     H.h = reinterpret_cast<const signed char*>(hidden);
     H.hs = hidden_scale;
     H.w = reinterpret_cast<const signed char*>(weight);
+    H.packed = packed;
     H.ws = weight_scale;
     H.rec = reinterpret_cast<HeadRec*>(ws + plan.o_rec);
     H.tiles = reinterpret_cast<TileRec*>(ws + plan.o_tiles);
@@ -3199,7 +3239,7 @@ int run_head(const int8_t* hidden, const float* hidden_scale, const int8_t* weig
         if (plan.bm == 256) hipLaunchKernelGGL(head_kernel_wide, grid, dim3(2 * NTH), 0, s, H);
         else if (plan.bm == 192) hipLaunchKernelGGL(head_kernel_mid, grid, dim3(NTH), 0, s, H);
         else if (plan.bm == 128) hipLaunchKernelGGL(head_kernel_narrow, grid, dim3(NTH), 0, s, H);
-        else if (d % 512 == 0) hipLaunchKernelGGL(head_kernel_tiny_w, grid, dim3(NTH / 2), 0, s, H);
+        else if (d % 512 == 0 && !packed) hipLaunchKernelGGL(head_kernel_tiny_w, grid, dim3(NTH / 2), 0, s, H);
         else hipLaunchKernelGGL(head_kernel_tiny, grid, dim3(NTH / 2), 0, s, H);
         e = hipGetLastError();
     }
@@ -3321,7 +3361,7 @@ hipError_t launch_head_sample(HeadParams& H, int bm, hipStream_t s) {
     else if (bm == 192) hipLaunchKernelGGL(head_kernel_mid_s, grid, dim3(NTH), 0, s, H);
     else if (bm == 128 && H.nmt == 1) hipLaunchKernelGGL(head_kernel_narrow_s1, grid, dim3(NTH), 0, s, H);
     else if (bm == 128) hipLaunchKernelGGL(head_kernel_narrow_s, grid, dim3(NTH), 0, s, H);
-    else if (H.d % 512 == 0) hipLaunchKernelGGL(head_kernel_tiny_ws, grid, dim3(NTH / 2), 0, s, H);
+    else if (H.d % 512 == 0 && !H.packed) hipLaunchKernelGGL(head_kernel_tiny_ws, grid, dim3(NTH / 2), 0, s, H);
     else hipLaunchKernelGGL(head_kernel_tiny_s, grid, dim3(NTH / 2), 0, s, H);
     return hipGetLastError();
 }
@@ -3331,7 +3371,7 @@ int run_head_sample(const int8_t* th, const float* ths, const int8_t* tw, const 
                     const float* uniforms, float temperature, int32_t B, int32_t k, int32_t V, int32_t d,
                     int32_t* accepted_len, int32_t* out_tokens, float* gap, float* target_prob,
                     float* draft_prob, void* workspace, size_t workspace_bytes, void* stream,
-                    void* const* events) {
+                    void* const* events, int packed = 0) {
     if (B < 1 || B > (1 << 21) || k < 0 || k > SPEC_MAX_K || V < 1 || V > (1 << 29))
         return fail(SPEC_ERR_SHAPE, "need 1 <= B <= 2^21, 0 <= k <= %d, 1 <= V <= 2^29 (got B=%d k=%d V=%d)",
                     SPEC_MAX_K, B, k, V);
@@ -3377,6 +3417,7 @@ int run_head_sample(const int8_t* th, const float* ths, const int8_t* tw, const 
     HeadParams HT{};
     HT.h = reinterpret_cast<const signed char*>(th); HT.hs = ths;
     HT.w = reinterpret_cast<const signed char*>(tw); HT.ws = tws;
+    HT.packed = packed;
     HT.recs = reinterpret_cast<HeadRecS*>(ws + plan.o_recT);
     HT.tiles = tiles;
     HT.M = B * (k + 1); HT.V = V; HT.d = d; HT.nvt = plan.nvt;
@@ -3599,6 +3640,35 @@ int spec_verify_lmhead_timed(const int8_t* hidden, const float* hidden_scale, co
                     out_tokens, gap, workspace, workspace_bytes, stream, events);
 }
 
+size_t spec_lmhead_packed_size(int32_t V, int32_t d) {
+    if (V < 1 || V > (1 << 29) || d < HK || d > HEAD_MAX_D || d % HK != 0) return 0;
+    return static_cast<size_t>((V + HV - 1) / HV) * HV * static_cast<size_t>(d);
+}
+
+int spec_lmhead_pack(const int8_t* weight, int32_t V, int32_t d, int8_t* packed, size_t packed_bytes, void* stream) {
+    const size_t need = spec_lmhead_packed_size(V, d);
+    if (need == 0) return fail(SPEC_ERR_SHAPE, "need 1 <= V <= 2^29 and d a multiple of %d in [%d, %d] (got V=%d d=%d)",
+                               HK, HK, HEAD_MAX_D, V, d);
+    if (!weight || !packed) return fail(SPEC_ERR_NULL, "weight and packed are required");
+    if (!aligned(weight, 16) || !aligned(packed, 16)) return fail(SPEC_ERR_ALIGN, "weight and packed must be 16-byte aligned");
+    if (packed_bytes < need) return fail(SPEC_ERR_WORKSPACE, "packed needs %zu bytes (got %zu)", need, packed_bytes);
+    const long long nchunks = static_cast<long long>(need / 16);
+    const unsigned grid = static_cast<unsigned>(std::min<long long>((nchunks + NT - 1) / NT, 1 << 16));
+    hipLaunchKernelGGL(head_pack_kernel, dim3(grid), dim3(NT), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<const signed char*>(weight), V, d, reinterpret_cast<signed char*>(packed),
+                       nchunks);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : fail(SPEC_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+}
+
+int spec_verify_lmhead_packed(const int8_t* hidden, const float* hidden_scale, const int8_t* packed_weight,
+                              const float* weight_scale, const int32_t* draft_tokens, int32_t B, int32_t k,
+                              int32_t V, int32_t d, int32_t* accepted_len, int32_t* out_tokens, float* gap,
+                              void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    return run_head(hidden, hidden_scale, packed_weight, weight_scale, draft_tokens, B, k, V, d, accepted_len,
+                    out_tokens, gap, workspace, workspace_bytes, stream, events, 1);
+}
+
 size_t spec_lmhead_sample_workspace_size(int32_t B, int32_t k, int32_t V, int32_t d) {
     HeadSamplePlan p;
     if (V > SPEC_MAX_V_SAMPLE || !make_head_sample_plan(B, k, V, d, p)) return 0;
@@ -3632,6 +3702,20 @@ int spec_verify_lmhead_sample_timed(const int8_t* target_hidden, const float* ta
                            draft_hidden_scale, draft_weight, draft_weight_scale, draft_tokens, uniforms,
                            temperature, B, k, V, d, accepted_len, out_tokens, gap, target_prob, draft_prob,
                            workspace, workspace_bytes, stream, events);
+}
+
+int spec_verify_lmhead_sample_packed(const int8_t* target_hidden, const float* target_hidden_scale,
+                                     const int8_t* target_packed_weight, const float* target_weight_scale,
+                                     const int8_t* draft_hidden, const float* draft_hidden_scale,
+                                     const int8_t* draft_packed_weight, const float* draft_weight_scale,
+                                     const int32_t* draft_tokens, const float* uniforms, float temperature,
+                                     int32_t B, int32_t k, int32_t V, int32_t d, int32_t* accepted_len,
+                                     int32_t* out_tokens, float* gap, float* target_prob, float* draft_prob,
+                                     void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    return run_head_sample(target_hidden, target_hidden_scale, target_packed_weight, target_weight_scale,
+                           draft_hidden, draft_hidden_scale, draft_packed_weight, draft_weight_scale, draft_tokens,
+                           uniforms, temperature, B, k, V, d, accepted_len, out_tokens, gap, target_prob, draft_prob,
+                           workspace, workspace_bytes, stream, events, 1);
 }
 
 const char* spec_verify_last_error(void) { return g_err; }
