@@ -138,6 +138,9 @@ def main() -> int:
                          "hidden rows; the draft shares the head unless --draft-head)")
     ap.add_argument("--draft-head", action="store_true",
                     help="with --lmhead-sample: the draft has an int8 head of its own")
+    ap.add_argument("--packed", action="store_true",
+                    help="with --lmhead / --lmhead-sample: the heads in the tile-major layout (pack_lmhead, "
+                         "written once before the timed region)")
     ap.add_argument("--no-context", action="store_true",
                     help="with --lmhead / --lmhead-sample: skip the library and unfused comparisons "
                          "(run after the timed region), so a profile holds only the fused call")
@@ -542,7 +545,8 @@ def lmhead_bench(args, torch, np) -> int:
     torch.cuda.set_device(dev)
     print(f"bench: generating the int8 LM head B={B} k={k} V={V} d={d}", file=sys.stderr, flush=True)
     x = workloads.make_lmhead(B, k, V, d, seed=0, device=dev)
-    a = (x["hidden"], x["hidden_scale"], x["weight"], x["weight_scale"], x["tokens"])
+    hw = tv.pack_lmhead(x["weight"]) if args.packed else x["weight"]
+    a = (x["hidden"], x["hidden_scale"], hw, x["weight_scale"], x["tokens"])
     out = tv.binding.VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
                                   torch.empty((B, k + 1), dtype=torch.int32, device=dev),
                                   torch.empty((B, k + 1), dtype=torch.float32, device=dev), None, None)
@@ -566,21 +570,23 @@ def lmhead_bench(args, torch, np) -> int:
     acc = out.accepted_len.cpu().numpy()
     line = {
         "metric": f"verified draft positions/sec, greedy verify fused with an int8 LM head, "
-                  f"B={B} k={k} V={V} d={d}",
+                  f"B={B} k={k} V={V} d={d}" + (", tile-major head" if args.packed else ""),
         "value": round(positions / (wall / args.steps), 1),
         "unit": "positions/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8", "data": "synthetic",
-        "config": {"workload": f"lmhead_b{B}_k{k}_v{V}_d{d}_int8", "B": B, "k": k, "V": V, "d": d,
-                   "hidden_rows": M},
+        "config": {"workload": f"lmhead_b{B}_k{k}_v{V}_d{d}_int8" + ("_packed" if args.packed else ""),
+                   "B": B, "k": k, "V": V, "d": d, "hidden_rows": M,
+                   "weight_layout": "tile-major" if args.packed else "row-major"},
         "gpu_us_per_step": round(k_ms * 1e3, 2),
         "phase_us": {"lmhead_kernel": round(float(head.mean()) * 1e3, 2),
                      "merge_and_decide": round(float(tail.mean()) * 1e3, 2),
                      "call": round(float(call.mean()) * 1e3, 2)},
         "roofline": head_roofline(ops, wbytes, float(head.mean()) * 1e-3,
-                                  counter_traffic(f"spec_verify_lmhead_b{B}_k{k}_v{V}_d{d}_int8",
+                                  counter_traffic(f"spec_verify_lmhead_b{B}_k{k}_v{V}_d{d}_int8"
+                                                  + ("_packed" if args.packed else ""),
                                                   "traffic_bytes_lmhead_kernel")),
         "hbm_context": {"weight_and_hidden_bytes": wbytes,
                         "GB_per_s": round(wbytes / (float(head.mean()) * 1e-3) / 1e9, 1)},
@@ -608,7 +614,7 @@ def lmhead_bench(args, torch, np) -> int:
         line["library_gemm_context"] = {"error": f"{type(ex).__name__}: {str(ex)[:120]}"}
     if args.cpu_seconds > 0:
         from oracle.lmhead import lmhead_greedy_ref
-        hh, hs, ww, wsc = (t.cpu().numpy() for t in a[:4])
+        hh, hs, ww, wsc = (t.cpu().numpy() for t in (x["hidden"], x["hidden_scale"], x["weight"], x["weight_scale"]))
         tok = a[4].cpu().numpy()
         n, t_cpu, b = 0, 0.0, 0
         while t_cpu < args.cpu_seconds:
@@ -639,6 +645,10 @@ def lmhead_sample_bench(args, torch, np) -> int:
           file=sys.stderr, flush=True)
     x = workloads.make_lmhead_sample(B, k, V, d, seed=0, device=dev, draft_head=own)
     T = 1.0
+    hw = tv.pack_lmhead(x["weight"]) if args.packed else x["weight"]
+    hdw = x["draft_weight"]
+    if args.packed and hdw is not None:
+        hdw = tv.pack_lmhead(hdw)
     out = tv.binding.VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
                                   torch.empty((B, k + 1), dtype=torch.int32, device=dev),
                                   torch.empty((B, k + 1), dtype=torch.float32, device=dev),
@@ -646,9 +656,9 @@ def lmhead_sample_bench(args, torch, np) -> int:
                                   torch.empty((B, k), dtype=torch.float32, device=dev))
 
     def call(**kw):
-        tv.spec_verify_lmhead_sample(x["hidden"], x["hidden_scale"], x["weight"], x["weight_scale"],
+        tv.spec_verify_lmhead_sample(x["hidden"], x["hidden_scale"], hw, x["weight_scale"],
                                      x["draft_hidden"], x["draft_hidden_scale"], x["tokens"], x["uniforms"], T,
-                                     draft_weight=x["draft_weight"], draft_weight_scale=x["draft_weight_scale"],
+                                     draft_weight=hdw, draft_weight_scale=x["draft_weight_scale"],
                                      out=out, **kw)
 
     for _ in range(args.warmup):
@@ -666,10 +676,11 @@ def lmhead_sample_bench(args, torch, np) -> int:
     wbytes = (2 if own else 1) * (V * d + 4 * V) + (MT + MD) * (d + 4)
     positions = B * k
     acc = out.accepted_len.cpu().numpy()
-    tag = f"lmhead_sample_b{B}_k{k}_v{V}_d{d}_int8" + ("_drafthead" if own else "")
+    tag = f"lmhead_sample_b{B}_k{k}_v{V}_d{d}_int8" + ("_drafthead" if own else "") + ("_packed" if args.packed else "")
     line = {
         "metric": f"verified draft positions/sec, sampling verify fused with int8 LM heads, "
-                  f"B={B} k={k} V={V} d={d}" + (", separate draft head" if own else ", shared head"),
+                  f"B={B} k={k} V={V} d={d}" + (", separate draft head" if own else ", shared head")
+                  + (", tile-major heads" if args.packed else ""),
         "value": round(positions / (wall / args.steps), 1),
         "unit": "positions/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -677,7 +688,8 @@ def lmhead_sample_bench(args, torch, np) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": tag, "B": B, "k": k, "V": V, "d": d, "T": T,
-                   "target_rows": MT, "draft_rows": MD, "draft_head": "own" if own else "shared"},
+                   "target_rows": MT, "draft_rows": MD, "draft_head": "own" if own else "shared",
+                   "weight_layout": "tile-major" if args.packed else "row-major"},
         "gpu_us_per_step": round(k_ms * 1e3, 2),
         "phase_us": {"head_passes": round(float(heads.mean()) * 1e3, 2),
                      "merges": round(float(ph[:, 1].mean()) * 1e3, 2),
