@@ -5,7 +5,7 @@ tests/emu/hip/hip_runtime.h maps the HIP subset the kernels use onto host C++
 and compare them with the oracle, with a random (uninitialised) workspace.
 SPEC_EMU_ASAN=1 builds the harness with AddressSanitizer and UndefinedBehavior-
 Sanitizer into a library of its own and runs every case under it (slow: the
-whole set took about 1 h 45 min on 8 cores; the per-case time limits grow to
+whole set took about 2 h 06 min on 8 cores; the per-case time limits grow to
 match).
 """
 import ctypes
